@@ -1,0 +1,176 @@
+/*
+ * ss.h -- Mamba selective scan (S6) on AMD MI355X (gfx950): the C ABI.
+ *
+ * The library (libss.so) runs the selective scan of Mamba-1 as hand-written
+ * HIP kernels.  All tensor arguments are DEVICE pointers allocated by the
+ * caller; the library allocates nothing and keeps no global state.  Every
+ * call validates its arguments on the host first and returns an error code
+ * without touching the GPU when they are invalid; otherwise it enqueues its
+ * kernels on `stream` (a hipStream_t, NULL = the null stream) and returns
+ * without synchronising.  A failed launch returns SS_ERR_HIP.
+ *
+ * Problem (page "Mamba", Part IV Stage 5, the selective_scan_fn interface):
+ *   per batch row b, channel d (d < dim = d_inner) and state n (n < dstate):
+ *     Delta_t  = softplus(delta[b,d,t] + bias[d])   (softplus only if flagged;
+ *                                                     the bias is always added)
+ *     Abar_t   = exp(Delta_t * A[d,n])               (Stage 4, zero-order hold)
+ *     h_t[n]   = Abar_t h_{t-1}[n] + Delta_t B[b,n,t] u[b,d,t]   (Euler for B)
+ *     y0_t     = sum_n C[b,n,t] h_t[n] + D[d] u[b,d,t]           (Stage 6 skip)
+ *     y[b,d,t] = y0_t * z_t * sigmoid(z_t)   (gate, Stage 6; y0_t if z absent)
+ *   with h_{-1} = 0.  "mamba-metal" README ("Long-context prompts") adds the
+ *   final state h_{L-1}, from which decode continues one token at a time.
+ *
+ * Layouts: every tensor is C-contiguous with the time axis innermost:
+ *   u, delta, z, y, dy, du, ddelta, dz : (batch, dim, seqlen)   io dtype
+ *   Bm, Cm, dB, dC                     : (batch, dstate, seqlen) io dtype (dB, dC: fp32)
+ *   A, dA                              : (dim, dstate)  fp32
+ *   D, bias, dD, dbias                 : (dim)          fp32
+ *   last_state, state_in, state_out    : (batch, dim, dstate) fp32
+ *   ckpt                               : (batch, dim, ceil(seqlen/64), dstate) fp32
+ * Data tensors may be fp32, fp16 or bf16 (`io_dtype`); the weights A, D,
+ * bias and every state are fp32, and all arithmetic is fp32 ("mamba-metal"
+ * README: data in half, weights in float, fp32 scan accumulation).  Outputs
+ * in fp16/bf16 are rounded to nearest-even.
+ *
+ * Limits: 1 <= dstate <= 16; batch, dim, seqlen >= 1; every pointer 16-byte
+ * aligned (SS_ERR_MISALIGNED otherwise).  Any finite A is accepted; A > 0
+ * makes the state grow and may overflow.
+ */
+#ifndef SS_H
+#define SS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ss_status {
+    SS_OK = 0,
+    SS_ERR_NULL_ARG = 1,     /* a required pointer is NULL, or an optional pair is half given */
+    SS_ERR_BAD_SHAPE = 2,    /* a size is < 1 or overflows */
+    SS_ERR_BAD_DTYPE = 3,    /* io_dtype is not one of ss_dtype */
+    SS_ERR_MISALIGNED = 4,   /* a pointer is not 16-byte aligned */
+    SS_ERR_UNSUPPORTED = 5,  /* dstate > 16, or a workspace smaller than required */
+    SS_ERR_HIP = 6           /* the HIP runtime reported an error at launch */
+} ss_status;
+
+typedef enum ss_dtype { SS_F32 = 0, SS_F16 = 1, SS_BF16 = 2 } ss_dtype;
+
+typedef struct ss_problem {
+    int64_t batch;           /* B */
+    int64_t dim;             /* D = d_inner, channels */
+    int64_t dstate;          /* N, 1..16 */
+    int64_t seqlen;          /* L */
+    int32_t io_dtype;        /* ss_dtype of the data tensors */
+    int32_t delta_softplus;  /* nonzero: Delta = softplus(delta + bias) */
+} ss_problem;
+
+/*
+ * Bytes of device workspace ss_fwd needs for this problem (0 when the
+ * problem has enough channels to fill the GPU without splitting time).  The
+ * workspace holds per-chunk partial states of the time-parallel scan: for a
+ * time chunk c of a channel, the decay product over the chunk and the state
+ * reached from zero (the associative pair of the page "Mamba", Part V
+ * "S6 ... forbids the convolution").  Returns 0 for an invalid problem.
+ */
+size_t ss_fwd_workspace_size(const ss_problem *p);
+
+/*
+ * Forward scan (the op of page "Mamba", Part IV Stage 5, with the final
+ * state of the "mamba-metal" README).  Writes y for every t < seqlen.
+ *   D, z, delta_bias  : optional (NULL = no skip / no gate / zero bias).
+ *   lengths           : optional device int32[batch]; row b runs
+ *                       min(max(lengths[b], 0), seqlen) steps from a zero
+ *                       state, y is exactly 0 past that length and
+ *                       last_state is the state after that many steps.
+ *                       Out-of-range values are clamped, not reported.
+ *   last_state        : optional (batch, dim, dstate) fp32 output.
+ *   ckpt              : optional (batch, dim, ceil(seqlen/64), dstate) fp32
+ *                       output: entry k is the state after min(64k, len)
+ *                       steps (entry 0 is zero), the checkpoints of page
+ *                       "Mamba, on a laptop GPU", "The state lives in
+ *                       registers", used by ss_bwd.
+ *   workspace         : device buffer of ss_fwd_workspace_size() bytes, or
+ *                       NULL when that size is 0 (SS_ERR_UNSUPPORTED when it
+ *                       is needed and missing or too small).
+ */
+ss_status ss_fwd(const ss_problem *p,
+                 const void *u, const void *delta, const float *A,
+                 const void *Bm, const void *Cm,
+                 const float *D, const void *z, const float *delta_bias,
+                 const int32_t *lengths,
+                 void *y, float *last_state, float *ckpt,
+                 void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/*
+ * One decode step from a carried state ("mamba-metal" README, "O(1) per
+ * token via state caching"; page "Mamba", Part IV Stage 7, single-step
+ * decoding updates the cached state in place).  p->seqlen is ignored.
+ *   u_t, delta_t, z_t, y_t : (batch, dim) io dtype;  B_t, C_t : (batch, dstate) io dtype
+ *   state_in, state_out    : (batch, dim, dstate) fp32; they may be the same
+ *                            buffer (in-place update); partial overlap is not allowed.
+ * D, z_t and delta_bias are optional as in ss_fwd.
+ */
+ss_status ss_fwd_step(const ss_problem *p,
+                      const void *u_t, const void *delta_t, const float *A,
+                      const void *B_t, const void *C_t,
+                      const float *D, const void *z_t, const float *delta_bias,
+                      const float *state_in, float *state_out, void *y_t,
+                      void *stream);
+
+/*
+ * Bytes of device workspace ss_bwd needs: per 64-step chunk of every channel
+ * and state, the chunk's decay product, its state-gradient from a zero
+ * carry and the carried gradient (3 * batch*dim*ceil(seqlen/64)*16 floats).
+ * Returns 0 for an invalid problem.
+ */
+size_t ss_bwd_workspace_size(const ss_problem *p);
+
+/*
+ * Backward scan for the loss sum(dy * y) (page "Mamba", Part IV Stage 7:
+ * the states are recomputed, here from the 64-step checkpoints that ss_fwd
+ * wrote, walking the chunks in reverse as page "Mamba, on a laptop GPU",
+ * "The state lives in registers", describes).
+ *   ckpt         : the checkpoints ss_fwd wrote for the same inputs (no lengths).
+ *   du, ddelta   : (batch, dim, seqlen) io dtype outputs.
+ *   dz           : output iff z is given.  dD iff D.  dbias iff delta_bias.
+ *   dA (dim, dstate), dB, dC (batch, dstate, seqlen), dD, dbias (dim): fp32,
+ *   summed over the dimensions their inputs are shared across (dB, dC over
+ *   channels; dA, dD, dbias over batch rows and time).  Every output is
+ *   overwritten; the library clears its accumulation targets itself.
+ *   workspace    : device buffer of ss_bwd_workspace_size() bytes.
+ * Returns SS_ERR_NULL_ARG when a gradient output and its input are not given
+ * together, SS_ERR_UNSUPPORTED when the workspace is missing or too small.
+ */
+ss_status ss_bwd(const ss_problem *p,
+                 const void *u, const void *delta, const float *A,
+                 const void *Bm, const void *Cm,
+                 const float *D, const void *z, const float *delta_bias,
+                 const float *ckpt, const void *dy,
+                 void *du, void *ddelta, void *dz,
+                 float *dA, float *dB, float *dC, float *dD, float *dbias,
+                 void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/* Number of floats of the checkpoint buffer: batch*dim*ceil(seqlen/64)*dstate (0 if invalid). */
+size_t ss_ckpt_count(const ss_problem *p);
+
+/* Static, human-readable text for a status code. */
+const char *ss_status_str(ss_status s);
+
+/*
+ * Measurement utility, not part of the scan: copies `bytes` (a nonzero
+ * multiple of 16) from src to dst on the device with a plain streaming
+ * kernel.  Used to measure achievable HBM bandwidth and to calibrate
+ * hardware traffic counters against a kernel of known traffic.
+ */
+ss_status ss_copy_probe(const void *src, void *dst, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_H */

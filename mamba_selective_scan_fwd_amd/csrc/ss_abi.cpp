@@ -1,0 +1,203 @@
+// ss_abi.cpp -- the C ABI of libss.so: host-side validation and dispatch.
+// Every check runs before any HIP call; a failing check returns its status
+// and leaves the device untouched.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/ss.h"
+#include "ss_internal.h"
+
+namespace {
+
+constexpr int64_t kTile = 64;
+constexpr int64_t kMaxDstate = 16;
+constexpr int64_t kChPerBlock = 16;
+// below this many wavefronts a forward splits the time axis into chunks
+constexpr int64_t kTargetWaves = 1024;
+constexpr int64_t kMaxGrid = (int64_t)1 << 31;
+
+bool aligned(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+int64_t elem_size(int32_t io) { return io == SS_F32 ? 4 : 2; }
+
+ss_status check_problem(const ss_problem* p, bool need_seqlen) {
+  if (!p) return SS_ERR_NULL_ARG;
+  if (p->batch < 1 || p->dim < 1 || p->dstate < 1) return SS_ERR_BAD_SHAPE;
+  if (need_seqlen && p->seqlen < 1) return SS_ERR_BAD_SHAPE;
+  if (p->dstate > kMaxDstate) return SS_ERR_UNSUPPORTED;
+  if (p->io_dtype != SS_F32 && p->io_dtype != SS_F16 && p->io_dtype != SS_BF16) return SS_ERR_BAD_DTYPE;
+  // keep every element index far from int64 overflow and grids within 2^31 blocks
+  const int64_t lim = (int64_t)1 << 40;
+  if (p->batch > lim || p->dim > lim || (need_seqlen && p->seqlen > lim)) return SS_ERR_BAD_SHAPE;
+  const double ch = (double)p->batch * (double)p->dim;
+  if (ch * (double)(need_seqlen ? p->seqlen : 1) * kMaxDstate > 9.0e18) return SS_ERR_BAD_SHAPE;
+  if (ch / kChPerBlock * 2.0 > (double)kMaxGrid) return SS_ERR_BAD_SHAPE;
+  return SS_OK;
+}
+
+struct FwdPlan {
+  int64_t nchunks;
+  int64_t chunk_len;
+  size_t workspace;
+};
+
+FwdPlan plan_fwd(const ss_problem* p) {
+  FwdPlan pl;
+  const int64_t tiles = (p->seqlen + kTile - 1) / kTile;
+  const int64_t ch_blocks = (p->dim + kChPerBlock - 1) / kChPerBlock;
+  const int64_t waves = p->batch * ch_blocks * 4;
+  int64_t k = 1;
+  if (waves < kTargetWaves) {
+    k = (kTargetWaves + waves - 1) / waves;
+    if (k > tiles) k = tiles;
+  }
+  const int64_t tiles_per_chunk = (tiles + k - 1) / k;
+  pl.chunk_len = tiles_per_chunk * kTile;
+  pl.nchunks = (p->seqlen + pl.chunk_len - 1) / pl.chunk_len;
+  if (p->batch * ch_blocks * pl.nchunks > kMaxGrid) {  // keep the grid legal
+    pl.nchunks = 1;
+    pl.chunk_len = tiles * kTile;
+  }
+  pl.workspace = pl.nchunks > 1 ? (size_t)3 * (size_t)(p->batch * p->dim * pl.nchunks * 16) * sizeof(float) : 0;
+  return pl;
+}
+
+ss_status from_hip(hipError_t e) { return e == hipSuccess ? SS_OK : SS_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ss_status_str(ss_status s) {
+  switch (s) {
+    case SS_OK: return "ok";
+    case SS_ERR_NULL_ARG: return "ss: a required pointer is NULL (or an optional input/output pair is half given)";
+    case SS_ERR_BAD_SHAPE: return "ss: invalid problem size";
+    case SS_ERR_BAD_DTYPE: return "ss: io_dtype must be SS_F32, SS_F16 or SS_BF16";
+    case SS_ERR_MISALIGNED: return "ss: every tensor pointer must be 16-byte aligned";
+    case SS_ERR_UNSUPPORTED: return "ss: unsupported request (dstate > 16, or workspace missing/too small)";
+    case SS_ERR_HIP: return "ss: HIP launch failed";
+  }
+  return "ss: unknown status";
+}
+
+size_t ss_ckpt_count(const ss_problem* p) {
+  if (check_problem(p, true) != SS_OK) return 0;
+  return (size_t)(p->batch * p->dim * ((p->seqlen + kTile - 1) / kTile) * p->dstate);
+}
+
+size_t ss_fwd_workspace_size(const ss_problem* p) {
+  if (check_problem(p, true) != SS_OK) return 0;
+  return plan_fwd(p).workspace;
+}
+
+ss_status ss_fwd(const ss_problem* p, const void* u, const void* delta, const float* A, const void* Bm,
+                 const void* Cm, const float* D, const void* z, const float* delta_bias, const int32_t* lengths,
+                 void* y, float* last_state, float* ckpt, void* workspace, size_t workspace_bytes, void* stream) {
+  ss_status s = check_problem(p, true);
+  if (s != SS_OK) return s;
+  if (!u || !delta || !A || !Bm || !Cm || !y) return SS_ERR_NULL_ARG;
+  const void* ptrs[] = {u, delta, A, Bm, Cm, D, z, delta_bias, lengths, y, last_state, ckpt, workspace};
+  for (const void* q : ptrs)
+    if (q && !aligned(q)) return SS_ERR_MISALIGNED;
+  const FwdPlan pl = plan_fwd(p);
+  if (pl.workspace > 0 && (!workspace || workspace_bytes < pl.workspace)) return SS_ERR_UNSUPPORTED;
+
+  ss::FwdParams k{};
+  k.io = p->io_dtype;
+  k.softplus = p->delta_softplus != 0;
+  k.u = u; k.delta = delta; k.z = z; k.Bm = Bm; k.Cm = Cm;
+  k.A = A; k.D = D; k.bias = delta_bias; k.lengths = lengths;
+  k.y = y; k.last_state = last_state; k.ckpt = ckpt;
+  k.batch = p->batch; k.dim = p->dim; k.dstate = p->dstate; k.seqlen = p->seqlen;
+  k.chunk_len = pl.chunk_len;
+  k.chunk_base = 0;
+  k.ch_blocks = (p->dim + kChPerBlock - 1) / kChPerBlock;
+  k.ckpt_per_row = (p->seqlen + kTile - 1) / kTile;
+  k.nchunks = (int32_t)pl.nchunks;
+  if (pl.nchunks > 1) {
+    const size_t per = (size_t)(p->batch * p->dim * pl.nchunks * 16);
+    float* ws = static_cast<float*>(workspace);
+    k.aggP = ws;
+    k.aggS = ws + per;
+    k.carry = ws + 2 * per;
+  }
+  return from_hip(ss::launch_fwd(k, pl.nchunks, static_cast<hipStream_t>(stream)));
+}
+
+ss_status ss_fwd_step(const ss_problem* p, const void* u_t, const void* delta_t, const float* A, const void* B_t,
+                      const void* C_t, const float* D, const void* z_t, const float* delta_bias,
+                      const float* state_in, float* state_out, void* y_t, void* stream) {
+  ss_status s = check_problem(p, false);
+  if (s != SS_OK) return s;
+  if (!u_t || !delta_t || !A || !B_t || !C_t || !state_in || !state_out || !y_t) return SS_ERR_NULL_ARG;
+  const void* ptrs[] = {u_t, delta_t, A, B_t, C_t, D, z_t, delta_bias, state_in, state_out, y_t};
+  for (const void* q : ptrs)
+    if (q && !aligned(q)) return SS_ERR_MISALIGNED;
+  // in-place is allowed; a partial overlap of the two state buffers is not
+  const uintptr_t a0 = (uintptr_t)state_in, b0 = (uintptr_t)state_out;
+  const uintptr_t bytes = (uintptr_t)(p->batch * p->dim * p->dstate) * sizeof(float);
+  if (a0 != b0 && a0 < b0 + bytes && b0 < a0 + bytes) return SS_ERR_UNSUPPORTED;
+
+  ss::StepParams k{};
+  k.io = p->io_dtype;
+  k.softplus = p->delta_softplus != 0;
+  k.u = u_t; k.delta = delta_t; k.z = z_t; k.Bt = B_t; k.Ct = C_t;
+  k.A = A; k.D = D; k.bias = delta_bias;
+  k.state_in = state_in; k.state_out = state_out; k.y = y_t;
+  k.batch = p->batch; k.dim = p->dim; k.dstate = p->dstate;
+  return from_hip(ss::launch_step(k, static_cast<hipStream_t>(stream)));
+}
+
+size_t ss_bwd_workspace_size(const ss_problem* p) {
+  if (check_problem(p, true) != SS_OK) return 0;
+  const int64_t nchunks = (p->seqlen + kTile - 1) / kTile;
+  return (size_t)3 * (size_t)(p->batch * p->dim * nchunks * 16) * sizeof(float);
+}
+
+ss_status ss_bwd(const ss_problem* p, const void* u, const void* delta, const float* A, const void* Bm,
+                 const void* Cm, const float* D, const void* z, const float* delta_bias, const float* ckpt,
+                 const void* dy, void* du, void* ddelta, void* dz, float* dA, float* dB, float* dC, float* dD,
+                 float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+  ss_status s = check_problem(p, true);
+  if (s != SS_OK) return s;
+  if (!u || !delta || !A || !Bm || !Cm || !ckpt || !dy || !du || !ddelta || !dA || !dB || !dC)
+    return SS_ERR_NULL_ARG;
+  if ((z == nullptr) != (dz == nullptr) || (D == nullptr) != (dD == nullptr) ||
+      (delta_bias == nullptr) != (dbias == nullptr))
+    return SS_ERR_NULL_ARG;
+  const void* ptrs[] = {u, delta, A, Bm, Cm, D, z, delta_bias, ckpt, dy, du, ddelta, dz, dA, dB, dC, dD, dbias,
+                        workspace};
+  for (const void* q : ptrs)
+    if (q && !aligned(q)) return SS_ERR_MISALIGNED;
+  const size_t need = ss_bwd_workspace_size(p);
+  if (!workspace || workspace_bytes < need) return SS_ERR_UNSUPPORTED;
+
+  ss::BwdParams k{};
+  k.io = p->io_dtype;
+  k.softplus = p->delta_softplus != 0;
+  k.u = u; k.delta = delta; k.z = z; k.Bm = Bm; k.Cm = Cm;
+  k.A = A; k.D = D; k.bias = delta_bias; k.ckpt = ckpt; k.dy = dy;
+  k.du = du; k.ddelta = ddelta; k.dz = dz;
+  k.dA = dA; k.dB = dB; k.dC = dC; k.dD = dD; k.dbias = dbias;
+  k.batch = p->batch; k.dim = p->dim; k.dstate = p->dstate; k.seqlen = p->seqlen;
+  k.ch_blocks = (p->dim + kChPerBlock - 1) / kChPerBlock;
+  k.nchunks = (p->seqlen + kTile - 1) / kTile;
+  const size_t per = (size_t)(p->batch * p->dim * k.nchunks * 16);
+  float* ws = static_cast<float*>(workspace);
+  k.gcarry = ws;
+  k.aggP = ws + per;
+  k.aggG = ws + 2 * per;
+  return from_hip(ss::launch_bwd(k, static_cast<hipStream_t>(stream)));
+}
+
+ss_status ss_copy_probe(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst) return SS_ERR_NULL_ARG;
+  if (!aligned(src) || !aligned(dst)) return SS_ERR_MISALIGNED;
+  if (bytes % 16 != 0 || bytes == 0) return SS_ERR_BAD_SHAPE;
+  return from_hip(ss::launch_copy(src, dst, (int64_t)bytes, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

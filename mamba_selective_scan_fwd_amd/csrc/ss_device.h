@@ -1,0 +1,108 @@
+// ss_device.h -- device helpers shared by the selective-scan kernels (gfx950).
+// Internal to libss.so; not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ss.h"
+
+namespace ss {
+
+constexpr int kTile = 64;      // time steps per tile; also the checkpoint interval
+constexpr int kStates = 16;    // state lanes per channel (dstate is padded to 16)
+constexpr int kChPerWave = 4;  // 64-lane wavefront = 4 channels x 16 states
+constexpr int kWaves = 4;      // waves per workgroup
+constexpr int kChPerBlock = kChPerWave * kWaves;  // 16 channels per workgroup
+constexpr int kThreads = 64 * kWaves;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- I/O element conversions (data tensors are fp32, fp16 or bf16) --------
+template <int IO> struct io_elem;
+template <> struct io_elem<SS_F32> { using T = float; };
+template <> struct io_elem<SS_F16> { using T = _Float16; };
+template <> struct io_elem<SS_BF16> { using T = uint16_t; };
+
+template <int IO> __device__ __forceinline__ float to_f32(typename io_elem<IO>::T v);
+template <> __device__ __forceinline__ float to_f32<SS_F32>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<SS_F16>(_Float16 v) { return (float)v; }
+template <> __device__ __forceinline__ float to_f32<SS_BF16>(uint16_t v) {
+  return __uint_as_float((uint32_t)v << 16);
+}
+
+template <int IO> __device__ __forceinline__ typename io_elem<IO>::T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<SS_F32>(float v) { return v; }
+template <> __device__ __forceinline__ _Float16 from_f32<SS_F16>(float v) { return (_Float16)v; }
+template <> __device__ __forceinline__ uint16_t from_f32<SS_BF16>(float v) {
+  // round to nearest even (NaN kept quiet)
+  uint32_t bits = __float_as_uint(v);
+  if ((bits & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((bits >> 16) | 0x40u);
+  bits += 0x7fffu + ((bits >> 16) & 1u);
+  return (uint16_t)(bits >> 16);
+}
+
+template <int IO>
+__device__ __forceinline__ float load_io(const void* base, int64_t i) {
+  return to_f32<IO>(reinterpret_cast<const typename io_elem<IO>::T*>(base)[i]);
+}
+template <int IO>
+__device__ __forceinline__ void store_io(void* base, int64_t i, float v) {
+  reinterpret_cast<typename io_elem<IO>::T*>(base)[i] = from_f32<IO>(v);
+}
+
+// ---- fast transcendental pieces (hardware exp2/log2/rcp) -------------------
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|).  log1p(e) for
+// e in (0, 1] uses the w = 1 + e correction log(w) * e / (w - 1), which keeps
+// full relative accuracy when e is tiny (w - 1 is exact there).
+__device__ __forceinline__ float softplus_f(float x) {
+  float e = exp2_hw(-fabsf(x) * kLog2e);
+  float w = 1.0f + e;
+  float wm1 = w - 1.0f;
+  float lp = (wm1 == 0.0f) ? e : (log2_hw(w) * kLn2) * (e * rcp_hw(wm1));
+  return fmaxf(x, 0.0f) + lp;
+}
+
+// d softplus / dx = sigmoid(x)
+__device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp2_hw(-x * kLog2e)); }
+
+// SiLU(z) = z * sigmoid(z)
+__device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
+
+// ---- cross-lane moves inside a 16-lane DPP row ------------------------------
+// value of lane J of this lane's row (DPP row_newbcast; folds into the VALU
+// instruction that consumes it)
+template <int J>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + J, 0xf, 0xf, false));
+}
+// value of lane (l + K) mod 16 of this lane's row (DPP row_ror)
+template <int K>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + K, 0xf, 0xf, false));
+}
+// sum over the 16 lanes of a row, result in every lane of the row
+__device__ __forceinline__ float row_sum(float v) {
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  v += row_ror<1>(v);
+  return v;
+}
+
+// Workgroup index remapped so that consecutive logical blocks share an XCD
+// (MI355X dispatches workgroups round-robin over its 8 XCDs, each with its
+// own L2): logical blocks that read the same B/C rows then hit one L2.
+__device__ __forceinline__ uint32_t xcd_logical_block() {
+  const uint32_t nb = gridDim.x, bid = blockIdx.x;
+  const uint32_t per = nb / 8u, rem = nb % 8u;
+  const uint32_t xcd = bid % 8u, local = bid / 8u;
+  return xcd < rem ? xcd * (per + 1u) + local : rem * (per + 1u) + (xcd - rem) * per + local;
+}
+
+}  // namespace ss

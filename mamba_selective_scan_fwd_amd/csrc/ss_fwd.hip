@@ -1,0 +1,397 @@
+// ss_fwd.hip -- selective-scan forward, decode step and chunk-carry kernels (gfx950).
+//
+// The recurrence (page "Mamba", Part IV Stages 4-6): per channel (b, d) and
+// state n,  h_t[n] = exp(Delta_t A[d,n]) h_{t-1}[n] + Delta_t B[b,n,t] u_t,
+// y_t = (sum_n C[b,n,t] h_t[n] + D[d] u_t) * SiLU(z_t),
+// Delta_t = softplus(delta_t + bias[d]).
+//
+// Mapping on CDNA4.  One 64-lane wavefront holds 4 channels x 16 states:
+// lane (c, n) keeps h[n] of channel c in a VGPR for the whole time walk.
+// The per-(t, d) work (softplus, Delta*u, the skip, the gate, conversions)
+// is spread over the 16 lanes of the channel's DPP row -- lane l owns the
+// steps t = l (mod 16) -- and Delta_t, Delta_t*u_t reach the other lanes of
+// the row through DPP row broadcasts folded into the multiplies.  The
+// readout sum over n is a transpose through LDS: each step's products
+// C[n,t] h_t[n] are written to a 16x16 tile per channel, and after 16 steps
+// lane l adds up row t = l.  B and C tiles (shared by the 16 channels of a
+// workgroup, which all belong to one batch row) are staged in LDS once per
+// 64-step tile.  No MFMA: the work is an elementwise recurrence plus a
+// 16-wide reduction, not a contraction.
+//
+// Time chunking (for problems with too few channels to fill 256 CUs): the
+// sequence is cut into K chunks of a multiple of 64 steps.  Pass 1
+// (ss_fwd_chunk_kernel<AGG>) computes for each chunk the pair (P, S) =
+// (prod of exp(Delta A) over the chunk, state reached from zero), pass 2
+// (ss_carry_kernel) scans the pairs with the associative operator
+// (P1,S1) then (P2,S2) = (P2 P1, P2 S1 + S2) (page "Mamba", Part V, the
+// combine for h_t = a_t h_{t-1} + b_t) to get each chunk's entry state, and
+// pass 3 (ss_fwd_chunk_kernel<FINAL>) reruns every chunk from its entry state
+// and writes y.  With K = 1 only pass 3 runs, from a zero state.
+#include "ss_device.h"
+#include "ss_internal.h"
+
+namespace ss {
+
+namespace {
+
+constexpr int kBCStride = kTile + 4;  // padded LDS row of a B/C tile (floats)
+constexpr int kPRow = 20;             // padded LDS row of the readout tile (16 states + 4)
+constexpr int kPChan = 16 * kPRow + 16;  // per-channel readout tile; 336 = 16 mod 64 banks
+
+struct FwdSmem {
+  float B[2][kStates][kBCStride];
+  float C[2][kStates][kBCStride];
+  float P[kWaves][kChPerWave * kPChan];
+};
+
+// Per-lane registers of the four steps this lane owns in a 64-step tile.
+struct Owned {
+  float dt[4];   // Delta_t (0 for masked steps)
+  float dtu[4];  // Delta_t * u_t
+  float u[4];
+  float z[4];
+  bool valid[4];
+};
+
+template <int IO>
+struct RawOwned {
+  float u[4], dl[4], z[4];
+};
+
+template <int IO>
+__device__ __forceinline__ void load_owned(RawOwned<IO>& r, const FwdParams& p, int64_t row_off, int64_t t0,
+                                           int l, bool ch_ok, bool need_z, int64_t t_load_end) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = t0 + 16 * i + l;
+    const bool ok = ch_ok && t < t_load_end;
+    r.u[i] = ok ? load_io<IO>(p.u, row_off + t) : 0.0f;
+    r.dl[i] = ok ? load_io<IO>(p.delta, row_off + t) : 0.0f;
+    r.z[i] = (ok && need_z) ? load_io<IO>(p.z, row_off + t) : 0.0f;
+  }
+}
+
+template <int IO>
+__device__ __forceinline__ void load_bc(float (&bv)[4], float (&cv)[4], const FwdParams& p, int64_t b,
+                                        int64_t t0, int tid, int64_t t_load_end) {
+  const int n = tid / 16, q = (tid % 16) * 4;
+  const bool n_ok = n < p.dstate;
+  const int64_t base = (b * p.dstate + n) * p.seqlen;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t t = t0 + q + k;
+    const bool ok = n_ok && t < t_load_end;
+    bv[k] = ok ? load_io<IO>(p.Bm, base + t) : 0.0f;
+    cv[k] = ok ? load_io<IO>(p.Cm, base + t) : 0.0f;
+  }
+}
+
+__device__ __forceinline__ void store_bc(FwdSmem& sm, int buf, const float (&bv)[4], const float (&cv)[4], int tid) {
+  const int n = tid / 16, q = (tid % 16) * 4;
+  *reinterpret_cast<float4*>(&sm.B[buf][n][q]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
+  *reinterpret_cast<float4*>(&sm.C[buf][n][q]) = make_float4(cv[0], cv[1], cv[2], cv[3]);
+}
+
+template <int IO>
+__device__ __forceinline__ void prep_owned(Owned& o, const RawOwned<IO>& r, int64_t t0, int l, float bias,
+                                           bool softplus, int64_t t_valid_end, float& dt_sum) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t t = t0 + 16 * i + l;
+    const bool v = t < t_valid_end;
+    const float x = r.dl[i] + bias;
+    float dt = softplus ? softplus_f(x) : x;
+    dt = v ? dt : 0.0f;
+    o.dt[i] = dt;
+    o.dtu[i] = dt * r.u[i];
+    o.u[i] = r.u[i];
+    o.z[i] = r.z[i];
+    o.valid[i] = v;
+    dt_sum += dt;
+  }
+}
+
+// 16 steps of block I of the tile.  Lane (c, n): h is its state; the readout
+// products of the 16 steps are left in the wave's LDS tile.
+template <int I, bool FINAL, int... J>
+__device__ __forceinline__ void scan_block(float& h, const Owned& o, float A2, const float* sBrow,
+                                           const float* sCrow, float* pcol, std::integer_sequence<int, J...>) {
+  float4 b4, c4;
+  (
+      [&] {
+        constexpr int s = 16 * I + J;
+        if constexpr (J % 4 == 0) {
+          b4 = *reinterpret_cast<const float4*>(sBrow + s);
+          if constexpr (FINAL) c4 = *reinterpret_cast<const float4*>(sCrow + s);
+        }
+        const float bj = (J % 4 == 0) ? b4.x : (J % 4 == 1) ? b4.y : (J % 4 == 2) ? b4.z : b4.w;
+        const float a = exp2_hw(row_bcast<J>(o.dt[I]) * A2);
+        h = fmaf(a, h, row_bcast<J>(o.dtu[I]) * bj);
+        if constexpr (FINAL) {
+          const float cj = (J % 4 == 0) ? c4.x : (J % 4 == 1) ? c4.y : (J % 4 == 2) ? c4.z : c4.w;
+          pcol[J * kPRow] = cj * h;
+        }
+      }(),
+      ...);
+}
+
+template <int IO, bool FINAL>
+__global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
+  __shared__ FwdSmem sm;
+  const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64;
+  const int cw = lane / 16;  // channel within the wave
+  const int n = lane % 16;   // state index; also the time-owner index l
+  const int l = n;
+
+  // logical block -> (chunk, batch row, channel block)
+  uint32_t lb = xcd_logical_block();
+  const int64_t cb = lb % p.ch_blocks;
+  lb /= p.ch_blocks;
+  const int64_t b = lb % p.batch;
+  const int64_t chunk = lb / p.batch + p.chunk_base;
+
+  const int64_t d = cb * kChPerBlock + wave * kChPerWave + cw;
+  const bool ch_ok = d < p.dim;
+  const bool n_ok = n < p.dstate;
+  const int64_t ch = b * p.dim + d;
+  const int64_t row_off = ch * p.seqlen;
+
+  int64_t len = p.seqlen;
+  if (p.lengths) {
+    int64_t v = p.lengths[b];
+    len = v < 0 ? 0 : (v > p.seqlen ? p.seqlen : v);
+  }
+  const int64_t t_begin = chunk * p.chunk_len;
+  const int64_t t_stop = t_begin + p.chunk_len < p.seqlen ? t_begin + p.chunk_len : p.seqlen;
+  const int64_t t_valid_end = t_stop < len ? t_stop : len;
+  // inputs are read only where they are used: steps before the row's length
+  const int64_t t_load_end = t_valid_end;
+
+  const float A2 = (ch_ok && n_ok) ? p.A[d * p.dstate + n] * kLog2e : 0.0f;
+  const float bias = (ch_ok && p.bias) ? p.bias[d] : 0.0f;
+  const float Dd = (ch_ok && p.D) ? p.D[d] : 0.0f;
+  const bool need_z = p.z != nullptr;
+  const bool softplus = p.softplus != 0;
+
+  float h = 0.0f;
+  if (FINAL && chunk > 0 && p.carry && ch_ok)
+    h = p.carry[(ch * p.nchunks + chunk) * kStates + n];
+
+  float* pwave = sm.P[wave] + cw * kPChan;
+  float* pcol = pwave + n;           // column n of this channel's readout tile
+  const float* prow = pwave + l * kPRow;  // row l (step l of the block)
+
+  float dt_sum = 0.0f;
+  RawOwned<IO> raw;
+  float bv[4], cv[4];
+  load_owned<IO>(raw, p, row_off, t_begin, l, ch_ok, FINAL && need_z, t_load_end);
+  load_bc<IO>(bv, cv, p, b, t_begin, tid, t_load_end);
+  store_bc(sm, 0, bv, cv, tid);
+  __syncthreads();
+
+  int buf = 0;
+  for (int64_t t0 = t_begin; t0 < t_stop; t0 += kTile) {
+    Owned o;
+    prep_owned<IO>(o, raw, t0, l, bias, softplus, t_valid_end, dt_sum);
+    if (FINAL && p.ckpt && ch_ok && n_ok)
+      p.ckpt[(ch * p.ckpt_per_row + t0 / kTile) * p.dstate + n] = h;
+
+    const int64_t t1 = t0 + kTile;
+    const bool more = t1 < t_stop;
+    if (more) {
+      load_owned<IO>(raw, p, row_off, t1, l, ch_ok, FINAL && need_z, t_load_end);
+      load_bc<IO>(bv, cv, p, b, t1, tid, t_load_end);
+    }
+
+    const float* sBrow = &sm.B[buf][n][0];
+    const float* sCrow = &sm.C[buf][n][0];
+    const auto seq = std::make_integer_sequence<int, 16>{};
+
+#define SS_BLOCK(I)                                                                        \
+    scan_block<I, FINAL>(h, o, A2, sBrow, sCrow, pcol, seq);                               \
+    if constexpr (FINAL) {                                                                 \
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");                               \
+      __builtin_amdgcn_wave_barrier();                                                     \
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");                               \
+      const float4 r0 = *reinterpret_cast<const float4*>(prow + 0);                        \
+      const float4 r1 = *reinterpret_cast<const float4*>(prow + 4);                        \
+      const float4 r2 = *reinterpret_cast<const float4*>(prow + 8);                        \
+      const float4 r3 = *reinterpret_cast<const float4*>(prow + 12);                       \
+      float y0 = ((r0.x + r0.y) + (r0.z + r0.w)) + ((r1.x + r1.y) + (r1.z + r1.w)) +       \
+                 (((r2.x + r2.y) + (r2.z + r2.w)) + ((r3.x + r3.y) + (r3.z + r3.w)));      \
+      float yv = fmaf(Dd, o.u[I], y0);                                                     \
+      if (need_z) yv *= silu_f(o.z[I]);                                                    \
+      yv = o.valid[I] ? yv : 0.0f;                                                         \
+      const int64_t t = t0 + 16 * (I) + l;                                                 \
+      if (ch_ok && t < t_stop) store_io<IO>(p.y, row_off + t, yv);                         \
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");                               \
+      __builtin_amdgcn_wave_barrier();                                                     \
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");                               \
+    }
+    SS_BLOCK(0)
+    SS_BLOCK(1)
+    SS_BLOCK(2)
+    SS_BLOCK(3)
+#undef SS_BLOCK
+
+    if (more) store_bc(sm, buf ^ 1, bv, cv, tid);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  if (FINAL) {
+    if (p.last_state && ch_ok && n_ok && chunk == p.nchunks - 1)
+      p.last_state[ch * p.dstate + n] = h;
+  } else if (ch_ok) {
+    // chunk summary: P = exp(A * sum Delta) (= prod of the step decays), S = h
+    const float dsum = row_sum(dt_sum);
+    const int64_t k = (ch * p.nchunks + chunk) * kStates + n;
+    p.aggP[k] = exp2_hw(A2 * dsum);
+    p.aggS[k] = h;
+  }
+}
+
+// Entry state of every chunk: an exclusive scan over the chunk pairs (P, S)
+// of one channel.  256 threads per channel: thread (n, g) serially combines
+// the chunks [g*per, (g+1)*per) of state n, the 16 groups of a state (one
+// DPP row) are then scanned with shuffles, and each group replays its
+// chunks from its exclusive prefix.
+__global__ void __launch_bounds__(256) ss_carry_kernel(const float* __restrict__ aggP, const float* __restrict__ aggS,
+                                                       float* __restrict__ carry, int64_t nch, int32_t nchunks) {
+  const int tid = threadIdx.x;
+  const int n = tid / 16, g = tid % 16;
+  const int64_t ch = blockIdx.x;
+  if (ch >= nch) return;
+  const int per = (nchunks + 15) / 16;
+  const int c0 = g * per;
+  const int c1 = c0 + per < nchunks ? c0 + per : nchunks;
+  const int64_t base = ch * nchunks;
+
+  // local pair over [c0, c1): applying it maps the state entering c0 to the
+  // state leaving c1 - 1
+  float P = 1.0f, S = 0.0f;
+  for (int c = c0; c < c1; ++c) {
+    const float pc = aggP[(base + c) * kStates + n];
+    const float sc = aggS[(base + c) * kStates + n];
+    S = fmaf(pc, S, sc);
+    P *= pc;
+  }
+  // inclusive scan across the 16 groups (earlier groups on the left)
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    const float Pl = __shfl_up(P, off, 16);
+    const float Sl = __shfl_up(S, off, 16);
+    if (g >= off) {
+      S = fmaf(P, Sl, S);
+      P *= Pl;
+    }
+  }
+  // exclusive prefix = inclusive prefix of the group on the left
+  float E = __shfl_up(S, 1, 16);
+  if (g == 0) E = 0.0f;
+  for (int c = c0; c < c1; ++c) {
+    carry[(base + c) * kStates + n] = E;
+    E = fmaf(aggP[(base + c) * kStates + n], E, aggS[(base + c) * kStates + n]);
+  }
+}
+
+// One decode step.  Lane (c, n) of the wave updates state n of channel c;
+// the readout sum over n is a DPP row reduction.
+template <int IO>
+__global__ void __launch_bounds__(kThreads) ss_step_kernel(StepParams p) {
+  const int tid = threadIdx.x;
+  const int n = tid % 16;
+  const int64_t ch = (int64_t)blockIdx.x * kChPerBlock + tid / 16;
+  const bool ok = ch < p.batch * p.dim;
+  const int64_t b = ok ? ch / p.dim : 0;
+  const int64_t d = ok ? ch % p.dim : 0;
+  const bool n_ok = n < p.dstate;
+
+  const float u = ok ? load_io<IO>(p.u, ch) : 0.0f;
+  const float dl = ok ? load_io<IO>(p.delta, ch) : 0.0f;
+  const float bias = (ok && p.bias) ? p.bias[d] : 0.0f;
+  const float x = dl + bias;
+  const float dt = p.softplus ? softplus_f(x) : x;
+  const float A2 = (ok && n_ok) ? p.A[d * p.dstate + n] * kLog2e : 0.0f;
+  const float Bn = (ok && n_ok) ? load_io<IO>(p.Bt, b * p.dstate + n) : 0.0f;
+  const float Cn = (ok && n_ok) ? load_io<IO>(p.Ct, b * p.dstate + n) : 0.0f;
+  const float h0 = (ok && n_ok) ? p.state_in[ch * p.dstate + n] : 0.0f;
+  const float h = fmaf(exp2_hw(dt * A2), h0, dt * u * Bn);
+  const float y0 = row_sum(Cn * h);
+  if (ok && n_ok) p.state_out[ch * p.dstate + n] = h;
+  if (ok && n == 0) {
+    float yv = y0 + (p.D ? p.D[d] * u : 0.0f);
+    if (p.z) yv *= silu_f(load_io<IO>(p.z, ch));
+    store_io<IO>(p.y, ch, yv);
+  }
+}
+
+// Plain device copy, 16 bytes per lane per iteration: the reference kernel
+// for HBM bandwidth and for calibrating traffic counters.
+__global__ void __launch_bounds__(256) ss_copy_kernel(const float4* __restrict__ src, float4* __restrict__ dst,
+                                                      int64_t n16) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+template <int IO>
+hipError_t launch_fwd_io(const FwdParams& p, int64_t nchunks, hipStream_t st) {
+  const int64_t blocks_per_chunk = p.batch * p.ch_blocks;
+  if (nchunks > 1) {
+    FwdParams q = p;
+    q.chunk_base = 0;
+    // pass 1: summaries of chunks 0 .. K-2 (the last chunk's summary is never needed)
+    hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, false>), dim3((uint32_t)(blocks_per_chunk * (nchunks - 1))),
+                       dim3(kThreads), 0, st, q);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // pass 2: entry states
+    hipLaunchKernelGGL(ss_carry_kernel, dim3((uint32_t)(p.batch * p.dim)), dim3(256), 0, st, p.aggP, p.aggS,
+                       p.carry, p.batch * p.dim, p.nchunks);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, true>), dim3((uint32_t)(blocks_per_chunk * nchunks)), dim3(kThreads),
+                     0, st, p);
+  return hipGetLastError();
+}
+
+template <int IO>
+hipError_t launch_step_io(const StepParams& p, hipStream_t st) {
+  const int64_t nch = p.batch * p.dim;
+  hipLaunchKernelGGL((ss_step_kernel<IO>), dim3((uint32_t)((nch + kChPerBlock - 1) / kChPerBlock)), dim3(kThreads),
+                     0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdParams& p, int64_t nchunks, hipStream_t st) {
+  switch (p.io) {
+    case SS_F32: return launch_fwd_io<SS_F32>(p, nchunks, st);
+    case SS_F16: return launch_fwd_io<SS_F16>(p, nchunks, st);
+    default: return launch_fwd_io<SS_BF16>(p, nchunks, st);
+  }
+}
+
+hipError_t launch_step(const StepParams& p, hipStream_t st) {
+  switch (p.io) {
+    case SS_F32: return launch_step_io<SS_F32>(p, st);
+    case SS_F16: return launch_step_io<SS_F16>(p, st);
+    default: return launch_step_io<SS_BF16>(p, st);
+  }
+}
+
+hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st) {
+  const int64_t n16 = bytes / 16;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 256 * 16) blocks = 256 * 16;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(ss_copy_kernel, dim3((uint32_t)blocks), dim3(256), 0, st,
+                     reinterpret_cast<const float4*>(src), reinterpret_cast<float4*>(dst), n16);
+  return hipGetLastError();
+}
+
+}  // namespace ss

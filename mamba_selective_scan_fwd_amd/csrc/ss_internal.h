@@ -1,0 +1,90 @@
+// ss_internal.h -- kernel parameter blocks and launch entry points shared by
+// the host ABI (ss_abi.cpp) and the kernel translation units.  Internal.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include <utility>
+
+namespace ss {
+
+struct FwdParams {
+  int32_t io;
+  int32_t softplus;
+  const void* u;
+  const void* delta;
+  const void* z;
+  const void* Bm;
+  const void* Cm;
+  const float* A;
+  const float* D;
+  const float* bias;
+  const int32_t* lengths;
+  void* y;
+  float* last_state;
+  float* ckpt;
+  // time-chunked scan workspace, each (batch*dim*nchunks*16) floats
+  float* aggP;
+  float* aggS;
+  float* carry;
+  int64_t batch, dim, dstate, seqlen;
+  int64_t chunk_len;     // multiple of 64
+  int64_t chunk_base;    // first chunk index covered by the launch
+  int64_t ch_blocks;     // ceil(dim / 16)
+  int64_t ckpt_per_row;  // ceil(seqlen / 64)
+  int32_t nchunks;
+};
+
+struct StepParams {
+  int32_t io;
+  int32_t softplus;
+  const void* u;
+  const void* delta;
+  const void* z;
+  const void* Bt;
+  const void* Ct;
+  const float* A;
+  const float* D;
+  const float* bias;
+  const float* state_in;
+  float* state_out;
+  void* y;
+  int64_t batch, dim, dstate;
+};
+
+struct BwdParams {
+  int32_t io;
+  int32_t softplus;
+  const void* u;
+  const void* delta;
+  const void* z;
+  const void* Bm;
+  const void* Cm;
+  const float* A;
+  const float* D;
+  const float* bias;
+  const float* ckpt;
+  const void* dy;
+  void* du;
+  void* ddelta;
+  void* dz;
+  float* dA;
+  float* dB;
+  float* dC;
+  float* dD;
+  float* dbias;
+  float* gcarry;  // workspace: reverse carries per (channel, chunk, state)
+  float* aggP;    // workspace: per-chunk decay product
+  float* aggG;    // workspace: per-chunk state gradient from a zero carry
+  int64_t batch, dim, dstate, seqlen;
+  int64_t ch_blocks;
+  int64_t nchunks;  // ceil(seqlen / 64)
+};
+
+hipError_t launch_fwd(const FwdParams& p, int64_t nchunks, hipStream_t st);
+hipError_t launch_step(const StepParams& p, hipStream_t st);
+hipError_t launch_bwd(const BwdParams& p, hipStream_t st);
+hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
+
+}  // namespace ss

@@ -1,0 +1,255 @@
+"""Thin Python binding over libss.so (the selective-scan C ABI).
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+libss.so.  torch provides device memory and the current stream.  There is no
+fallback path: if the library is missing or a call fails, an exception is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libss.so")
+
+SS_F32, SS_F16, SS_BF16 = 0, 1, 2
+_IO = {torch.float32: SS_F32, torch.float16: SS_F16, torch.bfloat16: SS_BF16}
+TILE = 64
+
+
+class ss_problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("seqlen", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("delta_softplus", ctypes.c_int32)]
+
+
+_vp = ctypes.c_void_p
+_lib = None
+
+# every symbol declared in include/ss.h
+EXPORTS = ("ss_fwd", "ss_fwd_step", "ss_bwd", "ss_fwd_workspace_size", "ss_bwd_workspace_size",
+           "ss_ckpt_count", "ss_status_str", "ss_copy_probe")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libss.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libss.so is not built (%s); run `python -m mamba_selective_scan_fwd_amd.build` "
+                           "or __graft_entry__.build()" % path)
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(ss_problem)
+    lib.ss_status_str.restype = ctypes.c_char_p
+    lib.ss_status_str.argtypes = [ctypes.c_int]
+    lib.ss_ckpt_count.restype = ctypes.c_size_t
+    lib.ss_ckpt_count.argtypes = [P]
+    lib.ss_fwd_workspace_size.restype = ctypes.c_size_t
+    lib.ss_fwd_workspace_size.argtypes = [P]
+    lib.ss_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.ss_bwd_workspace_size.argtypes = [P]
+    lib.ss_fwd.restype = ctypes.c_int
+    lib.ss_fwd.argtypes = [P] + [_vp] * 12 + [_vp, ctypes.c_size_t, _vp]
+    lib.ss_fwd_step.restype = ctypes.c_int
+    lib.ss_fwd_step.argtypes = [P] + [_vp] * 11 + [_vp]
+    lib.ss_bwd.restype = ctypes.c_int
+    lib.ss_bwd.argtypes = [P] + [_vp] * 18 + [_vp, ctypes.c_size_t, _vp]
+    lib.ss_copy_probe.restype = ctypes.c_int
+    lib.ss_copy_probe.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise RuntimeError(load_library().ss_status_str(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _prep(t, dtype, name, shape=None):
+    """Contiguous, 16-byte aligned device tensor of the given dtype (no conversion of values
+    beyond a dtype match check)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    t = t.contiguous()
+    if t.data_ptr() % 16:
+        t = t.clone()
+    return t
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def problem(batch, dim, dstate, seqlen, io_dtype, delta_softplus=True) -> ss_problem:
+    return ss_problem(batch, dim, dstate, seqlen, _IO[io_dtype], 1 if delta_softplus else 0)
+
+
+def ckpt_chunks(seqlen: int) -> int:
+    return (seqlen + TILE - 1) // TILE
+
+
+def fwd(u, delta, A, Bm, Cm, D=None, z=None, delta_bias=None, delta_softplus=True, lengths=None,
+        return_last_state=True, return_ckpt=False, y=None, workspace=None):
+    """Selective-scan forward.  Returns (y, last_state, ckpt) (None for what was not asked).
+
+    u, delta, z: (B, D, L); Bm, Cm: (B, N, L) in the same dtype (fp32/fp16/bf16);
+    A: (D, N) fp32; D, delta_bias: (D,) fp32; lengths: (B,) int32.
+    """
+    lib = load_library()
+    io = u.dtype
+    if io not in _IO:
+        raise TypeError("unsupported dtype %s" % io)
+    Bsz, Dd, L = u.shape
+    N = A.shape[1]
+    u = _prep(u, io, "u")
+    delta = _prep(delta, io, "delta", (Bsz, Dd, L))
+    z = _prep(z, io, "z", (Bsz, Dd, L))
+    Bm = _prep(Bm, io, "Bm", (Bsz, N, L))
+    Cm = _prep(Cm, io, "Cm", (Bsz, N, L))
+    A = _prep(A, torch.float32, "A", (Dd, N))
+    D = _prep(D, torch.float32, "D", (Dd,))
+    delta_bias = _prep(delta_bias, torch.float32, "delta_bias", (Dd,))
+    lengths = _prep(lengths, torch.int32, "lengths", (Bsz,))
+    dev = u.device
+    pr = problem(Bsz, Dd, N, L, io, delta_softplus)
+    if y is None:
+        y = torch.empty((Bsz, Dd, L), dtype=io, device=dev)
+    else:
+        y = _prep(y, io, "y", (Bsz, Dd, L))
+    last = torch.empty((Bsz, Dd, N), dtype=torch.float32, device=dev) if return_last_state else None
+    ck = None
+    if return_ckpt:
+        ck = torch.empty((Bsz, Dd, ckpt_chunks(L), N), dtype=torch.float32, device=dev)
+    wsz = lib.ss_fwd_workspace_size(ctypes.byref(pr))
+    ws = None
+    if wsz:
+        if workspace is not None and workspace.numel() * workspace.element_size() >= wsz:
+            ws = workspace
+        else:
+            ws = torch.empty((wsz + 3) // 4, dtype=torch.float32, device=dev)
+    _check(lib.ss_fwd(ctypes.byref(pr), _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z),
+                      _ptr(delta_bias), _ptr(lengths), _ptr(y), _ptr(last), _ptr(ck), _ptr(ws), wsz,
+                      _stream(dev)))
+    return y, last, ck
+
+
+def step(u_t, delta_t, A, B_t, C_t, state, D=None, z_t=None, delta_bias=None, delta_softplus=True,
+         state_out=None, y=None):
+    """One decode step.  Returns (y_t, state_out); pass state_out=state to update in place."""
+    lib = load_library()
+    io = u_t.dtype
+    if io not in _IO:
+        raise TypeError("unsupported dtype %s" % io)
+    Bsz, Dd = u_t.shape
+    N = A.shape[1]
+    u_t = _prep(u_t, io, "u_t")
+    delta_t = _prep(delta_t, io, "delta_t", (Bsz, Dd))
+    z_t = _prep(z_t, io, "z_t", (Bsz, Dd))
+    B_t = _prep(B_t, io, "B_t", (Bsz, N))
+    C_t = _prep(C_t, io, "C_t", (Bsz, N))
+    A = _prep(A, torch.float32, "A", (Dd, N))
+    D = _prep(D, torch.float32, "D", (Dd,))
+    delta_bias = _prep(delta_bias, torch.float32, "delta_bias", (Dd,))
+    if not (state.is_cuda and state.dtype == torch.float32 and state.is_contiguous()
+            and tuple(state.shape) == (Bsz, Dd, N) and state.data_ptr() % 16 == 0):
+        raise ValueError("state must be a contiguous, aligned fp32 device tensor of shape %s" % ((Bsz, Dd, N),))
+    if state_out is None:
+        state_out = torch.empty_like(state)
+    elif not (state_out.is_cuda and state_out.dtype == torch.float32 and state_out.is_contiguous()
+              and tuple(state_out.shape) == (Bsz, Dd, N) and state_out.data_ptr() % 16 == 0):
+        raise ValueError("state_out must match state")
+    if y is None:
+        y = torch.empty((Bsz, Dd), dtype=io, device=u_t.device)
+    pr = problem(Bsz, Dd, N, 1, io, delta_softplus)
+    _check(lib.ss_fwd_step(ctypes.byref(pr), _ptr(u_t), _ptr(delta_t), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(D),
+                           _ptr(z_t), _ptr(delta_bias), _ptr(state), _ptr(state_out), _ptr(y),
+                           _stream(u_t.device)))
+    return y, state_out
+
+
+def bwd(u, delta, A, Bm, Cm, ckpt, dy, D=None, z=None, delta_bias=None, delta_softplus=True, workspace=None):
+    """Selective-scan backward for the loss sum(dy * y).  Returns a dict of gradients
+    (du, ddelta, dA, dB, dC, and dz / dD / dbias for the inputs that were given)."""
+    lib = load_library()
+    io = u.dtype
+    Bsz, Dd, L = u.shape
+    N = A.shape[1]
+    u = _prep(u, io, "u")
+    delta = _prep(delta, io, "delta", (Bsz, Dd, L))
+    z = _prep(z, io, "z", (Bsz, Dd, L))
+    Bm = _prep(Bm, io, "Bm", (Bsz, N, L))
+    Cm = _prep(Cm, io, "Cm", (Bsz, N, L))
+    dy = _prep(dy, io, "dy", (Bsz, Dd, L))
+    A = _prep(A, torch.float32, "A", (Dd, N))
+    D = _prep(D, torch.float32, "D", (Dd,))
+    delta_bias = _prep(delta_bias, torch.float32, "delta_bias", (Dd,))
+    ckpt = _prep(ckpt, torch.float32, "ckpt", (Bsz, Dd, ckpt_chunks(L), N))
+    dev = u.device
+    g = {
+        "du": torch.empty((Bsz, Dd, L), dtype=io, device=dev),
+        "ddelta": torch.empty((Bsz, Dd, L), dtype=io, device=dev),
+        "dA": torch.empty((Dd, N), dtype=torch.float32, device=dev),
+        "dB": torch.empty((Bsz, N, L), dtype=torch.float32, device=dev),
+        "dC": torch.empty((Bsz, N, L), dtype=torch.float32, device=dev),
+        "dz": torch.empty((Bsz, Dd, L), dtype=io, device=dev) if z is not None else None,
+        "dD": torch.empty((Dd,), dtype=torch.float32, device=dev) if D is not None else None,
+        "dbias": torch.empty((Dd,), dtype=torch.float32, device=dev) if delta_bias is not None else None,
+    }
+    pr = problem(Bsz, Dd, N, L, io, delta_softplus)
+    wsz = lib.ss_bwd_workspace_size(ctypes.byref(pr))
+    if workspace is not None and workspace.numel() * workspace.element_size() >= wsz:
+        ws = workspace
+    else:
+        ws = torch.empty((wsz + 3) // 4, dtype=torch.float32, device=dev)
+    _check(lib.ss_bwd(ctypes.byref(pr), _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z),
+                      _ptr(delta_bias), _ptr(ckpt), _ptr(dy), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dz"]),
+                      _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dbias"]), _ptr(ws), wsz,
+                      _stream(dev)))
+    return {k: v for k, v in g.items() if v is not None}
+
+
+def copy_probe(src, dst):
+    """Device copy with the library's streaming copy kernel (bandwidth reference)."""
+    lib = load_library()
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    _check(lib.ss_copy_probe(_ptr(src), _ptr(dst), nbytes, _stream(src.device)))
+
+
+class SelectiveScanFn(torch.autograd.Function):
+    """autograd wrapper: forward = ss_fwd (with checkpoints), backward = ss_bwd."""
+
+    @staticmethod
+    def forward(ctx, u, delta, A, Bm, Cm, D, z, delta_bias, delta_softplus):
+        y, _, ck = fwd(u, delta, A, Bm, Cm, D=D, z=z, delta_bias=delta_bias, delta_softplus=delta_softplus,
+                       return_last_state=False, return_ckpt=True)
+        ctx.save_for_backward(u, delta, A, Bm, Cm, D, z, delta_bias, ck)
+        ctx.delta_softplus = delta_softplus
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        u, delta, A, Bm, Cm, D, z, delta_bias, ck = ctx.saved_tensors
+        g = bwd(u, delta, A, Bm, Cm, ck, dy.contiguous(), D=D, z=z, delta_bias=delta_bias,
+                delta_softplus=ctx.delta_softplus)
+        return (g["du"], g["ddelta"], g["dA"], g["dB"].to(Bm.dtype), g["dC"].to(Cm.dtype), g.get("dD"),
+                g.get("dz"), g.get("dbias"), None)
+
+
+def selective_scan_fn(u, delta, A, Bm, Cm, D=None, z=None, delta_bias=None, delta_softplus=False):
+    """y = selective_scan(u, delta, A, B, C, D, z, delta_bias, delta_softplus), differentiable."""
+    return SelectiveScanFn.apply(u, delta, A, Bm, Cm, D, z, delta_bias, delta_softplus)
