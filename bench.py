@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""Throughput of the selective-scan forward on one MI355X.
+
+One step = one ss_fwd over the mamba-130m layer workload (B=8, d_inner=1536,
+d_state=16, L=2048, fp16 I/O, fp32 state and arithmetic, softplus + bias,
+D skip, SiLU gate, final state), inputs resident in HBM.  Three independent
+input sets are rotated so that the 256 MB MALL cannot hold the working set
+between steps.  Prints ONE JSON line.
+
+Also measured (reported in "rows"): the long-sequence forward (B=1, D=16,
+L=32768, fp32), the ragged mamba-2.8b layer forward (bf16), 64 decode steps
+on the mamba-130m state, the backward (fp32, B=4, D=1536, L=4097), and a plain
+device copy (achievable HBM bandwidth).  The float64 CPU oracle is timed on a
+bounded sample of the same workload as "cpu_baseline".
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from mamba_selective_scan_fwd_amd import inputs, ss  # noqa: E402
+
+PEAK_HBM_GBPS = 8000.0
+# VALU issue slots per second: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz (fp32, no packed math)
+PEAK_SLOTS = 256 * 4 * 16 * 2.4e9
+# Algorithmic ALU work in issue slots (a transcendental issues at half rate = 2 slots):
+#   per (t, d, n): exp-argument mul, Bbar*u mul, recurrence fma, readout fma (4) + exp (2)
+#   per (t, d):   softplus (exp + log: 4, 4 VALU), Delta*u, skip fma, SiLU (exp + rcp: 4, 2 VALU),
+#                 gate mul = 9 VALU + 8 = 17; plus 4 conversions when the I/O is 16-bit
+SLOTS_PER_TDN = 6
+SLOTS_PER_TD = 17
+SLOTS_PER_TD_CVT16 = 4
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["mamba_selective_scan_fwd_amd/csrc/ss_fwd.hip", "mamba_selective_scan_fwd_amd/csrc/ss_device.h"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def fwd_alg_bytes(Bsz, Dd, N, L, s, lengths=None, ckpt=False):
+    """Algorithmic bytes of one forward: inputs read once, y written once, weights, final state."""
+    if lengths is None:
+        lengths = [L] * Bsz
+    valid = int(sum(lengths))
+    byt = valid * (Dd * (3 * s + s) + 2 * N * s)       # u, delta, z read + y written; B, C read once
+    byt += (L * Bsz - valid) * Dd * s                   # masked y written as zeros
+    byt += 4 * (Dd * N + 2 * Dd)                        # A, D, bias
+    byt += 4 * Bsz * Dd * N                             # final state
+    if ckpt:
+        byt += 4 * Bsz * Dd * ((L + 63) // 64) * N
+    return byt
+
+
+def fwd_alg_slots(Bsz, Dd, N, L, s, lengths=None):
+    valid = int(sum(lengths)) if lengths is not None else Bsz * L
+    per_td = SLOTS_PER_TDN * N + SLOTS_PER_TD + (SLOTS_PER_TD_CVT16 if s == 2 else 0)
+    return valid * Dd * per_td
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the headline kernel from the committed counter summary,
+    or None when it is missing or was taken on a different kernel source."""
+    path = os.path.join(PROFILE_DIR, "ss_fwd_final_mamba130m_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def timed(fn, reps, stream):
+    """Average ms per call of fn() over reps calls, HIP events on the launch stream."""
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(reps):
+        fn(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / reps
+
+
+def dev_problem(prob):
+    keys = ("u", "delta", "z", "Bm", "Cm", "A", "D", "bias", "lengths", "dy")
+    return {k: (None if prob.get(k) is None else prob[k].to("cuda")) for k in keys}
+
+
+def bench_headline(steps, warmup, stream):
+    sets = []
+    for r in range(3):
+        prob = inputs.make_config(2, seed=2 + 100 * r, decode_steps=0)
+        sets.append(dev_problem(prob))
+    Bsz, Dd, L = sets[0]["u"].shape
+    N = sets[0]["A"].shape[1]
+    ys = [torch.empty((Bsz, Dd, L), dtype=torch.float16, device="cuda") for _ in range(3)]
+
+    def step(i):
+        g = sets[i % 3]
+        ss.fwd(g["u"], g["delta"], g["A"], g["Bm"], g["Cm"], D=g["D"], z=g["z"], delta_bias=g["bias"],
+               delta_softplus=True, y=ys[i % 3])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms = timed(step, steps, stream)
+    wall = time.perf_counter() - t0
+    return ms, wall, (Bsz, Dd, N, L), sets, ys
+
+
+def bench_rows(stream):
+    rows = {}
+    # long sequence, few channels (time-chunked), fp32
+    p1 = dev_problem(inputs.make_config(1))
+    f1 = lambda i: ss.fwd(p1["u"], p1["delta"], p1["A"], p1["Bm"], p1["Cm"], D=p1["D"], z=p1["z"],
+                          delta_bias=p1["bias"])
+    f1(0)
+    ms = timed(f1, 20, stream)
+    tc = 1 * 16 * 32768
+    rows["fwd_long_B1_D16_L32768_f32"] = {"ms": ms, "token_channel_per_s": tc / (ms * 1e-3),
+                                          "tokens_per_s": 32768 / (ms * 1e-3)}
+    del p1
+    # ragged mamba-2.8b layer, bf16
+    prob3 = inputs.make_config(3)
+    lens = prob3["lengths"].tolist()
+    p3 = dev_problem(prob3)
+    del prob3
+    f3 = lambda i: ss.fwd(p3["u"], p3["delta"], p3["A"], p3["Bm"], p3["Cm"], D=p3["D"], z=p3["z"],
+                          delta_bias=p3["bias"], lengths=p3["lengths"])
+    f3(0)
+    ms = timed(f3, 10, stream)
+    byt = fwd_alg_bytes(4, 5120, 16, 8192, 2, lengths=lens)
+    rows["fwd_ragged_B4_D5120_L8192_bf16"] = {
+        "ms": ms, "lengths": lens, "token_channel_per_s": sum(lens) * 5120 / (ms * 1e-3),
+        "alg_GBps": byt / (ms * 1e-3) / 1e9, "hbm_frac": byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "alu_frac": fwd_alg_slots(4, 5120, 16, 8192, 2, lens) / (ms * 1e-3) / PEAK_SLOTS}
+    del p3
+    # decode: 64 single steps on the mamba-130m state
+    prob2 = inputs.make_config(2, decode_steps=64)
+    g2 = dev_problem(prob2)
+    toks = [{k: v.to("cuda") for k, v in t.items()} for t in prob2["decode"]]
+    state = torch.zeros((8, 1536, 16), dtype=torch.float32, device="cuda")
+    yt = torch.empty((8, 1536), dtype=torch.float16, device="cuda")
+
+    def fstep(i):
+        t = toks[i % 64]
+        ss.step(t["u_t"], t["delta_t"], g2["A"], t["B_t"], t["C_t"], state, D=g2["D"], z_t=t["z_t"],
+                delta_bias=g2["bias"], state_out=state, y=yt)
+
+    fstep(0)
+    ms = timed(fstep, 64, stream)
+    rows["decode_step_B8_D1536_f16"] = {"us_per_step": ms * 1e3,
+                                        "state_GBps": 2 * 8 * 1536 * 16 * 4 / (ms * 1e-3) / 1e9}
+    # graph-captured decode: 64 steps replayed as one graph
+    try:
+        g = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            fstep(0)
+        torch.cuda.current_stream().wait_stream(s2)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(64):
+                fstep(i)
+        g.replay()
+        torch.cuda.synchronize()
+        ms = timed(lambda i: g.replay(), 10, stream)
+        rows["decode_step_B8_D1536_f16"]["us_per_step_graph"] = ms * 1e3 / 64
+    except Exception as e:  # graph capture is a measurement extra, never the headline
+        rows["decode_step_B8_D1536_f16"]["graph_error"] = str(e)[:200]
+    del g2, toks
+    # backward, fp32
+    try:
+        prob4 = inputs.make_config(4)
+        p4 = dev_problem(prob4)
+        del prob4
+        _, _, ck = ss.fwd(p4["u"], p4["delta"], p4["A"], p4["Bm"], p4["Cm"], D=p4["D"], z=p4["z"],
+                          delta_bias=p4["bias"], return_ckpt=True)
+        fb = lambda i: ss.bwd(p4["u"], p4["delta"], p4["A"], p4["Bm"], p4["Cm"], ck, p4["dy"], D=p4["D"],
+                              z=p4["z"], delta_bias=p4["bias"])
+        fb(0)
+        ms = timed(fb, 5, stream)
+        Bsz, Dd, L, N = 4, 1536, 4097, 16
+        byt = (Bsz * Dd * L * 4 * 7 + 2 * Bsz * N * L * 4 * 2 + ck.numel() * 4 + 4 * (Dd * N + 2 * Dd) * 2)
+        rows["bwd_B4_D1536_L4097_f32"] = {"ms": ms, "token_channel_per_s": Bsz * Dd * L / (ms * 1e-3),
+                                          "alg_GBps": byt / (ms * 1e-3) / 1e9}
+        del p4, ck
+    except RuntimeError as e:
+        rows["bwd_B4_D1536_L4097_f32"] = {"error": str(e)[:200]}
+    torch.cuda.empty_cache()
+    return rows
+
+
+def copy_probe(stream):
+    nbytes = 1 << 30
+    src = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ss.copy_probe(src, dst)
+    ms = timed(lambda i: ss.copy_probe(src, dst), 10, stream)
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(sets_cpu_seed=2, target_s=12.0):
+    """The float64 oracle on a bounded sample of the headline workload: every batch row,
+    a block of channels, the full sequence; scaled to (token*channel)/s."""
+    import oracle
+    prob = inputs.make_config(2, seed=sets_cpu_seed, decode_steps=0)
+    L = prob["seqlen"]
+    threads = oracle.default_threads()
+    # calibrate on a small block, then size the sample to ~target_s of wall time
+    def run(nd):
+        sel = lambda t: inputs.to_f64(t[:, :nd])
+        args = dict(u=sel(prob["u"]), delta=sel(prob["delta"]), A=inputs.to_f64(prob["A"][:nd]),
+                    Bm=inputs.to_f64(prob["Bm"]), Cm=inputs.to_f64(prob["Cm"]), D=inputs.to_f64(prob["D"][:nd]),
+                    z=sel(prob["z"]), bias=inputs.to_f64(prob["bias"][:nd]))
+        t0 = time.perf_counter()
+        oracle.fwd(**args, threads=threads)
+        return time.perf_counter() - t0
+    nd = 16
+    t = run(nd)
+    nd2 = int(min(1536, max(16, nd * target_s / max(t, 1e-3))))
+    t2 = run(nd2)
+    tc = 8 * nd2 * L
+    return {"value": tc / t2, "unit": "(token*channel)/s", "cores": threads, "kind": "oracle",
+            "sample": "float64 oracle, all 8 batch rows x first %d of 1536 channels x L=%d of the mamba-130m "
+                      "workload (%d token*channel), %.2f s wall" % (nd2, L, tc, t2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-rows", action="store_true", help="headline only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the scan shards by batch "
+              "row or channel with no communication in the forward; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+    log("headline: %d warmup + %d timed steps" % (args.warmup, args.steps))
+    ms, wall, (Bsz, Dd, N, L), sets, ys = bench_headline(args.steps, args.warmup, stream)
+    del sets, ys
+    torch.cuda.empty_cache()
+    tc = Bsz * Dd * L
+    value = tc / (ms * 1e-3)
+    alg_bytes = fwd_alg_bytes(Bsz, Dd, N, L, 2)
+    alg_slots = fwd_alg_slots(Bsz, Dd, N, L, 2)
+    achieved_slots = alg_slots / (ms * 1e-3)
+    traffic = recorded_traffic()
+    result = {
+        "metric": "selective-scan fwd (token*channel)/s and HBM GB/s as % of MI355X peak",
+        "value": value,
+        "unit": "(token*channel)/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "mamba-130m layer selective-scan forward: B=8, d_inner=1536, d_state=16, "
+                               "L=2048, fp16 I/O, softplus+bias, D skip, SiLU gate, final state",
+                   "io_dtype": "f16", "batch": Bsz, "d_inner": Dd, "d_state": N, "seq_len": L,
+                   "input_sets_rotated": 3},
+        "roofline": {"bound": "alu", "achieved": achieved_slots / 1e12, "peak": PEAK_SLOTS / 1e12,
+                     "unit": "T VALU-slot/s", "frac": achieved_slots / PEAK_SLOTS,
+                     "traffic": traffic,
+                     "kernel": "ss_fwd_chunk_kernel<f16, FINAL>",
+                     "alg_slots_per_launch": alg_slots},
+        "hbm": {"alg_bytes_per_launch": alg_bytes, "achieved_GBps": alg_bytes / (ms * 1e-3) / 1e9,
+                "peak_GBps": PEAK_HBM_GBPS, "frac": alg_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
+        "wall_s_timed_region": wall,
+    }
+    try:
+        result["copy_probe_GBps"] = copy_probe(stream)
+    except Exception as e:
+        result["copy_probe_error"] = str(e)[:200]
+    if not args.no_rows:
+        log("other workloads")
+        result["rows"] = bench_rows(stream)
+    if not args.no_cpu:
+        log("cpu baseline (float64 oracle)")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -43,6 +43,47 @@ template <> __device__ __forceinline__ uint16_t from_f32<SS_BF16>(float v) {
   return (uint16_t)(bits >> 16);
 }
 
+// ---- buffer-resource access (hardware range check: loads past num_records
+// return 0, stores past it are dropped).  The base must be wave-uniform.
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
+}
+constexpr uint32_t kOffNone = 0x7fffffffu;  // an offset that is always out of range
+
+// raw element bits, kept in their storage width until converted at the point
+// of use (so a load's wait is not forced early by a widening instruction)
+template <int IO> struct raw_elem { using T = uint16_t; };
+template <> struct raw_elem<SS_F32> { using T = uint32_t; };
+template <int IO> using raw_t = typename raw_elem<IO>::T;
+
+template <int IO>
+__device__ __forceinline__ raw_t<IO> bload(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  if constexpr (IO == SS_F32)
+    return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+  else
+    return __builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0);
+}
+template <int IO>
+__device__ __forceinline__ float bits_f32(raw_t<IO> v) {
+  if constexpr (IO == SS_F32)
+    return __uint_as_float(v);
+  else if constexpr (IO == SS_F16)
+    return (float)__builtin_bit_cast(_Float16, v);
+  else
+    return __uint_as_float((uint32_t)v << 16);
+}
+template <int IO>
+__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, float v) {
+  if constexpr (IO == SS_F32)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, from_f32<IO>(v)), r, byte_off, 0, 0);
+}
+template <int IO> constexpr uint32_t io_bytes() { return IO == SS_F32 ? 4u : 2u; }
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 template <int IO>
 __device__ __forceinline__ float load_io(const void* base, int64_t i) {
   return to_f32<IO>(reinterpret_cast<const typename io_elem<IO>::T*>(base)[i]);

@@ -27,6 +27,8 @@
 // combine for h_t = a_t h_{t-1} + b_t) to get each chunk's entry state, and
 // pass 3 (ss_fwd_chunk_kernel<FINAL>) reruns every chunk from its entry state
 // and writes y.  With K = 1 only pass 3 runs, from a zero state.
+#include <type_traits>
+
 #include "ss_device.h"
 #include "ss_internal.h"
 
@@ -47,49 +49,95 @@ struct FwdSmem {
 // Per-lane registers of the four steps this lane owns in a 64-step tile.
 struct Owned {
   float dt[4];   // Delta_t (0 for masked steps)
-  float dtu[4];  // Delta_t * u_t
+  float dtu[4];  // Delta_t * u_t (0 for masked steps)
   float u[4];
   float z[4];
   bool valid[4];
 };
 
+// Raw element bits of the owned steps of the next tile: loaded one tile
+// ahead and converted only when used, so the loads stay in flight across a
+// whole tile of compute.
 template <int IO>
 struct RawOwned {
-  float u[4], dl[4], z[4];
+  raw_t<IO> u[4], dl[4], z[4];
+};
+
+// Wave-uniform views of the operands: one buffer resource per tensor region
+// (the 4 channel rows of this wave for u/delta/z/y, the batch row's (N, L)
+// block for B/C).  Lanes address them with 32-bit byte offsets; accesses past
+// the region return 0 / are dropped by the hardware range check.
+struct Views {
+  __amdgpu_buffer_rsrc_t u, dl, z, y, B, C;
 };
 
 template <int IO>
-__device__ __forceinline__ void load_owned(RawOwned<IO>& r, const FwdParams& p, int64_t row_off, int64_t t0,
-                                           int l, bool ch_ok, bool need_z, int64_t t_load_end) {
+__device__ __forceinline__ void load_owned(RawOwned<IO>& r, const Views& v, uint32_t lane_elem0, int64_t t0,
+                                           int l) {
+  constexpr uint32_t s = io_bytes<IO>();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t t = t0 + 16 * i + l;
-    const bool ok = ch_ok && t < t_load_end;
-    r.u[i] = ok ? load_io<IO>(p.u, row_off + t) : 0.0f;
-    r.dl[i] = ok ? load_io<IO>(p.delta, row_off + t) : 0.0f;
-    r.z[i] = (ok && need_z) ? load_io<IO>(p.z, row_off + t) : 0.0f;
+    const uint32_t off = (lane_elem0 + (uint32_t)(t0 + 16 * i + l)) * s;
+    r.u[i] = bload<IO>(v.u, off);
+    r.dl[i] = bload<IO>(v.dl, off);
+    r.z[i] = bload<IO>(v.z, off);  // a zero-size view when there is no gate
   }
 }
 
-template <int IO>
-__device__ __forceinline__ void load_bc(float (&bv)[4], float (&cv)[4], const FwdParams& p, int64_t b,
-                                        int64_t t0, int tid, int64_t t_load_end) {
-  const int n = tid / 16, q = (tid % 16) * 4;
-  const bool n_ok = n < p.dstate;
-  const int64_t base = (b * p.dstate + n) * p.seqlen;
+// Staging of the B/C tile.  Thread (n, j) covers state row n.  With PAIR
+// (16-bit data and an even seqlen, so that every element pair is 4-byte
+// aligned) it loads two 32-bit words = steps t0 + 32k + 2j, +1 (k < 2);
+// otherwise four single elements, steps t0 + j + 16k (k < 4).  Either way 16
+// lanes cover a contiguous run of the row per load.
+template <int IO, bool PAIR>
+struct BCRaw {
+  static constexpr int kN = PAIR ? 2 : 4;
+  using T = std::conditional_t<PAIR, uint32_t, raw_t<IO>>;
+  T b[kN], c[kN];
+};
+
+template <int IO, bool PAIR>
+__device__ __forceinline__ void load_bc(BCRaw<IO, PAIR>& r, const Views& v, uint32_t seqlen, int64_t t0, int tid,
+                                        bool need_c) {
+  constexpr uint32_t s = io_bytes<IO>();
+  const int n = tid / 16, j = tid % 16;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t t = t0 + q + k;
-    const bool ok = n_ok && t < t_load_end;
-    bv[k] = ok ? load_io<IO>(p.Bm, base + t) : 0.0f;
-    cv[k] = ok ? load_io<IO>(p.Cm, base + t) : 0.0f;
+  for (int k = 0; k < BCRaw<IO, PAIR>::kN; ++k) {
+    if constexpr (PAIR) {
+      const uint32_t off = ((uint32_t)n * seqlen + (uint32_t)(t0 + 32 * k + 2 * j)) * s;
+      r.b[k] = __builtin_amdgcn_raw_buffer_load_b32(v.B, off, 0, 0);
+      r.c[k] = need_c ? __builtin_amdgcn_raw_buffer_load_b32(v.C, off, 0, 0) : 0u;
+    } else {
+      const uint32_t off = ((uint32_t)n * seqlen + (uint32_t)(t0 + j + 16 * k)) * s;
+      r.b[k] = bload<IO>(v.B, off);
+      r.c[k] = need_c ? bload<IO>(v.C, off) : raw_t<IO>(0);
+    }
   }
 }
 
-__device__ __forceinline__ void store_bc(FwdSmem& sm, int buf, const float (&bv)[4], const float (&cv)[4], int tid) {
-  const int n = tid / 16, q = (tid % 16) * 4;
-  *reinterpret_cast<float4*>(&sm.B[buf][n][q]) = make_float4(bv[0], bv[1], bv[2], bv[3]);
-  *reinterpret_cast<float4*>(&sm.C[buf][n][q]) = make_float4(cv[0], cv[1], cv[2], cv[3]);
+// B/C of steps at or past the valid end are staged as exact zeros, so data
+// past a row's length (padding, NaN) never reaches the state.
+template <int IO, bool PAIR>
+__device__ __forceinline__ void store_bc(FwdSmem& sm, int buf, const BCRaw<IO, PAIR>& r, int tid, int64_t t0,
+                                         int64_t t_valid_end, int64_t dstate) {
+  const int n = tid / 16, j = tid % 16;
+  const bool n_ok = n < dstate;
+#pragma unroll
+  for (int k = 0; k < BCRaw<IO, PAIR>::kN; ++k) {
+    if constexpr (PAIR) {
+      const int e = 32 * k + 2 * j;
+      const bool ok0 = n_ok && t0 + e < t_valid_end, ok1 = n_ok && t0 + e + 1 < t_valid_end;
+      const float b0 = bits_f32<IO>((raw_t<IO>)(r.b[k] & 0xffffu)), b1 = bits_f32<IO>((raw_t<IO>)(r.b[k] >> 16));
+      const float c0 = bits_f32<IO>((raw_t<IO>)(r.c[k] & 0xffffu)), c1 = bits_f32<IO>((raw_t<IO>)(r.c[k] >> 16));
+      *reinterpret_cast<float2*>(&sm.B[buf][n][e]) = make_float2(ok0 ? b0 : 0.0f, ok1 ? b1 : 0.0f);
+      *reinterpret_cast<float2*>(&sm.C[buf][n][e]) = make_float2(ok0 ? c0 : 0.0f, ok1 ? c1 : 0.0f);
+    } else {
+      const int e = j + 16 * k;
+      const bool ok = n_ok && t0 + e < t_valid_end;
+      sm.B[buf][n][e] = ok ? bits_f32<IO>(r.b[k]) : 0.0f;
+      sm.C[buf][n][e] = ok ? bits_f32<IO>(r.c[k]) : 0.0f;
+    }
+  }
 }
 
 template <int IO>
@@ -99,13 +147,14 @@ __device__ __forceinline__ void prep_owned(Owned& o, const RawOwned<IO>& r, int6
   for (int i = 0; i < 4; ++i) {
     const int64_t t = t0 + 16 * i + l;
     const bool v = t < t_valid_end;
-    const float x = r.dl[i] + bias;
+    const float u = bits_f32<IO>(r.u[i]);
+    const float x = bits_f32<IO>(r.dl[i]) + bias;
     float dt = softplus ? softplus_f(x) : x;
     dt = v ? dt : 0.0f;
     o.dt[i] = dt;
-    o.dtu[i] = dt * r.u[i];
-    o.u[i] = r.u[i];
-    o.z[i] = r.z[i];
+    o.dtu[i] = v ? dt * u : 0.0f;
+    o.u[i] = u;
+    o.z[i] = bits_f32<IO>(r.z[i]);
     o.valid[i] = v;
     dt_sum += dt;
   }
@@ -135,11 +184,38 @@ __device__ __forceinline__ void scan_block(float& h, const Owned& o, float A2, c
       ...);
 }
 
-template <int IO, bool FINAL>
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Readout, skip, gate and store of step t0 + 16 I + l (owned by this lane).
+template <int IO, int I>
+__device__ __forceinline__ void finish_block(const Owned& o, const float* prow, float Dd, bool need_z,
+                                             const Views& v, uint32_t lane_elem0, int64_t t0, int l,
+                                             int64_t t_stop) {
+  const float4 r0 = *reinterpret_cast<const float4*>(prow + 0);
+  const float4 r1 = *reinterpret_cast<const float4*>(prow + 4);
+  const float4 r2 = *reinterpret_cast<const float4*>(prow + 8);
+  const float4 r3 = *reinterpret_cast<const float4*>(prow + 12);
+  const float y0 = (((r0.x + r0.y) + (r0.z + r0.w)) + ((r1.x + r1.y) + (r1.z + r1.w))) +
+                   (((r2.x + r2.y) + (r2.z + r2.w)) + ((r3.x + r3.y) + (r3.z + r3.w)));
+  float yv = fmaf(Dd, o.u[I], y0);
+  if (need_z) yv *= silu_f(o.z[I]);
+  yv = o.valid[I] ? yv : 0.0f;
+  const int64_t t = t0 + 16 * I + l;
+  const uint32_t off = t < t_stop ? (lane_elem0 + (uint32_t)t) * io_bytes<IO>() : kOffNone;
+  bstore<IO>(v.y, off, yv);
+}
+
+template <int IO, bool FINAL, bool PAIR>
 __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   __shared__ FwdSmem sm;
+  constexpr uint32_t s = io_bytes<IO>();
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
+  const int wave = uniform(tid / 64);
+  const int lane = tid % 64;
   const int cw = lane / 16;  // channel within the wave
   const int n = lane % 16;   // state index; also the time-owner index l
   const int l = n;
@@ -151,98 +227,118 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   const int64_t b = lb % p.batch;
   const int64_t chunk = lb / p.batch + p.chunk_base;
 
-  const int64_t d = cb * kChPerBlock + wave * kChPerWave + cw;
+  const int64_t d0 = cb * kChPerBlock + wave * kChPerWave;  // first channel of this wave
+  const int64_t d = d0 + cw;
   const bool ch_ok = d < p.dim;
   const bool n_ok = n < p.dstate;
   const int64_t ch = b * p.dim + d;
-  const int64_t row_off = ch * p.seqlen;
+  int64_t nch_w = p.dim - d0;
+  nch_w = nch_w < 0 ? 0 : (nch_w > kChPerWave ? kChPerWave : nch_w);
 
   int64_t len = p.seqlen;
   if (p.lengths) {
-    int64_t v = p.lengths[b];
+    const int64_t v = p.lengths[b];
     len = v < 0 ? 0 : (v > p.seqlen ? p.seqlen : v);
   }
   const int64_t t_begin = chunk * p.chunk_len;
   const int64_t t_stop = t_begin + p.chunk_len < p.seqlen ? t_begin + p.chunk_len : p.seqlen;
   const int64_t t_valid_end = t_stop < len ? t_stop : len;
-  // inputs are read only where they are used: steps before the row's length
-  const int64_t t_load_end = t_valid_end;
+  // tiles that hold at least one valid step; the rest of the chunk is zero-filled
+  const int64_t t_tile_end =
+      t_valid_end > t_begin ? t_begin + ((t_valid_end - t_begin + kTile - 1) / kTile) * kTile : t_begin;
+
+  const bool need_z = p.z != nullptr;
+  const bool softplus = p.softplus != 0;
+  const uint32_t L = (uint32_t)p.seqlen;
+  const int64_t row0 = (b * p.dim + d0) * p.seqlen;  // element offset of the wave's first row
+  const uint32_t wave_bytes = (uint32_t)(nch_w * p.seqlen) * s;
+  Views v;
+  v.u = make_rsrc(static_cast<const char*>(p.u) + row0 * s, wave_bytes);
+  v.dl = make_rsrc(static_cast<const char*>(p.delta) + row0 * s, wave_bytes);
+  const bool load_z = FINAL && need_z;
+  v.z = make_rsrc(load_z ? static_cast<const char*>(p.z) + row0 * s : static_cast<const char*>(p.u),
+                  load_z ? wave_bytes : 0u);
+  v.y = make_rsrc(FINAL ? static_cast<const char*>(p.y) + row0 * s : static_cast<const char*>(p.u), FINAL ? wave_bytes : 0u);
+  const uint32_t bc_bytes = (uint32_t)(p.dstate * p.seqlen) * s;
+  v.B = make_rsrc(static_cast<const char*>(p.Bm) + b * p.dstate * p.seqlen * s, bc_bytes);
+  v.C = make_rsrc(static_cast<const char*>(p.Cm) + b * p.dstate * p.seqlen * s, bc_bytes);
+  const uint32_t lane_elem0 = (uint32_t)cw * L;
 
   const float A2 = (ch_ok && n_ok) ? p.A[d * p.dstate + n] * kLog2e : 0.0f;
   const float bias = (ch_ok && p.bias) ? p.bias[d] : 0.0f;
   const float Dd = (ch_ok && p.D) ? p.D[d] : 0.0f;
-  const bool need_z = p.z != nullptr;
-  const bool softplus = p.softplus != 0;
 
   float h = 0.0f;
-  if (FINAL && chunk > 0 && p.carry && ch_ok)
-    h = p.carry[(ch * p.nchunks + chunk) * kStates + n];
+  if (FINAL && chunk > 0 && p.carry && ch_ok) h = p.carry[(ch * p.nchunks + chunk) * kStates + n];
 
   float* pwave = sm.P[wave] + cw * kPChan;
-  float* pcol = pwave + n;           // column n of this channel's readout tile
+  float* pcol = pwave + n;                // column n of this channel's readout tile
   const float* prow = pwave + l * kPRow;  // row l (step l of the block)
 
   float dt_sum = 0.0f;
   RawOwned<IO> raw;
-  float bv[4], cv[4];
-  load_owned<IO>(raw, p, row_off, t_begin, l, ch_ok, FINAL && need_z, t_load_end);
-  load_bc<IO>(bv, cv, p, b, t_begin, tid, t_load_end);
-  store_bc(sm, 0, bv, cv, tid);
+  BCRaw<IO, PAIR> bcr;
+  if (t_begin < t_tile_end) {
+    load_owned<IO>(raw, v, lane_elem0, t_begin, l);
+    load_bc<IO, PAIR>(bcr, v, L, t_begin, tid, FINAL);
+    store_bc<IO, PAIR>(sm, 0, bcr, tid, t_begin, t_valid_end, p.dstate);
+  }
   __syncthreads();
 
   int buf = 0;
-  for (int64_t t0 = t_begin; t0 < t_stop; t0 += kTile) {
+  for (int64_t t0 = t_begin; t0 < t_tile_end; t0 += kTile) {
     Owned o;
     prep_owned<IO>(o, raw, t0, l, bias, softplus, t_valid_end, dt_sum);
-    if (FINAL && p.ckpt && ch_ok && n_ok)
-      p.ckpt[(ch * p.ckpt_per_row + t0 / kTile) * p.dstate + n] = h;
+    if (FINAL && p.ckpt && ch_ok && n_ok) p.ckpt[(ch * p.ckpt_per_row + t0 / kTile) * p.dstate + n] = h;
 
     const int64_t t1 = t0 + kTile;
-    const bool more = t1 < t_stop;
+    const bool more = t1 < t_tile_end;
     if (more) {
-      load_owned<IO>(raw, p, row_off, t1, l, ch_ok, FINAL && need_z, t_load_end);
-      load_bc<IO>(bv, cv, p, b, t1, tid, t_load_end);
+      load_owned<IO>(raw, v, lane_elem0, t1, l);
+      load_bc<IO, PAIR>(bcr, v, L, t1, tid, FINAL);
     }
 
     const float* sBrow = &sm.B[buf][n][0];
     const float* sCrow = &sm.C[buf][n][0];
-    const auto seq = std::make_integer_sequence<int, 16>{};
-
-#define SS_BLOCK(I)                                                                        \
-    scan_block<I, FINAL>(h, o, A2, sBrow, sCrow, pcol, seq);                               \
-    if constexpr (FINAL) {                                                                 \
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");                               \
-      __builtin_amdgcn_wave_barrier();                                                     \
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");                               \
-      const float4 r0 = *reinterpret_cast<const float4*>(prow + 0);                        \
-      const float4 r1 = *reinterpret_cast<const float4*>(prow + 4);                        \
-      const float4 r2 = *reinterpret_cast<const float4*>(prow + 8);                        \
-      const float4 r3 = *reinterpret_cast<const float4*>(prow + 12);                       \
-      float y0 = ((r0.x + r0.y) + (r0.z + r0.w)) + ((r1.x + r1.y) + (r1.z + r1.w)) +       \
-                 (((r2.x + r2.y) + (r2.z + r2.w)) + ((r3.x + r3.y) + (r3.z + r3.w)));      \
-      float yv = fmaf(Dd, o.u[I], y0);                                                     \
-      if (need_z) yv *= silu_f(o.z[I]);                                                    \
-      yv = o.valid[I] ? yv : 0.0f;                                                         \
-      const int64_t t = t0 + 16 * (I) + l;                                                 \
-      if (ch_ok && t < t_stop) store_io<IO>(p.y, row_off + t, yv);                         \
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");                               \
-      __builtin_amdgcn_wave_barrier();                                                     \
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");                               \
+    constexpr auto seq = std::make_integer_sequence<int, 16>{};
+    scan_block<0, FINAL>(h, o, A2, sBrow, sCrow, pcol, seq);
+    if constexpr (FINAL) {
+      wave_lds_sync();
+      finish_block<IO, 0>(o, prow, Dd, need_z, v, lane_elem0, t0, l, t_stop);
+      wave_lds_sync();
     }
-    SS_BLOCK(0)
-    SS_BLOCK(1)
-    SS_BLOCK(2)
-    SS_BLOCK(3)
-#undef SS_BLOCK
+    scan_block<1, FINAL>(h, o, A2, sBrow, sCrow, pcol, seq);
+    if constexpr (FINAL) {
+      wave_lds_sync();
+      finish_block<IO, 1>(o, prow, Dd, need_z, v, lane_elem0, t0, l, t_stop);
+      wave_lds_sync();
+    }
+    scan_block<2, FINAL>(h, o, A2, sBrow, sCrow, pcol, seq);
+    if constexpr (FINAL) {
+      wave_lds_sync();
+      finish_block<IO, 2>(o, prow, Dd, need_z, v, lane_elem0, t0, l, t_stop);
+      wave_lds_sync();
+    }
+    scan_block<3, FINAL>(h, o, A2, sBrow, sCrow, pcol, seq);
+    if constexpr (FINAL) {
+      wave_lds_sync();
+      finish_block<IO, 3>(o, prow, Dd, need_z, v, lane_elem0, t0, l, t_stop);
+      wave_lds_sync();
+    }
 
-    if (more) store_bc(sm, buf ^ 1, bv, cv, tid);
+    if (more) store_bc<IO, PAIR>(sm, buf ^ 1, bcr, tid, t1, t_valid_end, p.dstate);
     __syncthreads();
     buf ^= 1;
   }
 
   if (FINAL) {
-    if (p.last_state && ch_ok && n_ok && chunk == p.nchunks - 1)
-      p.last_state[ch * p.dstate + n] = h;
+    // steps past the row's length: y = 0, checkpoints hold the frozen state
+    for (int64_t t = t_tile_end + l; t < t_stop; t += 16)
+      bstore<IO>(v.y, (lane_elem0 + (uint32_t)t) * s, 0.0f);
+    if (p.ckpt && ch_ok && n_ok)
+      for (int64_t t0 = t_tile_end; t0 < t_stop; t0 += kTile)
+        p.ckpt[(ch * p.ckpt_per_row + t0 / kTile) * p.dstate + n] = h;
+    if (p.last_state && ch_ok && n_ok && chunk == p.nchunks - 1) p.last_state[ch * p.dstate + n] = h;
   } else if (ch_ok) {
     // chunk summary: P = exp(A * sum Delta) (= prod of the step decays), S = h
     const float dsum = row_sum(dt_sum);
@@ -336,14 +432,14 @@ __global__ void __launch_bounds__(256) ss_copy_kernel(const float4* __restrict__
   for (; i < n16; i += stride) dst[i] = src[i];
 }
 
-template <int IO>
-hipError_t launch_fwd_io(const FwdParams& p, int64_t nchunks, hipStream_t st) {
+template <int IO, bool PAIR>
+hipError_t launch_fwd_variant(const FwdParams& p, int64_t nchunks, hipStream_t st) {
   const int64_t blocks_per_chunk = p.batch * p.ch_blocks;
   if (nchunks > 1) {
     FwdParams q = p;
     q.chunk_base = 0;
     // pass 1: summaries of chunks 0 .. K-2 (the last chunk's summary is never needed)
-    hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, false>), dim3((uint32_t)(blocks_per_chunk * (nchunks - 1))),
+    hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, false, PAIR>), dim3((uint32_t)(blocks_per_chunk * (nchunks - 1))),
                        dim3(kThreads), 0, st, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -353,9 +449,17 @@ hipError_t launch_fwd_io(const FwdParams& p, int64_t nchunks, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, true>), dim3((uint32_t)(blocks_per_chunk * nchunks)), dim3(kThreads),
-                     0, st, p);
+  hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, true, PAIR>), dim3((uint32_t)(blocks_per_chunk * nchunks)),
+                     dim3(kThreads), 0, st, p);
   return hipGetLastError();
+}
+
+template <int IO>
+hipError_t launch_fwd_io(const FwdParams& p, int64_t nchunks, hipStream_t st) {
+  if constexpr (IO != SS_F32) {
+    if (p.seqlen % 2 == 0) return launch_fwd_variant<IO, true>(p, nchunks, st);
+  }
+  return launch_fwd_variant<IO, false>(p, nchunks, st);
 }
 
 template <int IO>
