@@ -1,7 +1,461 @@
-// ss_bwd.hip -- selective-scan backward (placeholder until the kernels land).
+// ss_bwd.hip -- selective-scan backward (gfx950).
+//
+// Gradient of the loss sum_t dy_t y_t through the recurrence of page
+// "Mamba", Part IV Stages 4-6.  Per channel and state, the state gradient
+// G_t = dy0_t C_t + a_{t+1} G_{t+1} (dy0 = dy * SiLU(z)) runs backwards in
+// time; with it
+//   dC_t += dy0_t h_t         dB_t += G_t Delta_t u_t      (summed over channels)
+//   du_t  = Delta_t sum_n G_t B_t + dy0_t D
+//   dDelta_t = u_t sum_n G_t B_t + sum_n A G_t a_t h_{t-1}
+//   dA   += G_t a_t h_{t-1} Delta_t                         (summed over b, t)
+//   ddelta_t = dDelta_t * sigmoid(delta_t + bias) when softplus is on.
+// The forward states are not stored: they are recomputed chunk by chunk from
+// the 64-step checkpoints ss_fwd wrote ("Mamba, on a laptop GPU", "The state
+// lives in registers"; "Mamba", Part IV Stage 7).
+//
+// Passes (chunk = the 64 steps between two checkpoints):
+//   AGG   per chunk: P = prod a_t over the chunk, Gz = the gradient leaving the
+//         chunk's first step when nothing enters from the right;
+//   carry the right-to-left exclusive scan of (P, Gz) gives the gradient
+//         entering every chunk from the right (ss_carry_kernel, reversed);
+//   MAIN  per chunk: recompute h over the chunk into 65 registers per lane,
+//         walk it backwards with the true carried gradient, emit du, ddelta,
+//         dz, accumulate dB/dC in LDS and dA/dD/dbias partials;
+//   REDUCE sum the dA/dD/dbias partials over (batch row, chunk).
+// Lane layout as the forward: a wavefront holds 4 channels x 16 states; the
+// per-(t, d) work is owned by lane l = t mod 16 of the channel's row and
+// broadcast with DPP; sums over states go through an LDS transpose; sums over
+// channels (dB, dC) go through LDS float atomics and then one global atomic
+// per element per workgroup.
+#include <type_traits>
+
 #include "ss_device.h"
 #include "ss_internal.h"
 
 namespace ss {
-hipError_t launch_bwd(const BwdParams&, hipStream_t) { return hipErrorNotSupported; }
+
+hipError_t launch_carry(const float* aggP, const float* aggS, float* carry, int64_t nch, int32_t nchunks,
+                        bool reverse, hipStream_t st);
+
+namespace {
+
+constexpr int kBCStride = kTile + 4;
+constexpr int kPRow = 20;
+constexpr int kPChan = 16 * kPRow + 16;
+
+struct BwdSmem {
+  float B[kStates][kBCStride];
+  float C[kStates][kBCStride];
+  float T1[kWaves][kChPerWave * kPChan];
+  float T2[kWaves][kChPerWave * kPChan];
+  float dB[kStates][kBCStride];
+  float dC[kStates][kBCStride];
+};
+
+// values of the 4 steps t0 + 16 i + l this lane owns
+struct BwdOwned {
+  float dt[4], dtu[4], dy0[4], u[4], x[4], z[4], dy[4], y0[4];
+  bool valid[4];
+};
+
+template <int IO>
+struct BwdRaw {
+  raw_t<IO> u[4], dl[4], z[4], dy[4];
+};
+
+struct BwdViews {
+  __amdgpu_buffer_rsrc_t u, dl, z, dy, du, ddl, dz;
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float row16_sum(const float* row) {
+  const float4 r0 = *reinterpret_cast<const float4*>(row + 0);
+  const float4 r1 = *reinterpret_cast<const float4*>(row + 4);
+  const float4 r2 = *reinterpret_cast<const float4*>(row + 8);
+  const float4 r3 = *reinterpret_cast<const float4*>(row + 12);
+  return (((r0.x + r0.y) + (r0.z + r0.w)) + ((r1.x + r1.y) + (r1.z + r1.w))) +
+         (((r2.x + r2.y) + (r2.z + r2.w)) + ((r3.x + r3.y) + (r3.z + r3.w)));
+}
+
+template <int IO>
+__device__ __forceinline__ BwdViews make_views(const BwdParams& p, int64_t b, int64_t d0, bool need_z) {
+  constexpr uint32_t s = io_bytes<IO>();
+  int64_t nch_w = p.dim - d0;
+  nch_w = nch_w < 0 ? 0 : (nch_w > kChPerWave ? kChPerWave : nch_w);
+  const int64_t row0 = (b * p.dim + d0) * p.seqlen;
+  const uint32_t bytes = (uint32_t)(nch_w * p.seqlen) * s;
+  auto at = [&](const void* base) { return static_cast<const char*>(base) + row0 * s; };
+  BwdViews v;
+  v.u = make_rsrc(at(p.u), bytes);
+  v.dl = make_rsrc(at(p.delta), bytes);
+  v.dy = make_rsrc(at(p.dy), bytes);
+  v.du = make_rsrc(at(p.du), bytes);
+  v.ddl = make_rsrc(at(p.ddelta), bytes);
+  v.z = make_rsrc(need_z ? at(p.z) : static_cast<const char*>(p.u), need_z ? bytes : 0u);
+  v.dz = make_rsrc(need_z ? at(p.dz) : static_cast<const char*>(p.u), need_z ? bytes : 0u);
+  return v;
+}
+
+template <int IO>
+__device__ __forceinline__ void load_raw(BwdRaw<IO>& r, const BwdViews& v, uint32_t lane_elem0, int64_t t0, int l) {
+  constexpr uint32_t s = io_bytes<IO>();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t off = (lane_elem0 + (uint32_t)(t0 + 16 * i + l)) * s;
+    r.u[i] = bload<IO>(v.u, off);
+    r.dl[i] = bload<IO>(v.dl, off);
+    r.z[i] = bload<IO>(v.z, off);
+    r.dy[i] = bload<IO>(v.dy, off);
+  }
+}
+
+template <int IO>
+__device__ __forceinline__ void prep(BwdOwned& o, const BwdRaw<IO>& r, int64_t t0, int l, int64_t t_end, float bias,
+                                     bool softplus, bool need_z) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool v = t0 + 16 * i + l < t_end;
+    const float u = bits_f32<IO>(r.u[i]);
+    const float x = bits_f32<IO>(r.dl[i]) + bias;
+    float dt = softplus ? softplus_f(x) : x;
+    dt = v ? dt : 0.0f;
+    const float z = bits_f32<IO>(r.z[i]);
+    const float dy = v ? bits_f32<IO>(r.dy[i]) : 0.0f;
+    o.dt[i] = dt;
+    o.dtu[i] = v ? dt * u : 0.0f;
+    o.dy0[i] = v ? (need_z ? dy * silu_f(z) : dy) : 0.0f;
+    o.u[i] = u;
+    o.x[i] = x;
+    o.z[i] = z;
+    o.dy[i] = dy;
+    o.y0[i] = 0.0f;
+    o.valid[i] = v;
+  }
+}
+
+// ---- AGG: reverse walk of one chunk with a zero carry ------------------------
+template <int I, int... J>
+__device__ __forceinline__ void agg_block(float& g, const BwdOwned& o, float A2, const float* sCrow,
+                                          std::integer_sequence<int, J...>) {
+  // J runs 0..15; step s = 16 I + (15 - J) goes backwards
+  (
+      [&] {
+        constexpr int jj = 15 - J;
+        constexpr int s = 16 * I + jj;
+        const float a = exp2_hw(row_bcast<jj>(o.dt[I]) * A2);
+        const float G = fmaf(row_bcast<jj>(o.dy0[I]), sCrow[s], g);
+        g = G * a;
+      }(),
+      ...);
+}
+
+// ---- MAIN: forward recompute of block I (states into hs) ---------------------
+template <int I, bool WITH_Y, int... J>
+__device__ __forceinline__ void fwd_block(float (&hs)[kTile + 1], const BwdOwned& o, float A2, const float* sBrow,
+                                          const float* sCrow, float* t1col, std::integer_sequence<int, J...>) {
+  (
+      [&] {
+        constexpr int s = 16 * I + J;
+        const float a = exp2_hw(row_bcast<J>(o.dt[I]) * A2);
+        const float h = fmaf(a, hs[s], row_bcast<J>(o.dtu[I]) * sBrow[s]);
+        hs[s + 1] = h;
+        if constexpr (WITH_Y) t1col[J * kPRow] = sCrow[s] * h;
+      }(),
+      ...);
+}
+
+// ---- MAIN: reverse walk of block I -------------------------------------------
+template <int I, int... J>
+__device__ __forceinline__ void bwd_block(float& g, float& dA_acc, const float (&hs)[kTile + 1], const BwdOwned& o,
+                                          float A2, float Anat, const float* sBrow, const float* sCrow, float* dBrow,
+                                          float* dCrow, float* t1col, float* t2col,
+                                          std::integer_sequence<int, J...>) {
+  (
+      [&] {
+        constexpr int jj = 15 - J;
+        constexpr int s = 16 * I + jj;
+        const float dtb = row_bcast<jj>(o.dt[I]);
+        const float dy0b = row_bcast<jj>(o.dy0[I]);
+        const float a = exp2_hw(dtb * A2);
+        const float gh = fmaf(dy0b, sCrow[s], g);  // dLoss/dh_t
+        atomicAdd(dCrow + s, dy0b * hs[s + 1]);
+        atomicAdd(dBrow + s, gh * row_bcast<jj>(o.dtu[I]));
+        t1col[jj * kPRow] = gh * sBrow[s];
+        g = gh * a;                                 // to h_{t-1}
+        const float q = g * hs[s];                  // gh * a * h_{t-1}
+        t2col[jj * kPRow] = q * Anat;
+        dA_acc = fmaf(q, dtb, dA_acc);
+      }(),
+      ...);
+}
+
+template <int IO, bool MAIN>
+__global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int32_t groups, int32_t per_group) {
+  __shared__ BwdSmem sm;
+  constexpr uint32_t s = io_bytes<IO>();
+  const int tid = threadIdx.x;
+  const int wave = uniform(tid / 64);
+  const int lane = tid % 64;
+  const int cw = lane / 16, n = lane % 16, l = n;
+
+  uint32_t lb = xcd_logical_block();
+  const int64_t grp = lb % groups;
+  lb /= groups;
+  const int64_t k = lb % p.nchunks;
+  const int64_t b = lb / p.nchunks;
+  const int64_t K = p.nchunks;
+
+  const int64_t t0 = k * kTile;
+  const int64_t t_end = t0 + kTile < p.seqlen ? t0 + kTile : p.seqlen;
+  const bool need_z = p.z != nullptr;
+  const bool softplus = p.softplus != 0;
+  const uint32_t L = (uint32_t)p.seqlen;
+
+  // stage the chunk's B and C (shared by every channel of this batch row)
+  {
+    const uint32_t bc_bytes = (uint32_t)(p.dstate * p.seqlen) * s;
+    const char* bbase = static_cast<const char*>(p.Bm) + b * p.dstate * p.seqlen * s;
+    const char* cbase = static_cast<const char*>(p.Cm) + b * p.dstate * p.seqlen * s;
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(bbase, bc_bytes), rC = make_rsrc(cbase, bc_bytes);
+    const int sn = tid / 16, j = tid % 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = j + 16 * q;
+      const bool ok = sn < p.dstate && t0 + e < t_end;
+      const uint32_t off = ((uint32_t)sn * L + (uint32_t)(t0 + e)) * s;
+      const float bv = bits_f32<IO>(bload<IO>(rB, off));
+      const float cv = bits_f32<IO>(bload<IO>(rC, off));
+      sm.B[sn][e] = ok ? bv : 0.0f;
+      sm.C[sn][e] = ok ? cv : 0.0f;
+      if (MAIN) {
+        sm.dB[sn][e] = 0.0f;
+        sm.dC[sn][e] = 0.0f;
+      }
+    }
+  }
+  __syncthreads();
+
+  const float* sBrow = &sm.B[n][0];
+  const float* sCrow = &sm.C[n][0];
+  float* t1w = sm.T1[wave] + cw * kPChan;
+  float* t2w = sm.T2[wave] + cw * kPChan;
+  float* t1col = t1w + n;
+  float* t2col = t2w + n;
+  const float* t1row = t1w + l * kPRow;
+  const float* t2row = t2w + l * kPRow;
+  constexpr auto seq = std::make_integer_sequence<int, 16>{};
+
+  const int64_t cb_begin = grp * per_group;
+  int64_t cb_end = cb_begin + per_group;
+  if (cb_end > p.ch_blocks) cb_end = p.ch_blocks;
+
+  BwdRaw<IO> raw;
+  if (cb_begin < cb_end) {
+    const int64_t d0 = cb_begin * kChPerBlock + wave * kChPerWave;
+    const BwdViews v = make_views<IO>(p, b, d0, need_z);
+    load_raw<IO>(raw, v, (uint32_t)cw * L, t0, l);
+  }
+
+  for (int64_t cb = cb_begin; cb < cb_end; ++cb) {
+    const int64_t d0 = cb * kChPerBlock + wave * kChPerWave;
+    const int64_t d = d0 + cw;
+    const bool ch_ok = d < p.dim;
+    const bool n_ok = n < p.dstate;
+    const int64_t ch = b * p.dim + d;
+    const BwdViews v = make_views<IO>(p, b, d0, need_z);
+    const uint32_t lane_elem0 = (uint32_t)cw * L;
+
+    const float A = (ch_ok && n_ok) ? p.A[d * p.dstate + n] : 0.0f;
+    const float A2 = A * kLog2e;
+    const float bias = (ch_ok && p.bias) ? p.bias[d] : 0.0f;
+    const float Dd = (ch_ok && p.D) ? p.D[d] : 0.0f;
+
+    BwdOwned o;
+    prep<IO>(o, raw, t0, l, t_end, bias, softplus, need_z);
+    if (cb + 1 < cb_end) {  // prefetch the next channel block's operands
+      const BwdViews vn = make_views<IO>(p, b, d0 + kChPerBlock, need_z);
+      load_raw<IO>(raw, vn, lane_elem0, t0, l);
+    }
+    const int64_t wslot = ((ch * K + k) * kStates + n);
+
+    if constexpr (!MAIN) {
+      float g = 0.0f;
+      agg_block<3>(g, o, A2, sCrow, seq);
+      agg_block<2>(g, o, A2, sCrow, seq);
+      agg_block<1>(g, o, A2, sCrow, seq);
+      agg_block<0>(g, o, A2, sCrow, seq);
+      const float dsum = row_sum((o.dt[0] + o.dt[1]) + (o.dt[2] + o.dt[3]));
+      if (ch_ok) {
+        p.aggP[wslot] = exp2_hw(A2 * dsum);
+        p.aggG[wslot] = g;
+      }
+    } else {
+      float hs[kTile + 1];
+      hs[0] = (ch_ok && n_ok) ? p.ckpt[(ch * K + k) * p.dstate + n] : 0.0f;
+      if (need_z) {
+#define SS_FWD_Y(I)                                                        \
+  fwd_block<I, true>(hs, o, A2, sBrow, sCrow, t1col, seq);                 \
+  wave_lds_sync();                                                         \
+  o.y0[I] = fmaf(Dd, o.u[I], row16_sum(t1row));                            \
+  wave_lds_sync();
+        SS_FWD_Y(0)
+        SS_FWD_Y(1)
+        SS_FWD_Y(2)
+        SS_FWD_Y(3)
+#undef SS_FWD_Y
+      } else {
+        fwd_block<0, false>(hs, o, A2, sBrow, sCrow, t1col, seq);
+        fwd_block<1, false>(hs, o, A2, sBrow, sCrow, t1col, seq);
+        fwd_block<2, false>(hs, o, A2, sBrow, sCrow, t1col, seq);
+        fwd_block<3, false>(hs, o, A2, sBrow, sCrow, t1col, seq);
+      }
+
+      float g = (k < K - 1 && ch_ok) ? p.gcarry[wslot] : 0.0f;
+      float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
+      float* dBrow = &sm.dB[n][0];
+      float* dCrow = &sm.dC[n][0];
+#define SS_BWD(I)                                                                                   \
+  {                                                                                                 \
+    bwd_block<I>(g, dA_acc, hs, o, A2, A, sBrow, sCrow, dBrow, dCrow, t1col, t2col, seq);           \
+    wave_lds_sync();                                                                                \
+    const float sGB = row16_sum(t1row);                                                             \
+    const float sQA = row16_sum(t2row);                                                             \
+    const float du = fmaf(o.dt[I], sGB, o.dy0[I] * Dd);                                             \
+    const float dD = fmaf(o.u[I], sGB, sQA);                                                        \
+    float dx = softplus ? dD * sigmoid_f(o.x[I]) : dD;                                              \
+    dx = o.valid[I] ? dx : 0.0f;                                                                    \
+    const int64_t t = t0 + 16 * (I) + l;                                                            \
+    const uint32_t off = (o.valid[I] && ch_ok) ? (lane_elem0 + (uint32_t)t) * s : kOffNone;         \
+    bstore<IO>(v.du, off, o.valid[I] ? du : 0.0f);                                                  \
+    bstore<IO>(v.ddl, off, dx);                                                                     \
+    if (need_z) {                                                                                   \
+      const float sz = sigmoid_f(o.z[I]);                                                           \
+      const float dz = o.dy[I] * o.y0[I] * sz * fmaf(o.z[I], 1.0f - sz, 1.0f);                      \
+      bstore<IO>(v.dz, off, o.valid[I] ? dz : 0.0f);                                                \
+    }                                                                                               \
+    dD_acc = fmaf(o.dy0[I], o.u[I], dD_acc);                                                        \
+    db_acc += dx;                                                                                   \
+    wave_lds_sync();                                                                                \
+  }
+      SS_BWD(3)
+      SS_BWD(2)
+      SS_BWD(1)
+      SS_BWD(0)
+#undef SS_BWD
+      // partial sums of this (batch row, chunk) for the reduction pass
+      const int64_t bk = b * K + k;
+      if (ch_ok) p.aggP[(bk * p.dim + d) * kStates + n] = dA_acc;
+      const float dDs = row_sum(dD_acc);
+      const float dbs = row_sum(db_acc);
+      if (ch_ok && n == 0) {
+        p.aggG[bk * p.dim + d] = dDs;
+        p.aggG[p.batch * K * p.dim + bk * p.dim + d] = dbs;
+      }
+    }
+  }
+
+  if constexpr (MAIN) {
+    __syncthreads();
+    const int sn = tid / 16, j = tid % 16;
+    if (sn < p.dstate) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = j + 16 * q;
+        if (t0 + e < t_end) {
+          const int64_t gi = (b * p.dstate + sn) * p.seqlen + t0 + e;
+          unsafeAtomicAdd(p.dB + gi, sm.dB[sn][e]);
+          unsafeAtomicAdd(p.dC + gi, sm.dC[sn][e]);
+        }
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) ss_fill_kernel(float* __restrict__ dst, int64_t count, float value) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < count; i += stride) dst[i] = value;
+}
+
+// dA[d, n] = sum over (batch row, chunk) partials; dD, dbias likewise.
+__global__ void __launch_bounds__(256) ss_bwd_reduce_kernel(const float* __restrict__ dApart,
+                                                            const float* __restrict__ dDpart,
+                                                            const float* __restrict__ dbpart, float* __restrict__ dA,
+                                                            float* __restrict__ dD, float* __restrict__ dbias,
+                                                            int64_t dim, int64_t dstate, int64_t nbk) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t d = idx / kStates;
+  const int n = (int)(idx % kStates);
+  if (d >= dim) return;
+  float acc = 0.0f;
+  for (int64_t bk = 0; bk < nbk; ++bk) acc += dApart[(bk * dim + d) * kStates + n];
+  if (n < dstate) dA[d * dstate + n] = acc;
+  if (n == 0 && dD) {
+    float s = 0.0f;
+    for (int64_t bk = 0; bk < nbk; ++bk) s += dDpart[bk * dim + d];
+    dD[d] = s;
+  }
+  if (n == 1 && dbias) {
+    float s = 0.0f;
+    for (int64_t bk = 0; bk < nbk; ++bk) s += dbpart[bk * dim + d];
+    dbias[d] = s;
+  }
+}
+
+hipError_t fill(float* dst, int64_t count, hipStream_t st) {
+  int64_t blocks = (count + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(ss_fill_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, dst, count, 0.0f);
+  return hipGetLastError();
+}
+
+template <int IO>
+hipError_t launch_bwd_io(const BwdParams& p, hipStream_t st) {
+  const int64_t K = p.nchunks;
+  hipError_t e = fill(p.dB, p.batch * p.dstate * p.seqlen, st);
+  if (e != hipSuccess) return e;
+  e = fill(p.dC, p.batch * p.dstate * p.seqlen, st);
+  if (e != hipSuccess) return e;
+  // channel blocks per workgroup: enough workgroups to fill the chip
+  const int64_t bk = p.batch * K;
+  int64_t groups = (1024 + bk - 1) / bk;
+  if (groups > p.ch_blocks) groups = p.ch_blocks;
+  if (groups < 1) groups = 1;
+  const int64_t per = (p.ch_blocks + groups - 1) / groups;
+  groups = (p.ch_blocks + per - 1) / per;
+  const dim3 grid((uint32_t)(bk * groups));
+  if (K > 1) {
+    hipLaunchKernelGGL((ss_bwd_chunk_kernel<IO, false>), grid, dim3(kThreads), 0, st, p, (int32_t)groups,
+                       (int32_t)per);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_carry(p.aggP, p.aggG, p.gcarry, p.batch * p.dim, (int32_t)K, true, st);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((ss_bwd_chunk_kernel<IO, true>), grid, dim3(kThreads), 0, st, p, (int32_t)groups,
+                     (int32_t)per);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t threads = p.dim * kStates;
+  hipLaunchKernelGGL(ss_bwd_reduce_kernel, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, st, p.aggP, p.aggG,
+                     p.aggG + p.batch * K * p.dim, p.dA, p.dD, p.dbias, p.dim, p.dstate, bk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams& p, hipStream_t st) {
+  switch (p.io) {
+    case SS_F32: return launch_bwd_io<SS_F32>(p, st);
+    case SS_F16: return launch_bwd_io<SS_F16>(p, st);
+    default: return launch_bwd_io<SS_BF16>(p, st);
+  }
+}
+
 }  // namespace ss

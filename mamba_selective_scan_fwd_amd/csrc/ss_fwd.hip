@@ -34,6 +34,9 @@
 
 namespace ss {
 
+hipError_t launch_carry(const float* aggP, const float* aggS, float* carry, int64_t nch, int32_t nchunks,
+                        bool reverse, hipStream_t st);
+
 namespace {
 
 constexpr int kBCStride = kTile + 4;  // padded LDS row of a B/C tile (floats)
@@ -348,13 +351,16 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   }
 }
 
-// Entry state of every chunk: an exclusive scan over the chunk pairs (P, S)
-// of one channel.  256 threads per channel: thread (n, g) serially combines
-// the chunks [g*per, (g+1)*per) of state n, the 16 groups of a state (one
-// DPP row) are then scanned with shuffles, and each group replays its
-// chunks from its exclusive prefix.
+// Entry value of every chunk: an exclusive scan over the chunk pairs (P, S)
+// of one channel, left to right (forward states) or right to left (the
+// backward's carried state gradient, reverse = 1: chunk c is visited as
+// K-1-c).  256 threads per channel: thread (n, g) serially combines the
+// chunks [g*per, (g+1)*per) of state n, the 16 groups of a state (one DPP
+// row) are then scanned with shuffles, and each group replays its chunks
+// from its exclusive prefix.
 __global__ void __launch_bounds__(256) ss_carry_kernel(const float* __restrict__ aggP, const float* __restrict__ aggS,
-                                                       float* __restrict__ carry, int64_t nch, int32_t nchunks) {
+                                                       float* __restrict__ carry, int64_t nch, int32_t nchunks,
+                                                       int32_t reverse) {
   const int tid = threadIdx.x;
   const int n = tid / 16, g = tid % 16;
   const int64_t ch = blockIdx.x;
@@ -363,13 +369,14 @@ __global__ void __launch_bounds__(256) ss_carry_kernel(const float* __restrict__
   const int c0 = g * per;
   const int c1 = c0 + per < nchunks ? c0 + per : nchunks;
   const int64_t base = ch * nchunks;
+  auto slot = [&](int c) { return (base + (reverse ? nchunks - 1 - c : c)) * kStates + n; };
 
-  // local pair over [c0, c1): applying it maps the state entering c0 to the
-  // state leaving c1 - 1
+  // local pair over [c0, c1): applying it maps the value entering c0 to the
+  // value leaving c1 - 1
   float P = 1.0f, S = 0.0f;
   for (int c = c0; c < c1; ++c) {
-    const float pc = aggP[(base + c) * kStates + n];
-    const float sc = aggS[(base + c) * kStates + n];
+    const float pc = aggP[slot(c)];
+    const float sc = aggS[slot(c)];
     S = fmaf(pc, S, sc);
     P *= pc;
   }
@@ -387,8 +394,8 @@ __global__ void __launch_bounds__(256) ss_carry_kernel(const float* __restrict__
   float E = __shfl_up(S, 1, 16);
   if (g == 0) E = 0.0f;
   for (int c = c0; c < c1; ++c) {
-    carry[(base + c) * kStates + n] = E;
-    E = fmaf(aggP[(base + c) * kStates + n], E, aggS[(base + c) * kStates + n]);
+    carry[slot(c)] = E;
+    E = fmaf(aggP[slot(c)], E, aggS[slot(c)]);
   }
 }
 
@@ -444,9 +451,7 @@ hipError_t launch_fwd_variant(const FwdParams& p, int64_t nchunks, hipStream_t s
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // pass 2: entry states
-    hipLaunchKernelGGL(ss_carry_kernel, dim3((uint32_t)(p.batch * p.dim)), dim3(256), 0, st, p.aggP, p.aggS,
-                       p.carry, p.batch * p.dim, p.nchunks);
-    e = hipGetLastError();
+    e = launch_carry(p.aggP, p.aggS, p.carry, p.batch * p.dim, p.nchunks, false, st);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, true, PAIR>), dim3((uint32_t)(blocks_per_chunk * nchunks)),
@@ -486,6 +491,13 @@ hipError_t launch_step(const StepParams& p, hipStream_t st) {
     case SS_F16: return launch_step_io<SS_F16>(p, st);
     default: return launch_step_io<SS_BF16>(p, st);
   }
+}
+
+hipError_t launch_carry(const float* aggP, const float* aggS, float* carry, int64_t nch, int32_t nchunks,
+                        bool reverse, hipStream_t st) {
+  hipLaunchKernelGGL(ss_carry_kernel, dim3((uint32_t)nch), dim3(256), 0, st, aggP, aggS, carry, nch, nchunks,
+                     (int32_t)(reverse ? 1 : 0));
+  return hipGetLastError();
 }
 
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st) {
