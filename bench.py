@@ -115,11 +115,13 @@ def bench_headline(steps, warmup, stream):
     Bsz, Dd, L = sets[0]["u"].shape
     N = sets[0]["A"].shape[1]
     ys = [torch.empty((Bsz, Dd, L), dtype=torch.float16, device="cuda") for _ in range(3)]
+    lasts = [torch.empty((Bsz, Dd, N), dtype=torch.float32, device="cuda") for _ in range(3)]
+    calls = [ss.FwdCall(g["u"], g["delta"], g["A"], g["Bm"], g["Cm"], D=g["D"], z=g["z"], delta_bias=g["bias"],
+                        delta_softplus=True, y=ys[r], last_state=lasts[r], stream=stream)
+             for r, g in enumerate(sets)]
 
     def step(i):
-        g = sets[i % 3]
-        ss.fwd(g["u"], g["delta"], g["A"], g["Bm"], g["Cm"], D=g["D"], z=g["z"], delta_bias=g["bias"],
-               delta_softplus=True, y=ys[i % 3])
+        calls[i % 3]()
 
     for i in range(warmup):
         step(i)
@@ -134,21 +136,27 @@ def bench_rows(stream):
     rows = {}
     # long sequence, few channels (time-chunked), fp32
     p1 = dev_problem(inputs.make_config(1))
-    f1 = lambda i: ss.fwd(p1["u"], p1["delta"], p1["A"], p1["Bm"], p1["Cm"], D=p1["D"], z=p1["z"],
-                          delta_bias=p1["bias"])
+    y1 = torch.empty_like(p1["u"])
+    s1 = torch.empty((1, 16, 16), dtype=torch.float32, device="cuda")
+    c1 = ss.FwdCall(p1["u"], p1["delta"], p1["A"], p1["Bm"], p1["Cm"], D=p1["D"], z=p1["z"],
+                    delta_bias=p1["bias"], y=y1, last_state=s1, stream=stream)
+    f1 = lambda i: c1()
     f1(0)
     ms = timed(f1, 20, stream)
     tc = 1 * 16 * 32768
     rows["fwd_long_B1_D16_L32768_f32"] = {"ms": ms, "token_channel_per_s": tc / (ms * 1e-3),
                                           "tokens_per_s": 32768 / (ms * 1e-3)}
-    del p1
+    del p1, c1, y1
     # ragged mamba-2.8b layer, bf16
     prob3 = inputs.make_config(3)
     lens = prob3["lengths"].tolist()
     p3 = dev_problem(prob3)
     del prob3
-    f3 = lambda i: ss.fwd(p3["u"], p3["delta"], p3["A"], p3["Bm"], p3["Cm"], D=p3["D"], z=p3["z"],
-                          delta_bias=p3["bias"], lengths=p3["lengths"])
+    y3 = torch.empty_like(p3["u"])
+    s3 = torch.empty((4, 5120, 16), dtype=torch.float32, device="cuda")
+    c3 = ss.FwdCall(p3["u"], p3["delta"], p3["A"], p3["Bm"], p3["Cm"], D=p3["D"], z=p3["z"],
+                    delta_bias=p3["bias"], lengths=p3["lengths"], y=y3, last_state=s3, stream=stream)
+    f3 = lambda i: c3()
     f3(0)
     ms = timed(f3, 10, stream)
     byt = fwd_alg_bytes(4, 5120, 16, 8192, 2, lengths=lens)
@@ -156,7 +164,7 @@ def bench_rows(stream):
         "ms": ms, "lengths": lens, "token_channel_per_s": sum(lens) * 5120 / (ms * 1e-3),
         "alg_GBps": byt / (ms * 1e-3) / 1e9, "hbm_frac": byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "alu_frac": fwd_alg_slots(4, 5120, 16, 8192, 2, lens) / (ms * 1e-3) / PEAK_SLOTS}
-    del p3
+    del p3, c3, y3
     # decode: 64 single steps on the mamba-130m state
     prob2 = inputs.make_config(2, decode_steps=64)
     g2 = dev_problem(prob2)
