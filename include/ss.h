@@ -32,8 +32,8 @@
  * README: data in half, weights in float, fp32 scan accumulation).  Outputs
  * in fp16/bf16 are rounded to nearest-even.
  *
- * Limits: 1 <= dstate <= 16; batch, dim, seqlen >= 1; every pointer 16-byte
- * aligned (SS_ERR_MISALIGNED otherwise).  Any finite A is accepted; A > 0
+ * Limits: 1 <= dstate <= 16; batch, dim >= 1; 1 <= seqlen <= 2^24; every
+ * pointer 16-byte aligned (SS_ERR_MISALIGNED otherwise).  Any finite A is accepted; A > 0
  * makes the state grow and may overflow.
  */
 #ifndef SS_H

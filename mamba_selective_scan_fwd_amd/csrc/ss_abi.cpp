@@ -17,6 +17,7 @@ constexpr int64_t kChPerBlock = 16;
 // below this many wavefronts a forward splits the time axis into chunks
 constexpr int64_t kTargetWaves = 1024;
 constexpr int64_t kMaxGrid = (int64_t)1 << 31;
+constexpr int64_t kMaxSeqlen = (int64_t)1 << 24;
 
 bool aligned(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
@@ -30,7 +31,9 @@ ss_status check_problem(const ss_problem* p, bool need_seqlen) {
   if (p->io_dtype != SS_F32 && p->io_dtype != SS_F16 && p->io_dtype != SS_BF16) return SS_ERR_BAD_DTYPE;
   // keep every element index far from int64 overflow and grids within 2^31 blocks
   const int64_t lim = (int64_t)1 << 40;
-  if (p->batch > lim || p->dim > lim || (need_seqlen && p->seqlen > lim)) return SS_ERR_BAD_SHAPE;
+  if (p->batch > lim || p->dim > lim) return SS_ERR_BAD_SHAPE;
+  // kernels address a row with 32-bit offsets
+  if (need_seqlen && p->seqlen > kMaxSeqlen) return SS_ERR_BAD_SHAPE;
   const double ch = (double)p->batch * (double)p->dim;
   if (ch * (double)(need_seqlen ? p->seqlen : 1) * kMaxDstate > 9.0e18) return SS_ERR_BAD_SHAPE;
   if (ch / kChPerBlock * 2.0 > (double)kMaxGrid) return SS_ERR_BAD_SHAPE;

@@ -101,12 +101,18 @@ __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(
 // softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|).  log1p(e) for
 // e in (0, 1] uses the w = 1 + e correction log(w) * e / (w - 1), which keeps
 // full relative accuracy when e is tiny (w - 1 is exact there).
+//
+// When e < 2^-24, w rounds to 1 and log(w) = 0: the result then drops e,
+// which is below fp32 resolution of the result for x > 0 and below 6e-8 in
+// absolute terms for x < 0.  w - 1 is clamped away from 0 so that 0 * inf
+// never occurs.
 __device__ __forceinline__ float softplus_f(float x) {
-  float e = exp2_hw(-fabsf(x) * kLog2e);
-  float w = 1.0f + e;
-  float wm1 = w - 1.0f;
-  float lp = (wm1 == 0.0f) ? e : (log2_hw(w) * kLn2) * (e * rcp_hw(wm1));
-  return fmaxf(x, 0.0f) + lp;
+  const float e = exp2_hw(-fabsf(x) * kLog2e);
+  const float w = 1.0f + e;
+  const float wm1r = w - 1.0f;
+  const float wm1 = wm1r > 1e-30f ? wm1r : 1e-30f;
+  const float l2 = log2_hw(w) * (e * rcp_hw(wm1));  // log2(1 + e)
+  return fmaf(kLn2, l2, x > 0.0f ? x : 0.0f);
 }
 
 // d softplus / dx = sigmoid(x)

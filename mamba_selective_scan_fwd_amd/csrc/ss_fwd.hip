@@ -39,14 +39,15 @@ hipError_t launch_carry(const float* aggP, const float* aggS, float* carry, int6
 
 namespace {
 
-constexpr int kBCStride = kTile + 4;  // padded LDS row of a B/C tile (floats)
-constexpr int kPRow = 20;             // padded LDS row of the readout tile (16 states + 4)
-constexpr int kPChan = 16 * kPRow + 16;  // per-channel readout tile; 336 = 16 mod 64 banks
+constexpr int kBCStride = kTile + 4;     // padded LDS row of the B tile (floats)
+constexpr int kCTRow = 20;               // padded LDS row of the transposed C tile
+constexpr int kPRow = 20;                // padded LDS row of the state tile (16 states + 4)
+constexpr int kPChan = 16 * kPRow + 16;  // per-channel state tile; 336 = 16 mod 64 banks
 
 struct FwdSmem {
-  float B[2][kStates][kBCStride];
-  float C[2][kStates][kBCStride];
-  float P[kWaves][kChPerWave * kPChan];
+  float B[2][kStates][kBCStride];        // B[n][t], read by the state lanes
+  float CT[2][kTile][kCTRow];            // C[t][n], read by the lane that owns step t
+  float P[kWaves][kChPerWave * kPChan];  // h_t[n] of 16 steps, per channel
 };
 
 // Per-lane registers of the four steps this lane owns in a 64-step tile.
@@ -55,7 +56,6 @@ struct Owned {
   float dtu[4];  // Delta_t * u_t (0 for masked steps)
   float u[4];
   float z[4];
-  bool valid[4];
 };
 
 // Raw element bits of the owned steps of the next tile: loaded one tile
@@ -75,8 +75,7 @@ struct Views {
 };
 
 template <int IO>
-__device__ __forceinline__ void load_owned(RawOwned<IO>& r, const Views& v, uint32_t lane_elem0, int64_t t0,
-                                           int l) {
+__device__ __forceinline__ void load_owned(RawOwned<IO>& r, const Views& v, uint32_t lane_elem0, int t0, int l) {
   constexpr uint32_t s = io_bytes<IO>();
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -100,7 +99,7 @@ struct BCRaw {
 };
 
 template <int IO, bool PAIR>
-__device__ __forceinline__ void load_bc(BCRaw<IO, PAIR>& r, const Views& v, uint32_t seqlen, int64_t t0, int tid,
+__device__ __forceinline__ void load_bc(BCRaw<IO, PAIR>& r, const Views& v, uint32_t seqlen, int t0, int tid,
                                         bool need_c) {
   constexpr uint32_t s = io_bytes<IO>();
   const int n = tid / 16, j = tid % 16;
@@ -118,38 +117,41 @@ __device__ __forceinline__ void load_bc(BCRaw<IO, PAIR>& r, const Views& v, uint
   }
 }
 
-// B/C of steps at or past the valid end are staged as exact zeros, so data
-// past a row's length (padding, NaN) never reaches the state.
+// B (row-major, for the state lanes) and C (transposed, for the step owners)
+// of steps at or past the valid end are staged as exact zeros, so data past a
+// row's length (padding, NaN) never reaches the state or the output.
 template <int IO, bool PAIR>
-__device__ __forceinline__ void store_bc(FwdSmem& sm, int buf, const BCRaw<IO, PAIR>& r, int tid, int64_t t0,
-                                         int64_t t_valid_end, int64_t dstate) {
+__device__ __forceinline__ void store_bc(FwdSmem& sm, int buf, const BCRaw<IO, PAIR>& r, int tid, int nvalid,
+                                         bool n_ok, bool with_c) {
   const int n = tid / 16, j = tid % 16;
-  const bool n_ok = n < dstate;
 #pragma unroll
   for (int k = 0; k < BCRaw<IO, PAIR>::kN; ++k) {
     if constexpr (PAIR) {
       const int e = 32 * k + 2 * j;
-      const bool ok0 = n_ok && t0 + e < t_valid_end, ok1 = n_ok && t0 + e + 1 < t_valid_end;
+      const bool ok0 = n_ok && e < nvalid, ok1 = n_ok && e + 1 < nvalid;
       const float b0 = bits_f32<IO>((raw_t<IO>)(r.b[k] & 0xffffu)), b1 = bits_f32<IO>((raw_t<IO>)(r.b[k] >> 16));
-      const float c0 = bits_f32<IO>((raw_t<IO>)(r.c[k] & 0xffffu)), c1 = bits_f32<IO>((raw_t<IO>)(r.c[k] >> 16));
       *reinterpret_cast<float2*>(&sm.B[buf][n][e]) = make_float2(ok0 ? b0 : 0.0f, ok1 ? b1 : 0.0f);
-      *reinterpret_cast<float2*>(&sm.C[buf][n][e]) = make_float2(ok0 ? c0 : 0.0f, ok1 ? c1 : 0.0f);
+      if (with_c) {
+        const float c0 = bits_f32<IO>((raw_t<IO>)(r.c[k] & 0xffffu)), c1 = bits_f32<IO>((raw_t<IO>)(r.c[k] >> 16));
+        sm.CT[buf][e][n] = ok0 ? c0 : 0.0f;
+        sm.CT[buf][e + 1][n] = ok1 ? c1 : 0.0f;
+      }
     } else {
       const int e = j + 16 * k;
-      const bool ok = n_ok && t0 + e < t_valid_end;
+      const bool ok = n_ok && e < nvalid;
       sm.B[buf][n][e] = ok ? bits_f32<IO>(r.b[k]) : 0.0f;
-      sm.C[buf][n][e] = ok ? bits_f32<IO>(r.c[k]) : 0.0f;
+      if (with_c) sm.CT[buf][e][n] = ok ? bits_f32<IO>(r.c[k]) : 0.0f;
     }
   }
 }
 
+// Per-(t, d) work of the four owned steps: Delta, Delta*u (zero when masked).
 template <int IO>
-__device__ __forceinline__ void prep_owned(Owned& o, const RawOwned<IO>& r, int64_t t0, int l, float bias,
-                                           bool softplus, int64_t t_valid_end, float& dt_sum) {
+__device__ __forceinline__ void prep_owned(Owned& o, const RawOwned<IO>& r, int l, int nvalid, float bias,
+                                           bool softplus, float& dt_sum) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t t = t0 + 16 * i + l;
-    const bool v = t < t_valid_end;
+    const bool v = 16 * i + l < nvalid;
     const float u = bits_f32<IO>(r.u[i]);
     const float x = bits_f32<IO>(r.dl[i]) + bias;
     float dt = softplus ? softplus_f(x) : x;
@@ -158,33 +160,31 @@ __device__ __forceinline__ void prep_owned(Owned& o, const RawOwned<IO>& r, int6
     o.dtu[i] = v ? dt * u : 0.0f;
     o.u[i] = u;
     o.z[i] = bits_f32<IO>(r.z[i]);
-    o.valid[i] = v;
     dt_sum += dt;
   }
 }
 
-// 16 steps of block I of the tile.  Lane (c, n): h is its state; the readout
-// products of the 16 steps are left in the wave's LDS tile.
+// 16 steps of block I of the tile.  Lane (c, n) advances state n of channel c
+// and (FINAL) leaves h_t[n] in column n of the channel's LDS state tile.  The
+// block's 16 B values are read into registers up front, so no LDS wait sits
+// between two steps of the recurrence.
 template <int I, bool FINAL, int... J>
-__device__ __forceinline__ void scan_block(float& h, const Owned& o, float A2, const float* sBrow,
-                                           const float* sCrow, float* pcol, std::integer_sequence<int, J...>) {
-  float4 b4, c4;
+__device__ __forceinline__ void scan_block(float& h, const Owned& o, float A2, const float* sBrow, float* pcol,
+                                           std::integer_sequence<int, J...>) {
+  float bq[16];
+  *reinterpret_cast<float4*>(&bq[0]) = *reinterpret_cast<const float4*>(sBrow + 16 * I + 0);
+  *reinterpret_cast<float4*>(&bq[4]) = *reinterpret_cast<const float4*>(sBrow + 16 * I + 4);
+  *reinterpret_cast<float4*>(&bq[8]) = *reinterpret_cast<const float4*>(sBrow + 16 * I + 8);
+  *reinterpret_cast<float4*>(&bq[12]) = *reinterpret_cast<const float4*>(sBrow + 16 * I + 12);
   (
       [&] {
-        constexpr int s = 16 * I + J;
-        if constexpr (J % 4 == 0) {
-          b4 = *reinterpret_cast<const float4*>(sBrow + s);
-          if constexpr (FINAL) c4 = *reinterpret_cast<const float4*>(sCrow + s);
-        }
-        const float bj = (J % 4 == 0) ? b4.x : (J % 4 == 1) ? b4.y : (J % 4 == 2) ? b4.z : b4.w;
         const float a = exp2_hw(row_bcast<J>(o.dt[I]) * A2);
-        h = fmaf(a, h, row_bcast<J>(o.dtu[I]) * bj);
-        if constexpr (FINAL) {
-          const float cj = (J % 4 == 0) ? c4.x : (J % 4 == 1) ? c4.y : (J % 4 == 2) ? c4.z : c4.w;
-          pcol[J * kPRow] = cj * h;
-        }
+        h = fmaf(a, h, row_bcast<J>(o.dtu[I]) * bq[J]);
+        if constexpr (FINAL) pcol[J * kPRow] = h;
       }(),
       ...);
+  // keep the next block's exps from being hoisted here (register pressure)
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -193,22 +193,39 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Readout, skip, gate and store of step t0 + 16 I + l (owned by this lane).
+// C[t][n] of the owned step 16 I + l (read before the block's scan, so the
+// readout waits only for the state row)
+struct CRow {
+  float4 c0, c1, c2, c3;
+};
+__device__ __forceinline__ CRow load_crow(const float* crow) {
+  CRow r;
+  r.c0 = *reinterpret_cast<const float4*>(crow + 0);
+  r.c1 = *reinterpret_cast<const float4*>(crow + 4);
+  r.c2 = *reinterpret_cast<const float4*>(crow + 8);
+  r.c3 = *reinterpret_cast<const float4*>(crow + 12);
+  return r;
+}
+
+// Readout, skip, gate and store of the owned step 16 I + l of the tile:
+// y0 = sum_n C[t][n] h_t[n] (four independent FMA chains).
 template <int IO, int I>
-__device__ __forceinline__ void finish_block(const Owned& o, const float* prow, float Dd, bool need_z,
-                                             const Views& v, uint32_t lane_elem0, int64_t t0, int l,
-                                             int64_t t_stop) {
-  const float4 r0 = *reinterpret_cast<const float4*>(prow + 0);
-  const float4 r1 = *reinterpret_cast<const float4*>(prow + 4);
-  const float4 r2 = *reinterpret_cast<const float4*>(prow + 8);
-  const float4 r3 = *reinterpret_cast<const float4*>(prow + 12);
-  const float y0 = (((r0.x + r0.y) + (r0.z + r0.w)) + ((r1.x + r1.y) + (r1.z + r1.w))) +
-                   (((r2.x + r2.y) + (r2.z + r2.w)) + ((r3.x + r3.y) + (r3.z + r3.w)));
-  float yv = fmaf(Dd, o.u[I], y0);
+__device__ __forceinline__ void finish_block(const Owned& o, const float* prow, const CRow& c, float Dd,
+                                             bool need_z, const Views& v, uint32_t elem, int l, int nvalid,
+                                             int nstop) {
+  const float4 h0 = *reinterpret_cast<const float4*>(prow + 0);
+  const float4 h1 = *reinterpret_cast<const float4*>(prow + 4);
+  const float4 h2 = *reinterpret_cast<const float4*>(prow + 8);
+  const float4 h3 = *reinterpret_cast<const float4*>(prow + 12);
+  float y0 = c.c0.x * h0.x, y1 = c.c0.y * h0.y, y2 = c.c0.z * h0.z, y3 = c.c0.w * h0.w;
+  y0 = fmaf(c.c1.x, h1.x, y0); y1 = fmaf(c.c1.y, h1.y, y1); y2 = fmaf(c.c1.z, h1.z, y2); y3 = fmaf(c.c1.w, h1.w, y3);
+  y0 = fmaf(c.c2.x, h2.x, y0); y1 = fmaf(c.c2.y, h2.y, y1); y2 = fmaf(c.c2.z, h2.z, y2); y3 = fmaf(c.c2.w, h2.w, y3);
+  y0 = fmaf(c.c3.x, h3.x, y0); y1 = fmaf(c.c3.y, h3.y, y1); y2 = fmaf(c.c3.z, h3.z, y2); y3 = fmaf(c.c3.w, h3.w, y3);
+  float yv = fmaf(Dd, o.u[I], (y0 + y1) + (y2 + y3));
   if (need_z) yv *= silu_f(o.z[I]);
-  yv = o.valid[I] ? yv : 0.0f;
-  const int64_t t = t0 + 16 * I + l;
-  const uint32_t off = t < t_stop ? (lane_elem0 + (uint32_t)t) * io_bytes<IO>() : kOffNone;
+  const int tr = 16 * I + l;
+  yv = tr < nvalid ? yv : 0.0f;
+  const uint32_t off = tr < nstop ? (elem + (uint32_t)tr) * io_bytes<IO>() : kOffNone;
   bstore<IO>(v.y, off, yv);
 }
 
@@ -238,21 +255,22 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   int64_t nch_w = p.dim - d0;
   nch_w = nch_w < 0 ? 0 : (nch_w > kChPerWave ? kChPerWave : nch_w);
 
-  int64_t len = p.seqlen;
+  // time bounds (seqlen < 2^24, so 32-bit arithmetic is exact)
+  const int L = (int)p.seqlen;
+  int len = L;
   if (p.lengths) {
-    const int64_t v = p.lengths[b];
-    len = v < 0 ? 0 : (v > p.seqlen ? p.seqlen : v);
+    const int v = p.lengths[b];
+    len = v < 0 ? 0 : (v > L ? L : v);
   }
-  const int64_t t_begin = chunk * p.chunk_len;
-  const int64_t t_stop = t_begin + p.chunk_len < p.seqlen ? t_begin + p.chunk_len : p.seqlen;
-  const int64_t t_valid_end = t_stop < len ? t_stop : len;
+  const int t_begin = (int)(chunk * p.chunk_len);
+  const int t_stop = t_begin + (int)p.chunk_len < L ? t_begin + (int)p.chunk_len : L;
+  const int t_valid_end = t_stop < len ? t_stop : len;
   // tiles that hold at least one valid step; the rest of the chunk is zero-filled
-  const int64_t t_tile_end =
+  const int t_tile_end =
       t_valid_end > t_begin ? t_begin + ((t_valid_end - t_begin + kTile - 1) / kTile) * kTile : t_begin;
 
   const bool need_z = p.z != nullptr;
   const bool softplus = p.softplus != 0;
-  const uint32_t L = (uint32_t)p.seqlen;
   const int64_t row0 = (b * p.dim + d0) * p.seqlen;  // element offset of the wave's first row
   const uint32_t wave_bytes = (uint32_t)(nch_w * p.seqlen) * s;
   Views v;
@@ -261,11 +279,13 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   const bool load_z = FINAL && need_z;
   v.z = make_rsrc(load_z ? static_cast<const char*>(p.z) + row0 * s : static_cast<const char*>(p.u),
                   load_z ? wave_bytes : 0u);
-  v.y = make_rsrc(FINAL ? static_cast<const char*>(p.y) + row0 * s : static_cast<const char*>(p.u), FINAL ? wave_bytes : 0u);
+  v.y = make_rsrc(FINAL ? static_cast<const char*>(p.y) + row0 * s : static_cast<const char*>(p.u),
+                  FINAL ? wave_bytes : 0u);
   const uint32_t bc_bytes = (uint32_t)(p.dstate * p.seqlen) * s;
   v.B = make_rsrc(static_cast<const char*>(p.Bm) + b * p.dstate * p.seqlen * s, bc_bytes);
   v.C = make_rsrc(static_cast<const char*>(p.Cm) + b * p.dstate * p.seqlen * s, bc_bytes);
-  const uint32_t lane_elem0 = (uint32_t)cw * L;
+  const uint32_t lane_elem0 = (uint32_t)cw * (uint32_t)L;
+  const bool stage_n_ok = tid / 16 < p.dstate;
 
   const float A2 = (ch_ok && n_ok) ? p.A[d * p.dstate + n] * kLog2e : 0.0f;
   const float bias = (ch_ok && p.bias) ? p.bias[d] : 0.0f;
@@ -275,7 +295,7 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   if (FINAL && chunk > 0 && p.carry && ch_ok) h = p.carry[(ch * p.nchunks + chunk) * kStates + n];
 
   float* pwave = sm.P[wave] + cw * kPChan;
-  float* pcol = pwave + n;                // column n of this channel's readout tile
+  float* pcol = pwave + n;                // column n of this channel's state tile
   const float* prow = pwave + l * kPRow;  // row l (step l of the block)
 
   float dt_sum = 0.0f;
@@ -283,63 +303,57 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   BCRaw<IO, PAIR> bcr;
   if (t_begin < t_tile_end) {
     load_owned<IO>(raw, v, lane_elem0, t_begin, l);
-    load_bc<IO, PAIR>(bcr, v, L, t_begin, tid, FINAL);
-    store_bc<IO, PAIR>(sm, 0, bcr, tid, t_begin, t_valid_end, p.dstate);
+    load_bc<IO, PAIR>(bcr, v, (uint32_t)L, t_begin, tid, FINAL);
+    store_bc<IO, PAIR>(sm, 0, bcr, tid, t_valid_end - t_begin, stage_n_ok, FINAL);
   }
   __syncthreads();
 
   int buf = 0;
-  for (int64_t t0 = t_begin; t0 < t_tile_end; t0 += kTile) {
+  for (int t0 = t_begin; t0 < t_tile_end; t0 += kTile) {
+    const int nvalid = t_valid_end - t0;  // steps of this tile that advance the state
+    const int nstop = t_stop - t0;        // steps of this tile that exist in the chunk
     Owned o;
-    prep_owned<IO>(o, raw, t0, l, bias, softplus, t_valid_end, dt_sum);
+    prep_owned<IO>(o, raw, l, nvalid, bias, softplus, dt_sum);
     if (FINAL && p.ckpt && ch_ok && n_ok) p.ckpt[(ch * p.ckpt_per_row + t0 / kTile) * p.dstate + n] = h;
 
-    const int64_t t1 = t0 + kTile;
+    const int t1 = t0 + kTile;
     const bool more = t1 < t_tile_end;
     if (more) {
       load_owned<IO>(raw, v, lane_elem0, t1, l);
-      load_bc<IO, PAIR>(bcr, v, L, t1, tid, FINAL);
+      load_bc<IO, PAIR>(bcr, v, (uint32_t)L, t1, tid, FINAL);
     }
 
     const float* sBrow = &sm.B[buf][n][0];
-    const float* sCrow = &sm.C[buf][n][0];
+    const float* sCT = &sm.CT[buf][l][0];
+    const uint32_t elem = lane_elem0 + (uint32_t)t0;
     constexpr auto seq = std::make_integer_sequence<int, 16>{};
-    scan_block<0, FINAL>(h, o, A2, sBrow, sCrow, pcol, seq);
-    if constexpr (FINAL) {
-      wave_lds_sync();
-      finish_block<IO, 0>(o, prow, Dd, need_z, v, lane_elem0, t0, l, t_stop);
-      wave_lds_sync();
+#define SS_BLOCK(I)                                                                          \
+    {                                                                                        \
+      CRow cr;                                                                               \
+      if constexpr (FINAL) cr = load_crow(sCT + 16 * (I) * kCTRow);                          \
+      scan_block<I, FINAL>(h, o, A2, sBrow, pcol, seq);                                      \
+      if constexpr (FINAL) {                                                                 \
+        wave_lds_sync();                                                                     \
+        finish_block<IO, I>(o, prow, cr, Dd, need_z, v, elem, l, nvalid, nstop);             \
+        wave_lds_sync();                                                                     \
+      }                                                                                      \
     }
-    scan_block<1, FINAL>(h, o, A2, sBrow, sCrow, pcol, seq);
-    if constexpr (FINAL) {
-      wave_lds_sync();
-      finish_block<IO, 1>(o, prow, Dd, need_z, v, lane_elem0, t0, l, t_stop);
-      wave_lds_sync();
-    }
-    scan_block<2, FINAL>(h, o, A2, sBrow, sCrow, pcol, seq);
-    if constexpr (FINAL) {
-      wave_lds_sync();
-      finish_block<IO, 2>(o, prow, Dd, need_z, v, lane_elem0, t0, l, t_stop);
-      wave_lds_sync();
-    }
-    scan_block<3, FINAL>(h, o, A2, sBrow, sCrow, pcol, seq);
-    if constexpr (FINAL) {
-      wave_lds_sync();
-      finish_block<IO, 3>(o, prow, Dd, need_z, v, lane_elem0, t0, l, t_stop);
-      wave_lds_sync();
-    }
+    SS_BLOCK(0)
+    SS_BLOCK(1)
+    SS_BLOCK(2)
+    SS_BLOCK(3)
+#undef SS_BLOCK
 
-    if (more) store_bc<IO, PAIR>(sm, buf ^ 1, bcr, tid, t1, t_valid_end, p.dstate);
+    if (more) store_bc<IO, PAIR>(sm, buf ^ 1, bcr, tid, t_valid_end - t1, stage_n_ok, FINAL);
     __syncthreads();
     buf ^= 1;
   }
 
   if (FINAL) {
     // steps past the row's length: y = 0, checkpoints hold the frozen state
-    for (int64_t t = t_tile_end + l; t < t_stop; t += 16)
-      bstore<IO>(v.y, (lane_elem0 + (uint32_t)t) * s, 0.0f);
+    for (int t = t_tile_end + l; t < t_stop; t += 16) bstore<IO>(v.y, (lane_elem0 + (uint32_t)t) * s, 0.0f);
     if (p.ckpt && ch_ok && n_ok)
-      for (int64_t t0 = t_tile_end; t0 < t_stop; t0 += kTile)
+      for (int t0 = t_tile_end; t0 < t_stop; t0 += kTile)
         p.ckpt[(ch * p.ckpt_per_row + t0 / kTile) * p.dstate + n] = h;
     if (p.last_state && ch_ok && n_ok && chunk == p.nchunks - 1) p.last_state[ch * p.dstate + n] = h;
   } else if (ch_ok) {
