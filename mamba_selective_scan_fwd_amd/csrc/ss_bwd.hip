@@ -20,13 +20,15 @@
 //         entering every chunk from the right (ss_carry_kernel, reversed);
 //   MAIN  per chunk: recompute h over the chunk into 65 registers per lane,
 //         walk it backwards with the true carried gradient, emit du, ddelta,
-//         dz, accumulate dB/dC in LDS and dA/dD/dbias partials;
+//         dz, accumulate dB/dC and dA/dD/dbias partials;
 //   REDUCE sum the dA/dD/dbias partials over (batch row, chunk).
 // Lane layout as the forward: a wavefront holds 4 channels x 16 states; the
 // per-(t, d) work is owned by lane l = t mod 16 of the channel's row and
 // broadcast with DPP; sums over states go through an LDS transpose; sums over
-// channels (dB, dC) go through LDS float atomics and then one global atomic
-// per element per workgroup.
+// channels (dB, dC) go through a [step][state][channel] LDS tile per wave,
+// whose 4-channel sums each lane accumulates in registers over the
+// workgroup's channel loop, then one cross-wave sum and one global atomic per
+// element per workgroup (LDS float atomics serialise on gfx950).
 #include <type_traits>
 
 #include "ss_device.h"
@@ -40,17 +42,26 @@ hipError_t launch_carry(const float* aggP, const float* aggS, float* carry, int6
 namespace {
 
 constexpr int kBCStride = kTile + 4;
-constexpr int kPRow = 20;
-constexpr int kPChan = 16 * kPRow + 16;
+// Sum-over-states tiles: per channel 16 steps x 16 states, element (j, n) at
+// j*16 + 4*((n>>2) ^ ((j>>2)&3)) + (n&3) (a swizzle that keeps both the
+// per-step writes and the per-row reads free of bank conflicts); channels
+// 272 floats apart (16 banks).
+constexpr int kSChan = 16 * 16 + 16;
+// Sum-over-channels tiles: per wave [16 steps][16 states][4 channels].
+constexpr int kCTile = 16 * 16 * kChPerWave;
 
 struct BwdSmem {
   float B[kStates][kBCStride];
   float C[kStates][kBCStride];
-  float T1[kWaves][kChPerWave * kPChan];
-  float T2[kWaves][kChPerWave * kPChan];
-  float dB[kStates][kBCStride];
-  float dC[kStates][kBCStride];
+  float T1[kWaves][kChPerWave * kSChan];  // G B, summed over states per step
+  float T2[kWaves][kChPerWave * kSChan];  // A G a h_{t-1}, summed over states per step
+  float T3[kWaves][kCTile];               // G Delta u, summed over channels per (step, state)
+  float T4[kWaves][kCTile];               // dy0 h_t, summed over channels per (step, state)
 };
+static_assert(sizeof(float) * 2 * kWaves * kChPerWave * kSChan >= sizeof(float) * 2 * kWaves * kTile * kStates,
+              "the sum-over-states tiles double as the cross-wave staging of dB/dC");
+
+__device__ __forceinline__ int swz(int j, int n) { return j * 16 + 4 * ((n >> 2) ^ ((j >> 2) & 3)) + (n & 3); }
 
 // values of the 4 steps t0 + 16 i + l this lane owns
 struct BwdOwned {
@@ -73,11 +84,15 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ float row16_sum(const float* row) {
-  const float4 r0 = *reinterpret_cast<const float4*>(row + 0);
-  const float4 r1 = *reinterpret_cast<const float4*>(row + 4);
-  const float4 r2 = *reinterpret_cast<const float4*>(row + 8);
-  const float4 r3 = *reinterpret_cast<const float4*>(row + 12);
+// sum of row l of a swizzled tile (the four 16-byte groups are read in a
+// lane-dependent order so that lanes l, l+4, l+8, l+12 hit different banks)
+__device__ __forceinline__ float row16_sum(const float* tile, int l) {
+  const float* row = tile + l * 16;
+  const int x = (l >> 2) & 3;
+  const float4 r0 = *reinterpret_cast<const float4*>(row + 4 * (0 ^ x));
+  const float4 r1 = *reinterpret_cast<const float4*>(row + 4 * (1 ^ x));
+  const float4 r2 = *reinterpret_cast<const float4*>(row + 4 * (2 ^ x));
+  const float4 r3 = *reinterpret_cast<const float4*>(row + 4 * (3 ^ x));
   return (((r0.x + r0.y) + (r0.z + r0.w)) + ((r1.x + r1.y) + (r1.z + r1.w))) +
          (((r2.x + r2.y) + (r2.z + r2.w)) + ((r3.x + r3.y) + (r3.z + r3.w)));
 }
@@ -152,46 +167,83 @@ __device__ __forceinline__ void agg_block(float& g, const BwdOwned& o, float A2,
         g = G * a;
       }(),
       ...);
+  __builtin_amdgcn_sched_barrier(0);  // no hoisting across blocks (registers)
 }
 
 // ---- MAIN: forward recompute of block I (states into hs) ---------------------
 template <int I, bool WITH_Y, int... J>
 __device__ __forceinline__ void fwd_block(float (&hs)[kTile + 1], const BwdOwned& o, float A2, const float* sBrow,
-                                          const float* sCrow, float* t1col, std::integer_sequence<int, J...>) {
+                                          const float* sCrow, float* t1c, int n, std::integer_sequence<int, J...>) {
+  float4 b4, c4;
   (
       [&] {
         constexpr int s = 16 * I + J;
+        if constexpr (J % 4 == 0) {
+          b4 = *reinterpret_cast<const float4*>(sBrow + s);
+          if constexpr (WITH_Y) c4 = *reinterpret_cast<const float4*>(sCrow + s);
+        }
+        const float bj = (J % 4 == 0) ? b4.x : (J % 4 == 1) ? b4.y : (J % 4 == 2) ? b4.z : b4.w;
         const float a = exp2_hw(row_bcast<J>(o.dt[I]) * A2);
-        const float h = fmaf(a, hs[s], row_bcast<J>(o.dtu[I]) * sBrow[s]);
+        const float h = fmaf(a, hs[s], row_bcast<J>(o.dtu[I]) * bj);
         hs[s + 1] = h;
-        if constexpr (WITH_Y) t1col[J * kPRow] = sCrow[s] * h;
+        if constexpr (WITH_Y) {
+          const float cj = (J % 4 == 0) ? c4.x : (J % 4 == 1) ? c4.y : (J % 4 == 2) ? c4.z : c4.w;
+          t1c[swz(J, n)] = cj * h;
+        }
       }(),
       ...);
+  __builtin_amdgcn_sched_barrier(0);  // no hoisting across blocks (registers)
 }
 
 // ---- MAIN: reverse walk of block I -------------------------------------------
+// Per step: the per-state terms G B and A G a h_{t-1} go to the sum-over-states
+// tiles (their row sums give du and dDelta), the per-channel terms G Delta u
+// and dy0 h_t to the sum-over-channels tiles (dB and dC).
 template <int I, int... J>
 __device__ __forceinline__ void bwd_block(float& g, float& dA_acc, const float (&hs)[kTile + 1], const BwdOwned& o,
-                                          float A2, float Anat, const float* sBrow, const float* sCrow, float* dBrow,
-                                          float* dCrow, float* t1col, float* t2col,
+                                          float A2, float Anat, const float* sBrow, const float* sCrow, float* t1c,
+                                          float* t2c, float* t3w, float* t4w, int n, int cw,
                                           std::integer_sequence<int, J...>) {
+  float4 b4, c4;
   (
       [&] {
         constexpr int jj = 15 - J;
         constexpr int s = 16 * I + jj;
+        if constexpr (jj % 4 == 3) {  // steps s-3..s, read when the walk enters them
+          b4 = *reinterpret_cast<const float4*>(sBrow + s - 3);
+          c4 = *reinterpret_cast<const float4*>(sCrow + s - 3);
+        }
+        const float bqj = (jj % 4 == 0) ? b4.x : (jj % 4 == 1) ? b4.y : (jj % 4 == 2) ? b4.z : b4.w;
+        const float cqj = (jj % 4 == 0) ? c4.x : (jj % 4 == 1) ? c4.y : (jj % 4 == 2) ? c4.z : c4.w;
         const float dtb = row_bcast<jj>(o.dt[I]);
         const float dy0b = row_bcast<jj>(o.dy0[I]);
         const float a = exp2_hw(dtb * A2);
-        const float gh = fmaf(dy0b, sCrow[s], g);  // dLoss/dh_t
-        atomicAdd(dCrow + s, dy0b * hs[s + 1]);
-        atomicAdd(dBrow + s, gh * row_bcast<jj>(o.dtu[I]));
-        t1col[jj * kPRow] = gh * sBrow[s];
+        const float gh = fmaf(dy0b, cqj, g);  // dLoss/dh_t
+        t4w[(jj * 16 + n) * kChPerWave + cw] = dy0b * hs[s + 1];
+        t3w[(jj * 16 + n) * kChPerWave + cw] = gh * row_bcast<jj>(o.dtu[I]);
+        t1c[swz(jj, n)] = gh * bqj;
         g = gh * a;                                 // to h_{t-1}
         const float q = g * hs[s];                  // gh * a * h_{t-1}
-        t2col[jj * kPRow] = q * Anat;
+        t2c[swz(jj, n)] = q * Anat;
         dA_acc = fmaf(q, dtb, dA_acc);
       }(),
       ...);
+  __builtin_amdgcn_sched_barrier(0);  // no hoisting across blocks (registers)
+}
+
+// Sum of the wave's 4 channel rows for the (step, state) pairs this lane
+// collects: step (lane>>4) + 4q, state lane&15, q < 4.
+template <int I>
+__device__ __forceinline__ void collect_block(float (&accB)[4][4], float (&accC)[4][4], const float* t3w,
+                                              const float* t4w, int lane) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int jj = (lane >> 4) + 4 * q, sn = lane & 15;
+    const float4 b4 = *reinterpret_cast<const float4*>(t3w + (jj * 16 + sn) * kChPerWave);
+    const float4 c4 = *reinterpret_cast<const float4*>(t4w + (jj * 16 + sn) * kChPerWave);
+    accB[I][q] += (b4.x + b4.y) + (b4.z + b4.w);
+    accC[I][q] += (c4.x + c4.y) + (c4.z + c4.w);
+  }
 }
 
 template <int IO, bool MAIN>
@@ -232,23 +284,22 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
       const float cv = bits_f32<IO>(bload<IO>(rC, off));
       sm.B[sn][e] = ok ? bv : 0.0f;
       sm.C[sn][e] = ok ? cv : 0.0f;
-      if (MAIN) {
-        sm.dB[sn][e] = 0.0f;
-        sm.dC[sn][e] = 0.0f;
-      }
     }
   }
   __syncthreads();
 
   const float* sBrow = &sm.B[n][0];
   const float* sCrow = &sm.C[n][0];
-  float* t1w = sm.T1[wave] + cw * kPChan;
-  float* t2w = sm.T2[wave] + cw * kPChan;
-  float* t1col = t1w + n;
-  float* t2col = t2w + n;
-  const float* t1row = t1w + l * kPRow;
-  const float* t2row = t2w + l * kPRow;
+  float* t1c = sm.T1[wave] + cw * kSChan;  // this channel's sum-over-states tiles
+  float* t2c = sm.T2[wave] + cw * kSChan;
+  float* t3w = sm.T3[wave];
+  float* t4w = sm.T4[wave];
   constexpr auto seq = std::make_integer_sequence<int, 16>{};
+  float accB[4][4], accC[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) accB[i][q] = accC[i][q] = 0.0f;
 
   const int64_t cb_begin = grp * per_group;
   int64_t cb_end = cb_begin + per_group;
@@ -299,9 +350,9 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
       hs[0] = (ch_ok && n_ok) ? p.ckpt[(ch * K + k) * p.dstate + n] : 0.0f;
       if (need_z) {
 #define SS_FWD_Y(I)                                                        \
-  fwd_block<I, true>(hs, o, A2, sBrow, sCrow, t1col, seq);                 \
+  fwd_block<I, true>(hs, o, A2, sBrow, sCrow, t1c, n, seq);                \
   wave_lds_sync();                                                         \
-  o.y0[I] = fmaf(Dd, o.u[I], row16_sum(t1row));                            \
+  o.y0[I] = fmaf(Dd, o.u[I], row16_sum(t1c, l));                           \
   wave_lds_sync();
         SS_FWD_Y(0)
         SS_FWD_Y(1)
@@ -309,22 +360,21 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
         SS_FWD_Y(3)
 #undef SS_FWD_Y
       } else {
-        fwd_block<0, false>(hs, o, A2, sBrow, sCrow, t1col, seq);
-        fwd_block<1, false>(hs, o, A2, sBrow, sCrow, t1col, seq);
-        fwd_block<2, false>(hs, o, A2, sBrow, sCrow, t1col, seq);
-        fwd_block<3, false>(hs, o, A2, sBrow, sCrow, t1col, seq);
+        fwd_block<0, false>(hs, o, A2, sBrow, sCrow, t1c, n, seq);
+        fwd_block<1, false>(hs, o, A2, sBrow, sCrow, t1c, n, seq);
+        fwd_block<2, false>(hs, o, A2, sBrow, sCrow, t1c, n, seq);
+        fwd_block<3, false>(hs, o, A2, sBrow, sCrow, t1c, n, seq);
       }
 
       float g = (k < K - 1 && ch_ok) ? p.gcarry[wslot] : 0.0f;
       float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
-      float* dBrow = &sm.dB[n][0];
-      float* dCrow = &sm.dC[n][0];
 #define SS_BWD(I)                                                                                   \
   {                                                                                                 \
-    bwd_block<I>(g, dA_acc, hs, o, A2, A, sBrow, sCrow, dBrow, dCrow, t1col, t2col, seq);           \
+    bwd_block<I>(g, dA_acc, hs, o, A2, A, sBrow, sCrow, t1c, t2c, t3w, t4w, n, cw, seq);            \
     wave_lds_sync();                                                                                \
-    const float sGB = row16_sum(t1row);                                                             \
-    const float sQA = row16_sum(t2row);                                                             \
+    const float sGB = row16_sum(t1c, l);                                                            \
+    const float sQA = row16_sum(t2c, l);                                                            \
+    collect_block<I>(accB, accC, t3w, t4w, lane);                                                   \
     const float du = fmaf(o.dt[I], sGB, o.dy0[I] * Dd);                                             \
     const float dD = fmaf(o.u[I], sGB, sQA);                                                        \
     float dx = softplus ? dD * sigmoid_f(o.x[I]) : dD;                                              \
@@ -360,17 +410,33 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
   }
 
   if constexpr (MAIN) {
+    // sum the four waves' channel sums, then one global add per element
     __syncthreads();
-    const int sn = tid / 16, j = tid % 16;
-    if (sn < p.dstate) {
+    float* stB = &sm.T1[0][0];                      // [wave][64 steps][16 states]
+    float* stC = stB + kWaves * kTile * kStates;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int e = j + 16 * q;
-        if (t0 + e < t_end) {
-          const int64_t gi = (b * p.dstate + sn) * p.seqlen + t0 + e;
-          unsafeAtomicAdd(p.dB + gi, sm.dB[sn][e]);
-          unsafeAtomicAdd(p.dC + gi, sm.dC[sn][e]);
-        }
+        const int st = 16 * i + (lane >> 4) + 4 * q, sn = lane & 15;
+        stB[(wave * kTile + st) * kStates + sn] = accB[i][q];
+        stC[(wave * kTile + st) * kStates + sn] = accC[i][q];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int idx = tid + kThreads * r;  // (step, state) pair
+      const int st = idx / kStates, sn = idx % kStates;
+      float vb = 0.0f, vc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        vb += stB[(w * kTile + st) * kStates + sn];
+        vc += stC[(w * kTile + st) * kStates + sn];
+      }
+      if (sn < p.dstate && t0 + st < t_end) {
+        const int64_t gi = (b * p.dstate + sn) * p.seqlen + t0 + st;
+        unsafeAtomicAdd(p.dB + gi, vb);
+        unsafeAtomicAdd(p.dC + gi, vc);
       }
     }
   }
@@ -382,7 +448,9 @@ __global__ void __launch_bounds__(256) ss_fill_kernel(float* __restrict__ dst, i
   for (; i < count; i += stride) dst[i] = value;
 }
 
-// dA[d, n] = sum over (batch row, chunk) partials; dD, dbias likewise.
+// dA[d, n] = sum over (batch row, chunk) partials; dD, dbias likewise.  The
+// (batch row, chunk) range is split over gridDim.y groups whose partial sums
+// are added atomically into the zeroed outputs.
 __global__ void __launch_bounds__(256) ss_bwd_reduce_kernel(const float* __restrict__ dApart,
                                                             const float* __restrict__ dDpart,
                                                             const float* __restrict__ dbpart, float* __restrict__ dA,
@@ -392,18 +460,22 @@ __global__ void __launch_bounds__(256) ss_bwd_reduce_kernel(const float* __restr
   const int64_t d = idx / kStates;
   const int n = (int)(idx % kStates);
   if (d >= dim) return;
+  const int64_t per = (nbk + gridDim.y - 1) / gridDim.y;
+  const int64_t bk0 = (int64_t)blockIdx.y * per;
+  const int64_t bk1 = bk0 + per < nbk ? bk0 + per : nbk;
+  if (bk0 >= bk1) return;
   float acc = 0.0f;
-  for (int64_t bk = 0; bk < nbk; ++bk) acc += dApart[(bk * dim + d) * kStates + n];
-  if (n < dstate) dA[d * dstate + n] = acc;
+  for (int64_t bk = bk0; bk < bk1; ++bk) acc += dApart[(bk * dim + d) * kStates + n];
+  if (n < dstate) unsafeAtomicAdd(dA + d * dstate + n, acc);
   if (n == 0 && dD) {
     float s = 0.0f;
-    for (int64_t bk = 0; bk < nbk; ++bk) s += dDpart[bk * dim + d];
-    dD[d] = s;
+    for (int64_t bk = bk0; bk < bk1; ++bk) s += dDpart[bk * dim + d];
+    unsafeAtomicAdd(dD + d, s);
   }
   if (n == 1 && dbias) {
     float s = 0.0f;
-    for (int64_t bk = 0; bk < nbk; ++bk) s += dbpart[bk * dim + d];
-    dbias[d] = s;
+    for (int64_t bk = bk0; bk < bk1; ++bk) s += dbpart[bk * dim + d];
+    unsafeAtomicAdd(dbias + d, s);
   }
 }
 
@@ -442,9 +514,15 @@ hipError_t launch_bwd_io(const BwdParams& p, hipStream_t st) {
                      (int32_t)per);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  e = fill(p.dA, p.dim * p.dstate, st);
+  if (e == hipSuccess && p.dD) e = fill(p.dD, p.dim, st);
+  if (e == hipSuccess && p.dbias) e = fill(p.dbias, p.dim, st);
+  if (e != hipSuccess) return e;
   const int64_t threads = p.dim * kStates;
-  hipLaunchKernelGGL(ss_bwd_reduce_kernel, dim3((uint32_t)((threads + 255) / 256)), dim3(256), 0, st, p.aggP, p.aggG,
-                     p.aggG + p.batch * K * p.dim, p.dA, p.dD, p.dbias, p.dim, p.dstate, bk);
+  int64_t groups_y = (bk + 31) / 32;
+  if (groups_y > 64) groups_y = 64;
+  hipLaunchKernelGGL(ss_bwd_reduce_kernel, dim3((uint32_t)((threads + 255) / 256), (uint32_t)groups_y), dim3(256), 0,
+                     st, p.aggP, p.aggG, p.aggG + p.batch * K * p.dim, p.dA, p.dD, p.dbias, p.dim, p.dstate, bk);
   return hipGetLastError();
 }
 
