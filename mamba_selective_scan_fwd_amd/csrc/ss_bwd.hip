@@ -18,8 +18,9 @@
 //         chunk's first step when nothing enters from the right;
 //   carry the right-to-left exclusive scan of (P, Gz) gives the gradient
 //         entering every chunk from the right (ss_carry_kernel, reversed);
-//   MAIN  per chunk: recompute h over the chunk into 65 registers per lane,
-//         walk it backwards with the true carried gradient, emit du, ddelta,
+//   MAIN  per chunk: recompute the chunk's 16-step block entry states from
+//         the checkpoint, then per block (last first) recompute its 16 states
+//         and walk them backwards with the true carried gradient, emit du, ddelta,
 //         dz, accumulate dB/dC and dA/dD/dbias partials;
 //   REDUCE sum the dA/dD/dbias partials over (batch row, chunk).
 // Lane layout as the forward: a wavefront holds 4 channels x 16 states; the
@@ -50,7 +51,14 @@ constexpr int kSChan = 16 * 16 + 16;
 // Sum-over-channels tiles: per wave [16 steps][16 states][4 channels].
 constexpr int kCTile = 16 * 16 * kChPerWave;
 
+// AGG needs only the chunk's B and C; MAIN adds its reduction tiles.
+template <bool MAIN>
 struct BwdSmem {
+  float B[kStates][kBCStride];
+  float C[kStates][kBCStride];
+};
+template <>
+struct BwdSmem<true> {
   float B[kStates][kBCStride];
   float C[kStates][kBCStride];
   float T1[kWaves][kChPerWave * kSChan];  // G B, summed over states per step
@@ -158,22 +166,30 @@ template <int I, int... J>
 __device__ __forceinline__ void agg_block(float& g, const BwdOwned& o, float A2, const float* sCrow,
                                           std::integer_sequence<int, J...>) {
   // J runs 0..15; step s = 16 I + (15 - J) goes backwards
+  float4 c4;
   (
       [&] {
         constexpr int jj = 15 - J;
         constexpr int s = 16 * I + jj;
+        if constexpr (jj % 4 == 3) c4 = *reinterpret_cast<const float4*>(sCrow + s - 3);
+        const float cj = (jj % 4 == 0) ? c4.x : (jj % 4 == 1) ? c4.y : (jj % 4 == 2) ? c4.z : c4.w;
         const float a = exp2_hw(row_bcast<jj>(o.dt[I]) * A2);
-        const float G = fmaf(row_bcast<jj>(o.dy0[I]), sCrow[s], g);
+        const float G = fmaf(row_bcast<jj>(o.dy0[I]), cj, g);
         g = G * a;
       }(),
       ...);
+  g = fresh(g);
   __builtin_amdgcn_sched_barrier(0);  // no hoisting across blocks (registers)
 }
 
-// ---- MAIN: forward recompute of block I (states into hs) ---------------------
+// ---- MAIN: forward recompute ---------------------------------------------------
+// fwd_pass advances h through block I (and, WITH_Y, leaves the readout terms
+// C h in the sum-over-states tile); fwd_states recomputes block I's 16
+// states from its entry state into hs[0..16] just before the reverse walk
+// needs them, so that only 17 states (not 65) are live at once.
 template <int I, bool WITH_Y, int... J>
-__device__ __forceinline__ void fwd_block(float (&hs)[kTile + 1], const BwdOwned& o, float A2, const float* sBrow,
-                                          const float* sCrow, float* t1c, int n, std::integer_sequence<int, J...>) {
+__device__ __forceinline__ void fwd_pass(float& h, const BwdOwned& o, float A2, const float* sBrow,
+                                         const float* sCrow, float* t1c, int n, std::integer_sequence<int, J...>) {
   float4 b4, c4;
   (
       [&] {
@@ -184,15 +200,33 @@ __device__ __forceinline__ void fwd_block(float (&hs)[kTile + 1], const BwdOwned
         }
         const float bj = (J % 4 == 0) ? b4.x : (J % 4 == 1) ? b4.y : (J % 4 == 2) ? b4.z : b4.w;
         const float a = exp2_hw(row_bcast<J>(o.dt[I]) * A2);
-        const float h = fmaf(a, hs[s], row_bcast<J>(o.dtu[I]) * bj);
-        hs[s + 1] = h;
+        h = fmaf(a, h, row_bcast<J>(o.dtu[I]) * bj);
         if constexpr (WITH_Y) {
           const float cj = (J % 4 == 0) ? c4.x : (J % 4 == 1) ? c4.y : (J % 4 == 2) ? c4.z : c4.w;
           t1c[swz(J, n)] = cj * h;
         }
       }(),
       ...);
+  h = fresh(h);
   __builtin_amdgcn_sched_barrier(0);  // no hoisting across blocks (registers)
+}
+
+template <int I, int... J>
+__device__ __forceinline__ void fwd_states(float (&hs)[17], float h0, const BwdOwned& o, float A2,
+                                           const float* sBrow, std::integer_sequence<int, J...>) {
+  float4 b4;
+  hs[0] = h0;
+  (
+      [&] {
+        constexpr int s = 16 * I + J;
+        if constexpr (J % 4 == 0) b4 = *reinterpret_cast<const float4*>(sBrow + s);
+        const float bj = (J % 4 == 0) ? b4.x : (J % 4 == 1) ? b4.y : (J % 4 == 2) ? b4.z : b4.w;
+        const float a = exp2_hw(row_bcast<J>(o.dt[I]) * A2);
+        hs[J + 1] = fmaf(a, hs[J], row_bcast<J>(o.dtu[I]) * bj);
+      }(),
+      ...);
+  hs[16] = fresh(hs[16]);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // ---- MAIN: reverse walk of block I -------------------------------------------
@@ -200,7 +234,7 @@ __device__ __forceinline__ void fwd_block(float (&hs)[kTile + 1], const BwdOwned
 // tiles (their row sums give du and dDelta), the per-channel terms G Delta u
 // and dy0 h_t to the sum-over-channels tiles (dB and dC).
 template <int I, int... J>
-__device__ __forceinline__ void bwd_block(float& g, float& dA_acc, const float (&hs)[kTile + 1], const BwdOwned& o,
+__device__ __forceinline__ void bwd_block(float& g, float& dA_acc, const float (&hs)[17], const BwdOwned& o,
                                           float A2, float Anat, const float* sBrow, const float* sCrow, float* t1c,
                                           float* t2c, float* t3w, float* t4w, int n, int cw,
                                           std::integer_sequence<int, J...>) {
@@ -219,15 +253,17 @@ __device__ __forceinline__ void bwd_block(float& g, float& dA_acc, const float (
         const float dy0b = row_bcast<jj>(o.dy0[I]);
         const float a = exp2_hw(dtb * A2);
         const float gh = fmaf(dy0b, cqj, g);  // dLoss/dh_t
-        t4w[(jj * 16 + n) * kChPerWave + cw] = dy0b * hs[s + 1];
+        t4w[(jj * 16 + n) * kChPerWave + cw] = dy0b * hs[jj + 1];
         t3w[(jj * 16 + n) * kChPerWave + cw] = gh * row_bcast<jj>(o.dtu[I]);
         t1c[swz(jj, n)] = gh * bqj;
         g = gh * a;                                 // to h_{t-1}
-        const float q = g * hs[s];                  // gh * a * h_{t-1}
+        const float q = g * hs[jj];                 // gh * a * h_{t-1}
         t2c[swz(jj, n)] = q * Anat;
         dA_acc = fmaf(q, dtb, dA_acc);
       }(),
       ...);
+  g = fresh(g);
+  dA_acc = fresh(dA_acc);
   __builtin_amdgcn_sched_barrier(0);  // no hoisting across blocks (registers)
 }
 
@@ -241,14 +277,14 @@ __device__ __forceinline__ void collect_block(float (&accB)[4][4], float (&accC)
     const int jj = (lane >> 4) + 4 * q, sn = lane & 15;
     const float4 b4 = *reinterpret_cast<const float4*>(t3w + (jj * 16 + sn) * kChPerWave);
     const float4 c4 = *reinterpret_cast<const float4*>(t4w + (jj * 16 + sn) * kChPerWave);
-    accB[I][q] += (b4.x + b4.y) + (b4.z + b4.w);
-    accC[I][q] += (c4.x + c4.y) + (c4.z + c4.w);
+    accB[I][q] = fresh(accB[I][q] + ((b4.x + b4.y) + (b4.z + b4.w)));
+    accC[I][q] = fresh(accC[I][q] + ((c4.x + c4.y) + (c4.z + c4.w)));
   }
 }
 
 template <int IO, bool MAIN>
 __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int32_t groups, int32_t per_group) {
-  __shared__ BwdSmem sm;
+  __shared__ BwdSmem<MAIN> sm;
   constexpr uint32_t s = io_bytes<IO>();
   const int tid = threadIdx.x;
   const int wave = uniform(tid / 64);
@@ -290,10 +326,6 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
 
   const float* sBrow = &sm.B[n][0];
   const float* sCrow = &sm.C[n][0];
-  float* t1c = sm.T1[wave] + cw * kSChan;  // this channel's sum-over-states tiles
-  float* t2c = sm.T2[wave] + cw * kSChan;
-  float* t3w = sm.T3[wave];
-  float* t4w = sm.T4[wave];
   constexpr auto seq = std::make_integer_sequence<int, 16>{};
   float accB[4][4], accC[4][4];
 #pragma unroll
@@ -304,13 +336,6 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
   const int64_t cb_begin = grp * per_group;
   int64_t cb_end = cb_begin + per_group;
   if (cb_end > p.ch_blocks) cb_end = p.ch_blocks;
-
-  BwdRaw<IO> raw;
-  if (cb_begin < cb_end) {
-    const int64_t d0 = cb_begin * kChPerBlock + wave * kChPerWave;
-    const BwdViews v = make_views<IO>(p, b, d0, need_z);
-    load_raw<IO>(raw, v, (uint32_t)cw * L, t0, l);
-  }
 
   for (int64_t cb = cb_begin; cb < cb_end; ++cb) {
     const int64_t d0 = cb * kChPerBlock + wave * kChPerWave;
@@ -327,10 +352,10 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
     const float Dd = (ch_ok && p.D) ? p.D[d] : 0.0f;
 
     BwdOwned o;
-    prep<IO>(o, raw, t0, l, t_end, bias, softplus, need_z);
-    if (cb + 1 < cb_end) {  // prefetch the next channel block's operands
-      const BwdViews vn = make_views<IO>(p, b, d0 + kChPerBlock, need_z);
-      load_raw<IO>(raw, vn, lane_elem0, t0, l);
+    {
+      BwdRaw<IO> raw;
+      load_raw<IO>(raw, v, lane_elem0, t0, l);
+      prep<IO>(o, raw, t0, l, t_end, bias, softplus, need_z);
     }
     const int64_t wslot = ((ch * K + k) * kStates + n);
 
@@ -346,11 +371,17 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
         p.aggG[wslot] = g;
       }
     } else {
-      float hs[kTile + 1];
-      hs[0] = (ch_ok && n_ok) ? p.ckpt[(ch * K + k) * p.dstate + n] : 0.0f;
+      float* t1c = sm.T1[wave] + cw * kSChan;  // this channel's sum-over-states tiles
+      float* t2c = sm.T2[wave] + cw * kSChan;
+      float* t3w = sm.T3[wave];
+      float* t4w = sm.T4[wave];
+      // first pass: entry state of each 16-step block (and y0 when gated)
+      float hb[4];
+      float h = (ch_ok && n_ok) ? p.ckpt[(ch * K + k) * p.dstate + n] : 0.0f;
       if (need_z) {
 #define SS_FWD_Y(I)                                                        \
-  fwd_block<I, true>(hs, o, A2, sBrow, sCrow, t1c, n, seq);                \
+  hb[I] = h;                                                               \
+  fwd_pass<I, true>(h, o, A2, sBrow, sCrow, t1c, n, seq);                  \
   wave_lds_sync();                                                         \
   o.y0[I] = fmaf(Dd, o.u[I], row16_sum(t1c, l));                           \
   wave_lds_sync();
@@ -360,16 +391,24 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
         SS_FWD_Y(3)
 #undef SS_FWD_Y
       } else {
-        fwd_block<0, false>(hs, o, A2, sBrow, sCrow, t1c, n, seq);
-        fwd_block<1, false>(hs, o, A2, sBrow, sCrow, t1c, n, seq);
-        fwd_block<2, false>(hs, o, A2, sBrow, sCrow, t1c, n, seq);
-        fwd_block<3, false>(hs, o, A2, sBrow, sCrow, t1c, n, seq);
+        hb[0] = h;
+        fwd_pass<0, false>(h, o, A2, sBrow, sCrow, t1c, n, seq);
+        hb[1] = h;
+        fwd_pass<1, false>(h, o, A2, sBrow, sCrow, t1c, n, seq);
+        hb[2] = h;
+        fwd_pass<2, false>(h, o, A2, sBrow, sCrow, t1c, n, seq);
+        hb[3] = h;
       }
 
       float g = (k < K - 1 && ch_ok) ? p.gcarry[wslot] : 0.0f;
       float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
 #define SS_BWD(I)                                                                                   \
   {                                                                                                 \
+    float hs[17];                                                                                   \
+    o.dt[I] = fresh(o.dt[I]);                                                                       \
+    o.dtu[I] = fresh(o.dtu[I]);                                                                     \
+    o.dy0[I] = fresh(o.dy0[I]);                                                                     \
+    fwd_states<I>(hs, hb[I], o, A2, sBrow, seq);                                                    \
     bwd_block<I>(g, dA_acc, hs, o, A2, A, sBrow, sCrow, t1c, t2c, t3w, t4w, n, cw, seq);            \
     wave_lds_sync();                                                                                \
     const float sGB = row16_sum(t1c, l);                                                            \
@@ -494,7 +533,8 @@ hipError_t launch_bwd_io(const BwdParams& p, hipStream_t st) {
   if (e != hipSuccess) return e;
   e = fill(p.dC, p.batch * p.dstate * p.seqlen, st);
   if (e != hipSuccess) return e;
-  // channel blocks per workgroup: enough workgroups to fill the chip
+  // MAIN: channel blocks per workgroup chosen for enough workgroups to fill
+  // the chip (each workgroup adds its channel sums of dB/dC once per element)
   const int64_t bk = p.batch * K;
   int64_t groups = (1024 + bk - 1) / bk;
   if (groups > p.ch_blocks) groups = p.ch_blocks;
@@ -503,8 +543,9 @@ hipError_t launch_bwd_io(const BwdParams& p, hipStream_t st) {
   groups = (p.ch_blocks + per - 1) / per;
   const dim3 grid((uint32_t)(bk * groups));
   if (K > 1) {
-    hipLaunchKernelGGL((ss_bwd_chunk_kernel<IO, false>), grid, dim3(kThreads), 0, st, p, (int32_t)groups,
-                       (int32_t)per);
+    // AGG has nothing to reduce over channels: one channel block per workgroup
+    hipLaunchKernelGGL((ss_bwd_chunk_kernel<IO, false>), dim3((uint32_t)(bk * p.ch_blocks)), dim3(kThreads), 0, st, p,
+                       (int32_t)p.ch_blocks, 1);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_carry(p.aggP, p.aggG, p.gcarry, p.batch * p.dim, (int32_t)K, true, st);

@@ -121,12 +121,22 @@ __device__ __forceinline__ float sigmoid_f(float x) { return rcp_hw(1.0f + exp2_
 // SiLU(z) = z * sigmoid(z)
 __device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
 
+// An opaque copy of v.  Values derived from it are not merged with values
+// derived from v earlier, and, being ordered with scheduling barriers, it pins
+// the computation of v before the barrier that follows it: without such pins
+// the compiler floats the arithmetic of every unrolled block past the
+// barriers and keeps all blocks' broadcasts and exponentials live at once.
+__device__ __forceinline__ float fresh(float v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // ---- cross-lane moves inside a 16-lane DPP row ------------------------------
 // value of lane J of this lane's row (DPP row_newbcast; folds into the VALU
 // instruction that consumes it)
 template <int J>
 __device__ __forceinline__ float row_bcast(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + J, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + J, 0xf, 0xf, true));
 }
 // value of lane (l + K) mod 16 of this lane's row (DPP row_ror)
 template <int K>

@@ -44,11 +44,28 @@ constexpr int kCTRow = 20;               // padded LDS row of the transposed C t
 constexpr int kPRow = 20;                // padded LDS row of the state tile (16 states + 4)
 constexpr int kPChan = 16 * kPRow + 16;  // per-channel state tile; 336 = 16 mod 64 banks
 
+// FINAL keeps C and the state tiles for the readout; the chunk-summary pass
+// only needs B.
+template <bool FINAL>
 struct FwdSmem {
   float B[2][kStates][kBCStride];        // B[n][t], read by the state lanes
   float CT[2][kTile][kCTRow];            // C[t][n], read by the lane that owns step t
   float P[kWaves][kChPerWave * kPChan];  // h_t[n] of 16 steps, per channel
 };
+template <>
+struct FwdSmem<false> {
+  float B[2][kStates][kBCStride];
+};
+template <bool FINAL>
+__device__ __forceinline__ float* state_tile(FwdSmem<FINAL>& sm, int wave) {
+  if constexpr (FINAL) return sm.P[wave];
+  else return nullptr;
+}
+template <bool FINAL>
+__device__ __forceinline__ const float* ct_row(FwdSmem<FINAL>& sm, int buf, int l) {
+  if constexpr (FINAL) return &sm.CT[buf][l][0];
+  else return nullptr;
+}
 
 // Per-lane registers of the four steps this lane owns in a 64-step tile.
 struct Owned {
@@ -120,9 +137,9 @@ __device__ __forceinline__ void load_bc(BCRaw<IO, PAIR>& r, const Views& v, uint
 // B (row-major, for the state lanes) and C (transposed, for the step owners)
 // of steps at or past the valid end are staged as exact zeros, so data past a
 // row's length (padding, NaN) never reaches the state or the output.
-template <int IO, bool PAIR>
-__device__ __forceinline__ void store_bc(FwdSmem& sm, int buf, const BCRaw<IO, PAIR>& r, int tid, int nvalid,
-                                         bool n_ok, bool with_c) {
+template <int IO, bool PAIR, bool FINAL>
+__device__ __forceinline__ void store_bc(FwdSmem<FINAL>& sm, int buf, const BCRaw<IO, PAIR>& r, int tid, int nvalid,
+                                         bool n_ok) {
   const int n = tid / 16, j = tid % 16;
 #pragma unroll
   for (int k = 0; k < BCRaw<IO, PAIR>::kN; ++k) {
@@ -131,7 +148,7 @@ __device__ __forceinline__ void store_bc(FwdSmem& sm, int buf, const BCRaw<IO, P
       const bool ok0 = n_ok && e < nvalid, ok1 = n_ok && e + 1 < nvalid;
       const float b0 = bits_f32<IO>((raw_t<IO>)(r.b[k] & 0xffffu)), b1 = bits_f32<IO>((raw_t<IO>)(r.b[k] >> 16));
       *reinterpret_cast<float2*>(&sm.B[buf][n][e]) = make_float2(ok0 ? b0 : 0.0f, ok1 ? b1 : 0.0f);
-      if (with_c) {
+      if constexpr (FINAL) {
         const float c0 = bits_f32<IO>((raw_t<IO>)(r.c[k] & 0xffffu)), c1 = bits_f32<IO>((raw_t<IO>)(r.c[k] >> 16));
         sm.CT[buf][e][n] = ok0 ? c0 : 0.0f;
         sm.CT[buf][e + 1][n] = ok1 ? c1 : 0.0f;
@@ -140,7 +157,7 @@ __device__ __forceinline__ void store_bc(FwdSmem& sm, int buf, const BCRaw<IO, P
       const int e = j + 16 * k;
       const bool ok = n_ok && e < nvalid;
       sm.B[buf][n][e] = ok ? bits_f32<IO>(r.b[k]) : 0.0f;
-      if (with_c) sm.CT[buf][e][n] = ok ? bits_f32<IO>(r.c[k]) : 0.0f;
+      if constexpr (FINAL) sm.CT[buf][e][n] = ok ? bits_f32<IO>(r.c[k]) : 0.0f;
     }
   }
 }
@@ -183,6 +200,7 @@ __device__ __forceinline__ void scan_block(float& h, const Owned& o, float A2, c
         if constexpr (FINAL) pcol[J * kPRow] = h;
       }(),
       ...);
+  h = fresh(h);
   // keep the next block's exps from being hoisted here (register pressure)
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -231,7 +249,7 @@ __device__ __forceinline__ void finish_block(const Owned& o, const float* prow, 
 
 template <int IO, bool FINAL, bool PAIR>
 __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
-  __shared__ FwdSmem sm;
+  __shared__ FwdSmem<FINAL> sm;
   constexpr uint32_t s = io_bytes<IO>();
   const int tid = threadIdx.x;
   const int wave = uniform(tid / 64);
@@ -294,7 +312,7 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   float h = 0.0f;
   if (FINAL && chunk > 0 && p.carry && ch_ok) h = p.carry[(ch * p.nchunks + chunk) * kStates + n];
 
-  float* pwave = sm.P[wave] + cw * kPChan;
+  float* pwave = state_tile<FINAL>(sm, wave) + cw * kPChan;
   float* pcol = pwave + n;                // column n of this channel's state tile
   const float* prow = pwave + l * kPRow;  // row l (step l of the block)
 
@@ -304,7 +322,7 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   if (t_begin < t_tile_end) {
     load_owned<IO>(raw, v, lane_elem0, t_begin, l);
     load_bc<IO, PAIR>(bcr, v, (uint32_t)L, t_begin, tid, FINAL);
-    store_bc<IO, PAIR>(sm, 0, bcr, tid, t_valid_end - t_begin, stage_n_ok, FINAL);
+    store_bc<IO, PAIR, FINAL>(sm, 0, bcr, tid, t_valid_end - t_begin, stage_n_ok);
   }
   __syncthreads();
 
@@ -324,7 +342,7 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
     }
 
     const float* sBrow = &sm.B[buf][n][0];
-    const float* sCT = &sm.CT[buf][l][0];
+    const float* sCT = ct_row<FINAL>(sm, buf, l);
     const uint32_t elem = lane_elem0 + (uint32_t)t0;
     constexpr auto seq = std::make_integer_sequence<int, 16>{};
 #define SS_BLOCK(I)                                                                          \
@@ -344,7 +362,7 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
     SS_BLOCK(3)
 #undef SS_BLOCK
 
-    if (more) store_bc<IO, PAIR>(sm, buf ^ 1, bcr, tid, t_valid_end - t1, stage_n_ok, FINAL);
+    if (more) store_bc<IO, PAIR, FINAL>(sm, buf ^ 1, bcr, tid, t_valid_end - t1, stage_n_ok);
     __syncthreads();
     buf ^= 1;
   }
