@@ -30,14 +30,16 @@ sys.path.insert(0, ROOT)
 from mamba_selective_scan_fwd_amd import inputs, ss  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0
-# VALU issue slots per second: 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz (fp32, no packed math)
-PEAK_SLOTS = 256 * 4 * 16 * 2.4e9
-# Algorithmic ALU work in issue slots (a transcendental issues at half rate = 2 slots):
-#   per (t, d, n): exp-argument mul, Bbar*u mul, recurrence fma, readout fma (4) + exp (2)
-#   per (t, d):   softplus (exp + log: 4, 4 VALU), Delta*u, skip fma, SiLU (exp + rcp: 4, 2 VALU),
-#                 gate mul = 9 VALU + 8 = 17; plus 4 conversions when the I/O is 16-bit
-SLOTS_PER_TDN = 6
-SLOTS_PER_TD = 17
+# VALU lane-slots per second: the fp32 vector peak, 157.3 TFLOP/s, is
+# 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz FMA slots (no packed math).
+PEAK_SLOTS = 256 * 4 * 32 * 2.4e9
+# Algorithmic ALU work in lane-slots; a transcendental (exp2, log2, rcp) runs at
+# quarter rate and counts 4 slots:
+#   per (t, d, n): exp-argument mul, Bbar*u mul, recurrence fma, readout fma (4) + exp (4) = 8
+#   per (t, d):    softplus (exp + log: 8, 4 VALU), Delta*u, skip fma, SiLU (exp + rcp: 8, 2 VALU),
+#                  gate mul = 9 VALU + 16 = 25; plus 4 conversions when the I/O is 16-bit
+SLOTS_PER_TDN = 8
+SLOTS_PER_TD = 25
 SLOTS_PER_TD_CVT16 = 4
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["mamba_selective_scan_fwd_amd/csrc/ss_fwd.hip", "mamba_selective_scan_fwd_amd/csrc/ss_device.h"]

@@ -98,21 +98,19 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|).  log1p(e) for
-// e in (0, 1] uses the w = 1 + e correction log(w) * e / (w - 1), which keeps
-// full relative accuracy when e is tiny (w - 1 is exact there).
-//
-// When e < 2^-24, w rounds to 1 and log(w) = 0: the result then drops e,
-// which is below fp32 resolution of the result for x > 0 and below 6e-8 in
-// absolute terms for x < 0.  w - 1 is clamped away from 0 so that 0 * inf
-// never occurs.
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|).  For e in (0, 1],
+// w = fl(1 + e) carries a rounding error eps = (w - 1) - e, which is exact to
+// evaluate (w - 1 is exact by Sterbenz).  log1p(e) = log(w) - eps / w +
+// O(eps^2), and eps / w = eps to within e * eps, so
+//   log1p(e) = ln2 * log2(w) + (e - (w - 1))
+// to a few ulp relative, for every e (when w rounds to 1 the result is e
+// itself).  max(x, 0) = (x + |x|) / 2 exactly.  Two transcendentals, no
+// division, no clamp.
 __device__ __forceinline__ float softplus_f(float x) {
   const float e = exp2_hw(-fabsf(x) * kLog2e);
   const float w = 1.0f + e;
-  const float wm1r = w - 1.0f;
-  const float wm1 = wm1r > 1e-30f ? wm1r : 1e-30f;
-  const float l2 = log2_hw(w) * (e * rcp_hw(wm1));  // log2(1 + e)
-  return fmaf(kLn2, l2, x > 0.0f ? x : 0.0f);
+  const float d = e - (w - 1.0f);
+  return fmaf(0.5f, x + fabsf(x), fmaf(kLn2, log2_hw(w), d));
 }
 
 // d softplus / dx = sigmoid(x)
