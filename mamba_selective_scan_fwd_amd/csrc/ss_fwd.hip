@@ -258,14 +258,14 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   const int n = lane % 16;   // state index; also the time-owner index l
   const int l = n;
 
-  // logical block -> (chunk, channel block, batch row).  Batch rows vary
-  // fastest, so that every XCD's contiguous share of logical blocks holds all
-  // rows: with ragged lengths no XCD is left with only the long rows.
+  // logical block -> (chunk, batch row, channel block).  Channel blocks vary
+  // fastest: the blocks that share one batch row's B and C tiles run on one
+  // XCD, so each row's B and C come from HBM about once.
   uint32_t lb = xcd_logical_block();
-  const int64_t b = lb % p.batch;
-  lb /= p.batch;
   const int64_t cb = lb % p.ch_blocks;
-  const int64_t chunk = lb / p.ch_blocks + p.chunk_base;
+  lb /= p.ch_blocks;
+  const int64_t b = lb % p.batch;
+  const int64_t chunk = lb / p.batch + p.chunk_base;
 
   const int64_t d0 = cb * kChPerBlock + wave * kChPerWave;  // first channel of this wave
   const int64_t d = d0 + cw;

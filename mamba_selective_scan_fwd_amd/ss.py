@@ -228,6 +228,53 @@ def step(u_t, delta_t, A, B_t, C_t, state, D=None, z_t=None, delta_bias=None, de
     return y, state_out
 
 
+class StepCall:
+    """A decode step validated once and replayed with one C call per launch.
+
+    The serving pattern: the token buffers (u_t, delta_t, z_t, B_t, C_t) and
+    the state are preallocated and refilled in place between steps, so one
+    StepCall per set of buffers replays the step with no per-call checks.
+    The tensors must stay alive and unmoved.
+    """
+
+    def __init__(self, u_t, delta_t, A, B_t, C_t, state, D=None, z_t=None, delta_bias=None, delta_softplus=True,
+                 state_out=None, y=None, stream=None):
+        lib = load_library()
+        io = u_t.dtype
+        if io not in _IO:
+            raise TypeError("unsupported dtype %s" % io)
+        Bsz, Dd = u_t.shape
+        N = A.shape[1]
+        if state_out is None:
+            state_out = state
+        checks = [(u_t, io, "u_t", (Bsz, Dd)), (delta_t, io, "delta_t", (Bsz, Dd)), (z_t, io, "z_t", (Bsz, Dd)),
+                  (B_t, io, "B_t", (Bsz, N)), (C_t, io, "C_t", (Bsz, N)), (A, torch.float32, "A", (Dd, N)),
+                  (D, torch.float32, "D", (Dd,)), (delta_bias, torch.float32, "delta_bias", (Dd,)),
+                  (state, torch.float32, "state", (Bsz, Dd, N)), (state_out, torch.float32, "state_out", (Bsz, Dd, N)),
+                  (y, io, "y", (Bsz, Dd))]
+        for t, dt, name, shape in checks:
+            if t is None:
+                continue
+            if not (t.is_cuda and t.dtype == dt and tuple(t.shape) == shape and t.is_contiguous()
+                    and t.data_ptr() % 16 == 0):
+                raise ValueError("%s must be a contiguous, 16-byte aligned %s device tensor of shape %s"
+                                 % (name, dt, shape))
+        if y is None:
+            raise ValueError("StepCall needs its output y")
+        self.pr = problem(Bsz, Dd, N, 1, io, delta_softplus)
+        self.keep = (u_t, delta_t, A, B_t, C_t, state, D, z_t, delta_bias, state_out, y)
+        st = stream if stream is not None else torch.cuda.current_stream(u_t.device)
+        self.args = (ctypes.byref(self.pr), _ptr(u_t), _ptr(delta_t), _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(D),
+                     _ptr(z_t), _ptr(delta_bias), _ptr(state), _ptr(state_out), _ptr(y),
+                     ctypes.c_void_p(st.cuda_stream))
+        self.fn = lib.ss_fwd_step
+
+    def __call__(self):
+        status = self.fn(*self.args)
+        if status != 0:
+            _check(status)
+
+
 def bwd(u, delta, A, Bm, Cm, ckpt, dy, D=None, z=None, delta_bias=None, delta_softplus=True, workspace=None):
     """Selective-scan backward for the loss sum(dy * y).  Returns a dict of gradients
     (du, ddelta, dA, dB, dC, and dz / dD / dbias for the inputs that were given)."""

@@ -238,3 +238,56 @@ def test_forward_then_steps_equals_longer_forward():
     ycat = torch.cat([y0, torch.stack(ys, dim=-1)], dim=-1)
     assert rel_err(f64(ycat), f64(yfull)) <= 1e-5
     assert rel_err(f64(st), f64(lastfull)) <= 1e-5
+
+
+# --------------------------------------------------------------- prepared calls
+
+def test_prepared_forward_call_matches_fwd():
+    """FwdCall (validated once, replayed) gives the same bits as fwd on the same buffers,
+    on the single-pass and on the time-chunked paths, over repeated launches."""
+    ss = _ss()
+    for Bsz, Dd, L, io in [(2, 40, 300, "f16"), (1, 16, 4096, "f32")]:
+        prob = inputs.make_problem(Bsz, Dd, 16, L, io, seed=95)
+        g = to_dev(prob)
+        say("FwdCall B=%d D=%d L=%d io=%s" % (Bsz, Dd, L, io))
+        y_ref, last_ref, _ = ss.fwd(g["u"], g["delta"], g["A"], g["Bm"], g["Cm"], D=g["D"], z=g["z"],
+                                    delta_bias=g["bias"])
+        y = torch.empty_like(y_ref)
+        last = torch.empty_like(last_ref)
+        call = ss.FwdCall(g["u"], g["delta"], g["A"], g["Bm"], g["Cm"], D=g["D"], z=g["z"], delta_bias=g["bias"],
+                          y=y, last_state=last)
+        for _ in range(3):
+            y.fill_(float("nan"))
+            call()
+            torch.cuda.synchronize()
+            assert torch.equal(y, y_ref) and torch.equal(last, last_ref)
+
+
+@pytest.mark.parametrize("io", ["f32", "f16"])
+def test_prepared_step_call_matches_step(io):
+    """StepCall updating the state in place over several steps == ss.step == the oracle."""
+    ss = _ss()
+    Bsz, Dd, N = 3, 50, 16
+    prob = inputs.make_problem(Bsz, Dd, N, 1, io, seed=96, decode_steps=4)
+    g = to_dev(prob)
+    st0 = torch.from_numpy(np.random.default_rng(97).standard_normal((Bsz, Dd, N))).float()
+    st_a = st0.to("cuda")
+    st_b = st0.to("cuda")
+    st_ref = f64(st0)
+    ya = torch.empty((Bsz, Dd), dtype=g["u"].dtype, device="cuda")
+    toks = [{k: v.to("cuda") for k, v in t.items()} for t in prob["decode"]]
+    calls = [ss.StepCall(t["u_t"], t["delta_t"], g["A"], t["B_t"], t["C_t"], st_a, D=g["D"], z_t=t["z_t"],
+                         delta_bias=g["bias"], y=ya) for t in toks]
+    for k, (tok, call) in enumerate(zip(prob["decode"], calls)):
+        say("StepCall io=%s k=%d" % (io, k))
+        call()
+        t = toks[k]
+        yb, st_b = ss.step(t["u_t"], t["delta_t"], g["A"], t["B_t"], t["C_t"], st_b, D=g["D"], z_t=t["z_t"],
+                           delta_bias=g["bias"])
+        yr, st_ref = oracle.step(f64(tok["u_t"]), f64(tok["delta_t"]), f64(prob["A"]), f64(tok["B_t"]),
+                                 f64(tok["C_t"]), st_ref, D=f64(prob["D"]), z_t=f64(tok["z_t"]),
+                                 bias=f64(prob["bias"]))
+        torch.cuda.synchronize()
+        assert torch.equal(ya, yb) and torch.equal(st_a, st_b)
+        assert rel_err(f64(ya), yr) <= TOL[io]
+        assert rel_err(f64(st_a), st_ref) <= TOL[io]
