@@ -96,6 +96,78 @@ def make_problem(batch: int, dim: int, dstate: int, seqlen: int, io: str = "f32"
     return p
 
 
+# Packed-document layouts ("niverel-mamba" README, "seq_idx strict reset"
+# names nine structural cases).  Each case gives, per batch row, the list of
+# document lengths (summing to L); consecutive documents get distinct ids.
+SEQ_CASES = ("single_document", "length1_docs", "consecutive_boundaries", "tile_edges", "inside_one_tile",
+             "misaligned_rows", "terminal_padding", "nonzero_first_id", "many_short_docs")
+
+
+def _doc_lengths(case: str, b: int, L: int, rng) -> list:
+    def fill(first, total=L):
+        out, tot = [], 0
+        for x in first:
+            x = min(x, total - tot)
+            if x > 0:
+                out.append(x)
+                tot += x
+        if tot < total:
+            out.append(total - tot)
+        return out
+    if case == "single_document":      # the only boundary is position 0
+        return [L]
+    if case == "length1_docs":
+        return fill([1, 3, 1, 1, 7, 1] * (L // 14 + 1))
+    if case == "consecutive_boundaries":
+        return fill([5, 1, 1, 1, 1, 9, 1, 1])
+    if case == "tile_edges":           # boundaries on 16-step block and 64-step tile edges
+        return fill([16, 48, 64, 128, 32, 16])
+    if case == "inside_one_tile":      # a document strictly inside one 64-step tile
+        return fill([70, 20, 40])
+    if case == "misaligned_rows":      # every row cut elsewhere
+        return fill([int(x) for x in rng.integers(1, max(2, L // 3), size=8)])
+    if case == "terminal_padding":     # documents, then a padding segment (id -1)
+        if L < 2:
+            return [L]
+        pad = max(1, L // 4)
+        return fill([int(x) for x in rng.integers(1, max(2, L // 2), size=3)], L - pad) + [pad]
+    if case == "nonzero_first_id":
+        return fill([L // 3, L // 3])
+    if case == "many_short_docs":
+        return fill([int(x) for x in rng.integers(1, 9, size=L)])
+    raise ValueError("unknown seq_idx case %r" % case)
+
+
+def make_seq_idx(case: str, batch: int, seqlen: int, seed: int = 0) -> torch.Tensor:
+    """Document ids (B, L) int32 for one of SEQ_CASES, from a seeded generator."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((batch, seqlen), dtype=np.int32)
+    for b in range(batch):
+        lens = _doc_lengths(case, b, seqlen, rng)
+        first = 7 + 3 * b if case == "nonzero_first_id" else 0
+        t = 0
+        for k, ln in enumerate(lens):
+            pad = case == "terminal_padding" and k == len(lens) - 1 and len(lens) > 1
+            out[b, t:t + ln] = -1 if pad else first + k
+            t += ln
+        assert t == seqlen
+    return torch.from_numpy(out)
+
+
+def packed_documents(seqlen: int, batch: int, max_len: int, seed: int) -> torch.Tensor:
+    """Rows packed with documents of length U[1, max_len] (ids 0, 1, 2, ...), int32 (B, L)."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((batch, seqlen), dtype=np.int32)
+    for b in range(batch):
+        t, k = 0, 0
+        while t < seqlen:
+            ln = int(rng.integers(1, max_len, endpoint=True))
+            out[b, t:t + ln] = k
+            t += ln
+            k += 1
+    return torch.from_numpy(out)
+
+
 # The five synthetic workloads: shapes of the pages' long-sequence throughput
 # run (B=1, D=16, N=16, L=32k) and of mamba-130m / mamba-2.8b layers.
 CONFIGS = {

@@ -34,15 +34,15 @@ def _load():
         lib = ctypes.CDLL(path)
         lib.sso_fwd.restype = ctypes.c_int
         lib.sso_fwd.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int,
-                                _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _ip, _dp, _ip, _i64,
+                                _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _ip, _ip, _dp, _ip, _i64,
                                 _dp, _dp, _dp, _i64, ctypes.c_int]
         lib.sso_step.restype = ctypes.c_int
         lib.sso_step.argtypes = [_i64, _i64, _i64, ctypes.c_int,
                                  _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
         lib.sso_bwd.restype = ctypes.c_int
         lib.sso_bwd.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int,
-                                _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _ip, _dp, _dp,
-                                _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int]
+                                _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _ip, _ip, _dp, _dp, _dp,
+                                _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -67,14 +67,25 @@ def _ptr(a, typ=_dp):
     return None if a is None else a.ctypes.data_as(typ)
 
 
+def _seq(seq_idx, Bsz, L):
+    if seq_idx is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(seq_idx, dtype=np.int64))
+    if a.shape != (Bsz, L):
+        raise ValueError("oracle: seq_idx must have shape %s" % ((Bsz, L),))
+    return a
+
+
 def fwd(u, delta, A, Bm, Cm, D=None, z=None, bias=None, softplus=True,
-        lengths=None, h0=None, rows=None, states_every=None, threads=None):
+        lengths=None, h0=None, rows=None, states_every=None, threads=None, seq_idx=None):
     """Forward scan in float64.
 
     Returns ``(y, last_state)``, or ``(y, last_state, states)`` when
     ``states_every`` is given (states[b,d,k] = state after min(k*every, len_b)
     steps).  With ``rows`` (flat channel indices b*D+d) only those channels
-    are computed; the other entries of y / last_state are NaN.
+    are computed; the other entries of y / last_state are NaN.  ``seq_idx``
+    (B,L) integer document ids: the state restarts from zero wherever the id
+    changes.
     """
     u = _f64(u)
     Bsz, Dd, L = u.shape
@@ -104,9 +115,10 @@ def fwd(u, delta, A, Bm, Cm, D=None, z=None, bias=None, softplus=True,
         every = int(states_every)
         K = -(-L // every)
         states = np.full((Bsz, Dd, K, N), np.nan)
+    seq = _seq(seq_idx, Bsz, L)
     rc = _load().sso_fwd(Bsz, Dd, N, L, int(bool(softplus)),
                          _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z),
-                         _ptr(bias), _ptr(lens, _ip), _ptr(h0), _ptr(rws, _ip),
+                         _ptr(bias), _ptr(lens, _ip), _ptr(seq, _ip), _ptr(h0), _ptr(rws, _ip),
                          0 if rws is None else rws.size,
                          _ptr(y), _ptr(last), _ptr(states), every, threads or default_threads())
     if rc != 0:
@@ -143,11 +155,12 @@ def step(u_t, delta_t, A, B_t, C_t, state_in, D=None, z_t=None, bias=None, softp
 
 
 def bwd(u, delta, A, Bm, Cm, dy, D=None, z=None, bias=None, softplus=True,
-        lengths=None, h0=None, threads=None):
-    """Backward scan for the loss sum(dy * out), in float64.
+        lengths=None, h0=None, threads=None, seq_idx=None, dlast=None, want_dh0=False):
+    """Backward scan for the loss sum(dy * out) + sum(dlast * h_final), in float64.
 
     Returns a dict with du, ddelta, dA, dB, dC and, when the matching input
-    is given, dz, dD, dbias.
+    is given, dz, dD, dbias; with ``want_dh0`` also dh0, the gradient w.r.t.
+    the initial state (B,D,N).
     """
     u = _f64(u)
     Bsz, Dd, L = u.shape
@@ -172,12 +185,15 @@ def bwd(u, delta, A, Bm, Cm, dy, D=None, z=None, bias=None, softplus=True,
     out["dz"] = np.empty((Bsz, Dd, L)) if z is not None else None
     out["dD"] = np.empty((Dd,)) if D is not None else None
     out["dbias"] = np.empty((Dd,)) if bias is not None else None
+    out["dh0"] = np.empty((Bsz, Dd, N)) if want_dh0 else None
+    seq = _seq(seq_idx, Bsz, L)
+    dlast = _f64(dlast, (Bsz, Dd, N))
     rc = _load().sso_bwd(Bsz, Dd, N, L, int(bool(softplus)),
                          _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z),
-                         _ptr(bias), _ptr(lens, _ip), _ptr(h0), _ptr(dy),
+                         _ptr(bias), _ptr(lens, _ip), _ptr(seq, _ip), _ptr(h0), _ptr(dy), _ptr(dlast),
                          _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dz"]), _ptr(out["dA"]),
                          _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dbias"]),
-                         threads or default_threads())
+                         _ptr(out["dh0"]), threads or default_threads())
     if rc != 0:
         raise RuntimeError("oracle sso_bwd failed (%d)" % rc)
     return {k: v for k, v in out.items() if v is not None}

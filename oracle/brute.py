@@ -14,20 +14,26 @@ def _softplus(x):
     return math.log1p(math.exp(x)) if x < 30 else x + math.log1p(math.exp(-x))
 
 
-def unrolled_fwd(u, delta, A, Bm, Cm, D=None, z=None, bias=None, softplus=True):
+def unrolled_fwd(u, delta, A, Bm, Cm, D=None, z=None, bias=None, softplus=True, seq_idx=None, h0=None):
     """Unrolled (non-recursive) form of the selective scan, O(L^2 N) per channel.
 
     "Mamba" walkthrough, Part V "S6, and why selectivity forbids the
     convolution": the output at t is a weighted sum over all past inputs s,
     with weight C_t * Abar_t * ... * Abar_{s+1} * Bbar_s, where
     Abar_r = exp(Delta_r A) and Bbar_s = Delta_s B_s (Part IV Stage 4).
-    Pure-Python loops: tiny inputs only.
+    An initial state h0 enters with weight C_t * Abar_t * ... * Abar_0.
+    With document ids ("niverel-mamba" README, "seq_idx strict reset") a
+    term reaches t only if no document starts in (s, t]: its weight is zero
+    otherwise.  Pure-Python loops: tiny inputs only.
     """
     u = np.asarray(u, np.float64)
     Bsz, Dd, L = u.shape
     N = np.asarray(A).shape[1]
     y = np.zeros((Bsz, Dd, L))
     for b in range(Bsz):
+        starts = set()
+        if seq_idx is not None:
+            starts = {r for r in range(1, L) if int(seq_idx[b][r]) != int(seq_idx[b][r - 1])}
         for d in range(Dd):
             dts = []
             for t in range(L):
@@ -36,7 +42,14 @@ def unrolled_fwd(u, delta, A, Bm, Cm, D=None, z=None, bias=None, softplus=True):
             for t in range(L):
                 total = 0.0
                 for n in range(N):
+                    if h0 is not None and not any(r in starts for r in range(1, t + 1)):
+                        w = float(Cm[b][n][t]) * float(h0[b][d][n])
+                        for r in range(0, t + 1):
+                            w *= math.exp(dts[r] * float(A[d][n]))
+                        total += w
                     for s in range(t + 1):
+                        if any(r in starts for r in range(s + 1, t + 1)):
+                            continue
                         w = float(Cm[b][n][t])
                         for r in range(s + 1, t + 1):
                             w *= math.exp(dts[r] * float(A[d][n]))

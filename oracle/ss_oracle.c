@@ -33,8 +33,14 @@
  *   - ragged rows: row b runs lengths[b] steps from a zero state (or h0),
  *     the outputs past that length are exactly 0 and the final state is the
  *     state after lengths[b] steps;
- *   - the loss for the backward is sum(dy * out); gradients of B and C sum
- *     over channels d, those of A, D and bias over batch rows and time.
+ *   - packed documents ("niverel-mamba" README, "seq_idx strict reset"):
+ *     wherever seq_idx[b,t] differs from seq_idx[b,t-1] (t >= 1) the state
+ *     is set to zero before step t, so every document starts from zero and a
+ *     packed row equals its documents run one by one;
+ *   - the loss for the backward is sum(dy * out) + sum(dlast * h_final);
+ *     gradients of B and C sum over channels d, those of A, D and bias over
+ *     batch rows and time; dh0 is the gradient of that loss w.r.t. the
+ *     initial state.
  *
  * Everything is computed per channel (b, d) independently; threads split the
  * channels and never change the arithmetic of a channel.
@@ -65,6 +71,9 @@ typedef struct {
     int softplus;
     const double *u, *delta, *A, *Bm, *Cm, *Dskip, *z, *bias, *h0, *dy;
     const int64_t *lengths;
+    const int64_t *seq_idx; /* optional (B,L) document ids */
+    const double *dlast;    /* optional (B,D,N) gradient w.r.t. the final state */
+    double *dh0;            /* optional (B,D,N) gradient w.r.t. the initial state */
     const int64_t *rows; /* optional subset of channels b*dim+d */
     int64_t nrows;
     /* forward outputs */
@@ -80,6 +89,13 @@ typedef struct {
     /* per-thread partial sums for the backward's reduced gradients */
     double *dA, *dB, *dC, *dD, *dbias;
 } slice_t;
+
+/* Step t of row b starts a new document: the state is reset to zero. */
+static int resets(const job_t *j, int64_t b, int64_t t)
+{
+    const int64_t *s = j->seq_idx;
+    return s != NULL && t > 0 && s[b * j->seqlen + t] != s[b * j->seqlen + t - 1];
+}
 
 static int64_t row_len(const job_t *j, int64_t b)
 {
@@ -114,6 +130,9 @@ static void forward_channel(const job_t *j, int64_t b, int64_t d)
     }
 
     for (int64_t t = 0; t < len; ++t) {
+        if (resets(j, b, t))                       /* a new document starts */
+            for (int64_t n = 0; n < N; ++n)
+                h[n] = 0.0;
         double x = dl[t] + bias;
         double dt = j->softplus ? softplus(x) : x;
         double acc = 0.0;
@@ -146,9 +165,11 @@ static void forward_channel(const job_t *j, int64_t b, int64_t d)
 
 /*
  * Backward of one channel: reverse-mode differentiation of forward_channel
- * for the loss sum_t dy_t * out_t.  The forward states are recomputed and
- * kept for every step (Stage 7: the states are recomputed, not stored by the
- * forward).  g[n] carries dLoss/dh_t[n] from step t+1 back to step t.
+ * for the loss sum_t dy_t * out_t + sum_n dlast[n] * h_final[n].  The
+ * forward states are recomputed and kept for every step (Stage 7: the states
+ * are recomputed, not stored by the forward).  g[n] carries dLoss/dh_t[n]
+ * from step t+1 back to step t.  At a document start the carried state is
+ * multiplied by keep = 0 (the reset), so nothing flows back through it.
  */
 static void backward_channel(const slice_t *s, int64_t b, int64_t d, double *hist)
 {
@@ -171,12 +192,13 @@ static void backward_channel(const slice_t *s, int64_t b, int64_t d, double *his
     for (int64_t t = 0; t < len; ++t) {
         double x = dl[t] + bias;
         double dt = j->softplus ? softplus(x) : x;
+        double keep = resets(j, b, t) ? 0.0 : 1.0;
         for (int64_t n = 0; n < N; ++n)
-            hist[(t + 1) * N + n] = exp(dt * Arow[n]) * hist[t * N + n] + dt * Bb[n * L + t] * u[t];
+            hist[(t + 1) * N + n] = exp(dt * Arow[n]) * keep * hist[t * N + n] + dt * Bb[n * L + t] * u[t];
     }
 
     for (int64_t n = 0; n < N; ++n)
-        g[n] = 0.0;
+        g[n] = j->dlast ? j->dlast[ch * N + n] : 0.0;
     for (int64_t t = L - 1; t >= len; --t) {
         j->du[ch * L + t] = 0.0;
         j->ddelta[ch * L + t] = 0.0;
@@ -197,6 +219,7 @@ static void backward_channel(const slice_t *s, int64_t b, int64_t d, double *his
         }
         double du = dy0 * Dd;
         double ddt = 0.0;
+        double keep = resets(j, b, t) ? 0.0 : 1.0;      /* h_t = a keep h_{t-1} + ... */
         if (j->Dskip) s->dD[d] += dy0 * u[t];
         for (int64_t n = 0; n < N; ++n) {
             double a = exp(dt * Arow[n]);
@@ -204,15 +227,18 @@ static void backward_channel(const slice_t *s, int64_t b, int64_t d, double *his
             s->dC[b * N * L + n * L + t] += dy0 * hcur[n];
             s->dB[b * N * L + n * L + t] += gh * dt * u[t];
             du += gh * dt * Bb[n * L + t];
-            ddt += gh * (Bb[n * L + t] * u[t] + a * Arow[n] * hprev[n]);
-            s->dA[d * N + n] += gh * a * dt * hprev[n];
-            g[n] = gh * a;                              /* to h_{t-1}            */
+            ddt += gh * (Bb[n * L + t] * u[t] + a * Arow[n] * keep * hprev[n]);
+            s->dA[d * N + n] += gh * a * dt * keep * hprev[n];
+            g[n] = gh * a * keep;                       /* to h_{t-1}            */
         }
         double dx = j->softplus ? ddt * sigmoid(x) : ddt;
         j->du[ch * L + t] = du;
         j->ddelta[ch * L + t] = dx;
         if (j->bias) s->dbias[d] += dx;
     }
+    if (j->dh0)
+        for (int64_t n = 0; n < N; ++n)
+            j->dh0[ch * N + n] = g[n];                  /* dLoss/dh0             */
 }
 
 static void *run_forward(void *arg)
@@ -303,8 +329,8 @@ static int check_shape(int64_t Bsz, int64_t D, int64_t N, int64_t L)
 /*
  * Forward scan.  All arrays are C-contiguous doubles in the layouts of the
  * problem statement: u, delta, z, y (B,D,L); A (D,N); Bm, Cm (B,N,L);
- * Dskip, bias (D); h0, last_state (B,D,N).  Dskip, z, bias, lengths, h0,
- * last_state and states may be NULL.  rows (nrows entries of b*D+d) limits
+ * Dskip, bias (D); h0, last_state (B,D,N); seq_idx (B,L).  Dskip, z, bias,
+ * lengths, seq_idx, h0, last_state and states may be NULL.  rows (nrows entries of b*D+d) limits
  * the work to those channels; NULL means every channel.  states, when given,
  * receives for every channel K = ceil(L/every) states: entry k is the state
  * after min(k*every, len_b) steps.  Returns 0, or a negative code for a bad
@@ -314,7 +340,7 @@ int sso_fwd(int64_t Bsz, int64_t D, int64_t N, int64_t L, int softplus_flag,
             const double *u, const double *delta, const double *A,
             const double *Bm, const double *Cm, const double *Dskip,
             const double *z, const double *bias, const int64_t *lengths,
-            const double *h0, const int64_t *rows, int64_t nrows,
+            const int64_t *seq_idx, const double *h0, const int64_t *rows, int64_t nrows,
             double *y, double *last_state, double *states, int64_t states_every,
             int nthreads)
 {
@@ -327,6 +353,7 @@ int sso_fwd(int64_t Bsz, int64_t D, int64_t N, int64_t L, int softplus_flag,
     job.softplus = softplus_flag;
     job.u = u; job.delta = delta; job.A = A; job.Bm = Bm; job.Cm = Cm;
     job.Dskip = Dskip; job.z = z; job.bias = bias; job.lengths = lengths; job.h0 = h0;
+    job.seq_idx = seq_idx;
     job.rows = rows; job.nrows = nrows;
     job.y = y; job.last_state = last_state; job.states = states; job.states_every = states_every;
     int64_t nitems = rows ? nrows : Bsz * D;
@@ -369,18 +396,19 @@ int sso_step(int64_t Bsz, int64_t D, int64_t N, int softplus_flag,
 }
 
 /*
- * Backward scan for the loss sum(dy * out).  Inputs as sso_fwd (lengths and
- * h0 optional); every output is overwritten.  du, ddelta, dz: (B,D,L);
- * dA: (D,N); dB, dC: (B,N,L) summed over d; dD, dbias: (D) summed over b
- * and t.  dz must be given iff z is; dD iff Dskip; dbias iff bias.
+ * Backward scan for the loss sum(dy * out) + sum(dlast * h_final).  Inputs
+ * as sso_fwd (lengths, seq_idx, h0 and dlast optional); every output is
+ * overwritten.  du, ddelta, dz: (B,D,L); dA: (D,N); dB, dC: (B,N,L) summed
+ * over d; dD, dbias: (D) summed over b and t; dh0 (B,D,N), optional.  dz
+ * must be given iff z is; dD iff Dskip; dbias iff bias.
  */
 int sso_bwd(int64_t Bsz, int64_t D, int64_t N, int64_t L, int softplus_flag,
             const double *u, const double *delta, const double *A,
             const double *Bm, const double *Cm, const double *Dskip,
             const double *z, const double *bias, const int64_t *lengths,
-            const double *h0, const double *dy,
+            const int64_t *seq_idx, const double *h0, const double *dy, const double *dlast,
             double *du, double *ddelta, double *dz, double *dA,
-            double *dB, double *dC, double *dD, double *dbias, int nthreads)
+            double *dB, double *dC, double *dD, double *dbias, double *dh0, int nthreads)
 {
     if (check_shape(Bsz, D, N, L)) return -1;
     if (!u || !delta || !A || !Bm || !Cm || !dy || !du || !ddelta || !dA || !dB || !dC) return -1;
@@ -392,7 +420,8 @@ int sso_bwd(int64_t Bsz, int64_t D, int64_t N, int64_t L, int softplus_flag,
     job.softplus = softplus_flag;
     job.u = u; job.delta = delta; job.A = A; job.Bm = Bm; job.Cm = Cm;
     job.Dskip = Dskip; job.z = z; job.bias = bias; job.lengths = lengths; job.h0 = h0; job.dy = dy;
+    job.seq_idx = seq_idx; job.dlast = dlast;
     job.du = du; job.ddelta = ddelta; job.dz = dz; job.dA = dA; job.dB = dB; job.dC = dC;
-    job.dD = dD; job.dbias = dbias;
+    job.dD = dD; job.dbias = dbias; job.dh0 = dh0;
     return spawn(&job, Bsz * D, nthreads, 1);
 }

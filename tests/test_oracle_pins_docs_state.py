@@ -1,0 +1,188 @@
+"""Pins of the oracle's packed-document resets and initial/final-state gradients.
+
+"niverel-mamba" README, "seq_idx strict reset": at every change of the
+document id the state restarts from zero, so a packed row equals its
+documents run one by one; the README names nine structural cases, drawn by
+``inputs.make_seq_idx``.  Checked against (a) the oracle's plain forward on
+each document separately, (b) the brute-force unrolled form with resets,
+(c) central finite differences of the backward, including the gradients
+w.r.t. the initial state (dh0) and from the final state (dlast).  CPU only.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+from mamba_selective_scan_fwd_amd import inputs
+
+
+def _rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+def _rand(rng, Bsz, Dd, N, L):
+    return dict(u=rng.standard_normal((Bsz, Dd, L)), delta=rng.standard_normal((Bsz, Dd, L)),
+                A=-rng.uniform(0.1, 2.0, size=(Dd, N)), Bm=rng.standard_normal((Bsz, N, L)),
+                Cm=rng.standard_normal((Bsz, N, L)), D=rng.standard_normal(Dd),
+                z=rng.standard_normal((Bsz, Dd, L)), bias=rng.uniform(-2.0, 0.5, size=Dd))
+
+
+def _docs(row):
+    """[start, end) spans of the documents of one row of ids."""
+    cuts = [0] + [t for t in range(1, len(row)) if row[t] != row[t - 1]] + [len(row)]
+    return list(zip(cuts[:-1], cuts[1:]))
+
+
+@pytest.mark.parametrize("case", inputs.SEQ_CASES)
+def test_packed_row_equals_documents_one_by_one(case):
+    rng = np.random.default_rng(31)
+    Bsz, Dd, N, L = 3, 4, 5, 150
+    p = _rand(rng, Bsz, Dd, N, L)
+    seq = inputs.make_seq_idx(case, Bsz, L, seed=32).numpy()
+    y, last = oracle.fwd(p["u"], p["delta"], p["A"], p["Bm"], p["Cm"], D=p["D"], z=p["z"], bias=p["bias"],
+                         seq_idx=seq, threads=2)
+    for b in range(Bsz):
+        for s0, s1 in _docs(seq[b]):
+            yd, ld = oracle.fwd(p["u"][b:b + 1, :, s0:s1], p["delta"][b:b + 1, :, s0:s1], p["A"],
+                                p["Bm"][b:b + 1, :, s0:s1], p["Cm"][b:b + 1, :, s0:s1], D=p["D"],
+                                z=p["z"][b:b + 1, :, s0:s1], bias=p["bias"], threads=1)
+            assert _rel(y[b:b + 1, :, s0:s1], yd) < 1e-13
+        assert _rel(last[b:b + 1], ld) < 1e-13          # the last document's final state
+
+
+def test_packed_with_lengths_and_initial_state():
+    """Resets and ragged lengths together; the initial state feeds only the first document."""
+    rng = np.random.default_rng(33)
+    Bsz, Dd, N, L = 2, 3, 4, 90
+    p = _rand(rng, Bsz, Dd, N, L)
+    h0 = rng.standard_normal((Bsz, Dd, N))
+    seq = inputs.make_seq_idx("misaligned_rows", Bsz, L, seed=34).numpy()
+    lens = np.array([61, 90])
+    y, last = oracle.fwd(p["u"], p["delta"], p["A"], p["Bm"], p["Cm"], D=p["D"], z=p["z"], bias=p["bias"],
+                         seq_idx=seq, lengths=lens, h0=h0, threads=1)
+    for b in range(Bsz):
+        spans = [(s0, min(s1, lens[b])) for s0, s1 in _docs(seq[b]) if s0 < lens[b]]
+        for k, (s0, s1) in enumerate(spans):
+            yd, ld = oracle.fwd(p["u"][b:b + 1, :, s0:s1], p["delta"][b:b + 1, :, s0:s1], p["A"],
+                                p["Bm"][b:b + 1, :, s0:s1], p["Cm"][b:b + 1, :, s0:s1], D=p["D"],
+                                z=p["z"][b:b + 1, :, s0:s1], bias=p["bias"], h0=h0[b:b + 1] if k == 0 else None,
+                                threads=1)
+            assert _rel(y[b:b + 1, :, s0:s1], yd) < 1e-13
+        assert _rel(last[b:b + 1], ld) < 1e-13
+        assert np.all(y[b, :, lens[b]:] == 0.0)
+
+
+@pytest.mark.parametrize("with_h0", [False, True])
+def test_resets_and_h0_match_unrolled_form(with_h0):
+    rng = np.random.default_rng(35)
+    Bsz, Dd, N, L = 2, 2, 3, 11
+    p = _rand(rng, Bsz, Dd, N, L)
+    seq = np.array([[0, 0, 1, 2, 2, 2, 3, 3, 3, 3, 4], [5, 5, 5, 5, 5, 6, 6, 7, 7, 7, 7]])
+    h0 = rng.standard_normal((Bsz, Dd, N)) if with_h0 else None
+    y, _ = oracle.fwd(p["u"], p["delta"], p["A"], p["Bm"], p["Cm"], D=p["D"], z=p["z"], bias=p["bias"],
+                      seq_idx=seq, h0=h0, threads=1)
+    yb = brute.unrolled_fwd(p["u"], p["delta"], p["A"], p["Bm"], p["Cm"], D=p["D"], z=p["z"], bias=p["bias"],
+                            seq_idx=seq, h0=h0)
+    assert _rel(y, yb) < 1e-12
+
+
+# ------------------------------------------------------------- backward pins
+
+def _loss(p, dy, seq, dlast, **over):
+    q = dict(p)
+    q.update(over)
+    y, last = oracle.fwd(q["u"], q["delta"], q["A"], q["Bm"], q["Cm"], D=q["D"], z=q["z"], bias=q["bias"],
+                         seq_idx=seq, h0=q.get("h0"), threads=1)
+    out = float(np.sum(dy * y))
+    if dlast is not None:
+        out += float(np.sum(dlast * last))
+    return out
+
+
+def _fd(p, dy, seq, h0, dlast, names, tol):
+    g = oracle.bwd(p["u"], p["delta"], p["A"], p["Bm"], p["Cm"], dy, D=p["D"], z=p["z"], bias=p["bias"],
+                   seq_idx=seq, h0=h0, dlast=dlast, want_dh0=True, threads=1)
+    q0 = dict(p)
+    if h0 is not None:
+        q0["h0"] = h0
+    for name, gname in names.items():
+        base = q0[name]
+        fd = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            h = 1e-3 * max(1.0, abs(base[idx]))
+            f = {}
+            for k in (-2, -1, 1, 2):
+                q = base.copy()
+                q[idx] += k * h
+                f[k] = _loss(q0, dy, seq, dlast, **{name: q})
+            fd[idx] = (8.0 * (f[1] - f[-1]) - (f[2] - f[-2])) / (12.0 * h)
+        assert _rel(g[gname], fd) < tol, (gname, _rel(g[gname], fd))
+    return g
+
+
+ALL = {"u": "du", "delta": "ddelta", "A": "dA", "Bm": "dB", "Cm": "dC", "z": "dz", "D": "dD", "bias": "dbias"}
+
+
+def test_backward_fd_with_resets():
+    rng = np.random.default_rng(36)
+    Bsz, Dd, N, L = 2, 2, 3, 9
+    p = _rand(rng, Bsz, Dd, N, L)
+    dy = rng.standard_normal((Bsz, Dd, L))
+    seq = np.array([[0, 0, 1, 1, 1, 2, 3, 3, 3], [4, 5, 5, 5, 5, 5, 5, 6, 6]])
+    _fd(p, dy, seq, None, None, ALL, 1e-7)
+
+
+def test_backward_fd_initial_and_final_state():
+    """dh0 and the dlast term of the loss, with and without resets."""
+    rng = np.random.default_rng(37)
+    Bsz, Dd, N, L = 2, 2, 3, 8
+    p = _rand(rng, Bsz, Dd, N, L)
+    dy = rng.standard_normal((Bsz, Dd, L))
+    h0 = rng.standard_normal((Bsz, Dd, N))
+    dlast = rng.standard_normal((Bsz, Dd, N))
+    _fd(p, dy, None, h0, dlast, dict(ALL, h0="dh0"), 1e-7)
+    seq = np.array([[0, 0, 0, 1, 1, 1, 1, 1], [2, 2, 2, 2, 2, 2, 2, 2]])
+    g = _fd(p, dy, seq, h0, dlast, dict(ALL, h0="dh0"), 1e-7)
+    # row 0: the initial state reaches only the first document [0, 3), and the
+    # final state belongs to the second, so dh0 is the first document's alone
+    sl = lambda a: np.ascontiguousarray(a[:1, :, :3])
+    g1 = oracle.bwd(sl(p["u"]), sl(p["delta"]), p["A"], sl(p["Bm"]), sl(p["Cm"]), sl(dy), D=p["D"], z=sl(p["z"]),
+                    bias=p["bias"], h0=h0[:1], want_dh0=True, threads=1)
+    assert _rel(g["dh0"][:1], g1["dh0"]) < 1e-13
+
+
+def test_dh0_without_outputs_is_the_decayed_dlast():
+    """With dy = 0 the loss is dlast . h_L, and h_L depends on h0 through prod_t exp(Delta_t A):
+    dh0 = dlast * exp(A * sum_t Delta_t) (closed form)."""
+    rng = np.random.default_rng(38)
+    Bsz, Dd, N, L = 2, 3, 4, 13
+    p = _rand(rng, Bsz, Dd, N, L)
+    dlast = rng.standard_normal((Bsz, Dd, N))
+    g = oracle.bwd(p["u"], p["delta"], p["A"], p["Bm"], p["Cm"], np.zeros((Bsz, Dd, L)), D=p["D"], z=p["z"],
+                   bias=p["bias"], dlast=dlast, want_dh0=True, threads=1)
+    x = p["delta"] + p["bias"][None, :, None]
+    dsum = np.sum(np.logaddexp(0.0, x), axis=2)                     # softplus, summed over t
+    expect = dlast * np.exp(p["A"][None, :, :] * dsum[:, :, None])
+    assert _rel(g["dh0"], expect) < 1e-13
+
+
+def test_backward_packed_equals_documents():
+    """Gradients of a packed row == the documents' gradients, each run on its own."""
+    rng = np.random.default_rng(39)
+    Bsz, Dd, N, L = 1, 3, 4, 70
+    p = _rand(rng, Bsz, Dd, N, L)
+    dy = rng.standard_normal((Bsz, Dd, L))
+    seq = inputs.make_seq_idx("inside_one_tile", Bsz, L, seed=40).numpy()
+    g = oracle.bwd(p["u"], p["delta"], p["A"], p["Bm"], p["Cm"], dy, D=p["D"], z=p["z"], bias=p["bias"],
+                   seq_idx=seq, threads=1)
+    acc = {k: 0.0 for k in ("dA", "dD", "dbias")}
+    for s0, s1 in _docs(seq[0]):
+        sl = lambda a: np.ascontiguousarray(a[:, :, s0:s1])
+        gd = oracle.bwd(sl(p["u"]), sl(p["delta"]), p["A"], sl(p["Bm"]), sl(p["Cm"]), sl(dy), D=p["D"],
+                        z=sl(p["z"]), bias=p["bias"], threads=1)
+        for k in ("du", "ddelta", "dz", "dB", "dC"):
+            assert _rel(g[k][:, :, s0:s1], gd[k]) < 1e-12, k
+        for k in acc:
+            acc[k] = acc[k] + gd[k]
+    for k in acc:
+        assert _rel(g[k], acc[k]) < 1e-12, k
