@@ -177,6 +177,24 @@ def bench_rows(stream):
         "alg_GBps": byt / (ms * 1e-3) / 1e9, "hbm_frac": byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "alu_frac": fwd_alg_slots(4, 5120, 16, 8192, 2, lens) / (ms * 1e-3) / PEAK_SLOTS}
     del p3, c3, y3
+    # packed documents (lengths U[1, 512]) and an initial state on the mamba-130m layer
+    prob2p = inputs.make_config(2, decode_steps=0)
+    g2p = dev_problem(prob2p)
+    del prob2p
+    seq = inputs.packed_documents(2048, 8, 512, seed=7).to("cuda")
+    h0 = torch.randn((8, 1536, 16), dtype=torch.float32, device="cuda")
+    y2p = torch.empty_like(g2p["u"])
+    s2p = torch.empty((8, 1536, 16), dtype=torch.float32, device="cuda")
+    c2p = ss.FwdCall(g2p["u"], g2p["delta"], g2p["A"], g2p["Bm"], g2p["Cm"], D=g2p["D"], z=g2p["z"],
+                     delta_bias=g2p["bias"], y=y2p, last_state=s2p, stream=stream, seq_idx=seq, h0=h0)
+    fp = lambda i: c2p()
+    fp(0)
+    ms = timed(fp, 20, stream)
+    docs = int((seq[:, 1:] != seq[:, :-1]).sum().item()) + 8
+    rows["fwd_packed_docs_h0_B8_D1536_L2048_f16"] = {
+        "ms": ms, "documents": docs, "token_channel_per_s": 8 * 1536 * 2048 / (ms * 1e-3),
+        "alu_frac": fwd_alg_slots(8, 1536, 16, 2048, 2) / (ms * 1e-3) / PEAK_SLOTS}
+    del g2p, c2p, y2p, s2p, seq, h0
     # decode: 64 single steps on the mamba-130m state
     prob2 = inputs.make_config(2, decode_steps=64)
     g2 = dev_problem(prob2)
@@ -234,7 +252,18 @@ def bench_rows(stream):
         byt = (Bsz * Dd * L * 4 * 7 + 2 * Bsz * N * L * 4 * 2 + ck.numel() * 4 + 4 * (Dd * N + 2 * Dd) * 2)
         rows["bwd_B4_D1536_L4097_f32"] = {"ms": ms, "token_channel_per_s": Bsz * Dd * L / (ms * 1e-3),
                                           "alg_GBps": byt / (ms * 1e-3) / 1e9}
-        del p4, ck
+        # the same with packed documents (lengths U[1, 600]), a final-state gradient and dh0
+        seq = inputs.packed_documents(L, Bsz, 600, seed=8).to("cuda")
+        dlast = torch.randn((Bsz, Dd, N), dtype=torch.float32, device="cuda")
+        _, _, ck2 = ss.fwd(p4["u"], p4["delta"], p4["A"], p4["Bm"], p4["Cm"], D=p4["D"], z=p4["z"],
+                           delta_bias=p4["bias"], return_ckpt=True, seq_idx=seq)
+        fb2 = lambda i: ss.bwd(p4["u"], p4["delta"], p4["A"], p4["Bm"], p4["Cm"], ck2, p4["dy"], D=p4["D"],
+                               z=p4["z"], delta_bias=p4["bias"], seq_idx=seq, dlast=dlast, want_dh0=True)
+        fb2(0)
+        ms = timed(fb2, 5, stream)
+        rows["bwd_packed_docs_dlast_dh0_B4_D1536_L4097_f32"] = {
+            "ms": ms, "token_channel_per_s": Bsz * Dd * L / (ms * 1e-3)}
+        del p4, ck, ck2, seq, dlast
     except RuntimeError as e:
         rows["bwd_B4_D1536_L4097_f32"] = {"error": str(e)[:200]}
     torch.cuda.empty_cache()

@@ -17,15 +17,20 @@
  *     h_t[n]   = Abar_t h_{t-1}[n] + Delta_t B[b,n,t] u[b,d,t]   (Euler for B)
  *     y0_t     = sum_n C[b,n,t] h_t[n] + D[d] u[b,d,t]           (Stage 6 skip)
  *     y[b,d,t] = y0_t * z_t * sigmoid(z_t)   (gate, Stage 6; y0_t if z absent)
- *   with h_{-1} = 0.  "mamba-metal" README ("Long-context prompts") adds the
- *   final state h_{L-1}, from which decode continues one token at a time.
+ *   with h_{-1} = 0 (or a given initial state h0).  "mamba-metal" README
+ *   ("Long-context prompts") adds the final state h_{L-1}, from which decode
+ *   continues one token at a time.  With packed documents ("niverel-mamba"
+ *   README, "seq_idx strict reset") the state is zero before every step t >= 1
+ *   whose document id seq_idx[b,t] differs from seq_idx[b,t-1].
  *
  * Layouts: every tensor is C-contiguous with the time axis innermost:
  *   u, delta, z, y, dy, du, ddelta, dz : (batch, dim, seqlen)   io dtype
  *   Bm, Cm, dB, dC                     : (batch, dstate, seqlen) io dtype (dB, dC: fp32)
  *   A, dA                              : (dim, dstate)  fp32
  *   D, bias, dD, dbias                 : (dim)          fp32
- *   last_state, state_in, state_out    : (batch, dim, dstate) fp32
+ *   last_state, state_in, state_out,
+ *   h0, dh0, dlast                     : (batch, dim, dstate) fp32
+ *   seq_idx                            : (batch, seqlen) int32
  *   ckpt                               : (batch, dim, ceil(seqlen/64), dstate) fp32
  * Data tensors may be fp32, fp16 or bf16 (`io_dtype`); the weights A, D,
  * bias and every state are fp32, and all arithmetic is fp32 ("mamba-metal"
@@ -82,14 +87,25 @@ size_t ss_fwd_workspace_size(const ss_problem *p);
  * state of the "mamba-metal" README).  Writes y for every t < seqlen.
  *   D, z, delta_bias  : optional (NULL = no skip / no gate / zero bias).
  *   lengths           : optional device int32[batch]; row b runs
- *                       min(max(lengths[b], 0), seqlen) steps from a zero
- *                       state, y is exactly 0 past that length and
+ *                       min(max(lengths[b], 0), seqlen) steps from its
+ *                       initial state, y is exactly 0 past that length and
  *                       last_state is the state after that many steps.
  *                       Out-of-range values are clamped, not reported.
+ *   seq_idx           : optional device int32 (batch, seqlen) document ids
+ *                       ("niverel-mamba" README, "seq_idx strict reset"):
+ *                       the state is reset to zero before every step whose
+ *                       id differs from the previous step's, so a packed row
+ *                       gives the same y as its documents run one by one.
+ *                       Any int32 values; only changes matter.
+ *   h0                : optional (batch, dim, dstate) fp32 initial state
+ *                       (NULL = zero): prefill in pieces, each piece started
+ *                       from the previous piece's last_state, equals one
+ *                       prefill of the whole sequence.  It feeds only the
+ *                       row's first document.
  *   last_state        : optional (batch, dim, dstate) fp32 output.
  *   ckpt              : optional (batch, dim, ceil(seqlen/64), dstate) fp32
  *                       output: entry k is the state after min(64k, len)
- *                       steps (entry 0 is zero), the checkpoints of page
+ *                       steps (entry 0 is h0, or zero), the checkpoints of page
  *                       "Mamba, on a laptop GPU", "The state lives in
  *                       registers", used by ss_bwd.
  *   workspace         : device buffer of ss_fwd_workspace_size() bytes, or
@@ -100,7 +116,7 @@ ss_status ss_fwd(const ss_problem *p,
                  const void *u, const void *delta, const float *A,
                  const void *Bm, const void *Cm,
                  const float *D, const void *z, const float *delta_bias,
-                 const int32_t *lengths,
+                 const int32_t *lengths, const int32_t *seq_idx, const float *h0,
                  void *y, float *last_state, float *ckpt,
                  void *workspace, size_t workspace_bytes,
                  void *stream);
@@ -130,11 +146,17 @@ ss_status ss_fwd_step(const ss_problem *p,
 size_t ss_bwd_workspace_size(const ss_problem *p);
 
 /*
- * Backward scan for the loss sum(dy * y) (page "Mamba", Part IV Stage 7:
- * the states are recomputed, here from the 64-step checkpoints that ss_fwd
- * wrote, walking the chunks in reverse as page "Mamba, on a laptop GPU",
- * "The state lives in registers", describes).
- *   ckpt         : the checkpoints ss_fwd wrote for the same inputs (no lengths).
+ * Backward scan for the loss sum(dy * y) + sum(dlast * last_state) (page
+ * "Mamba", Part IV Stage 7: the states are recomputed, here from the 64-step
+ * checkpoints that ss_fwd wrote, walking the chunks in reverse as page
+ * "Mamba, on a laptop GPU", "The state lives in registers", describes).
+ *   ckpt         : the checkpoints ss_fwd wrote for the same inputs (the same
+ *                  seq_idx and h0; no lengths).
+ *   seq_idx      : optional document ids, as in ss_fwd.
+ *   dlast        : optional (batch, dim, dstate) fp32 gradient of the loss
+ *                  w.r.t. the final state (NULL = zero).
+ *   dh0          : optional (batch, dim, dstate) fp32 output, the gradient
+ *                  w.r.t. the initial state.
  *   du, ddelta   : (batch, dim, seqlen) io dtype outputs.
  *   dz           : output iff z is given.  dD iff D.  dbias iff delta_bias.
  *   dA (dim, dstate), dB, dC (batch, dstate, seqlen), dD, dbias (dim): fp32,
@@ -149,9 +171,9 @@ ss_status ss_bwd(const ss_problem *p,
                  const void *u, const void *delta, const float *A,
                  const void *Bm, const void *Cm,
                  const float *D, const void *z, const float *delta_bias,
-                 const float *ckpt, const void *dy,
+                 const int32_t *seq_idx, const float *ckpt, const void *dy, const float *dlast,
                  void *du, void *ddelta, void *dz,
-                 float *dA, float *dB, float *dC, float *dD, float *dbias,
+                 float *dA, float *dB, float *dC, float *dD, float *dbias, float *dh0,
                  void *workspace, size_t workspace_bytes,
                  void *stream);
 

@@ -98,11 +98,12 @@ size_t ss_fwd_workspace_size(const ss_problem* p) {
 
 ss_status ss_fwd(const ss_problem* p, const void* u, const void* delta, const float* A, const void* Bm,
                  const void* Cm, const float* D, const void* z, const float* delta_bias, const int32_t* lengths,
-                 void* y, float* last_state, float* ckpt, void* workspace, size_t workspace_bytes, void* stream) {
+                 const int32_t* seq_idx, const float* h0, void* y, float* last_state, float* ckpt, void* workspace,
+                 size_t workspace_bytes, void* stream) {
   ss_status s = check_problem(p, true);
   if (s != SS_OK) return s;
   if (!u || !delta || !A || !Bm || !Cm || !y) return SS_ERR_NULL_ARG;
-  const void* ptrs[] = {u, delta, A, Bm, Cm, D, z, delta_bias, lengths, y, last_state, ckpt, workspace};
+  const void* ptrs[] = {u, delta, A, Bm, Cm, D, z, delta_bias, lengths, seq_idx, h0, y, last_state, ckpt, workspace};
   for (const void* q : ptrs)
     if (q && !aligned(q)) return SS_ERR_MISALIGNED;
   const FwdPlan pl = plan_fwd(p);
@@ -112,7 +113,7 @@ ss_status ss_fwd(const ss_problem* p, const void* u, const void* delta, const fl
   k.io = p->io_dtype;
   k.softplus = p->delta_softplus != 0;
   k.u = u; k.delta = delta; k.z = z; k.Bm = Bm; k.Cm = Cm;
-  k.A = A; k.D = D; k.bias = delta_bias; k.lengths = lengths;
+  k.A = A; k.D = D; k.bias = delta_bias; k.lengths = lengths; k.seq_idx = seq_idx; k.h0 = h0;
   k.y = y; k.last_state = last_state; k.ckpt = ckpt;
   k.batch = p->batch; k.dim = p->dim; k.dstate = p->dstate; k.seqlen = p->seqlen;
   k.chunk_len = pl.chunk_len;
@@ -161,9 +162,10 @@ size_t ss_bwd_workspace_size(const ss_problem* p) {
 }
 
 ss_status ss_bwd(const ss_problem* p, const void* u, const void* delta, const float* A, const void* Bm,
-                 const void* Cm, const float* D, const void* z, const float* delta_bias, const float* ckpt,
-                 const void* dy, void* du, void* ddelta, void* dz, float* dA, float* dB, float* dC, float* dD,
-                 float* dbias, void* workspace, size_t workspace_bytes, void* stream) {
+                 const void* Cm, const float* D, const void* z, const float* delta_bias, const int32_t* seq_idx,
+                 const float* ckpt, const void* dy, const float* dlast, void* du, void* ddelta, void* dz, float* dA,
+                 float* dB, float* dC, float* dD, float* dbias, float* dh0, void* workspace, size_t workspace_bytes,
+                 void* stream) {
   ss_status s = check_problem(p, true);
   if (s != SS_OK) return s;
   if (!u || !delta || !A || !Bm || !Cm || !ckpt || !dy || !du || !ddelta || !dA || !dB || !dC)
@@ -171,8 +173,8 @@ ss_status ss_bwd(const ss_problem* p, const void* u, const void* delta, const fl
   if ((z == nullptr) != (dz == nullptr) || (D == nullptr) != (dD == nullptr) ||
       (delta_bias == nullptr) != (dbias == nullptr))
     return SS_ERR_NULL_ARG;
-  const void* ptrs[] = {u, delta, A, Bm, Cm, D, z, delta_bias, ckpt, dy, du, ddelta, dz, dA, dB, dC, dD, dbias,
-                        workspace};
+  const void* ptrs[] = {u, delta, A, Bm, Cm, D, z, delta_bias, seq_idx, ckpt, dy, dlast, du, ddelta, dz, dA, dB, dC,
+                        dD, dbias, dh0, workspace};
   for (const void* q : ptrs)
     if (q && !aligned(q)) return SS_ERR_MISALIGNED;
   const size_t need = ss_bwd_workspace_size(p);
@@ -183,6 +185,7 @@ ss_status ss_bwd(const ss_problem* p, const void* u, const void* delta, const fl
   k.softplus = p->delta_softplus != 0;
   k.u = u; k.delta = delta; k.z = z; k.Bm = Bm; k.Cm = Cm;
   k.A = A; k.D = D; k.bias = delta_bias; k.ckpt = ckpt; k.dy = dy;
+  k.seq_idx = seq_idx; k.dlast = dlast; k.dh0 = dh0;
   k.du = du; k.ddelta = ddelta; k.dz = dz;
   k.dA = dA; k.dB = dB; k.dC = dC; k.dD = dD; k.dbias = dbias;
   k.batch = p->batch; k.dim = p->dim; k.dstate = p->dstate; k.seqlen = p->seqlen;

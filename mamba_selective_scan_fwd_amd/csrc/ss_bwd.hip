@@ -23,6 +23,11 @@
 //         and walk them backwards with the true carried gradient, emit du, ddelta,
 //         dz, accumulate dB/dC and dA/dD/dbias partials;
 //   REDUCE sum the dA/dD/dbias partials over (batch row, chunk).
+// Packed documents: the decay of a step that starts a new document is 0 in
+// every recomputation and in the reverse walk, so no gradient crosses a
+// document start.  The caller's gradient of the final state seeds the walk
+// at the last step, and the gradient left after step 0 is returned as the
+// gradient w.r.t. the initial state.
 // Lane layout as the forward: a wavefront holds 4 channels x 16 states; the
 // per-(t, d) work is owned by lane l = t mod 16 of the channel's row and
 // broadcast with DPP; sums over states go through an LDS transpose; sums over
@@ -162,8 +167,8 @@ __device__ __forceinline__ void prep(BwdOwned& o, const BwdRaw<IO>& r, int64_t t
 }
 
 // ---- AGG: reverse walk of one chunk with a zero carry ------------------------
-template <int I, int... J>
-__device__ __forceinline__ void agg_block(float& g, const BwdOwned& o, float A2, const float* sCrow,
+template <int I, bool RESET, int... J>
+__device__ __forceinline__ void agg_block(float& g, const BwdOwned& o, float A2, const float* sCrow, uint64_t starts,
                                           std::integer_sequence<int, J...>) {
   // J runs 0..15; step s = 16 I + (15 - J) goes backwards
   float4 c4;
@@ -173,7 +178,7 @@ __device__ __forceinline__ void agg_block(float& g, const BwdOwned& o, float A2,
         constexpr int s = 16 * I + jj;
         if constexpr (jj % 4 == 3) c4 = *reinterpret_cast<const float4*>(sCrow + s - 3);
         const float cj = (jj % 4 == 0) ? c4.x : (jj % 4 == 1) ? c4.y : (jj % 4 == 2) ? c4.z : c4.w;
-        const float a = exp2_hw(row_bcast<jj>(o.dt[I]) * A2);
+        const float a = reset_decay<RESET, s>(exp2_hw(row_bcast<jj>(o.dt[I]) * A2), starts);
         const float G = fmaf(row_bcast<jj>(o.dy0[I]), cj, g);
         g = G * a;
       }(),
@@ -187,9 +192,10 @@ __device__ __forceinline__ void agg_block(float& g, const BwdOwned& o, float A2,
 // C h in the sum-over-states tile); fwd_states recomputes block I's 16
 // states from its entry state into hs[0..16] just before the reverse walk
 // needs them, so that only 17 states (not 65) are live at once.
-template <int I, bool WITH_Y, int... J>
+template <int I, bool WITH_Y, bool RESET, int... J>
 __device__ __forceinline__ void fwd_pass(float& h, const BwdOwned& o, float A2, const float* sBrow,
-                                         const float* sCrow, float* t1c, int n, std::integer_sequence<int, J...>) {
+                                         const float* sCrow, float* t1c, int n, uint64_t starts,
+                                         std::integer_sequence<int, J...>) {
   float4 b4, c4;
   (
       [&] {
@@ -199,7 +205,7 @@ __device__ __forceinline__ void fwd_pass(float& h, const BwdOwned& o, float A2, 
           if constexpr (WITH_Y) c4 = *reinterpret_cast<const float4*>(sCrow + s);
         }
         const float bj = (J % 4 == 0) ? b4.x : (J % 4 == 1) ? b4.y : (J % 4 == 2) ? b4.z : b4.w;
-        const float a = exp2_hw(row_bcast<J>(o.dt[I]) * A2);
+        const float a = reset_decay<RESET, s>(exp2_hw(row_bcast<J>(o.dt[I]) * A2), starts);
         h = fmaf(a, h, row_bcast<J>(o.dtu[I]) * bj);
         if constexpr (WITH_Y) {
           const float cj = (J % 4 == 0) ? c4.x : (J % 4 == 1) ? c4.y : (J % 4 == 2) ? c4.z : c4.w;
@@ -211,9 +217,9 @@ __device__ __forceinline__ void fwd_pass(float& h, const BwdOwned& o, float A2, 
   __builtin_amdgcn_sched_barrier(0);  // no hoisting across blocks (registers)
 }
 
-template <int I, int... J>
+template <int I, bool RESET, int... J>
 __device__ __forceinline__ void fwd_states(float (&hs)[17], float h0, const BwdOwned& o, float A2,
-                                           const float* sBrow, std::integer_sequence<int, J...>) {
+                                           const float* sBrow, uint64_t starts, std::integer_sequence<int, J...>) {
   float4 b4;
   hs[0] = h0;
   (
@@ -221,7 +227,7 @@ __device__ __forceinline__ void fwd_states(float (&hs)[17], float h0, const BwdO
         constexpr int s = 16 * I + J;
         if constexpr (J % 4 == 0) b4 = *reinterpret_cast<const float4*>(sBrow + s);
         const float bj = (J % 4 == 0) ? b4.x : (J % 4 == 1) ? b4.y : (J % 4 == 2) ? b4.z : b4.w;
-        const float a = exp2_hw(row_bcast<J>(o.dt[I]) * A2);
+        const float a = reset_decay<RESET, s>(exp2_hw(row_bcast<J>(o.dt[I]) * A2), starts);
         hs[J + 1] = fmaf(a, hs[J], row_bcast<J>(o.dtu[I]) * bj);
       }(),
       ...);
@@ -233,10 +239,10 @@ __device__ __forceinline__ void fwd_states(float (&hs)[17], float h0, const BwdO
 // Per step: the per-state terms G B and A G a h_{t-1} go to the sum-over-states
 // tiles (their row sums give du and dDelta), the per-channel terms G Delta u
 // and dy0 h_t to the sum-over-channels tiles (dB and dC).
-template <int I, int... J>
+template <int I, bool RESET, int... J>
 __device__ __forceinline__ void bwd_block(float& g, float& dA_acc, const float (&hs)[17], const BwdOwned& o,
                                           float A2, float Anat, const float* sBrow, const float* sCrow, float* t1c,
-                                          float* t2c, float* t3w, float* t4w, int n, int cw,
+                                          float* t2c, float* t3w, float* t4w, int n, int cw, uint64_t starts,
                                           std::integer_sequence<int, J...>) {
   float4 b4, c4;
   (
@@ -251,7 +257,7 @@ __device__ __forceinline__ void bwd_block(float& g, float& dA_acc, const float (
         const float cqj = (jj % 4 == 0) ? c4.x : (jj % 4 == 1) ? c4.y : (jj % 4 == 2) ? c4.z : c4.w;
         const float dtb = row_bcast<jj>(o.dt[I]);
         const float dy0b = row_bcast<jj>(o.dy0[I]);
-        const float a = exp2_hw(dtb * A2);
+        const float a = reset_decay<RESET, s>(exp2_hw(dtb * A2), starts);
         const float gh = fmaf(dy0b, cqj, g);  // dLoss/dh_t
         t4w[(jj * 16 + n) * kChPerWave + cw] = dy0b * hs[jj + 1];
         t3w[(jj * 16 + n) * kChPerWave + cw] = gh * row_bcast<jj>(o.dtu[I]);
@@ -282,7 +288,7 @@ __device__ __forceinline__ void collect_block(float (&accB)[4][4], float (&accC)
   }
 }
 
-template <int IO, bool MAIN>
+template <int IO, bool MAIN, bool SEQ>
 __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int32_t groups, int32_t per_group) {
   __shared__ BwdSmem<MAIN> sm;
   constexpr uint32_t s = io_bytes<IO>();
@@ -322,6 +328,14 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
       sm.C[sn][e] = ok ? cv : 0.0f;
     }
   }
+  // document starts among the chunk's steps (every wave computes the mask)
+  uint64_t starts = 0;
+  if constexpr (SEQ) {
+    const __amdgpu_buffer_rsrc_t ids = make_rsrc(p.seq_idx + b * p.seqlen, L * 4u);
+    uint32_t id_t, id_prev;
+    load_doc_ids(ids, (int)t0 + lane, id_t, id_prev);
+    starts = doc_starts(id_t, id_prev, (int)t0 + lane, (int)t_end);
+  }
   __syncthreads();
 
   const float* sBrow = &sm.B[n][0];
@@ -359,15 +373,18 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
     }
     const int64_t wslot = ((ch * K + k) * kStates + n);
 
+    // gradient entering the chunk from the right with a zero carry; the last
+    // chunk also receives the caller's gradient of the final state
+    const float g_last = (k == K - 1 && p.dlast && ch_ok && n_ok) ? p.dlast[ch * p.dstate + n] : 0.0f;
     if constexpr (!MAIN) {
-      float g = 0.0f;
-      agg_block<3>(g, o, A2, sCrow, seq);
-      agg_block<2>(g, o, A2, sCrow, seq);
-      agg_block<1>(g, o, A2, sCrow, seq);
-      agg_block<0>(g, o, A2, sCrow, seq);
+      float g = g_last;
+      agg_block<3, SEQ>(g, o, A2, sCrow, starts, seq);
+      agg_block<2, SEQ>(g, o, A2, sCrow, starts, seq);
+      agg_block<1, SEQ>(g, o, A2, sCrow, starts, seq);
+      agg_block<0, SEQ>(g, o, A2, sCrow, starts, seq);
       const float dsum = row_sum((o.dt[0] + o.dt[1]) + (o.dt[2] + o.dt[3]));
       if (ch_ok) {
-        p.aggP[wslot] = exp2_hw(A2 * dsum);
+        p.aggP[wslot] = starts != 0 ? 0.0f : exp2_hw(A2 * dsum);
         p.aggG[wslot] = g;
       }
     } else {
@@ -381,7 +398,7 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
       if (need_z) {
 #define SS_FWD_Y(I)                                                        \
   hb[I] = h;                                                               \
-  fwd_pass<I, true>(h, o, A2, sBrow, sCrow, t1c, n, seq);                  \
+  fwd_pass<I, true, SEQ>(h, o, A2, sBrow, sCrow, t1c, n, starts, seq);     \
   wave_lds_sync();                                                         \
   o.y0[I] = fmaf(Dd, o.u[I], row16_sum(t1c, l));                           \
   wave_lds_sync();
@@ -392,15 +409,15 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
 #undef SS_FWD_Y
       } else {
         hb[0] = h;
-        fwd_pass<0, false>(h, o, A2, sBrow, sCrow, t1c, n, seq);
+        fwd_pass<0, false, SEQ>(h, o, A2, sBrow, sCrow, t1c, n, starts, seq);
         hb[1] = h;
-        fwd_pass<1, false>(h, o, A2, sBrow, sCrow, t1c, n, seq);
+        fwd_pass<1, false, SEQ>(h, o, A2, sBrow, sCrow, t1c, n, starts, seq);
         hb[2] = h;
-        fwd_pass<2, false>(h, o, A2, sBrow, sCrow, t1c, n, seq);
+        fwd_pass<2, false, SEQ>(h, o, A2, sBrow, sCrow, t1c, n, starts, seq);
         hb[3] = h;
       }
 
-      float g = (k < K - 1 && ch_ok) ? p.gcarry[wslot] : 0.0f;
+      float g = (k < K - 1 && ch_ok) ? p.gcarry[wslot] : g_last;
       float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
 #define SS_BWD(I)                                                                                   \
   {                                                                                                 \
@@ -408,8 +425,8 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
     o.dt[I] = fresh(o.dt[I]);                                                                       \
     o.dtu[I] = fresh(o.dtu[I]);                                                                     \
     o.dy0[I] = fresh(o.dy0[I]);                                                                     \
-    fwd_states<I>(hs, hb[I], o, A2, sBrow, seq);                                                    \
-    bwd_block<I>(g, dA_acc, hs, o, A2, A, sBrow, sCrow, t1c, t2c, t3w, t4w, n, cw, seq);            \
+    fwd_states<I, SEQ>(hs, hb[I], o, A2, sBrow, starts, seq);                                       \
+    bwd_block<I, SEQ>(g, dA_acc, hs, o, A2, A, sBrow, sCrow, t1c, t2c, t3w, t4w, n, cw, starts, seq);\
     wave_lds_sync();                                                                                \
     const float sGB = row16_sum(t1c, l);                                                            \
     const float sQA = row16_sum(t2c, l);                                                            \
@@ -436,6 +453,8 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
       SS_BWD(1)
       SS_BWD(0)
 #undef SS_BWD
+      // the gradient left after step 0 is the gradient w.r.t. the initial state
+      if (k == 0 && p.dh0 && ch_ok && n_ok) p.dh0[ch * p.dstate + n] = g;
       // partial sums of this (batch row, chunk) for the reduction pass
       const int64_t bk = b * K + k;
       if (ch_ok) p.aggP[(bk * p.dim + d) * kStates + n] = dA_acc;
@@ -526,8 +545,8 @@ hipError_t fill(float* dst, int64_t count, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int IO>
-hipError_t launch_bwd_io(const BwdParams& p, hipStream_t st) {
+template <int IO, bool SEQ>
+hipError_t launch_bwd_seq(const BwdParams& p, hipStream_t st) {
   const int64_t K = p.nchunks;
   hipError_t e = fill(p.dB, p.batch * p.dstate * p.seqlen, st);
   if (e != hipSuccess) return e;
@@ -544,14 +563,14 @@ hipError_t launch_bwd_io(const BwdParams& p, hipStream_t st) {
   const dim3 grid((uint32_t)(bk * groups));
   if (K > 1) {
     // AGG has nothing to reduce over channels: one channel block per workgroup
-    hipLaunchKernelGGL((ss_bwd_chunk_kernel<IO, false>), dim3((uint32_t)(bk * p.ch_blocks)), dim3(kThreads), 0, st, p,
-                       (int32_t)p.ch_blocks, 1);
+    hipLaunchKernelGGL((ss_bwd_chunk_kernel<IO, false, SEQ>), dim3((uint32_t)(bk * p.ch_blocks)), dim3(kThreads), 0,
+                       st, p, (int32_t)p.ch_blocks, 1);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_carry(p.aggP, p.aggG, p.gcarry, p.batch * p.dim, (int32_t)K, true, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((ss_bwd_chunk_kernel<IO, true>), grid, dim3(kThreads), 0, st, p, (int32_t)groups,
+  hipLaunchKernelGGL((ss_bwd_chunk_kernel<IO, true, SEQ>), grid, dim3(kThreads), 0, st, p, (int32_t)groups,
                      (int32_t)per);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -565,6 +584,11 @@ hipError_t launch_bwd_io(const BwdParams& p, hipStream_t st) {
   hipLaunchKernelGGL(ss_bwd_reduce_kernel, dim3((uint32_t)((threads + 255) / 256), (uint32_t)groups_y), dim3(256), 0,
                      st, p.aggP, p.aggG, p.aggG + p.batch * K * p.dim, p.dA, p.dD, p.dbias, p.dim, p.dstate, bk);
   return hipGetLastError();
+}
+
+template <int IO>
+hipError_t launch_bwd_io(const BwdParams& p, hipStream_t st) {
+  return p.seq_idx ? launch_bwd_seq<IO, true>(p, st) : launch_bwd_seq<IO, false>(p, st);
 }
 
 }  // namespace

@@ -84,6 +84,26 @@ template <int IO> constexpr uint32_t io_bytes() { return IO == SS_F32 ? 4u : 2u;
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// ---- packed documents ("niverel-mamba" README, "seq_idx strict reset") -----
+// Lane i of a wave holds the document ids of step t = t0 + i and of t - 1
+// (raw 32-bit words from a range-checked view of the row's ids; t - 1 = -1
+// reads as out of range).  Bit i of the result is set when step t starts a new
+// document inside [1, t_end): the state is zero before that step.
+__device__ __forceinline__ uint64_t doc_starts(uint32_t id_t, uint32_t id_prev, int t, int t_end) {
+  return __builtin_amdgcn_ballot_w64(t > 0 && t < t_end && id_t != id_prev);
+}
+__device__ __forceinline__ void load_doc_ids(__amdgpu_buffer_rsrc_t ids, int t, uint32_t& id_t, uint32_t& id_prev) {
+  id_t = __builtin_amdgcn_raw_buffer_load_b32(ids, (uint32_t)t * 4u, 0, 0);
+  id_prev = __builtin_amdgcn_raw_buffer_load_b32(ids, (uint32_t)(t - 1) * 4u, 0, 0);
+}
+// decay of step S of a tile with the reset applied: a new document multiplies
+// the carried state by zero
+template <bool RESET, int S>
+__device__ __forceinline__ float reset_decay(float a, uint64_t starts) {
+  if constexpr (RESET) return ((starts >> S) & 1ull) ? 0.0f : a;
+  else return a;
+}
+
 template <int IO>
 __device__ __forceinline__ float load_io(const void* base, int64_t i) {
   return to_f32<IO>(reinterpret_cast<const typename io_elem<IO>::T*>(base)[i]);

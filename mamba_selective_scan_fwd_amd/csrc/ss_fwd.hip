@@ -21,12 +21,19 @@
 // Time chunking (for problems with too few channels to fill 256 CUs): the
 // sequence is cut into K chunks of a multiple of 64 steps.  Pass 1
 // (ss_fwd_chunk_kernel<AGG>) computes for each chunk the pair (P, S) =
-// (prod of exp(Delta A) over the chunk, state reached from zero), pass 2
+// (prod of exp(Delta A) over the chunk, state reached from the chunk's start
+// with a zero carry; the first chunk starts from the caller's initial state), pass 2
 // (ss_carry_kernel) scans the pairs with the associative operator
 // (P1,S1) then (P2,S2) = (P2 P1, P2 S1 + S2) (page "Mamba", Part V, the
 // combine for h_t = a_t h_{t-1} + b_t) to get each chunk's entry state, and
 // pass 3 (ss_fwd_chunk_kernel<FINAL>) reruns every chunk from its entry state
-// and writes y.  With K = 1 only pass 3 runs, from a zero state.
+// and writes y.  With K = 1 only pass 3 runs, from the initial state (zero
+// unless given).
+//
+// Packed documents ("niverel-mamba" README, "seq_idx strict reset"): where
+// the row's document id changes the state restarts from zero; the decay of
+// that step is replaced by 0 (so a chunk holding a document start has P = 0).
+// Tiles without a start run the plain code.
 #include <type_traits>
 
 #include "ss_device.h"
@@ -185,9 +192,9 @@ __device__ __forceinline__ void prep_owned(Owned& o, const RawOwned<IO>& r, int 
 // and (FINAL) leaves h_t[n] in column n of the channel's LDS state tile.  The
 // block's 16 B values are read into registers up front, so no LDS wait sits
 // between two steps of the recurrence.
-template <int I, bool FINAL, int... J>
+template <int I, bool FINAL, bool RESET, int... J>
 __device__ __forceinline__ void scan_block(float& h, const Owned& o, float A2, const float* sBrow, float* pcol,
-                                           std::integer_sequence<int, J...>) {
+                                           uint64_t starts, std::integer_sequence<int, J...>) {
   float bq[16];
   *reinterpret_cast<float4*>(&bq[0]) = *reinterpret_cast<const float4*>(sBrow + 16 * I + 0);
   *reinterpret_cast<float4*>(&bq[4]) = *reinterpret_cast<const float4*>(sBrow + 16 * I + 4);
@@ -195,7 +202,7 @@ __device__ __forceinline__ void scan_block(float& h, const Owned& o, float A2, c
   *reinterpret_cast<float4*>(&bq[12]) = *reinterpret_cast<const float4*>(sBrow + 16 * I + 12);
   (
       [&] {
-        const float a = exp2_hw(row_bcast<J>(o.dt[I]) * A2);
+        const float a = reset_decay<RESET, 16 * I + J>(exp2_hw(row_bcast<J>(o.dt[I]) * A2), starts);
         h = fmaf(a, h, row_bcast<J>(o.dtu[I]) * bq[J]);
         if constexpr (FINAL) pcol[J * kPRow] = h;
       }(),
@@ -247,7 +254,7 @@ __device__ __forceinline__ void finish_block(const Owned& o, const float* prow, 
   bstore<IO>(v.y, off, yv);
 }
 
-template <int IO, bool FINAL, bool PAIR>
+template <int IO, bool FINAL, bool PAIR, bool SEQ>
 __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   __shared__ FwdSmem<FINAL> sm;
   constexpr uint32_t s = io_bytes<IO>();
@@ -311,8 +318,20 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   const float bias = (ch_ok && p.bias) ? p.bias[d] : 0.0f;
   const float Dd = (ch_ok && p.D) ? p.D[d] : 0.0f;
 
+  // entry state: the caller's initial state for the first chunk (both
+  // passes), the carried state for later chunks of the readout pass
   float h = 0.0f;
-  if (FINAL && chunk > 0 && p.carry && ch_ok) h = p.carry[(ch * p.nchunks + chunk) * kStates + n];
+  if (chunk == 0) {
+    if (p.h0 && ch_ok && n_ok) h = p.h0[ch * p.dstate + n];
+  } else if (FINAL && p.carry && ch_ok) {
+    h = p.carry[(ch * p.nchunks + chunk) * kStates + n];
+  }
+
+  // document ids of this row, one tile ahead like the other operands
+  const __amdgpu_buffer_rsrc_t ids =
+      make_rsrc(SEQ ? static_cast<const void*>(p.seq_idx + b * p.seqlen) : p.u, SEQ ? (uint32_t)L * 4u : 0u);
+  uint32_t id_t = 0, id_prev = 0;
+  bool any_start = false;  // a document starts inside this chunk (chunk decay = 0)
 
   float* pwave = state_tile<FINAL>(sm, wave) + cw * kPChan;
   float* pcol = pwave + n;                // column n of this channel's state tile
@@ -322,6 +341,7 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   RawOwned<IO> raw;
   BCRaw<IO, PAIR> bcr;
   if (t_begin < t_tile_end) {
+    if constexpr (SEQ) load_doc_ids(ids, t_begin + lane, id_t, id_prev);
     load_owned<IO>(raw, v, lane_elem0, t_begin, l);
     load_bc<IO, PAIR>(bcr, v, (uint32_t)L, t_begin, tid, FINAL);
     store_bc<IO, PAIR, FINAL>(sm, 0, bcr, tid, t_valid_end - t_begin, stage_n_ok);
@@ -336,9 +356,16 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
     prep_owned<IO>(o, raw, l, nvalid, bias, softplus, dt_sum);
     if (FINAL && p.ckpt && ch_ok && n_ok) p.ckpt[(ch * p.ckpt_per_row + t0 / kTile) * p.dstate + n] = h;
 
+    uint64_t starts = 0;
+    if constexpr (SEQ) {
+      starts = doc_starts(id_t, id_prev, t0 + lane, t_valid_end);
+      any_start |= starts != 0;
+    }
+
     const int t1 = t0 + kTile;
     const bool more = t1 < t_tile_end;
     if (more) {
+      if constexpr (SEQ) load_doc_ids(ids, t1 + lane, id_t, id_prev);
       load_owned<IO>(raw, v, lane_elem0, t1, l);
       load_bc<IO, PAIR>(bcr, v, (uint32_t)L, t1, tid, FINAL);
     }
@@ -347,22 +374,33 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
     const float* sCT = ct_row<FINAL>(sm, buf, l);
     const uint32_t elem = lane_elem0 + (uint32_t)t0;
     constexpr auto seq = std::make_integer_sequence<int, 16>{};
+    // the 64 steps of the tile; tiles in which a document starts take the
+    // copy with the resets
+    auto run_tile = [&](auto reset_tag) {
+      constexpr bool RESET = decltype(reset_tag)::value;
 #define SS_BLOCK(I)                                                                          \
-    {                                                                                        \
-      CRow cr;                                                                               \
-      if constexpr (FINAL) cr = load_crow(sCT + 16 * (I) * kCTRow);                          \
-      scan_block<I, FINAL>(h, o, A2, sBrow, pcol, seq);                                      \
-      if constexpr (FINAL) {                                                                 \
-        wave_lds_sync();                                                                     \
-        finish_block<IO, I>(o, prow, cr, Dd, need_z, v, elem, l, nvalid, nstop);             \
-        wave_lds_sync();                                                                     \
-      }                                                                                      \
-    }
-    SS_BLOCK(0)
-    SS_BLOCK(1)
-    SS_BLOCK(2)
-    SS_BLOCK(3)
+      {                                                                                      \
+        CRow cr;                                                                             \
+        if constexpr (FINAL) cr = load_crow(sCT + 16 * (I) * kCTRow);                        \
+        scan_block<I, FINAL, RESET>(h, o, A2, sBrow, pcol, starts, seq);                     \
+        if constexpr (FINAL) {                                                               \
+          wave_lds_sync();                                                                   \
+          finish_block<IO, I>(o, prow, cr, Dd, need_z, v, elem, l, nvalid, nstop);           \
+          wave_lds_sync();                                                                   \
+        }                                                                                    \
+      }
+      SS_BLOCK(0)
+      SS_BLOCK(1)
+      SS_BLOCK(2)
+      SS_BLOCK(3)
 #undef SS_BLOCK
+    };
+    if constexpr (SEQ) {
+      if (starts != 0) run_tile(std::true_type{});
+      else run_tile(std::false_type{});
+    } else {
+      run_tile(std::false_type{});
+    }
 
     if (more) store_bc<IO, PAIR, FINAL>(sm, buf ^ 1, bcr, tid, t_valid_end - t1, stage_n_ok);
     __syncthreads();
@@ -380,7 +418,7 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
     // chunk summary: P = exp(A * sum Delta) (= prod of the step decays), S = h
     const float dsum = row_sum(dt_sum);
     const int64_t k = (ch * p.nchunks + chunk) * kStates + n;
-    p.aggP[k] = exp2_hw(A2 * dsum);
+    p.aggP[k] = any_start ? 0.0f : exp2_hw(A2 * dsum);
     p.aggS[k] = h;
   }
 }
@@ -473,32 +511,37 @@ __global__ void __launch_bounds__(256) ss_copy_kernel(const float4* __restrict__
   for (; i < n16; i += stride) dst[i] = src[i];
 }
 
-template <int IO, bool PAIR>
+template <int IO, bool PAIR, bool SEQ>
 hipError_t launch_fwd_variant(const FwdParams& p, int64_t nchunks, hipStream_t st) {
   const int64_t blocks_per_chunk = p.batch * p.ch_blocks;
   if (nchunks > 1) {
     FwdParams q = p;
     q.chunk_base = 0;
     // pass 1: summaries of chunks 0 .. K-2 (the last chunk's summary is never needed)
-    hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, false, PAIR>), dim3((uint32_t)(blocks_per_chunk * (nchunks - 1))),
-                       dim3(kThreads), 0, st, q);
+    hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, false, PAIR, SEQ>),
+                       dim3((uint32_t)(blocks_per_chunk * (nchunks - 1))), dim3(kThreads), 0, st, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // pass 2: entry states
     e = launch_carry(p.aggP, p.aggS, p.carry, p.batch * p.dim, p.nchunks, false, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, true, PAIR>), dim3((uint32_t)(blocks_per_chunk * nchunks)),
+  hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, true, PAIR, SEQ>), dim3((uint32_t)(blocks_per_chunk * nchunks)),
                      dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 
+template <int IO, bool SEQ>
+hipError_t launch_fwd_seq(const FwdParams& p, int64_t nchunks, hipStream_t st) {
+  if constexpr (IO != SS_F32) {
+    if (p.seqlen % 2 == 0) return launch_fwd_variant<IO, true, SEQ>(p, nchunks, st);
+  }
+  return launch_fwd_variant<IO, false, SEQ>(p, nchunks, st);
+}
+
 template <int IO>
 hipError_t launch_fwd_io(const FwdParams& p, int64_t nchunks, hipStream_t st) {
-  if constexpr (IO != SS_F32) {
-    if (p.seqlen % 2 == 0) return launch_fwd_variant<IO, true>(p, nchunks, st);
-  }
-  return launch_fwd_variant<IO, false>(p, nchunks, st);
+  return p.seq_idx ? launch_fwd_seq<IO, true>(p, nchunks, st) : launch_fwd_seq<IO, false>(p, nchunks, st);
 }
 
 template <int IO>

@@ -21,6 +21,8 @@ struct FwdParams {
   const float* D;
   const float* bias;
   const int32_t* lengths;
+  const int32_t* seq_idx;  // (batch, seqlen) document ids, or null
+  const float* h0;         // (batch, dim, dstate) initial state, or null
   void* y;
   float* last_state;
   float* ckpt;
@@ -65,7 +67,10 @@ struct BwdParams {
   const float* D;
   const float* bias;
   const float* ckpt;
+  const int32_t* seq_idx;  // (batch, seqlen) document ids, or null
   const void* dy;
+  const float* dlast;      // (batch, dim, dstate) gradient from the final state, or null
+  float* dh0;              // (batch, dim, dstate) gradient w.r.t. the initial state, or null
   void* du;
   void* ddelta;
   void* dz;

@@ -52,11 +52,11 @@ def load_library(path: str = LIB_PATH):
     lib.ss_bwd_workspace_size.restype = ctypes.c_size_t
     lib.ss_bwd_workspace_size.argtypes = [P]
     lib.ss_fwd.restype = ctypes.c_int
-    lib.ss_fwd.argtypes = [P] + [_vp] * 12 + [_vp, ctypes.c_size_t, _vp]
+    lib.ss_fwd.argtypes = [P] + [_vp] * 14 + [_vp, ctypes.c_size_t, _vp]
     lib.ss_fwd_step.restype = ctypes.c_int
     lib.ss_fwd_step.argtypes = [P] + [_vp] * 11 + [_vp]
     lib.ss_bwd.restype = ctypes.c_int
-    lib.ss_bwd.argtypes = [P] + [_vp] * 18 + [_vp, ctypes.c_size_t, _vp]
+    lib.ss_bwd.argtypes = [P] + [_vp] * 21 + [_vp, ctypes.c_size_t, _vp]
     lib.ss_copy_probe.restype = ctypes.c_int
     lib.ss_copy_probe.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
     _lib = lib
@@ -102,11 +102,12 @@ def ckpt_chunks(seqlen: int) -> int:
 
 
 def fwd(u, delta, A, Bm, Cm, D=None, z=None, delta_bias=None, delta_softplus=True, lengths=None,
-        return_last_state=True, return_ckpt=False, y=None, workspace=None):
+        return_last_state=True, return_ckpt=False, y=None, workspace=None, seq_idx=None, h0=None):
     """Selective-scan forward.  Returns (y, last_state, ckpt) (None for what was not asked).
 
     u, delta, z: (B, D, L); Bm, Cm: (B, N, L) in the same dtype (fp32/fp16/bf16);
-    A: (D, N) fp32; D, delta_bias: (D,) fp32; lengths: (B,) int32.
+    A: (D, N) fp32; D, delta_bias: (D,) fp32; lengths: (B,) int32; seq_idx: (B, L) int32
+    document ids (the state restarts at every change); h0: (B, D, N) fp32 initial state.
     """
     lib = load_library()
     io = u.dtype
@@ -123,6 +124,8 @@ def fwd(u, delta, A, Bm, Cm, D=None, z=None, delta_bias=None, delta_softplus=Tru
     D = _prep(D, torch.float32, "D", (Dd,))
     delta_bias = _prep(delta_bias, torch.float32, "delta_bias", (Dd,))
     lengths = _prep(lengths, torch.int32, "lengths", (Bsz,))
+    seq_idx = _prep(seq_idx, torch.int32, "seq_idx", (Bsz, L))
+    h0 = _prep(h0, torch.float32, "h0", (Bsz, Dd, N))
     dev = u.device
     pr = problem(Bsz, Dd, N, L, io, delta_softplus)
     if y is None:
@@ -141,8 +144,8 @@ def fwd(u, delta, A, Bm, Cm, D=None, z=None, delta_bias=None, delta_softplus=Tru
         else:
             ws = torch.empty((wsz + 3) // 4, dtype=torch.float32, device=dev)
     _check(lib.ss_fwd(ctypes.byref(pr), _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z),
-                      _ptr(delta_bias), _ptr(lengths), _ptr(y), _ptr(last), _ptr(ck), _ptr(ws), wsz,
-                      _stream(dev)))
+                      _ptr(delta_bias), _ptr(lengths), _ptr(seq_idx), _ptr(h0), _ptr(y), _ptr(last), _ptr(ck),
+                      _ptr(ws), wsz, _stream(dev)))
     return y, last, ck
 
 
@@ -156,7 +159,7 @@ class FwdCall:
     """
 
     def __init__(self, u, delta, A, Bm, Cm, D=None, z=None, delta_bias=None, delta_softplus=True, lengths=None,
-                 y=None, last_state=None, ckpt=None, stream=None):
+                 y=None, last_state=None, ckpt=None, stream=None, seq_idx=None, h0=None):
         lib = load_library()
         io = u.dtype
         if io not in _IO:
@@ -166,7 +169,8 @@ class FwdCall:
         checks = [(u, io, "u", (Bsz, Dd, L)), (delta, io, "delta", (Bsz, Dd, L)), (z, io, "z", (Bsz, Dd, L)),
                   (Bm, io, "Bm", (Bsz, N, L)), (Cm, io, "Cm", (Bsz, N, L)), (A, torch.float32, "A", (Dd, N)),
                   (D, torch.float32, "D", (Dd,)), (delta_bias, torch.float32, "delta_bias", (Dd,)),
-                  (lengths, torch.int32, "lengths", (Bsz,)), (y, io, "y", (Bsz, Dd, L)),
+                  (lengths, torch.int32, "lengths", (Bsz,)), (seq_idx, torch.int32, "seq_idx", (Bsz, L)),
+                  (h0, torch.float32, "h0", (Bsz, Dd, N)), (y, io, "y", (Bsz, Dd, L)),
                   (last_state, torch.float32, "last_state", (Bsz, Dd, N)),
                   (ckpt, torch.float32, "ckpt", (Bsz, Dd, ckpt_chunks(L), N))]
         for t, dt, name, shape in checks:
@@ -181,10 +185,11 @@ class FwdCall:
         self.pr = problem(Bsz, Dd, N, L, io, delta_softplus)
         wsz = lib.ss_fwd_workspace_size(ctypes.byref(self.pr))
         self.ws = torch.empty((wsz + 3) // 4, dtype=torch.float32, device=u.device) if wsz else None
-        self.keep = (u, delta, A, Bm, Cm, D, z, delta_bias, lengths, y, last_state, ckpt, self.ws)
+        self.keep = (u, delta, A, Bm, Cm, D, z, delta_bias, lengths, seq_idx, h0, y, last_state, ckpt, self.ws)
         st = stream if stream is not None else torch.cuda.current_stream(u.device)
         self.args = (ctypes.byref(self.pr), _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z),
-                     _ptr(delta_bias), _ptr(lengths), _ptr(y), _ptr(last_state), _ptr(ckpt), _ptr(self.ws), wsz,
+                     _ptr(delta_bias), _ptr(lengths), _ptr(seq_idx), _ptr(h0), _ptr(y), _ptr(last_state),
+                     _ptr(ckpt), _ptr(self.ws), wsz,
                      ctypes.c_void_p(st.cuda_stream))
         self.fn = lib.ss_fwd
 
@@ -275,9 +280,12 @@ class StepCall:
             _check(status)
 
 
-def bwd(u, delta, A, Bm, Cm, ckpt, dy, D=None, z=None, delta_bias=None, delta_softplus=True, workspace=None):
-    """Selective-scan backward for the loss sum(dy * y).  Returns a dict of gradients
-    (du, ddelta, dA, dB, dC, and dz / dD / dbias for the inputs that were given)."""
+def bwd(u, delta, A, Bm, Cm, ckpt, dy, D=None, z=None, delta_bias=None, delta_softplus=True, workspace=None,
+        seq_idx=None, dlast=None, want_dh0=False):
+    """Selective-scan backward for the loss sum(dy * y) + sum(dlast * last_state).  Returns a dict
+    of gradients (du, ddelta, dA, dB, dC, dz / dD / dbias for the inputs that were given, and
+    dh0, the gradient w.r.t. the initial state, when want_dh0).  ckpt must come from a forward
+    with the same seq_idx and initial state."""
     lib = load_library()
     io = u.dtype
     Bsz, Dd, L = u.shape
@@ -292,6 +300,8 @@ def bwd(u, delta, A, Bm, Cm, ckpt, dy, D=None, z=None, delta_bias=None, delta_so
     D = _prep(D, torch.float32, "D", (Dd,))
     delta_bias = _prep(delta_bias, torch.float32, "delta_bias", (Dd,))
     ckpt = _prep(ckpt, torch.float32, "ckpt", (Bsz, Dd, ckpt_chunks(L), N))
+    seq_idx = _prep(seq_idx, torch.int32, "seq_idx", (Bsz, L))
+    dlast = _prep(dlast, torch.float32, "dlast", (Bsz, Dd, N))
     dev = u.device
     g = {
         "du": torch.empty((Bsz, Dd, L), dtype=io, device=dev),
@@ -302,6 +312,7 @@ def bwd(u, delta, A, Bm, Cm, ckpt, dy, D=None, z=None, delta_bias=None, delta_so
         "dz": torch.empty((Bsz, Dd, L), dtype=io, device=dev) if z is not None else None,
         "dD": torch.empty((Dd,), dtype=torch.float32, device=dev) if D is not None else None,
         "dbias": torch.empty((Dd,), dtype=torch.float32, device=dev) if delta_bias is not None else None,
+        "dh0": torch.empty((Bsz, Dd, N), dtype=torch.float32, device=dev) if want_dh0 else None,
     }
     pr = problem(Bsz, Dd, N, L, io, delta_softplus)
     wsz = lib.ss_bwd_workspace_size(ctypes.byref(pr))
@@ -310,9 +321,9 @@ def bwd(u, delta, A, Bm, Cm, ckpt, dy, D=None, z=None, delta_bias=None, delta_so
     else:
         ws = torch.empty((wsz + 3) // 4, dtype=torch.float32, device=dev)
     _check(lib.ss_bwd(ctypes.byref(pr), _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z),
-                      _ptr(delta_bias), _ptr(ckpt), _ptr(dy), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dz"]),
-                      _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dbias"]), _ptr(ws), wsz,
-                      _stream(dev)))
+                      _ptr(delta_bias), _ptr(seq_idx), _ptr(ckpt), _ptr(dy), _ptr(dlast), _ptr(g["du"]),
+                      _ptr(g["ddelta"]), _ptr(g["dz"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+                      _ptr(g["dbias"]), _ptr(g["dh0"]), _ptr(ws), wsz, _stream(dev)))
     return {k: v for k, v in g.items() if v is not None}
 
 
@@ -326,25 +337,35 @@ def copy_probe(src, dst):
 
 
 class SelectiveScanFn(torch.autograd.Function):
-    """autograd wrapper: forward = ss_fwd (with checkpoints), backward = ss_bwd."""
+    """autograd wrapper: forward = ss_fwd (with checkpoints), backward = ss_bwd.
+
+    Differentiable in u, delta, A, B, C, D, z, delta_bias and the initial
+    state h0; with return_last_state the final state is a second output whose
+    incoming gradient seeds the backward walk."""
 
     @staticmethod
-    def forward(ctx, u, delta, A, Bm, Cm, D, z, delta_bias, delta_softplus):
-        y, _, ck = fwd(u, delta, A, Bm, Cm, D=D, z=z, delta_bias=delta_bias, delta_softplus=delta_softplus,
-                       return_last_state=False, return_ckpt=True)
-        ctx.save_for_backward(u, delta, A, Bm, Cm, D, z, delta_bias, ck)
+    def forward(ctx, u, delta, A, Bm, Cm, D, z, delta_bias, delta_softplus, return_last_state, seq_idx, h0):
+        y, last, ck = fwd(u, delta, A, Bm, Cm, D=D, z=z, delta_bias=delta_bias, delta_softplus=delta_softplus,
+                          return_last_state=return_last_state, return_ckpt=True, seq_idx=seq_idx, h0=h0)
+        ctx.save_for_backward(u, delta, A, Bm, Cm, D, z, delta_bias, ck, seq_idx)
         ctx.delta_softplus = delta_softplus
-        return y
+        ctx.has_h0 = h0 is not None
+        return (y, last) if return_last_state else y
 
     @staticmethod
-    def backward(ctx, dy):
-        u, delta, A, Bm, Cm, D, z, delta_bias, ck = ctx.saved_tensors
+    def backward(ctx, dy, dlast=None):
+        u, delta, A, Bm, Cm, D, z, delta_bias, ck, seq_idx = ctx.saved_tensors
         g = bwd(u, delta, A, Bm, Cm, ck, dy.contiguous(), D=D, z=z, delta_bias=delta_bias,
-                delta_softplus=ctx.delta_softplus)
+                delta_softplus=ctx.delta_softplus, seq_idx=seq_idx,
+                dlast=None if dlast is None else dlast.contiguous(), want_dh0=ctx.has_h0)
         return (g["du"], g["ddelta"], g["dA"], g["dB"].to(Bm.dtype), g["dC"].to(Cm.dtype), g.get("dD"),
-                g.get("dz"), g.get("dbias"), None)
+                g.get("dz"), g.get("dbias"), None, None, None, g.get("dh0"))
 
 
-def selective_scan_fn(u, delta, A, Bm, Cm, D=None, z=None, delta_bias=None, delta_softplus=False):
-    """y = selective_scan(u, delta, A, B, C, D, z, delta_bias, delta_softplus), differentiable."""
-    return SelectiveScanFn.apply(u, delta, A, Bm, Cm, D, z, delta_bias, delta_softplus)
+def selective_scan_fn(u, delta, A, Bm, Cm, D=None, z=None, delta_bias=None, delta_softplus=False,
+                      return_last_state=False, seq_idx=None, h0=None):
+    """y = selective_scan(u, delta, A, B, C, D, z, delta_bias, delta_softplus), differentiable;
+    (y, last_state) with return_last_state.  seq_idx (B, L) int32 restarts the state at every
+    change of document id; h0 (B, D, N) fp32 is the initial state."""
+    return SelectiveScanFn.apply(u, delta, A, Bm, Cm, D, z, delta_bias, delta_softplus, return_last_state,
+                                 seq_idx, h0)

@@ -36,10 +36,10 @@ FAKE = 1 << 20  # aligned host-side stand-in address; never dereferenced (valida
 
 def _fwd(p, **ptrs):
     lib = ss.load_library()
-    args = dict(u=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, D=None, z=None, bias=None, lengths=None, y=FAKE,
-                last=None, ckpt=None, ws=None)
+    args = dict(u=FAKE, delta=FAKE, A=FAKE, Bm=FAKE, Cm=FAKE, D=None, z=None, bias=None, lengths=None,
+                seq_idx=None, h0=None, y=FAKE, last=None, ckpt=None, ws=None)
     args.update(ptrs)
-    order = ["u", "delta", "A", "Bm", "Cm", "D", "z", "bias", "lengths", "y", "last", "ckpt", "ws"]
+    order = ["u", "delta", "A", "Bm", "Cm", "D", "z", "bias", "lengths", "seq_idx", "h0", "y", "last", "ckpt", "ws"]
     return lib.ss_fwd(ctypes.byref(p), *[args[k] for k in order], 0, None)
 
 
@@ -75,10 +75,12 @@ def test_fwd_rejects_null_and_misaligned():
     assert _fwd(p, y=None) == 1
     assert _fwd(p, Bm=FAKE + 4) == 4
     assert _fwd(p, D=FAKE + 8) == 4
+    assert _fwd(p, seq_idx=FAKE + 4) == 4
+    assert _fwd(p, h0=FAKE + 12) == 4
     # a time-chunked problem without its workspace
     assert _fwd(_prob(batch=1, dim=16, seqlen=32768)) == 5
     lib = ss.load_library()
-    assert lib.ss_fwd(None, *([FAKE] * 12), None, 0, None) == 1
+    assert lib.ss_fwd(None, *([FAKE] * 14), None, 0, None) == 1
 
 
 def test_step_and_bwd_validation():
@@ -87,10 +89,17 @@ def test_step_and_bwd_validation():
     assert lib.ss_fwd_step(ctypes.byref(p), *([FAKE] * 5), None, None, None, None, FAKE, FAKE, None) == 1
     # partial overlap of state_in/state_out
     assert lib.ss_fwd_step(ctypes.byref(p), *([FAKE] * 5), None, None, None, FAKE, FAKE + 16, FAKE, None) == 5
+    # argument order after the problem: u delta A Bm Cm | D z bias | seq_idx ckpt dy dlast |
+    # du ddelta dz | dA dB dC dD dbias dh0
     # dz without z
-    args = [FAKE] * 5 + [None, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None]
+    args = [FAKE] * 5 + [None, None, None] + [None, FAKE, FAKE, None] + [FAKE, FAKE, FAKE] + [FAKE] * 3 + [None] * 3
     assert lib.ss_bwd(ctypes.byref(p), *args, FAKE, 1 << 30, None) == 1
     # missing workspace
-    args = [FAKE] * 5 + [None, None, None, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None]
+    args = [FAKE] * 5 + [None, None, None] + [None, FAKE, FAKE, None] + [FAKE, FAKE, None] + [FAKE] * 3 + [None] * 3
     assert lib.ss_bwd(ctypes.byref(p), *args, None, 0, None) == 5
+    # misaligned document ids, final-state gradient, initial-state gradient
+    for k in (8, 11, 20):
+        bad = list(args)
+        bad[k] = FAKE + 4
+        assert lib.ss_bwd(ctypes.byref(p), *bad, FAKE, 1 << 30, None) == 4
     assert lib.ss_copy_probe(FAKE, FAKE, 15, None) == 2
