@@ -43,6 +43,10 @@ def _load():
         lib.sso_bwd.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int,
                                 _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _ip, _ip, _dp, _dp, _dp,
                                 _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, ctypes.c_int]
+        lib.sso_conv1d_fwd.restype = ctypes.c_int
+        lib.sso_conv1d_fwd.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, _dp, _dp, _dp, _ip, _dp, _dp, _dp]
+        lib.sso_conv1d_step.restype = ctypes.c_int
+        lib.sso_conv1d_step.argtypes = [_i64, _i64, _i64, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp]
         _lib = lib
     return _lib
 
@@ -197,3 +201,41 @@ def bwd(u, delta, A, Bm, Cm, dy, D=None, z=None, bias=None, softplus=True,
     if rc != 0:
         raise RuntimeError("oracle sso_bwd failed (%d)" % rc)
     return {k: v for k, v in out.items() if v is not None}
+
+
+def conv1d_fwd(x, w, bias=None, silu=True, seq_idx=None, conv_init=None):
+    """Depthwise causal conv1d (+ SiLU) in float64.  x (B,D,L), w (D,W), bias (D,),
+    seq_idx (B,L), conv_init (B,D,W-1).  Returns (out (B,D,L), conv_final (B,D,W-1))."""
+    x = _f64(x)
+    Bsz, Dd, L = x.shape
+    w = _f64(w)
+    W = w.shape[1]
+    w = _f64(w, (Dd, W))
+    bias = _f64(bias, (Dd,))
+    conv_init = _f64(conv_init, (Bsz, Dd, W - 1))
+    seq = _seq(seq_idx, Bsz, L)
+    out = np.empty((Bsz, Dd, L))
+    fin = np.empty((Bsz, Dd, W - 1))
+    rc = _load().sso_conv1d_fwd(Bsz, Dd, L, W, int(bool(silu)), _ptr(x), _ptr(w), _ptr(bias), _ptr(seq, _ip),
+                                _ptr(conv_init), _ptr(out), _ptr(fin))
+    if rc != 0:
+        raise RuntimeError("oracle sso_conv1d_fwd failed (%d)" % rc)
+    return out, fin
+
+
+def conv1d_step(x_t, w, window, bias=None, silu=True):
+    """One decode step of the convolution.  x_t (B,D), window (B,D,W-1).
+    Returns (out_t (B,D), new window (B,D,W-1))."""
+    x_t = _f64(x_t)
+    Bsz, Dd = x_t.shape
+    w = _f64(w)
+    W = w.shape[1]
+    window = _f64(window, (Bsz, Dd, W - 1))
+    bias = _f64(bias, (Dd,))
+    out = np.empty((Bsz, Dd))
+    win = np.empty((Bsz, Dd, W - 1))
+    rc = _load().sso_conv1d_step(Bsz, Dd, W, int(bool(silu)), _ptr(x_t), _ptr(w), _ptr(bias), _ptr(window),
+                                 _ptr(win), _ptr(out))
+    if rc != 0:
+        raise RuntimeError("oracle sso_conv1d_step failed (%d)" % rc)
+    return out, win

@@ -425,3 +425,95 @@ int sso_bwd(int64_t Bsz, int64_t D, int64_t N, int64_t L, int softplus_flag,
     job.dD = dD; job.dbias = dbias; job.dh0 = dh0;
     return spawn(&job, Bsz * D, nthreads, 1);
 }
+
+/*
+ * Depthwise causal convolution + SiLU, the step before the scan ("Mamba"
+ * walkthrough, Part IV Stage 2: each channel has its own filter of width
+ * d_conv; the input is padded on the left only, so position t sees inputs
+ * t-W+1 .. t; a SiLU follows).  Plain definition per output:
+ *   pre[b,d,t] = bias[d] + sum_{k<W} w[d,k] * x[b,d,t-W+1+k]
+ *   out[b,d,t] = silu ? pre * sigmoid(pre) : pre
+ * Inputs before t = 0 come from conv_init[b,d,0..W-2] (oldest first) when
+ * given, else 0.  With document ids ("niverel-mamba" README, "seq_idx strict
+ * reset": the convolution state resets too) an input of another document
+ * than step t's counts as 0, and conv_init reaches only the first document.
+ * conv_final[b,d,j] = the input at t = L-W+1+j (0 when that is before 0 and
+ * no conv_init covers it, or when it belongs to another document than the
+ * last step's), the window a decode step continues from.
+ * x, out: (B,D,L); w: (D,W); bias: (D) or NULL; seq_idx: (B,L) or NULL;
+ * conv_init, conv_final: (B,D,W-1) or NULL.
+ */
+int sso_conv1d_fwd(int64_t Bsz, int64_t D, int64_t L, int64_t W, int silu,
+                   const double *x, const double *w, const double *bias,
+                   const int64_t *seq_idx, const double *conv_init,
+                   double *out, double *conv_final)
+{
+    if (Bsz < 1 || D < 1 || L < 1 || W < 1 || W > 16 || !x || !w || !out) return -1;
+    for (int64_t b = 0; b < Bsz; ++b) {
+        for (int64_t d = 0; d < D; ++d) {
+            const int64_t ch = b * D + d;
+            const double *xr = x + ch * L;
+            /* the input at time s (s may be negative) as seen from step t */
+            for (int64_t t = 0; t < L; ++t) {
+                double pre = bias ? bias[d] : 0.0;
+                for (int64_t k = 0; k < W; ++k) {
+                    int64_t s = t - (W - 1) + k;
+                    double v = 0.0;
+                    if (s >= 0) {
+                        int same = !seq_idx || seq_idx[b * L + s] == seq_idx[b * L + t];
+                        v = same ? xr[s] : 0.0;
+                    } else if (conv_init) {
+                        /* before the row: only the first document sees it */
+                        int first = !seq_idx || seq_idx[b * L + t] == seq_idx[b * L];
+                        v = first ? conv_init[ch * (W - 1) + (W - 1 + s)] : 0.0;
+                    }
+                    pre += w[d * W + k] * v;
+                }
+                out[ch * L + t] = silu ? pre * sigmoid(pre) : pre;
+            }
+            if (conv_final) {
+                for (int64_t j = 0; j < W - 1; ++j) {
+                    int64_t s = L - (W - 1) + j;
+                    double v = 0.0;
+                    if (s >= 0) {
+                        int same = !seq_idx || seq_idx[b * L + s] == seq_idx[b * L + L - 1];
+                        v = same ? xr[s] : 0.0;
+                    } else if (conv_init) {
+                        int first = !seq_idx || seq_idx[b * L + L - 1] == seq_idx[b * L];
+                        v = first ? conv_init[ch * (W - 1) + (W - 1 + s)] : 0.0;
+                    }
+                    conv_final[ch * (W - 1) + j] = v;
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * One decode step of the convolution: out = silu(bias + sum_{k<W-1} w[k] *
+ * window[k] + w[W-1] * x_t); the window (B,D,W-1, oldest first) then drops
+ * its oldest input and appends x_t ("mamba-metal" README: the conv1d sliding
+ * window is carried across calls).  window_in and window_out may be the same
+ * array.  x_t, out_t: (B,D).
+ */
+int sso_conv1d_step(int64_t Bsz, int64_t D, int64_t W, int silu,
+                    const double *x_t, const double *w, const double *bias,
+                    const double *window_in, double *window_out, double *out_t)
+{
+    if (Bsz < 1 || D < 1 || W < 1 || W > 16 || !x_t || !w || !window_in || !window_out || !out_t) return -1;
+    for (int64_t b = 0; b < Bsz; ++b) {
+        for (int64_t d = 0; d < D; ++d) {
+            const int64_t ch = b * D + d;
+            double win[16];
+            for (int64_t k = 0; k < W - 1; ++k) win[k] = window_in[ch * (W - 1) + k];
+            double pre = bias ? bias[d] : 0.0;
+            for (int64_t k = 0; k < W - 1; ++k) pre += w[d * W + k] * win[k];
+            pre += w[d * W + W - 1] * x_t[ch];
+            out_t[ch] = silu ? pre * sigmoid(pre) : pre;
+            for (int64_t k = 0; k + 1 < W - 1; ++k) window_out[ch * (W - 1) + k] = win[k + 1];
+            if (W > 1) window_out[ch * (W - 1) + W - 2] = x_t[ch];
+        }
+    }
+    return 0;
+}
