@@ -195,6 +195,26 @@ def bench_rows(stream):
         "ms": ms, "documents": docs, "token_channel_per_s": 8 * 1536 * 2048 / (ms * 1e-3),
         "alu_frac": fwd_alg_slots(8, 1536, 16, 2048, 2) / (ms * 1e-3) / PEAK_SLOTS}
     del g2p, c2p, y2p, s2p, seq, h0
+    # the step before the scan: depthwise causal conv1d (width 4) + SiLU on the mamba-130m
+    # layer's x branch (fp16), three rotated input sets (the 256 MB MALL cannot hold them)
+    gcv = torch.Generator(device="cuda")
+    gcv.manual_seed(9)
+    xs = [torch.randn((8, 1536, 2048), device="cuda", generator=gcv).half() for _ in range(3)]
+    outs = [torch.empty_like(xs[0]) for _ in range(3)]
+    wcv = torch.randn((1536, 4), device="cuda", generator=gcv) * 0.5
+    bcv = torch.randn((1536,), device="cuda", generator=gcv) * 0.1
+    fc = lambda i: ss.conv1d(xs[i % 3], wcv, bcv, out=outs[i % 3])
+    fc(0)
+    ms = timed(fc, 30, stream)
+    cbytes = 2 * 8 * 1536 * 2048 * 2 + 1536 * 5 * 4
+    rows["conv1d_silu_B8_D1536_L2048_W4_f16"] = {
+        "ms": ms, "alg_GBps": cbytes / (ms * 1e-3) / 1e9, "hbm_frac": cbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    win = torch.zeros((8, 1536, 3), dtype=torch.float32, device="cuda")
+    fcs = lambda i: ss.conv1d_step(xs[0][..., i % 2048].contiguous(), wcv, win, bcv)
+    fcs(0)
+    ms = timed(fcs, 64, stream)
+    rows["conv1d_silu_B8_D1536_L2048_W4_f16"]["decode_us_per_step_checked_call"] = ms * 1e3
+    del xs, outs, win
     # decode: 64 single steps on the mamba-130m state
     prob2 = inputs.make_config(2, decode_steps=64)
     g2 = dev_problem(prob2)

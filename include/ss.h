@@ -177,6 +177,57 @@ ss_status ss_bwd(const ss_problem *p,
                  void *workspace, size_t workspace_bytes,
                  void *stream);
 
+/*
+ * ---- the step before the scan: depthwise causal conv1d + SiLU -------------
+ * Page "Mamba" (walkthrough), Part IV Stage 2: every channel d has its own
+ * filter of width W (d_conv, 4 by default); the input is padded on the left
+ * only, so output t sees inputs t-W+1 .. t; a SiLU follows:
+ *   out[b,d,t] = silu(bias[d] + sum_{k<W} w[d,k] * x[b,d,t-W+1+k])
+ * (w[d,W-1] multiplies the current input; the layout of a (dim, 1, W)
+ * depthwise weight with the middle axis dropped).  All arithmetic is fp32.
+ */
+typedef struct ss_conv_problem {
+    int64_t batch;      /* B */
+    int64_t dim;        /* D = d_inner */
+    int64_t seqlen;     /* L (ignored by ss_conv1d_step) */
+    int32_t width;      /* W = d_conv, 1..4 */
+    int32_t io_dtype;   /* ss_dtype of x and out */
+    int32_t silu;       /* nonzero: out = SiLU(pre); zero: out = pre */
+    int32_t reserved;   /* must be 0 */
+} ss_conv_problem;
+
+/*
+ * Forward convolution over whole rows.
+ *   x, out     : (batch, dim, seqlen) io dtype; out must not overlap x.
+ *   w          : (dim, W) fp32.  bias: (dim) fp32 or NULL.
+ *   seq_idx    : optional (batch, seqlen) int32 document ids ("niverel-mamba"
+ *                README, "seq_idx strict reset": the convolution resets with
+ *                the scan): an input of another document than step t's
+ *                counts as 0.
+ *   conv_init  : optional (batch, dim, W-1) fp32, the W-1 inputs before t = 0
+ *                (oldest first; NULL = zeros), e.g. the conv_final of the
+ *                previous piece of the row.  It reaches only the first document.
+ *   conv_final : optional (batch, dim, W-1) fp32 output, the last W-1 inputs of
+ *                each row (0 where they belong to an earlier document, or
+ *                precede the row without conv_init): the window that
+ *                ss_conv1d_step continues from ("mamba-metal" README: the
+ *                conv1d sliding window is carried across calls).
+ * Errors as ss_fwd; SS_ERR_UNSUPPORTED when W is outside 1..4 or out overlaps x.
+ */
+ss_status ss_conv1d_fwd(const ss_conv_problem *p, const void *x, const float *w, const float *bias,
+                        const int32_t *seq_idx, const float *conv_init, void *out, float *conv_final,
+                        void *stream);
+
+/*
+ * One decode step of the convolution: out_t = silu(bias + w . [window, x_t]),
+ * then the window drops its oldest input and appends x_t.
+ *   x_t, out_t             : (batch, dim) io dtype.
+ *   window_in, window_out  : (batch, dim, W-1) fp32; they may be the same buffer
+ *                            (in-place); partial overlap is not allowed.
+ */
+ss_status ss_conv1d_step(const ss_conv_problem *p, const void *x_t, const float *w, const float *bias,
+                         const float *window_in, float *window_out, void *out_t, void *stream);
+
 /* Number of floats of the checkpoint buffer: batch*dim*ceil(seqlen/64)*dstate (0 if invalid). */
 size_t ss_ckpt_count(const ss_problem *p);
 

@@ -199,6 +199,63 @@ ss_status ss_bwd(const ss_problem* p, const void* u, const void* delta, const fl
   return from_hip(ss::launch_bwd(k, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+ss_status check_conv(const ss_conv_problem* p, bool need_seqlen) {
+  if (!p) return SS_ERR_NULL_ARG;
+  if (p->batch < 1 || p->dim < 1) return SS_ERR_BAD_SHAPE;
+  if (need_seqlen && (p->seqlen < 1 || p->seqlen > kMaxSeqlen)) return SS_ERR_BAD_SHAPE;
+  if (p->io_dtype != SS_F32 && p->io_dtype != SS_F16 && p->io_dtype != SS_BF16) return SS_ERR_BAD_DTYPE;
+  if (p->width < 1 || p->width > 4 || p->reserved != 0) return SS_ERR_UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 40;
+  if (p->batch > lim || p->dim > lim) return SS_ERR_BAD_SHAPE;
+  if (need_seqlen && (double)p->batch * (double)p->dim * (double)ss::conv_tblocks(p->seqlen) > (double)kMaxGrid)
+    return SS_ERR_BAD_SHAPE;
+  if (!need_seqlen && (double)p->batch * (double)p->dim / 256.0 > (double)kMaxGrid) return SS_ERR_BAD_SHAPE;
+  return SS_OK;
+}
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+}  // namespace
+
+ss_status ss_conv1d_fwd(const ss_conv_problem* p, const void* x, const float* w, const float* bias,
+                        const int32_t* seq_idx, const float* conv_init, void* out, float* conv_final,
+                        void* stream) {
+  ss_status s = check_conv(p, true);
+  if (s != SS_OK) return s;
+  if (!x || !w || !out) return SS_ERR_NULL_ARG;
+  const void* ptrs[] = {x, w, bias, seq_idx, conv_init, out, conv_final};
+  for (const void* q : ptrs)
+    if (q && !aligned(q)) return SS_ERR_MISALIGNED;
+  const size_t bytes = (size_t)(p->batch * p->dim * p->seqlen * elem_size(p->io_dtype));
+  if (overlaps(x, bytes, out, bytes)) return SS_ERR_UNSUPPORTED;
+  ss::ConvParams k{};
+  k.io = p->io_dtype; k.width = p->width; k.silu = p->silu != 0;
+  k.x = x; k.w = w; k.bias = bias; k.seq_idx = seq_idx; k.conv_init = conv_init;
+  k.out = out; k.conv_final = conv_final;
+  k.batch = p->batch; k.dim = p->dim; k.seqlen = p->seqlen;
+  k.tblocks = ss::conv_tblocks(p->seqlen);
+  return from_hip(ss::launch_conv(k, static_cast<hipStream_t>(stream)));
+}
+
+ss_status ss_conv1d_step(const ss_conv_problem* p, const void* x_t, const float* w, const float* bias,
+                         const float* window_in, float* window_out, void* out_t, void* stream) {
+  ss_status s = check_conv(p, false);
+  if (s != SS_OK) return s;
+  if (!x_t || !w || !out_t || ((!window_in || !window_out) && p->width > 1)) return SS_ERR_NULL_ARG;
+  const void* ptrs[] = {x_t, w, bias, window_in, window_out, out_t};
+  for (const void* q : ptrs)
+    if (q && !aligned(q)) return SS_ERR_MISALIGNED;
+  const size_t wbytes = (size_t)(p->batch * p->dim * (p->width - 1)) * sizeof(float);
+  if (window_in != window_out && wbytes && overlaps(window_in, wbytes, window_out, wbytes)) return SS_ERR_UNSUPPORTED;
+  ss::ConvStepParams k{};
+  k.io = p->io_dtype; k.width = p->width; k.silu = p->silu != 0;
+  k.x = x_t; k.w = w; k.bias = bias; k.window_in = window_in; k.window_out = window_out; k.out = out_t;
+  k.batch = p->batch; k.dim = p->dim;
+  return from_hip(ss::launch_conv_step(k, static_cast<hipStream_t>(stream)));
+}
+
 ss_status ss_copy_probe(const void* src, void* dst, size_t bytes, void* stream) {
   if (!src || !dst) return SS_ERR_NULL_ARG;
   if (!aligned(src) || !aligned(dst)) return SS_ERR_MISALIGNED;

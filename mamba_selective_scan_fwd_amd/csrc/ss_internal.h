@@ -87,7 +87,38 @@ struct BwdParams {
   int64_t nchunks;  // ceil(seqlen / 64)
 };
 
+struct ConvParams {
+  int32_t io;
+  int32_t width;  // W = d_conv, 1..4
+  int32_t silu;
+  const void* x;
+  const float* w;     // (dim, W)
+  const float* bias;  // (dim) or null
+  const int32_t* seq_idx;
+  const float* conv_init;  // (batch, dim, W-1) or null
+  void* out;
+  float* conv_final;       // (batch, dim, W-1) or null
+  int64_t batch, dim, seqlen;
+  int64_t tblocks;         // workgroups per row
+};
+
+struct ConvStepParams {
+  int32_t io;
+  int32_t width;
+  int32_t silu;
+  const void* x;  // (batch, dim)
+  const float* w;
+  const float* bias;
+  const float* window_in;  // (batch, dim, W-1)
+  float* window_out;
+  void* out;               // (batch, dim)
+  int64_t batch, dim;
+};
+
 hipError_t launch_fwd(const FwdParams& p, int64_t nchunks, hipStream_t st);
+hipError_t launch_conv(const ConvParams& p, hipStream_t st);
+hipError_t launch_conv_step(const ConvStepParams& p, hipStream_t st);
+int64_t conv_tblocks(int64_t seqlen);
 hipError_t launch_step(const StepParams& p, hipStream_t st);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t st);
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);

@@ -25,12 +25,18 @@ class ss_problem(ctypes.Structure):
                 ("seqlen", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("delta_softplus", ctypes.c_int32)]
 
 
+class ss_conv_problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("dim", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("width", ctypes.c_int32), ("io_dtype", ctypes.c_int32), ("silu", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
 _vp = ctypes.c_void_p
 _lib = None
 
 # every symbol declared in include/ss.h
 EXPORTS = ("ss_fwd", "ss_fwd_step", "ss_bwd", "ss_fwd_workspace_size", "ss_bwd_workspace_size",
-           "ss_ckpt_count", "ss_status_str", "ss_copy_probe")
+           "ss_ckpt_count", "ss_status_str", "ss_copy_probe", "ss_conv1d_fwd", "ss_conv1d_step")
 
 
 def load_library(path: str = LIB_PATH):
@@ -57,6 +63,11 @@ def load_library(path: str = LIB_PATH):
     lib.ss_fwd_step.argtypes = [P] + [_vp] * 11 + [_vp]
     lib.ss_bwd.restype = ctypes.c_int
     lib.ss_bwd.argtypes = [P] + [_vp] * 21 + [_vp, ctypes.c_size_t, _vp]
+    CP = ctypes.POINTER(ss_conv_problem)
+    lib.ss_conv1d_fwd.restype = ctypes.c_int
+    lib.ss_conv1d_fwd.argtypes = [CP] + [_vp] * 7 + [_vp]
+    lib.ss_conv1d_step.restype = ctypes.c_int
+    lib.ss_conv1d_step.argtypes = [CP] + [_vp] * 6 + [_vp]
     lib.ss_copy_probe.restype = ctypes.c_int
     lib.ss_copy_probe.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
     _lib = lib
@@ -325,6 +336,59 @@ def bwd(u, delta, A, Bm, Cm, ckpt, dy, D=None, z=None, delta_bias=None, delta_so
                       _ptr(g["ddelta"]), _ptr(g["dz"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
                       _ptr(g["dbias"]), _ptr(g["dh0"]), _ptr(ws), wsz, _stream(dev)))
     return {k: v for k, v in g.items() if v is not None}
+
+
+def conv1d(x, w, bias=None, silu=True, seq_idx=None, conv_init=None, return_final=False, out=None):
+    """Depthwise causal conv1d (+ SiLU), the step before the scan.  x: (B, D, L) fp32/fp16/bf16;
+    w: (D, W) fp32 (W <= 4, w[:, W-1] multiplies the current input); bias: (D,) fp32;
+    seq_idx: (B, L) int32 document ids; conv_init: (B, D, W-1) fp32 inputs before t = 0.
+    Returns out (B, D, L), or (out, conv_final (B, D, W-1)) with return_final."""
+    lib = load_library()
+    io = x.dtype
+    if io not in _IO:
+        raise TypeError("unsupported dtype %s" % io)
+    Bsz, Dd, L = x.shape
+    W = w.shape[-1]
+    x = _prep(x, io, "x")
+    w = _prep(w.reshape(Dd, W), torch.float32, "w", (Dd, W))
+    bias = _prep(bias, torch.float32, "bias", (Dd,))
+    seq_idx = _prep(seq_idx, torch.int32, "seq_idx", (Bsz, L))
+    conv_init = _prep(conv_init, torch.float32, "conv_init", (Bsz, Dd, W - 1))
+    out = torch.empty_like(x) if out is None else _prep(out, io, "out", (Bsz, Dd, L))
+    fin = torch.empty((Bsz, Dd, W - 1), dtype=torch.float32, device=x.device) if return_final and W > 1 else None
+    pr = ss_conv_problem(Bsz, Dd, L, W, _IO[io], 1 if silu else 0, 0)
+    _check(lib.ss_conv1d_fwd(ctypes.byref(pr), _ptr(x), _ptr(w), _ptr(bias), _ptr(seq_idx), _ptr(conv_init),
+                             _ptr(out), _ptr(fin), _stream(x.device)))
+    if return_final:
+        return out, fin if fin is not None else torch.empty((Bsz, Dd, 0), dtype=torch.float32, device=x.device)
+    return out
+
+
+def conv1d_step(x_t, w, window, bias=None, silu=True, window_out=None, out=None):
+    """One decode step of the convolution.  x_t: (B, D); window: (B, D, W-1) fp32, updated in place
+    unless window_out is given.  Returns (out_t (B, D), window_out)."""
+    lib = load_library()
+    io = x_t.dtype
+    if io not in _IO:
+        raise TypeError("unsupported dtype %s" % io)
+    Bsz, Dd = x_t.shape
+    W = w.shape[-1]
+    x_t = _prep(x_t, io, "x_t")
+    w = _prep(w.reshape(Dd, W), torch.float32, "w", (Dd, W))
+    bias = _prep(bias, torch.float32, "bias", (Dd,))
+    if W > 1:
+        if not (window.is_cuda and window.dtype == torch.float32 and window.is_contiguous()
+                and tuple(window.shape) == (Bsz, Dd, W - 1) and window.data_ptr() % 16 == 0):
+            raise ValueError("window must be a contiguous, aligned fp32 device tensor of shape %s"
+                             % ((Bsz, Dd, W - 1),))
+    if window_out is None:
+        window_out = window
+    out = torch.empty_like(x_t) if out is None else _prep(out, io, "out", (Bsz, Dd))
+    pr = ss_conv_problem(Bsz, Dd, 1, W, _IO[io], 1 if silu else 0, 0)
+    _check(lib.ss_conv1d_step(ctypes.byref(pr), _ptr(x_t), _ptr(w), _ptr(bias),
+                              _ptr(window) if W > 1 else None, _ptr(window_out) if W > 1 else None, _ptr(out),
+                              _stream(x_t.device)))
+    return out, window_out
 
 
 def copy_probe(src, dst):

@@ -103,3 +103,31 @@ def test_step_and_bwd_validation():
         bad[k] = FAKE + 4
         assert lib.ss_bwd(ctypes.byref(p), *bad, FAKE, 1 << 30, None) == 4
     assert lib.ss_copy_probe(FAKE, FAKE, 15, None) == 2
+
+
+def _conv_prob(**kw):
+    d = dict(batch=2, dim=3, seqlen=10, width=4, io_dtype=0, silu=1, reserved=0)
+    d.update(kw)
+    return ss.ss_conv_problem(d["batch"], d["dim"], d["seqlen"], d["width"], d["io_dtype"], d["silu"], d["reserved"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), 2), (dict(seqlen=0), 2), (dict(width=0), 5), (dict(width=5), 5), (dict(io_dtype=7), 3),
+    (dict(reserved=1), 5)])
+def test_conv_rejects_bad_problem(kw, code):
+    lib = ss.load_library()
+    assert lib.ss_conv1d_fwd(ctypes.byref(_conv_prob(**kw)), FAKE, FAKE, None, None, None, FAKE * 2, None,
+                             None) == code
+
+
+def test_conv_rejects_null_misaligned_and_overlap():
+    lib = ss.load_library()
+    p = _conv_prob()
+    assert lib.ss_conv1d_fwd(ctypes.byref(p), None, FAKE, None, None, None, FAKE * 2, None, None) == 1
+    assert lib.ss_conv1d_fwd(ctypes.byref(p), FAKE, FAKE + 4, None, None, None, FAKE * 2, None, None) == 4
+    assert lib.ss_conv1d_fwd(ctypes.byref(p), FAKE, FAKE, None, FAKE + 8, None, FAKE * 2, None, None) == 4
+    # out overlapping x (in place is a race between neighbouring taps)
+    assert lib.ss_conv1d_fwd(ctypes.byref(p), FAKE, FAKE, None, None, None, FAKE + 16, None, None) == 5
+    assert lib.ss_conv1d_step(ctypes.byref(p), FAKE, FAKE, None, None, FAKE, FAKE, None) == 1
+    # partial overlap of the two windows
+    assert lib.ss_conv1d_step(ctypes.byref(p), FAKE, FAKE, None, FAKE * 2, FAKE * 2 + 16, FAKE * 3, None) == 5
