@@ -329,8 +329,9 @@ def cpu_baseline(sets_cpu_seed=2, target_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps first: the GPU needs ~100 ms of load to reach its working clock")
     ap.add_argument("--no-rows", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     args = ap.parse_args()
