@@ -47,6 +47,9 @@ def _load():
         lib.sso_conv1d_fwd.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, _dp, _dp, _dp, _ip, _dp, _dp, _dp]
         lib.sso_conv1d_step.restype = ctypes.c_int
         lib.sso_conv1d_step.argtypes = [_i64, _i64, _i64, ctypes.c_int, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.sso_ssd_fwd.restype = ctypes.c_int
+        lib.sso_ssd_fwd.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                    _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _ip, _dp, _dp, _dp]
         _lib = lib
     return _lib
 
@@ -239,3 +242,29 @@ def conv1d_step(x_t, w, window, bias=None, silu=True):
     if rc != 0:
         raise RuntimeError("oracle sso_conv1d_step failed (%d)" % rc)
     return out, win
+
+
+def ssd_fwd(x, dt, A, Bm, Cm, D=None, z=None, dt_bias=None, softplus=True, seq_idx=None, h0=None):
+    """Mamba-2 SSD scan in float64 (plain recurrence).  x, z: (B,L,H,P); dt: (B,L,H);
+    A, D, dt_bias: (H,); Bm, Cm: (B,L,G,N); seq_idx: (B,L); h0: (B,H,P,N).
+    Returns (y (B,L,H,P), final_state (B,H,P,N))."""
+    x = _f64(x)
+    Bsz, L, Hn, P = x.shape
+    Bm = _f64(Bm)
+    G, N = Bm.shape[2], Bm.shape[3]
+    dt = _f64(dt, (Bsz, L, Hn))
+    A = _f64(A, (Hn,))
+    Bm = _f64(Bm, (Bsz, L, G, N))
+    Cm = _f64(Cm, (Bsz, L, G, N))
+    D = _f64(D, (Hn,))
+    z = _f64(z, (Bsz, L, Hn, P))
+    dt_bias = _f64(dt_bias, (Hn,))
+    h0 = _f64(h0, (Bsz, Hn, P, N))
+    seq = _seq(seq_idx, Bsz, L)
+    y = np.empty((Bsz, L, Hn, P))
+    fin = np.empty((Bsz, Hn, P, N))
+    rc = _load().sso_ssd_fwd(Bsz, L, Hn, P, G, N, int(bool(softplus)), _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm),
+                             _ptr(Cm), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(seq, _ip), _ptr(h0), _ptr(y), _ptr(fin))
+    if rc != 0:
+        raise RuntimeError("oracle sso_ssd_fwd failed (%d)" % rc)
+    return y, fin

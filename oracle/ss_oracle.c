@@ -517,3 +517,64 @@ int sso_conv1d_step(int64_t Bsz, int64_t D, int64_t W, int silu,
     }
     return 0;
 }
+
+/*
+ * Mamba-2 structured state-space (SSD) scan, forward ("Mamba" walkthrough,
+ * "Deep dive: Mamba-2 and state-space duality": A is a scalar times the
+ * identity per head, heads share grouped B and C).  Plain recurrence per
+ * (batch b, head h), state H[p][n] (headdim x dstate):
+ *   Delta_t  = softplus(dt[b,t,h] + dt_bias[h])   (softplus only if flagged)
+ *   a_t      = exp(Delta_t * A[h])
+ *   H[p][n]  = a_t H[p][n] + Delta_t x[b,t,h,p] B[b,t,g,n]       g = h / (H/G)
+ *   y[b,t,h,p] = sum_n C[b,t,g,n] H[p][n] + D[h] x[b,t,h,p]   (* SiLU(z) if z)
+ * starting from h0 (or 0); with document ids the state is zero before every
+ * step whose id differs from the previous step's ("niverel-mamba" README,
+ * "seq_idx strict reset").  Layouts: x, z, y (B,L,H,P); dt (B,L,H);
+ * A, D, dt_bias (H); Bm, Cm (B,L,G,N); h0, final_state (B,H,P,N).
+ */
+int sso_ssd_fwd(int64_t Bsz, int64_t L, int64_t Hn, int64_t P, int64_t G, int64_t N, int softplus_flag,
+                const double *x, const double *dt, const double *A, const double *Bm, const double *Cm,
+                const double *Dskip, const double *z, const double *dt_bias, const int64_t *seq_idx,
+                const double *h0, double *y, double *final_state)
+{
+    if (Bsz < 1 || L < 1 || Hn < 1 || P < 1 || G < 1 || N < 1 || Hn % G != 0) return -1;
+    if (!x || !dt || !A || !Bm || !Cm || !y) return -1;
+    double *Hs = (double *)malloc(sizeof(double) * (size_t)(P * N));
+    if (!Hs) return -2;
+    const int64_t hpg = Hn / G;
+    for (int64_t b = 0; b < Bsz; ++b) {
+        for (int64_t h = 0; h < Hn; ++h) {
+            const int64_t g = h / hpg;
+            for (int64_t i = 0; i < P * N; ++i)
+                Hs[i] = h0 ? h0[(b * Hn + h) * P * N + i] : 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                if (seq_idx && t > 0 && seq_idx[b * L + t] != seq_idx[b * L + t - 1])
+                    for (int64_t i = 0; i < P * N; ++i) Hs[i] = 0.0;      /* a new document */
+                double xd = dt[(b * L + t) * Hn + h] + (dt_bias ? dt_bias[h] : 0.0);
+                double delta = softplus_flag ? softplus(xd) : xd;
+                double a = exp(delta * A[h]);
+                const double *Bt = Bm + ((b * L + t) * G + g) * N;
+                const double *Ct = Cm + ((b * L + t) * G + g) * N;
+                const double *xt = x + ((b * L + t) * Hn + h) * P;
+                double *yt = y + ((b * L + t) * Hn + h) * P;
+                for (int64_t p = 0; p < P; ++p) {
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        Hs[p * N + n] = a * Hs[p * N + n] + delta * xt[p] * Bt[n];
+                        acc += Ct[n] * Hs[p * N + n];
+                    }
+                    if (Dskip) acc += Dskip[h] * xt[p];
+                    if (z) {
+                        double zz = z[((b * L + t) * Hn + h) * P + p];
+                        acc *= zz * sigmoid(zz);
+                    }
+                    yt[p] = acc;
+                }
+            }
+            if (final_state)
+                for (int64_t i = 0; i < P * N; ++i) final_state[(b * Hn + h) * P * N + i] = Hs[i];
+        }
+    }
+    free(Hs);
+    return 0;
+}
