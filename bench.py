@@ -215,6 +215,10 @@ def bench_rows(stream):
     ms = timed(fcs, 64, stream)
     rows["conv1d_silu_B8_D1536_L2048_W4_f16"]["decode_us_per_step_checked_call"] = ms * 1e3
     del xs, outs, win
+    # Mamba-2 SSD chunked scan on the matrix cores: d_model 768, expand 2 -> 24 heads of 64,
+    # d_state 128, one group, chunk 256 (the "niverel-mamba" README's V3 configuration), B=8,
+    # L=2048, bf16, with D, z gate and dt_bias; two rotated input sets
+    rows["ssd_fwd_B8_L2048_H24_P64_N128_bf16"] = bench_ssd(stream)
     # decode: 64 single steps on the mamba-130m state
     prob2 = inputs.make_config(2, decode_steps=64)
     g2 = dev_problem(prob2)
@@ -288,6 +292,38 @@ def bench_rows(stream):
         rows["bwd_B4_D1536_L4097_f32"] = {"error": str(e)[:200]}
     torch.cuda.empty_cache()
     return rows
+
+
+def bench_ssd(stream):
+    Bsz, L, Hn, P, G, N, Q = 8, 2048, 24, 64, 1, 128, 256
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(11)
+    rnd = lambda *shape: torch.randn(shape, device="cuda", generator=gen)
+    sets = []
+    for _ in range(2):
+        sets.append(dict(x=rnd(Bsz, L, Hn, P).bfloat16(), dt=(rnd(Bsz, L, Hn) * 0.5).bfloat16(),
+                         Bm=rnd(Bsz, L, G, N).bfloat16(), Cm=rnd(Bsz, L, G, N).bfloat16(),
+                         z=rnd(Bsz, L, Hn, P).bfloat16(), y=torch.empty((Bsz, L, Hn, P), dtype=torch.bfloat16,
+                                                                       device="cuda")))
+    A = -torch.exp(torch.rand(Hn, device="cuda", generator=gen) * 2.77)
+    D = rnd(Hn)
+    dt_bias = torch.log(torch.expm1(torch.exp(torch.rand(Hn, device="cuda", generator=gen) * 4.6 - 6.9)))
+    ws = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
+    f = lambda i: ss.ssd_fwd(sets[i % 2]["x"], sets[i % 2]["dt"], A, sets[i % 2]["Bm"], sets[i % 2]["Cm"], D=D,
+                             z=sets[i % 2]["z"], dt_bias=dt_bias, y=sets[i % 2]["y"], workspace=ws)
+    for i in range(20):
+        f(i)
+    ms = timed(f, 50, stream)
+    nchunks = (L + Q - 1) // Q
+    # dense work of the chunked algorithm per (row, chunk, head): C B^T and M x over the causal half,
+    # the chunk state and the state readout
+    flop = 2 * Bsz * nchunks * Hn * (Q * Q * N // 2 + Q * Q * P // 2 + 2 * Q * N * P)
+    byt = Bsz * L * Hn * P * 2 * 3 + Bsz * L * Hn * 2 + 2 * Bsz * L * G * N * 2   # x, z, y, dt, B, C once
+    del sets, ws
+    return {"ms": ms, "token_channel_per_s": Bsz * L * Hn * P / (ms * 1e-3),
+            "state_updates_per_s": Bsz * L * Hn * P * N / (ms * 1e-3),
+            "mfma_TFLOPs": flop / (ms * 1e-3) / 1e12, "mfma_frac_of_bf16_peak": flop / (ms * 1e-3) / 2.5e15,
+            "alg_GBps": byt / (ms * 1e-3) / 1e9, "hbm_frac": byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
 
 
 def copy_probe(stream):

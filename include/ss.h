@@ -228,6 +228,52 @@ ss_status ss_conv1d_fwd(const ss_conv_problem *p, const void *x, const float *w,
 ss_status ss_conv1d_step(const ss_conv_problem *p, const void *x_t, const float *w, const float *bias,
                          const float *window_in, float *window_out, void *out_t, void *stream);
 
+/*
+ * ---- Mamba-2 SSD chunked scan ----------------------------------------------
+ * Page "Mamba" (walkthrough), "Deep dive: Mamba-2 and state-space duality":
+ * A is a scalar per head and a group of heads shares B and C.  Per batch row
+ * b and head h (state H[p][n], headdim x dstate, g = h / (nheads/ngroups)):
+ *   Delta_t  = softplus(dt[b,t,h] + dt_bias[h])     (softplus only if flagged)
+ *   H_t      = exp(Delta_t A[h]) H_{t-1} + Delta_t x[b,t,h,:] B[b,t,g,:]^T
+ *   y[b,t,h,p] = sum_n H_t[p][n] C[b,t,g,n] + D[h] x[b,t,h,p]   (* SiLU(z) if z)
+ * from H_{-1} = h0 (or 0).  Computed by the chunked algorithm the page
+ * describes (quadratic, attention-like matmuls inside 256-step chunks, one
+ * state passed between chunks) on the matrix cores, fp32 accumulation.
+ * Layouts (time-major, as Mamba-2 stores them):
+ *   x, z, y : (batch, seqlen, nheads, headdim)  io dtype
+ *   dt      : (batch, seqlen, nheads)           io dtype
+ *   Bm, Cm  : (batch, seqlen, ngroups, dstate)  io dtype
+ *   A, D, dt_bias : (nheads) fp32
+ *   h0, final_state : (batch, nheads, headdim, dstate) fp32
+ */
+typedef struct ss_ssd_problem {
+    int64_t batch;
+    int64_t seqlen;
+    int64_t nheads;
+    int64_t ngroups;      /* divides nheads */
+    int32_t headdim;      /* 64 */
+    int32_t dstate;       /* 32, 64, 96 or 128 */
+    int32_t io_dtype;     /* SS_F16 or SS_BF16 */
+    int32_t dt_softplus;  /* nonzero: Delta = softplus(dt + dt_bias) */
+} ss_ssd_problem;
+
+/* Bytes of device workspace ss_ssd_fwd needs: per 256-step chunk of every
+ * (batch row, head), the chunk's own state (fp32), its entry state (io dtype)
+ * and its decay.  Returns 0 for an invalid problem. */
+size_t ss_ssd_workspace_size(const ss_ssd_problem *p);
+
+/*
+ * SSD forward.  D, z, dt_bias, h0 and final_state are optional (NULL).
+ * Every pointer must be 16-byte aligned.  Returns SS_ERR_BAD_DTYPE for fp32
+ * I/O (the matrix-core path takes 16-bit data), SS_ERR_UNSUPPORTED for a
+ * headdim other than 64, a dstate outside {32, 64, 96, 128}, ngroups not
+ * dividing nheads, or a workspace missing or too small.
+ */
+ss_status ss_ssd_fwd(const ss_ssd_problem *p, const void *x, const void *dt, const float *A,
+                     const void *Bm, const void *Cm, const float *D, const void *z, const float *dt_bias,
+                     const float *h0, void *y, float *final_state,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
 /* Number of floats of the checkpoint buffer: batch*dim*ceil(seqlen/64)*dstate (0 if invalid). */
 size_t ss_ckpt_count(const ss_problem *p);
 

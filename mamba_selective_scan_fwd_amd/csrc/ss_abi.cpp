@@ -256,6 +256,61 @@ ss_status ss_conv1d_step(const ss_conv_problem* p, const void* x_t, const float*
   return from_hip(ss::launch_conv_step(k, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+constexpr int64_t kSsdChunk = 256;
+ss_status check_ssd(const ss_ssd_problem* p) {
+  if (!p) return SS_ERR_NULL_ARG;
+  if (p->batch < 1 || p->seqlen < 1 || p->nheads < 1 || p->ngroups < 1) return SS_ERR_BAD_SHAPE;
+  if (p->io_dtype != SS_F16 && p->io_dtype != SS_BF16) return SS_ERR_BAD_DTYPE;
+  if (p->headdim != 64) return SS_ERR_UNSUPPORTED;
+  if (p->dstate != 32 && p->dstate != 64 && p->dstate != 96 && p->dstate != 128) return SS_ERR_UNSUPPORTED;
+  if (p->nheads % p->ngroups != 0) return SS_ERR_UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 31;
+  if (p->batch > lim || p->seqlen > lim || p->nheads > lim) return SS_ERR_BAD_SHAPE;
+  const double nchunks = (double)((p->seqlen + kSsdChunk - 1) / kSsdChunk);
+  if ((double)p->batch * nchunks * (double)p->nheads > (double)kMaxGrid) return SS_ERR_BAD_SHAPE;
+  if ((double)p->batch * (double)p->seqlen * (double)p->nheads * 64.0 > 9.0e18) return SS_ERR_BAD_SHAPE;
+  return SS_OK;
+}
+size_t ssd_state_elems(const ss_ssd_problem* p) {
+  const int64_t nchunks = (p->seqlen + kSsdChunk - 1) / kSsdChunk;
+  return (size_t)(p->batch * nchunks * p->nheads) * (size_t)(64 * p->dstate);
+}
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+}  // namespace
+
+size_t ss_ssd_workspace_size(const ss_ssd_problem* p) {
+  if (check_ssd(p) != SS_OK) return 0;
+  const size_t e = ssd_state_elems(p);
+  const int64_t nchunks = (p->seqlen + kSsdChunk - 1) / kSsdChunk;
+  return align256(e * 4) + align256(e * 2) + align256((size_t)(p->batch * nchunks * p->nheads) * 4);
+}
+
+ss_status ss_ssd_fwd(const ss_ssd_problem* p, const void* x, const void* dt, const float* A, const void* Bm,
+                     const void* Cm, const float* D, const void* z, const float* dt_bias, const float* h0, void* y,
+                     float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+  ss_status s = check_ssd(p);
+  if (s != SS_OK) return s;
+  if (!x || !dt || !A || !Bm || !Cm || !y) return SS_ERR_NULL_ARG;
+  const void* ptrs[] = {x, dt, A, Bm, Cm, D, z, dt_bias, h0, y, final_state, workspace};
+  for (const void* q : ptrs)
+    if (q && !aligned(q)) return SS_ERR_MISALIGNED;
+  const size_t need = ss_ssd_workspace_size(p);
+  if (!workspace || workspace_bytes < need) return SS_ERR_UNSUPPORTED;
+  const size_t e = ssd_state_elems(p);
+  ss::SsdParams k{};
+  k.io = p->io_dtype; k.softplus = p->dt_softplus != 0;
+  k.x = x; k.dt = dt; k.A = A; k.Bm = Bm; k.Cm = Cm; k.D = D; k.z = z; k.dt_bias = dt_bias; k.h0 = h0;
+  k.y = y; k.final_state = final_state;
+  char* ws = static_cast<char*>(workspace);
+  k.ws_state = reinterpret_cast<float*>(ws);
+  k.ws_entry = reinterpret_cast<uint16_t*>(ws + align256(e * 4));
+  k.ws_decay = reinterpret_cast<float*>(ws + align256(e * 4) + align256(e * 2));
+  k.batch = p->batch; k.seqlen = p->seqlen; k.nheads = p->nheads; k.ngroups = p->ngroups; k.dstate = p->dstate;
+  k.nchunks = (p->seqlen + kSsdChunk - 1) / kSsdChunk;
+  return from_hip(ss::launch_ssd(k, static_cast<hipStream_t>(stream)));
+}
+
 ss_status ss_copy_probe(const void* src, void* dst, size_t bytes, void* stream) {
   if (!src || !dst) return SS_ERR_NULL_ARG;
   if (!aligned(src) || !aligned(dst)) return SS_ERR_MISALIGNED;

@@ -115,7 +115,29 @@ struct ConvStepParams {
   int64_t batch, dim;
 };
 
+struct SsdParams {
+  int32_t io;        // SS_F16 or SS_BF16
+  int32_t softplus;
+  const void* x;     // (batch, seqlen, nheads, 64)
+  const void* dt;    // (batch, seqlen, nheads)
+  const float* A;    // (nheads)
+  const void* Bm;    // (batch, seqlen, ngroups, dstate)
+  const void* Cm;
+  const float* D;        // (nheads) or null
+  const void* z;         // like x, or null
+  const float* dt_bias;  // (nheads) or null
+  const float* h0;       // (batch, nheads, 64, dstate) or null
+  void* y;
+  float* final_state;    // (batch, nheads, 64, dstate) or null
+  // workspace
+  float* ws_state;       // (batch, nchunks, nheads, 64, dstate) fp32: each chunk's own state
+  uint16_t* ws_entry;    // same shape, I/O dtype bits: each chunk's entry state
+  float* ws_decay;       // (batch, nchunks, nheads)
+  int64_t batch, seqlen, nheads, ngroups, dstate, nchunks;
+};
+
 hipError_t launch_fwd(const FwdParams& p, int64_t nchunks, hipStream_t st);
+hipError_t launch_ssd(const SsdParams& p, hipStream_t st);
 hipError_t launch_conv(const ConvParams& p, hipStream_t st);
 hipError_t launch_conv_step(const ConvStepParams& p, hipStream_t st);
 int64_t conv_tblocks(int64_t seqlen);

@@ -31,12 +31,19 @@ class ss_conv_problem(ctypes.Structure):
                 ("reserved", ctypes.c_int32)]
 
 
+class ss_ssd_problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("ngroups", ctypes.c_int64), ("headdim", ctypes.c_int32), ("dstate", ctypes.c_int32),
+                ("io_dtype", ctypes.c_int32), ("dt_softplus", ctypes.c_int32)]
+
+
 _vp = ctypes.c_void_p
 _lib = None
 
 # every symbol declared in include/ss.h
 EXPORTS = ("ss_fwd", "ss_fwd_step", "ss_bwd", "ss_fwd_workspace_size", "ss_bwd_workspace_size",
-           "ss_ckpt_count", "ss_status_str", "ss_copy_probe", "ss_conv1d_fwd", "ss_conv1d_step")
+           "ss_ckpt_count", "ss_status_str", "ss_copy_probe", "ss_conv1d_fwd", "ss_conv1d_step",
+           "ss_ssd_fwd", "ss_ssd_workspace_size")
 
 
 def load_library(path: str = LIB_PATH):
@@ -68,6 +75,11 @@ def load_library(path: str = LIB_PATH):
     lib.ss_conv1d_fwd.argtypes = [CP] + [_vp] * 7 + [_vp]
     lib.ss_conv1d_step.restype = ctypes.c_int
     lib.ss_conv1d_step.argtypes = [CP] + [_vp] * 6 + [_vp]
+    SP = ctypes.POINTER(ss_ssd_problem)
+    lib.ss_ssd_workspace_size.restype = ctypes.c_size_t
+    lib.ss_ssd_workspace_size.argtypes = [SP]
+    lib.ss_ssd_fwd.restype = ctypes.c_int
+    lib.ss_ssd_fwd.argtypes = [SP] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]
     lib.ss_copy_probe.restype = ctypes.c_int
     lib.ss_copy_probe.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
     _lib = lib
@@ -389,6 +401,39 @@ def conv1d_step(x_t, w, window, bias=None, silu=True, window_out=None, out=None)
                               _ptr(window) if W > 1 else None, _ptr(window_out) if W > 1 else None, _ptr(out),
                               _stream(x_t.device)))
     return out, window_out
+
+
+def ssd_fwd(x, dt, A, Bm, Cm, D=None, z=None, dt_bias=None, dt_softplus=True, h0=None, return_final_state=False,
+            y=None, workspace=None):
+    """Mamba-2 SSD scan on the matrix cores.  x, z: (B, L, H, 64); dt: (B, L, H); Bm, Cm: (B, L, G, N)
+    in fp16 or bf16; A, D, dt_bias: (H,) fp32; h0: (B, H, 64, N) fp32.  Returns y, or (y, final_state)."""
+    lib = load_library()
+    io = x.dtype
+    if io not in (torch.float16, torch.bfloat16):
+        raise TypeError("ssd_fwd takes fp16 or bf16 data, got %s" % io)
+    Bsz, L, Hn, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    x = _prep(x, io, "x")
+    dt = _prep(dt, io, "dt", (Bsz, L, Hn))
+    Bm = _prep(Bm, io, "Bm", (Bsz, L, G, N))
+    Cm = _prep(Cm, io, "Cm", (Bsz, L, G, N))
+    z = _prep(z, io, "z", (Bsz, L, Hn, P))
+    A = _prep(A, torch.float32, "A", (Hn,))
+    D = _prep(D, torch.float32, "D", (Hn,))
+    dt_bias = _prep(dt_bias, torch.float32, "dt_bias", (Hn,))
+    h0 = _prep(h0, torch.float32, "h0", (Bsz, Hn, P, N))
+    pr = ss_ssd_problem(Bsz, L, Hn, G, P, N, _IO[io], 1 if dt_softplus else 0)
+    y = torch.empty_like(x) if y is None else _prep(y, io, "y", (Bsz, L, Hn, P))
+    fin = torch.empty((Bsz, Hn, P, N), dtype=torch.float32, device=x.device) if return_final_state else None
+    wsz = lib.ss_ssd_workspace_size(ctypes.byref(pr))
+    if wsz == 0:
+        raise RuntimeError("ss_ssd_fwd: unsupported problem (headdim must be 64, dstate 32/64/96/128, "
+                           "ngroups dividing nheads)")
+    if workspace is None or workspace.numel() * workspace.element_size() < wsz:
+        workspace = torch.empty((wsz + 255) // 256 * 64, dtype=torch.float32, device=x.device)
+    _check(lib.ss_ssd_fwd(ctypes.byref(pr), _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z),
+                          _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(fin), _ptr(workspace), wsz, _stream(x.device)))
+    return (y, fin) if return_final_state else y
 
 
 def copy_probe(src, dst):

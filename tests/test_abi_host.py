@@ -131,3 +131,35 @@ def test_conv_rejects_null_misaligned_and_overlap():
     assert lib.ss_conv1d_step(ctypes.byref(p), FAKE, FAKE, None, None, FAKE, FAKE, None) == 1
     # partial overlap of the two windows
     assert lib.ss_conv1d_step(ctypes.byref(p), FAKE, FAKE, None, FAKE * 2, FAKE * 2 + 16, FAKE * 3, None) == 5
+
+
+def _ssd_prob(**kw):
+    d = dict(batch=2, seqlen=300, nheads=4, ngroups=2, headdim=64, dstate=64, io_dtype=2, dt_softplus=1)
+    d.update(kw)
+    return ss.ss_ssd_problem(d["batch"], d["seqlen"], d["nheads"], d["ngroups"], d["headdim"], d["dstate"],
+                             d["io_dtype"], d["dt_softplus"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), 2), (dict(seqlen=0), 2), (dict(io_dtype=0), 3), (dict(headdim=32), 5), (dict(dstate=16), 5),
+    (dict(dstate=80), 5), (dict(ngroups=3), 5)])
+def test_ssd_rejects_bad_problem(kw, code):
+    lib = ss.load_library()
+    p = _ssd_prob(**kw)
+    assert lib.ss_ssd_workspace_size(ctypes.byref(p)) == 0
+    assert lib.ss_ssd_fwd(ctypes.byref(p), *([FAKE] * 5), None, None, None, None, FAKE, None, FAKE, 1 << 30,
+                          None) == code
+
+
+def test_ssd_workspace_and_validation():
+    lib = ss.load_library()
+    p = _ssd_prob()
+    wsz = lib.ss_ssd_workspace_size(ctypes.byref(p))
+    # 2 chunks of 256 steps x 2 rows x 4 heads: states (64 x 64) fp32 + 16-bit, decays
+    assert wsz == 16 * 4096 * 4 + 16 * 4096 * 2 + 256
+    assert lib.ss_ssd_fwd(ctypes.byref(p), *([FAKE] * 5), None, None, None, None, FAKE, None, FAKE, wsz - 1,
+                          None) == 5
+    assert lib.ss_ssd_fwd(ctypes.byref(p), None, *([FAKE] * 4), None, None, None, None, FAKE, None, FAKE, wsz,
+                          None) == 1
+    assert lib.ss_ssd_fwd(ctypes.byref(p), *([FAKE] * 5), None, None, None, FAKE + 4, FAKE, None, FAKE, wsz,
+                          None) == 4

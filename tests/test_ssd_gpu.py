@@ -1,0 +1,120 @@
+"""GPU parity of ss_ssd_fwd (the Mamba-2 SSD chunked scan on the matrix cores) against
+the float64 oracle's plain recurrence, through the C ABI.  16-bit data with fp32
+accumulation: the fp16/bf16 tolerance (2e-2 of max|y|) applies."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _util import TOL, f64, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _ss():
+    from mamba_selective_scan_fwd_amd import ss
+    ss.load_library()
+    return ss
+
+
+def _data(Bsz, L, Hn, G, N, io, seed, P=64):
+    rng = np.random.default_rng(seed)
+    t = lambda a: torch.from_numpy(a).to(DT[io])
+    dt0 = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), Hn))
+    return dict(x=t(rng.standard_normal((Bsz, L, Hn, P))), dt=t(rng.standard_normal((Bsz, L, Hn)) * 0.5),
+                A=torch.from_numpy(-np.exp(rng.uniform(0.0, np.log(16.0), Hn))).float(),
+                Bm=t(rng.standard_normal((Bsz, L, G, N))), Cm=t(rng.standard_normal((Bsz, L, G, N))),
+                D=torch.from_numpy(rng.standard_normal(Hn)).float(), z=t(rng.standard_normal((Bsz, L, Hn, P))),
+                dt_bias=torch.from_numpy(np.log(np.expm1(dt0))).float(),
+                h0=torch.from_numpy(rng.standard_normal((Bsz, Hn, P, N)) * 0.5).float())
+
+
+def _run(q, use=("D", "z", "dt_bias", "h0")):
+    ss = _ss()
+    g = {k: v.cuda() for k, v in q.items()}
+    y, fin = ss.ssd_fwd(g["x"], g["dt"], g["A"], g["Bm"], g["Cm"], D=g["D"] if "D" in use else None,
+                        z=g["z"] if "z" in use else None, dt_bias=g["dt_bias"] if "dt_bias" in use else None,
+                        h0=g["h0"] if "h0" in use else None, return_final_state=True)
+    torch.cuda.synchronize()
+    return y, fin
+
+
+def _ref(q, use=("D", "z", "dt_bias", "h0"), heads=None):
+    sel = (lambda a, ax: a) if heads is None else (lambda a, ax: a.index_select(ax, torch.as_tensor(heads)))
+    return oracle.ssd_fwd(f64(sel(q["x"], 2)), f64(sel(q["dt"], 2)), f64(sel(q["A"], 0)), f64(q["Bm"]), f64(q["Cm"]),
+                          D=f64(sel(q["D"], 0)) if "D" in use else None, z=f64(sel(q["z"], 2)) if "z" in use else None,
+                          dt_bias=f64(sel(q["dt_bias"], 0)) if "dt_bias" in use else None,
+                          h0=f64(sel(q["h0"], 1)) if "h0" in use else None)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f16"])
+@pytest.mark.parametrize("N", [32, 64, 96, 128])
+def test_state_sizes_and_dtypes(io, N):
+    say("ssd io=%s N=%d" % (io, N))
+    q = _data(2, 300, 4, 2, N, io, seed=N)
+    y, fin = _run(q)
+    yr, fr = _ref(q)
+    ey, ef = rel_err(f64(y), yr), rel_err(f64(fin), fr)
+    say("  errors y=%.2e final=%.2e" % (ey, ef))
+    assert ey <= TOL[io] and ef <= TOL[io]
+
+
+@pytest.mark.parametrize("L", [1, 2, 100, 255, 256, 257, 512, 777])
+def test_lengths(L):
+    q = _data(1, L, 2, 1, 64, "bf16", seed=L)
+    y, fin = _run(q)
+    yr, fr = _ref(q)
+    assert rel_err(f64(y), yr) <= TOL["bf16"] and rel_err(f64(fin), fr) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("use", [(), ("D",), ("z",), ("dt_bias",), ("h0",), ("D", "z", "dt_bias", "h0")])
+def test_optional_operands(use):
+    q = _data(2, 400, 4, 4, 64, "bf16", seed=7)
+    y, fin = _run(q, use)
+    yr, fr = _ref(q, use)
+    assert rel_err(f64(y), yr) <= TOL["bf16"] and rel_err(f64(fin), fr) <= TOL["bf16"]
+
+
+def test_softplus_off():
+    ss = _ss()
+    q = _data(1, 300, 2, 1, 64, "bf16", seed=8)
+    q["dt"] = (q["dt"].float().abs() * 0.05 + 0.001).to(torch.bfloat16)   # a positive Delta, used as given
+    g = {k: v.cuda() for k, v in q.items()}
+    y = ss.ssd_fwd(g["x"], g["dt"], g["A"], g["Bm"], g["Cm"], D=g["D"], dt_softplus=False)
+    torch.cuda.synchronize()
+    yr, _ = oracle.ssd_fwd(f64(q["x"]), f64(q["dt"]), f64(q["A"]), f64(q["Bm"]), f64(q["Cm"]), D=f64(q["D"]),
+                           softplus=False)
+    assert rel_err(f64(y), yr) <= TOL["bf16"]
+
+
+def test_prefill_in_pieces():
+    """ssd(x[:k]) -> final state -> ssd(x[k:], h0=final) == ssd(x), on the device."""
+    ss = _ss()
+    q = _data(2, 900, 4, 2, 64, "bf16", seed=9)
+    g = {k: v.cuda() for k, v in q.items()}
+    y, fin = ss.ssd_fwd(g["x"], g["dt"], g["A"], g["Bm"], g["Cm"], D=g["D"], dt_bias=g["dt_bias"],
+                        return_final_state=True)
+    k = 300
+    a = lambda t: t[:, :k].contiguous()
+    c = lambda t: t[:, k:].contiguous()
+    y1, f1 = ss.ssd_fwd(a(g["x"]), a(g["dt"]), g["A"], a(g["Bm"]), a(g["Cm"]), D=g["D"], dt_bias=g["dt_bias"],
+                        return_final_state=True)
+    y2, f2 = ss.ssd_fwd(c(g["x"]), c(g["dt"]), g["A"], c(g["Bm"]), c(g["Cm"]), D=g["D"], dt_bias=g["dt_bias"],
+                        h0=f1, return_final_state=True)
+    torch.cuda.synchronize()
+    assert rel_err(f64(torch.cat([y1, y2], dim=1)), f64(y)) <= TOL["bf16"]
+    assert rel_err(f64(f2), f64(fin)) <= TOL["bf16"]
+
+
+def test_mamba2_layer_shape_sampled_heads():
+    """d_model 768, expand 2 -> 24 heads of 64, d_state 128, one group (the "niverel-mamba"
+    README's V3 configuration), B=2, L=2048, bf16: five heads against the oracle."""
+    q = _data(2, 2048, 24, 1, 128, "bf16", seed=10)
+    y, fin = _run(q)
+    heads = [0, 5, 11, 17, 23]
+    yr, fr = _ref(q, heads=heads)
+    hi = torch.as_tensor(heads).cuda()
+    assert rel_err(f64(y.index_select(2, hi)), yr) <= TOL["bf16"]
+    assert rel_err(f64(fin.index_select(1, hi)), fr) <= TOL["bf16"]
