@@ -269,6 +269,7 @@ ss_status check_ssd(const ss_ssd_problem* p) {
   if (p->batch > lim || p->seqlen > lim || p->nheads > lim) return SS_ERR_BAD_SHAPE;
   const double nchunks = (double)((p->seqlen + kSsdChunk - 1) / kSsdChunk);
   if ((double)p->batch * nchunks * (double)p->nheads > (double)kMaxGrid) return SS_ERR_BAD_SHAPE;
+  if ((double)p->batch * nchunks * (double)p->ngroups * (kSsdChunk / 16) > (double)kMaxGrid) return SS_ERR_BAD_SHAPE;
   if ((double)p->batch * (double)p->seqlen * (double)p->nheads * 64.0 > 9.0e18) return SS_ERR_BAD_SHAPE;
   return SS_OK;
 }
@@ -283,7 +284,8 @@ size_t ss_ssd_workspace_size(const ss_ssd_problem* p) {
   if (check_ssd(p) != SS_OK) return 0;
   const size_t e = ssd_state_elems(p);
   const int64_t nchunks = (p->seqlen + kSsdChunk - 1) / kSsdChunk;
-  return align256(e * 4) + align256(e * 2) + align256((size_t)(p->batch * nchunks * p->nheads) * 4);
+  return align256(e * 4) + align256(e * 2) + align256((size_t)(p->batch * nchunks * p->nheads) * 4) +
+         align256((size_t)(p->batch * nchunks * p->ngroups) * (size_t)(kSsdChunk * kSsdChunk) * 4);
 }
 
 ss_status ss_ssd_fwd(const ss_ssd_problem* p, const void* x, const void* dt, const float* A, const void* Bm,
@@ -306,6 +308,9 @@ ss_status ss_ssd_fwd(const ss_ssd_problem* p, const void* x, const void* dt, con
   k.ws_state = reinterpret_cast<float*>(ws);
   k.ws_entry = reinterpret_cast<uint16_t*>(ws + align256(e * 4));
   k.ws_decay = reinterpret_cast<float*>(ws + align256(e * 4) + align256(e * 2));
+  k.ws_cb = reinterpret_cast<float*>(ws + align256(e * 4) + align256(e * 2) +
+                                     align256((size_t)(p->batch * ((p->seqlen + kSsdChunk - 1) / kSsdChunk) *
+                                                       p->nheads) * 4));
   k.batch = p->batch; k.seqlen = p->seqlen; k.nheads = p->nheads; k.ngroups = p->ngroups; k.dstate = p->dstate;
   k.nchunks = (p->seqlen + kSsdChunk - 1) / kSsdChunk;
   return from_hip(ss::launch_ssd(k, static_cast<hipStream_t>(stream)));

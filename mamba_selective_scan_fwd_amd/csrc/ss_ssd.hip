@@ -95,14 +95,54 @@ __device__ __forceinline__ void chunk_cumsum(const SsdParams& p, int64_t b, int6
   __syncthreads();
 }
 
+// Stage a 64-step piece of a (time x width) row-major 16-bit tensor into LDS
+// transposed, dst[col][j] (j contiguous, row stride kXR): work item (jq, co)
+// reads steps 4 jq .. 4 jq + 3 of columns 8 co .. 8 co + 7 with four 16-byte
+// loads and writes each column's 4 steps with one 8-byte store.  `scale`
+// (per step, optional) multiplies the values first.
+template <int IO, int WIDTH, int kXR>
+__device__ __forceinline__ void stage_transposed(uint16_t (*dst)[kXR], const char* base, int64_t row_stride_bytes,
+                                                 int64_t t0, int64_t seqlen, const float* scale, int item) {
+  constexpr int kOct = WIDTH / 8;
+  const int jq = item / kOct, co = item % kOct;
+  uint32_t w[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t t = t0 + 4 * jq + r;
+    u32x4v v = u32x4v{0u, 0u, 0u, 0u};
+    if (t < seqlen) v = *reinterpret_cast<const u32x4v*>(base + t * row_stride_bytes + co * 16);
+    if (scale) {
+      const float sc = scale[4 * jq + r];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = bits_f32<IO>((raw_t<IO>)(v[q] & 0xffffu)) * sc;
+        const float hi = bits_f32<IO>((raw_t<IO>)(v[q] >> 16)) * sc;
+        v[q] = (uint32_t)bits16<IO>(lo) | ((uint32_t)bits16<IO>(hi) << 16);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[r][q] = v[q];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {  // column 8 co + e: its 4 steps
+    const int q = e / 2, sh = 16 * (e % 2);
+    const uint32_t a0 = (w[0][q] >> sh) & 0xffffu, a1 = (w[1][q] >> sh) & 0xffffu;
+    const uint32_t a2 = (w[2][q] >> sh) & 0xffffu, a3 = (w[3][q] >> sh) & 0xffffu;
+    uint2 pk;
+    pk.x = a0 | (a1 << 16);
+    pk.y = a2 | (a3 << 16);
+    *reinterpret_cast<uint2*>(&dst[8 * co + e][4 * jq]) = pk;
+  }
+}
+
 // ---- pass 1: the chunk's own state S_c[p][n] = sum_j w_j x_j[p] B_j[n] ----
 template <int IO, int N>
 __global__ void __launch_bounds__(kSsdThreads) ssd_state_kernel(SsdParams p) {
   using M = mfma_t<IO>;
-  constexpr int kXR = kJB + 8;  // padded LDS row (16-bit elements) of the transposed tiles
-  __shared__ float sDelta[kQ], sCs[kQ], sWave[4];
-  __shared__ uint16_t sXT[kP][kXR];  // (x * w)^T of one 64-step piece: [p][j]
-  __shared__ uint16_t sBT[N][kXR];   // B^T of the piece: [n][j]
+  constexpr int kXR = kJB + 8;  // padded LDS row (16-bit elements; 144 B keeps 16-byte reads aligned)
+  __shared__ float sDelta[kQ], sCs[kQ], sWave[4], sW[kQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sXT[kP][kXR];  // (x * w)^T of one 64-step piece: [p][j]
+  __shared__ __attribute__((aligned(16))) uint16_t sBT[N][kXR];   // B^T of the piece: [n][j]
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const int64_t h = blockIdx.x % p.nheads;
   const int64_t c = (blockIdx.x / p.nheads) % p.nchunks;
@@ -111,31 +151,21 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_state_kernel(SsdParams p) {
   const float A = p.A[h];
   chunk_cumsum<IO>(p, b, c, h, A, sDelta, sCs, sWave);
   const float cs_last = sCs[kQ - 1];
+  sW[tid] = exp2_hw((cs_last - sCs[tid]) * kLog2e) * sDelta[tid];  // 0 past the sequence (Delta = 0)
+  __syncthreads();
 
   f32x4 acc[N / 16];
 #pragma unroll
   for (int i = 0; i < N / 16; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const char* xbase = static_cast<const char*>(p.x) + ((b * p.seqlen) * p.nheads + h) * kP * 2;
+  const char* bbase = static_cast<const char*>(p.Bm) + ((b * p.seqlen) * p.ngroups + g) * N * 2;
 
   for (int jb = 0; jb < kQ; jb += kJB) {
-    // stage: thread covers step j = jb + tid / 4, 16 of the 64 headdim lanes and N/4 states
-    {
-      const int jj = tid / 4, part = tid % 4;
-      const int64_t t = c * kQ + jb + jj;
-      const bool ok = t < p.seqlen;
-      const float w = ok ? exp2_hw((cs_last - sCs[jb + jj]) * kLog2e) * sDelta[jb + jj] : 0.0f;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int pp = part * 16 + q;
-        const float xv = ok ? load_io<IO>(p.x, ((b * p.seqlen + t) * p.nheads + h) * kP + pp) : 0.0f;
-        sXT[pp][jj] = bits16<IO>(xv * w);
-      }
-#pragma unroll
-      for (int q = 0; q < N / 4; ++q) {
-        const int n = part * (N / 4) + q;
-        const float bv = ok ? load_io<IO>(p.Bm, ((b * p.seqlen + t) * p.ngroups + g) * N + n) : 0.0f;
-        sBT[n][jj] = bits16<IO>(bv);
-      }
-    }
+    const int64_t t0 = c * kQ + jb;
+    if (tid < 16 * (kP / 8))
+      stage_transposed<IO, kP, kXR>(sXT, xbase, p.nheads * kP * 2, t0, p.seqlen, sW + jb, tid);
+    if (tid < 16 * (N / 8))
+      stage_transposed<IO, N, kXR>(sBT, bbase, p.ngroups * N * 2, t0, p.seqlen, nullptr, tid);
     __syncthreads();
     // wave w: rows p in [16w, 16w + 16), all N/16 column tiles; K = 64 in two steps
 #pragma unroll
@@ -177,151 +207,220 @@ __global__ void __launch_bounds__(256) ssd_pass_kernel(SsdParams p) {
   if (p.final_state) p.final_state[e] = H;
 }
 
+// ---- C B^T of a chunk, once per group ---------------------------------------------
+// CB[i][j] = sum_n C_i[n] B_j[n] in fp32 for the chunk's rows i and the columns j
+// of every 64-step piece up to the one holding i (the causal half plus the rest
+// of the diagonal pieces, so that the scan never reads an unwritten value).
+// Workgroup = (batch, chunk, group, 16-row tile); wave w takes column tiles
+// w, w + 4, ... .  Shared by all heads of the group.
+template <int IO, int N>
+__global__ void __launch_bounds__(kSsdThreads) ssd_cb_kernel(SsdParams p) {
+  using M = mfma_t<IO>;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int rt = blockIdx.x % (kQ / 16);
+  const int64_t bcg = blockIdx.x / (kQ / 16);
+  const int64_t g = bcg % p.ngroups;
+  const int64_t c = (bcg / p.ngroups) % p.nchunks;
+  const int64_t b = bcg / (p.ngroups * p.nchunks);
+  const int64_t t0 = c * kQ;
+  const int64_t crow = p.ngroups * N * 2;
+  const char* cbase = static_cast<const char*>(p.Cm) + ((b * p.seqlen) * p.ngroups + g) * N * 2;
+  const char* bbase = static_cast<const char*>(p.Bm) + ((b * p.seqlen) * p.ngroups + g) * N * 2;
+  auto frag = [&](const char* base, int64_t t, int n0) -> u32x4v {
+    if (t >= p.seqlen) return u32x4v{0u, 0u, 0u, 0u};
+    return *reinterpret_cast<const u32x4v*>(base + t * crow + n0 * 2);
+  };
+  const int last_tile = 4 * (rt / 4) + 3;
+  u32x4v af[N / 32], bf[4][N / 32];
+#pragma unroll
+  for (int ks = 0; ks < N / 32; ++ks) af[ks] = frag(cbase, t0 + 16 * rt + lane % 16, 32 * ks + 8 * (lane / 16));
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int jt = wave + 4 * u;
+#pragma unroll
+    for (int ks = 0; ks < N / 32; ++ks)
+      bf[u][ks] = jt <= last_tile ? frag(bbase, t0 + 16 * jt + lane % 16, 32 * ks + 8 * (lane / 16))
+                                  : u32x4v{0u, 0u, 0u, 0u};
+  }
+  float* CB = p.ws_cb + (bcg * kQ) * (int64_t)kQ;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int jt = wave + 4 * u;
+    if (jt > last_tile) break;
+    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < N / 32; ++ks) acc = M::run(as_vec<IO>(af[ks]), as_vec<IO>(bf[u][ks]), acc);
+    // lane holds rows i = 16 rt + 4 (lane / 16) + r of column j = 16 jt + lane % 16
+#pragma unroll
+    for (int r = 0; r < 4; ++r) CB[(16 * rt + 4 * (lane / 16) + r) * kQ + 16 * jt + lane % 16] = acc[r];
+  }
+}
+
 // ---- pass 3: outputs of a chunk -------------------------------------------------
+// Y is built transposed, Y^T[p][i], so that each lane ends up with 4
+// consecutive channels p of one step i.  The chunk's 256 rows are 8 blocks of
+// 32; wave w takes blocks w and 7 - w, so every wave does the same causal work
+// (block r needs column pieces 0 .. r / 2 of 64 steps).
+//   Y^T = diag-scaled H_in C^T       (entry state: A = H_in, B = C^T)
+//       + x^T M^T                    (A = x^T from LDS, B = M^T built in registers)
+// with M[i][j] = CB[i][j] exp(cs_i - cs_j) Delta_j for j <= i.  Off the
+// diagonal piece the decay factors through the piece's last step e:
+// exp(cs_i - cs_e) * exp(cs_e - cs_j), both at most 1 there, so only one exp
+// per lane is needed; the diagonal piece takes the exp per element.
 template <int IO, int N>
 __global__ void __launch_bounds__(kSsdThreads) ssd_scan_kernel(SsdParams p) {
   using M = mfma_t<IO>;
-  constexpr int kXR = kJB + 8;
-  constexpr int kMR = kJB + 8;
-  __shared__ float sDelta[kQ], sCs[kQ], sWave[4];
-  __shared__ uint16_t sXT[kP][kXR];              // x^T of one 64-step piece: [p][j]
-  __shared__ uint16_t sM[4][64][kMR];            // per wave: masked, decayed C B^T block [i][j]
+  constexpr int kXR = kQ + 8;  // x^T row: 264 elements (528 B keeps 16-byte reads aligned)
+  __shared__ __attribute__((aligned(16))) float sDelta[kQ];
+  __shared__ __attribute__((aligned(16))) float sCs[kQ];
+  __shared__ float sWave[4];
+  __shared__ __attribute__((aligned(16))) float sWp[kQ];           // exp(cs_e - cs_j) Delta_j, e = end of j's piece
+  __shared__ __attribute__((aligned(16))) uint16_t sXT[kP][kXR];   // x^T of the chunk: [p][j]
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const int64_t h = blockIdx.x % p.nheads;
   const int64_t c = (blockIdx.x / p.nheads) % p.nchunks;
   const int64_t b = blockIdx.x / (p.nheads * p.nchunks);
   const int64_t g = h / (p.nheads / p.ngroups);
   const float A = p.A[h];
-  chunk_cumsum<IO>(p, b, c, h, A, sDelta, sCs, sWave);
-
-  const int row0 = 64 * wave;  // this wave's 64 rows (steps) of the chunk
   const int64_t t0 = c * kQ;
-  // C fragment of row tile mt, k step ks: C[t][n], n = ks + 8 (lane / 16) .. + 7
-  auto load_c = [&](int mt, int ks) -> u32x4v {
-    const int64_t t = t0 + row0 + 16 * mt + lane % 16;
-    if (t >= p.seqlen) return u32x4v{0u, 0u, 0u, 0u};
-    const char* base = static_cast<const char*>(p.Cm) + (((b * p.seqlen + t) * p.ngroups + g) * N + ks + 8 * (lane / 16)) * 2;
-    return *reinterpret_cast<const u32x4v*>(base);
-  };
+  const char* xbase = static_cast<const char*>(p.x) + ((b * p.seqlen) * p.nheads + h) * kP * 2;
+#pragma unroll
+  for (int it = 0; it < 2; ++it)  // 512 work items: 4 pieces of 64 steps x 128
+    stage_transposed<IO, kP, kXR>(reinterpret_cast<uint16_t(*)[kXR]>(&sXT[0][64 * (2 * it + tid / 128)]), xbase,
+                                  p.nheads * kP * 2, t0 + 64 * (2 * it + tid / 128), p.seqlen, nullptr, tid % 128);
+  chunk_cumsum<IO>(p, b, c, h, A, sDelta, sCs, sWave);  // ends with a barrier
+  sWp[tid] = exp2_hw((sCs[tid | 63] - sCs[tid]) * kLog2e) * sDelta[tid];
 
-  // Y starts as Y_off = diag(exp(cs_i)) C H_in: acc[mt][nt], rows i = row0 + 16 mt + 4 (lane/16) + r, col p = 16 nt + lane%16
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const char* cbase = static_cast<const char*>(p.Cm) + ((b * p.seqlen) * p.ngroups + g) * N * 2;
+  const int64_t crow = p.ngroups * N * 2;
+  auto cfrag = [&](int64_t t, int n0) -> u32x4v {
+    if (t >= p.seqlen) return u32x4v{0u, 0u, 0u, 0u};
+    return *reinterpret_cast<const u32x4v*>(cbase + t * crow + n0 * 2);
+  };
+  const int blk[2] = {wave, 7 - wave};
+  f32x4 acc[2][4][2];  // [block][p tile][i tile]: p = 16 pt + 4 (lane / 16) + r, i = 32 blk + 16 it + lane % 16
   {
     const uint16_t* Hin = p.ws_entry + ((b * p.nchunks + c) * p.nheads + h) * (int64_t)(kP * N);
 #pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int it = 0; it < 2; ++it) acc[q][pt][it] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
     for (int ks = 0; ks < N; ks += 32) {
-      u32x4v bfrag[4];
+      const int n0 = ks + 8 * (lane / 16);
+      u32x4v hf[4], cf[2][2];
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)  // B[k = n][col = p] = H_in[p][n]: 8 consecutive n
-        bfrag[nt] = *reinterpret_cast<const u32x4v*>(Hin + (16 * nt + lane % 16) * N + ks + 8 * (lane / 16));
+      for (int pt = 0; pt < 4; ++pt) hf[pt] = *reinterpret_cast<const u32x4v*>(Hin + (16 * pt + lane % 16) * N + n0);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const u32x4v a = load_c(mt, ks);
+      for (int q = 0; q < 2; ++q)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = M::run(as_vec<IO>(a), as_vec<IO>(bfrag[nt]), acc[mt][nt]);
-      }
+        for (int it = 0; it < 2; ++it) cf[q][it] = cfrag(t0 + 32 * blk[q] + 16 * it + lane % 16, n0);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+          for (int it = 0; it < 2; ++it)
+            acc[q][pt][it] = M::run(as_vec<IO>(hf[pt]), as_vec<IO>(cf[q][it]), acc[q][pt][it]);
     }
+    __syncthreads();  // sWp
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float sc = exp2_hw(sCs[row0 + 16 * mt + 4 * (lane / 16) + r] * kLog2e);
+      for (int it = 0; it < 2; ++it) {
+        const float sc = exp2_hw(sCs[32 * blk[q] + 16 * it + lane % 16] * kLog2e);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt][r] *= sc;
+        for (int pt = 0; pt < 4; ++pt) acc[q][pt][it] *= sc;
       }
   }
 
-  // Y_diag: column pieces jb <= row0 (causal), all waves stage every piece
-  for (int jb = 0; jb < kQ; jb += kJB) {
-    {  // stage x^T of the piece: thread covers step jb + tid / 4 and 16 headdim lanes
-      const int jj = tid / 4, part = tid % 4;
-      const int64_t t = t0 + jb + jj;
-      const bool ok = t < p.seqlen;
+  const float* CBbase = p.ws_cb + ((b * p.nchunks + c) * p.ngroups + g) * (int64_t)(kQ * kQ);
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int pp = part * 16 + q;
-        sXT[pp][jj] = ok ? bits16<IO>(load_io<IO>(p.x, ((b * p.seqlen + t) * p.nheads + h) * kP + pp)) : (uint16_t)0;
-      }
+  for (int q = 0; q < 2; ++q) {
+    const int i0 = 32 * blk[q];
+    const int dpiece = blk[q] / 2;  // the piece holding this block's rows
+    float csi[2];
+    const float* cbrow[2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      csi[it] = sCs[i0 + 16 * it + lane % 16];
+      cbrow[it] = CBbase + (i0 + 16 * it + lane % 16) * kQ;
     }
-    __syncthreads();
-    if (jb <= row0) {
-      // C B^T block: rows i of this wave x the piece's 64 columns j
-      f32x4 cb[4][4];
+    for (int piece = 0; piece <= dpiece; ++piece) {
+      const int jb = 64 * piece;
+      const bool diag = piece == dpiece;
+      float ei[2];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) cb[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ks = 0; ks < N; ks += 32) {
-        u32x4v bfrag[4];
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {  // B[k = n][col = j] = B_j[n]
-          const int64_t t = t0 + jb + 16 * nt + lane % 16;
-          bfrag[nt] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(
-                                         static_cast<const char*>(p.Bm) +
-                                         (((b * p.seqlen + t) * p.ngroups + g) * N + ks + 8 * (lane / 16)) * 2)
-                                   : u32x4v{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const u32x4v a = load_c(mt, ks);
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) cb[mt][nt] = M::run(as_vec<IO>(a), as_vec<IO>(bfrag[nt]), cb[mt][nt]);
-        }
-      }
-      // mask and decay: M[i][j] = CB[i][j] exp(cs_i - cs_j) Delta_j for j <= i, into LDS as [i][j]
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int j = jb + 16 * nt + lane % 16;
-        const float csj = sCs[j], dj = sDelta[j];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = row0 + 16 * mt + 4 * (lane / 16) + r;
-            const float m = j <= i ? cb[mt][nt][r] * exp2_hw((sCs[i] - csj) * kLog2e) * dj : 0.0f;
-            sM[wave][16 * mt + 4 * (lane / 16) + r][16 * nt + lane % 16] = bits16<IO>(m);
-          }
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // Y += M (64 x 64, A from LDS) x^T-piece (B from LDS)
+      for (int it = 0; it < 2; ++it) ei[it] = exp2_hw((csi[it] - sCs[jb + 63]) * kLog2e);
 #pragma unroll
       for (int ks = 0; ks < kJB; ks += 32) {
-        const int k0 = ks + 8 * (lane / 16);
-        u32x4v bfrag[4];
+        const int j0 = jb + ks + 8 * (lane / 16);
+        u32x4v xa[4];
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) bfrag[nt] = *reinterpret_cast<const u32x4v*>(&sXT[16 * nt + lane % 16][k0]);
+        for (int pt = 0; pt < 4; ++pt) xa[pt] = *reinterpret_cast<const u32x4v*>(&sXT[16 * pt + lane % 16][j0]);
+        const float4 w0 = *reinterpret_cast<const float4*>(&sWp[j0]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&sWp[j0 + 4]);
+        const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const u32x4v a = *reinterpret_cast<const u32x4v*>(&sM[wave][16 * mt + lane % 16][k0]);
+        for (int it = 0; it < 2; ++it) {
+          const int i = i0 + 16 * it + lane % 16;
+          const float4 c0 = *reinterpret_cast<const float4*>(cbrow[it] + j0);
+          const float4 c1 = *reinterpret_cast<const float4*>(cbrow[it] + j0 + 4);
+          const float cb[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+          float m[8];
+          if (diag) {
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = M::run(as_vec<IO>(a), as_vec<IO>(bfrag[nt]), acc[mt][nt]);
+            for (int e = 0; e < 8; ++e) {
+              const int j = j0 + e;
+              const float v = cb[e] * exp2_hw((csi[it] - sCs[j]) * kLog2e) * sDelta[j];
+              m[e] = j <= i ? v : 0.0f;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m[e] = cb[e] * (wj[e] * ei[it]);
+          }
+          u32x4v bop;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            bop[e] = (uint32_t)bits16<IO>(m[2 * e]) | ((uint32_t)bits16<IO>(m[2 * e + 1]) << 16);
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt) acc[q][pt][it] = M::run(as_vec<IO>(xa[pt]), as_vec<IO>(bop), acc[q][pt][it]);
         }
       }
     }
-    __syncthreads();
   }
 
-  // D skip, gate, store
+  // D skip, gate, store: lane has channels 16 pt + 4 (lane / 16) .. + 3 of step i
   const float Dh = p.D ? p.D[h] : 0.0f;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t t = t0 + row0 + 16 * mt + 4 * (lane / 16) + r;
+    for (int it = 0; it < 2; ++it) {
+      const int64_t t = t0 + 32 * blk[q] + 16 * it + lane % 16;
       if (t >= p.seqlen) continue;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int64_t idx = ((b * p.seqlen + t) * p.nheads + h) * kP + 16 * nt + lane % 16;
-        float yv = fmaf(Dh, load_io<IO>(p.x, idx), acc[mt][nt][r]);
-        if (p.z) yv *= silu_f(load_io<IO>(p.z, idx));
-        store_io<IO>(p.y, idx, yv);
+      for (int pt = 0; pt < 4; ++pt) {
+        const int64_t idx = ((b * p.seqlen + t) * p.nheads + h) * kP + 16 * pt + 4 * (lane / 16);
+        const uint2 xv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.x) + idx);
+        uint2 zv = make_uint2(0u, 0u);
+        if (p.z) zv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.z) + idx);
+        const uint32_t xw[2] = {xv.x, xv.y}, zw[2] = {zv.x, zv.y};
+        uint32_t yw[2];
+#pragma unroll
+        for (int hw = 0; hw < 2; ++hw) {
+          float yy[2];
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const float xf = bits_f32<IO>((raw_t<IO>)((xw[hw] >> (16 * s2)) & 0xffffu));
+            float yv = fmaf(Dh, xf, acc[q][pt][it][2 * hw + s2]);
+            if (p.z) yv *= silu_f(bits_f32<IO>((raw_t<IO>)((zw[hw] >> (16 * s2)) & 0xffffu)));
+            yy[s2] = yv;
+          }
+          yw[hw] = (uint32_t)bits16<IO>(yy[0]) | ((uint32_t)bits16<IO>(yy[1]) << 16);
+        }
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + idx) = make_uint2(yw[0], yw[1]);
       }
     }
 }
@@ -331,6 +430,10 @@ hipError_t launch_ssd_n(const SsdParams& p, hipStream_t st) {
   const dim3 grid((uint32_t)(p.batch * p.nchunks * p.nheads));
   hipLaunchKernelGGL((ssd_state_kernel<IO, N>), grid, dim3(kSsdThreads), 0, st, p);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((ssd_cb_kernel<IO, N>), dim3((uint32_t)(p.batch * p.nchunks * p.ngroups * (kQ / 16))),
+                     dim3(kSsdThreads), 0, st, p);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t elems = p.batch * p.nheads * kP * N;
   hipLaunchKernelGGL((ssd_pass_kernel<IO>), dim3((uint32_t)((elems + 255) / 256)), dim3(256), 0, st, p);
