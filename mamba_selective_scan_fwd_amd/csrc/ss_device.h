@@ -36,11 +36,8 @@ template <int IO> __device__ __forceinline__ typename io_elem<IO>::T from_f32(fl
 template <> __device__ __forceinline__ float from_f32<SS_F32>(float v) { return v; }
 template <> __device__ __forceinline__ _Float16 from_f32<SS_F16>(float v) { return (_Float16)v; }
 template <> __device__ __forceinline__ uint16_t from_f32<SS_BF16>(float v) {
-  // round to nearest even (NaN kept quiet)
-  uint32_t bits = __float_as_uint(v);
-  if ((bits & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((bits >> 16) | 0x40u);
-  bits += 0x7fffu + ((bits >> 16) & 1u);
-  return (uint16_t)(bits >> 16);
+  // round to nearest even in hardware (v_cvt_pk_bf16_f32 on gfx950)
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
 // ---- buffer-resource access (hardware range check: loads past num_records

@@ -63,6 +63,18 @@ template <int IO>
 __device__ __forceinline__ uint16_t bits16(float v) {
   return __builtin_bit_cast(uint16_t, from_f32<IO>(v));
 }
+// two values packed low-first into one word of the I/O dtype (one packed
+// hardware conversion, round to nearest even)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <int IO>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (IO == SS_BF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+}
 template <int IO>
 __device__ __forceinline__ typename mfma_t<IO>::V as_vec(u32x4v w) {
   return __builtin_bit_cast(typename mfma_t<IO>::V, w);
@@ -117,7 +129,7 @@ __device__ __forceinline__ void stage_transposed(uint16_t (*dst)[kXR], const cha
       for (int q = 0; q < 4; ++q) {
         const float lo = bits_f32<IO>((raw_t<IO>)(v[q] & 0xffffu)) * sc;
         const float hi = bits_f32<IO>((raw_t<IO>)(v[q] >> 16)) * sc;
-        v[q] = (uint32_t)bits16<IO>(lo) | ((uint32_t)bits16<IO>(hi) << 16);
+        v[q] = pack2<IO>(lo, hi);
       }
     }
 #pragma unroll
@@ -136,40 +148,143 @@ __device__ __forceinline__ void stage_transposed(uint16_t (*dst)[kXR], const cha
 }
 
 // ---- pass 1: the chunk's own state S_c[p][n] = sum_j w_j x_j[p] B_j[n] ----
+// w_j = exp(cs_last - cs_j) Delta_j.  Every global operand of the chunk (x,
+// B, dt) is loaded at once into registers, then moved to LDS transposed
+// (time contiguous) two 64-step pieces at a time for the MFMAs: wave w takes
+// rows p in [16w, 16w + 16) and all states n.  The workgroups of a group's
+// heads also share out the group's C B^T: head k of the group takes the
+// 16-row tiles k, k + heads_per_group, ...
+template <int IO, int N>
+__device__ __forceinline__ void cb_row_tile(const SsdParams& p, int64_t b, int64_t c, int64_t g, int rt, int lane,
+                                            int wave) {
+  using M = mfma_t<IO>;
+  const int64_t t0 = c * kQ;
+  const int64_t crow = p.ngroups * N * 2;
+  const char* cbase = static_cast<const char*>(p.Cm) + ((b * p.seqlen) * p.ngroups + g) * N * 2;
+  const char* bbase = static_cast<const char*>(p.Bm) + ((b * p.seqlen) * p.ngroups + g) * N * 2;
+  auto frag = [&](const char* base, int64_t t, int n0) -> u32x4v {
+    if (t >= p.seqlen) return u32x4v{0u, 0u, 0u, 0u};
+    return *reinterpret_cast<const u32x4v*>(base + t * crow + n0 * 2);
+  };
+  // columns of every 64-step piece up to the one holding the row tile
+  const int last_tile = 4 * (rt / 4) + 3;
+  u32x4v af[N / 32], bf[4][N / 32];
+#pragma unroll
+  for (int ks = 0; ks < N / 32; ++ks) af[ks] = frag(cbase, t0 + 16 * rt + lane % 16, 32 * ks + 8 * (lane / 16));
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int jt = wave + 4 * u;
+#pragma unroll
+    for (int ks = 0; ks < N / 32; ++ks)
+      bf[u][ks] = jt <= last_tile ? frag(bbase, t0 + 16 * jt + lane % 16, 32 * ks + 8 * (lane / 16))
+                                  : u32x4v{0u, 0u, 0u, 0u};
+  }
+  float* CB = p.ws_cb + ((b * p.nchunks + c) * p.ngroups + g) * (int64_t)(kQ * kQ);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int jt = wave + 4 * u;
+    if (jt > last_tile) break;
+    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < N / 32; ++ks) acc = M::run(as_vec<IO>(af[ks]), as_vec<IO>(bf[u][ks]), acc);
+    // lane holds rows i = 16 rt + 4 (lane / 16) + r of column j = 16 jt + lane % 16
+#pragma unroll
+    for (int r = 0; r < 4; ++r) CB[(16 * rt + 4 * (lane / 16) + r) * kQ + 16 * jt + lane % 16] = acc[r];
+  }
+}
+
 template <int IO, int N>
 __global__ void __launch_bounds__(kSsdThreads) ssd_state_kernel(SsdParams p) {
   using M = mfma_t<IO>;
-  constexpr int kXR = kJB + 8;  // padded LDS row (16-bit elements; 144 B keeps 16-byte reads aligned)
-  __shared__ float sDelta[kQ], sCs[kQ], sWave[4], sW[kQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sXT[kP][kXR];  // (x * w)^T of one 64-step piece: [p][j]
-  __shared__ __attribute__((aligned(16))) uint16_t sBT[N][kXR];   // B^T of the piece: [n][j]
+  constexpr int kXR = 2 * kJB + 8;  // LDS row: two pieces of time, padded (272 B keeps 16-byte reads aligned)
+  __shared__ __attribute__((aligned(16))) float sW[kQ];
+  __shared__ float sDelta[kQ], sCs[kQ], sWave[4];
+  __shared__ __attribute__((aligned(16))) uint16_t sXT[kP][kXR];  // (x * w)^T of two pieces: [p][j]
+  __shared__ __attribute__((aligned(16))) uint16_t sBT[N][kXR];   // B^T of two pieces: [n][j]
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-  const int64_t h = blockIdx.x % p.nheads;
-  const int64_t c = (blockIdx.x / p.nheads) % p.nchunks;
-  const int64_t b = blockIdx.x / (p.nheads * p.nchunks);
-  const int64_t g = h / (p.nheads / p.ngroups);
-  const float A = p.A[h];
-  chunk_cumsum<IO>(p, b, c, h, A, sDelta, sCs, sWave);
-  const float cs_last = sCs[kQ - 1];
-  sW[tid] = exp2_hw((cs_last - sCs[tid]) * kLog2e) * sDelta[tid];  // 0 past the sequence (Delta = 0)
+  const int64_t lb = xcd_logical_block();  // the heads of one chunk run on one XCD and share its B, C in L2
+  const int64_t h = lb % p.nheads;
+  const int64_t c = (lb / p.nheads) % p.nchunks;
+  const int64_t b = lb / (p.nheads * p.nchunks);
+  const int64_t hpg = p.nheads / p.ngroups;
+  const int64_t g = h / hpg;
+  const int64_t t0 = c * kQ;
+  const int64_t xrow = p.nheads * kP * 2, brow = p.ngroups * N * 2;
+  const char* xbase = static_cast<const char*>(p.x) + ((b * p.seqlen) * p.nheads + h) * kP * 2;
+  const char* bbase = static_cast<const char*>(p.Bm) + ((b * p.seqlen) * p.ngroups + g) * N * 2;
+
+  // x: 512 items (4 steps x 8 channels); item = tid + 256 k, piece 2 k + tid / 128
+  u32x4v xr[2][4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int item = tid + kSsdThreads * k, pc = item / 128, jq = (item % 128) / 8, co = item % 8;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = t0 + 64 * pc + 4 * jq + r;
+      xr[k][r] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(xbase + t * xrow + co * 16) : u32x4v{0u, 0u, 0u, 0u};
+    }
+  }
+  // B: 8 N items (4 steps x 8 states), N / 32 per thread; item = tid + 256 k
+  constexpr int kBI = N / 32;
+  u32x4v br[kBI][4];
+#pragma unroll
+  for (int k = 0; k < kBI; ++k) {
+    const int item = tid + kSsdThreads * k, pc = item / (2 * N), rem = item % (2 * N);
+    const int jq = rem / (N / 8), co = rem % (N / 8);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t t = t0 + 64 * pc + 4 * jq + r;
+      br[k][r] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(bbase + t * brow + co * 16) : u32x4v{0u, 0u, 0u, 0u};
+    }
+  }
+  chunk_cumsum<IO>(p, b, c, h, p.A[h], sDelta, sCs, sWave);  // ends with a barrier
+  sW[tid] = exp2_hw((sCs[kQ - 1] - sCs[tid]) * kLog2e) * sDelta[tid];  // 0 past the sequence (Delta = 0)
   __syncthreads();
 
   f32x4 acc[N / 16];
 #pragma unroll
   for (int i = 0; i < N / 16; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  const char* xbase = static_cast<const char*>(p.x) + ((b * p.seqlen) * p.nheads + h) * kP * 2;
-  const char* bbase = static_cast<const char*>(p.Bm) + ((b * p.seqlen) * p.ngroups + g) * N * 2;
-
-  for (int jb = 0; jb < kQ; jb += kJB) {
-    const int64_t t0 = c * kQ + jb;
-    if (tid < 16 * (kP / 8))
-      stage_transposed<IO, kP, kXR>(sXT, xbase, p.nheads * kP * 2, t0, p.seqlen, sW + jb, tid);
-    if (tid < 16 * (N / 8))
-      stage_transposed<IO, N, kXR>(sBT, bbase, p.ngroups * N * 2, t0, p.seqlen, nullptr, tid);
-    __syncthreads();
-    // wave w: rows p in [16w, 16w + 16), all N/16 column tiles; K = 64 in two steps
 #pragma unroll
-    for (int ks = 0; ks < kJB; ks += 32) {
+  for (int round = 0; round < 2; ++round) {
+    {  // x * w, transposed
+      const int item = tid + kSsdThreads * round, pc = item / 128, jq = (item % 128) / 8, co = item % 8;
+      uint32_t v[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sc = sW[64 * pc + 4 * jq + r];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = bits_f32<IO>((raw_t<IO>)(xr[round][r][q] & 0xffffu)) * sc;
+          const float hi = bits_f32<IO>((raw_t<IO>)(xr[round][r][q] >> 16)) * sc;
+          v[r][q] = pack2<IO>(lo, hi);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int q = e / 2, sh = 16 * (e % 2);
+        uint2 pk;
+        pk.x = ((v[0][q] >> sh) & 0xffffu) | (((v[1][q] >> sh) & 0xffffu) << 16);
+        pk.y = ((v[2][q] >> sh) & 0xffffu) | (((v[3][q] >> sh) & 0xffffu) << 16);
+        *reinterpret_cast<uint2*>(&sXT[8 * co + e][64 * (pc % 2) + 4 * jq]) = pk;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kBI; ++k) {  // B, transposed
+      const int item = tid + kSsdThreads * k, pc = item / (2 * N), rem = item % (2 * N);
+      if (pc / 2 != round) continue;
+      const int jq = rem / (N / 8), co = rem % (N / 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int q = e / 2, sh = 16 * (e % 2);
+        uint2 pk;
+        pk.x = ((br[k][0][q] >> sh) & 0xffffu) | (((br[k][1][q] >> sh) & 0xffffu) << 16);
+        pk.y = ((br[k][2][q] >> sh) & 0xffffu) | (((br[k][3][q] >> sh) & 0xffffu) << 16);
+        *reinterpret_cast<uint2*>(&sBT[8 * co + e][64 * (pc % 2) + 4 * jq]) = pk;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 2 * kJB; ks += 32) {
       const int k0 = ks + 8 * (lane / 16);
       const u32x4v a = *reinterpret_cast<const u32x4v*>(&sXT[16 * wave + lane % 16][k0]);
 #pragma unroll
@@ -186,7 +301,9 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_state_kernel(SsdParams p) {
   for (int nt = 0; nt < N / 16; ++nt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) S[(16 * wave + 4 * (lane / 16) + r) * N + 16 * nt + lane % 16] = acc[nt][r];
-  if (tid == 0) p.ws_decay[(b * p.nchunks + c) * p.nheads + h] = exp2_hw(cs_last * kLog2e);
+  if (tid == 0) p.ws_decay[(b * p.nchunks + c) * p.nheads + h] = exp2_hw(sCs[kQ - 1] * kLog2e);
+  // this head's share of the group's C B^T
+  for (int64_t rt = h % hpg; rt < kQ / 16; rt += hpg) cb_row_tile<IO, N>(p, b, c, g, (int)rt, lane, wave);
 }
 
 // ---- pass 2: entry state of every chunk, H_in(c + 1) = decay_c H_in(c) + S_c ----
@@ -207,222 +324,241 @@ __global__ void __launch_bounds__(256) ssd_pass_kernel(SsdParams p) {
   if (p.final_state) p.final_state[e] = H;
 }
 
-// ---- C B^T of a chunk, once per group ---------------------------------------------
-// CB[i][j] = sum_n C_i[n] B_j[n] in fp32 for the chunk's rows i and the columns j
-// of every 64-step piece up to the one holding i (the causal half plus the rest
-// of the diagonal pieces, so that the scan never reads an unwritten value).
-// Workgroup = (batch, chunk, group, 16-row tile); wave w takes column tiles
-// w, w + 4, ... .  Shared by all heads of the group.
-template <int IO, int N>
-__global__ void __launch_bounds__(kSsdThreads) ssd_cb_kernel(SsdParams p) {
-  using M = mfma_t<IO>;
-  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
-  const int rt = blockIdx.x % (kQ / 16);
-  const int64_t bcg = blockIdx.x / (kQ / 16);
-  const int64_t g = bcg % p.ngroups;
-  const int64_t c = (bcg / p.ngroups) % p.nchunks;
-  const int64_t b = bcg / (p.ngroups * p.nchunks);
-  const int64_t t0 = c * kQ;
-  const int64_t crow = p.ngroups * N * 2;
-  const char* cbase = static_cast<const char*>(p.Cm) + ((b * p.seqlen) * p.ngroups + g) * N * 2;
-  const char* bbase = static_cast<const char*>(p.Bm) + ((b * p.seqlen) * p.ngroups + g) * N * 2;
-  auto frag = [&](const char* base, int64_t t, int n0) -> u32x4v {
-    if (t >= p.seqlen) return u32x4v{0u, 0u, 0u, 0u};
-    return *reinterpret_cast<const u32x4v*>(base + t * crow + n0 * 2);
-  };
-  const int last_tile = 4 * (rt / 4) + 3;
-  u32x4v af[N / 32], bf[4][N / 32];
-#pragma unroll
-  for (int ks = 0; ks < N / 32; ++ks) af[ks] = frag(cbase, t0 + 16 * rt + lane % 16, 32 * ks + 8 * (lane / 16));
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int jt = wave + 4 * u;
-#pragma unroll
-    for (int ks = 0; ks < N / 32; ++ks)
-      bf[u][ks] = jt <= last_tile ? frag(bbase, t0 + 16 * jt + lane % 16, 32 * ks + 8 * (lane / 16))
-                                  : u32x4v{0u, 0u, 0u, 0u};
-  }
-  float* CB = p.ws_cb + (bcg * kQ) * (int64_t)kQ;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int jt = wave + 4 * u;
-    if (jt > last_tile) break;
-    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ks = 0; ks < N / 32; ++ks) acc = M::run(as_vec<IO>(af[ks]), as_vec<IO>(bf[u][ks]), acc);
-    // lane holds rows i = 16 rt + 4 (lane / 16) + r of column j = 16 jt + lane % 16
-#pragma unroll
-    for (int r = 0; r < 4; ++r) CB[(16 * rt + 4 * (lane / 16) + r) * kQ + 16 * jt + lane % 16] = acc[r];
-  }
-}
-
 // ---- pass 3: outputs of a chunk -------------------------------------------------
 // Y is built transposed, Y^T[p][i], so that each lane ends up with 4
 // consecutive channels p of one step i.  The chunk's 256 rows are 8 blocks of
-// 32; wave w takes blocks w and 7 - w, so every wave does the same causal work
-// (block r needs column pieces 0 .. r / 2 of 64 steps).
-//   Y^T = diag-scaled H_in C^T       (entry state: A = H_in, B = C^T)
-//       + x^T M^T                    (A = x^T from LDS, B = M^T built in registers)
+// 32; waves w and w + 4 take the two 16-row halves of blocks w and 7 - w, so
+// every wave does the same causal work (block r needs column pieces
+// 0 .. r / 2 of 64 steps).
+//   Y^T = H_in C^T scaled by exp(cs_i)   (A = H_in from LDS, B = C^T)
+//       + x^T M^T                        (A = x^T from LDS, B = M^T built in registers)
 // with M[i][j] = CB[i][j] exp(cs_i - cs_j) Delta_j for j <= i.  Off the
 // diagonal piece the decay factors through the piece's last step e:
-// exp(cs_i - cs_e) * exp(cs_e - cs_j), both at most 1 there, so only one exp
-// per lane is needed; the diagonal piece takes the exp per element.
+// exp(cs_i - cs_e) * exp(cs_e - cs_j), both at most 1 there, so one exp per
+// lane is enough; the diagonal piece takes the exp per element.  Global loads
+// are issued ahead of their use: all prologue operands at once, the next
+// piece's CB during the current piece, the gate z before the main loop.
+constexpr int kScanThreads = 512;
 template <int IO, int N>
-__global__ void __launch_bounds__(kSsdThreads) ssd_scan_kernel(SsdParams p) {
+__global__ void __launch_bounds__(kScanThreads) ssd_scan_kernel(SsdParams p) {
   using M = mfma_t<IO>;
   constexpr int kXR = kQ + 8;  // x^T row: 264 elements (528 B keeps 16-byte reads aligned)
+  constexpr int kHR = N + 8;   // H_in row
   __shared__ __attribute__((aligned(16))) float sDelta[kQ];
   __shared__ __attribute__((aligned(16))) float sCs[kQ];
-  __shared__ float sWave[4];
   __shared__ __attribute__((aligned(16))) float sWp[kQ];           // exp(cs_e - cs_j) Delta_j, e = end of j's piece
+  __shared__ float sWave[4];
   __shared__ __attribute__((aligned(16))) uint16_t sXT[kP][kXR];   // x^T of the chunk: [p][j]
+  __shared__ __attribute__((aligned(16))) uint16_t sH[kP][kHR];    // entry state H_in[p][n]
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-  const int64_t h = blockIdx.x % p.nheads;
-  const int64_t c = (blockIdx.x / p.nheads) % p.nchunks;
-  const int64_t b = blockIdx.x / (p.nheads * p.nchunks);
+  const int64_t lb = xcd_logical_block();  // the heads of one chunk run on one XCD and share its C, CB in L2
+  const int64_t h = lb % p.nheads;
+  const int64_t c = (lb / p.nheads) % p.nchunks;
+  const int64_t b = lb / (p.nheads * p.nchunks);
   const int64_t g = h / (p.nheads / p.ngroups);
-  const float A = p.A[h];
   const int64_t t0 = c * kQ;
-  const char* xbase = static_cast<const char*>(p.x) + ((b * p.seqlen) * p.nheads + h) * kP * 2;
-#pragma unroll
-  for (int it = 0; it < 2; ++it)  // 512 work items: 4 pieces of 64 steps x 128
-    stage_transposed<IO, kP, kXR>(reinterpret_cast<uint16_t(*)[kXR]>(&sXT[0][64 * (2 * it + tid / 128)]), xbase,
-                                  p.nheads * kP * 2, t0 + 64 * (2 * it + tid / 128), p.seqlen, nullptr, tid % 128);
-  chunk_cumsum<IO>(p, b, c, h, A, sDelta, sCs, sWave);  // ends with a barrier
-  sWp[tid] = exp2_hw((sCs[tid | 63] - sCs[tid]) * kLog2e) * sDelta[tid];
-
+  const int half = wave / 4;
+  const int blk[2] = {wave % 4, 7 - wave % 4};
+  const int64_t crow = p.ngroups * N * 2;  // bytes between steps of B and C
+  const int64_t xrow = p.nheads * kP * 2;  // bytes between steps of x, z, y
   const char* cbase = static_cast<const char*>(p.Cm) + ((b * p.seqlen) * p.ngroups + g) * N * 2;
-  const int64_t crow = p.ngroups * N * 2;
+  const char* xbase = static_cast<const char*>(p.x) + ((b * p.seqlen) * p.nheads + h) * kP * 2;
+  const uint16_t* Hin = p.ws_entry + ((b * p.nchunks + c) * p.nheads + h) * (int64_t)(kP * N);
+
+  // ---- prologue: issue every operand load, then scan Delta A and fill LDS
+  const int pc = tid / 128, jq = (tid % 128) / 8, co = tid % 8;  // x item: steps 64 pc + 4 jq .. + 3, channels 8 co ..
+  u32x4v xr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t t = t0 + 64 * pc + 4 * jq + r;
+    xr[r] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(xbase + t * xrow + co * 16) : u32x4v{0u, 0u, 0u, 0u};
+  }
+  constexpr int kHPieces = kP * (N / 8);  // 16-byte pieces of H_in
+  constexpr int kHItems = (kHPieces + kScanThreads - 1) / kScanThreads;
+  u32x4v hr[kHItems];
+#pragma unroll
+  for (int k = 0; k < kHItems; ++k) {
+    const int item = tid + kScanThreads * k;
+    hr[k] = item < kHPieces ? *reinterpret_cast<const u32x4v*>(Hin + (item / (N / 8)) * N + 8 * (item % (N / 8)))
+                            : u32x4v{0u, 0u, 0u, 0u};
+  }
+  float dt_raw = 0.0f;
+  if (tid < kQ && t0 + tid < p.seqlen) dt_raw = load_io<IO>(p.dt, (b * p.seqlen + t0 + tid) * p.nheads + h);
   auto cfrag = [&](int64_t t, int n0) -> u32x4v {
     if (t >= p.seqlen) return u32x4v{0u, 0u, 0u, 0u};
     return *reinterpret_cast<const u32x4v*>(cbase + t * crow + n0 * 2);
   };
-  const int blk[2] = {wave, 7 - wave};
-  f32x4 acc[2][4][2];  // [block][p tile][i tile]: p = 16 pt + 4 (lane / 16) + r, i = 32 blk + 16 it + lane % 16
-  {
-    const uint16_t* Hin = p.ws_entry + ((b * p.nchunks + c) * p.nheads + h) * (int64_t)(kP * N);
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-        for (int it = 0; it < 2; ++it) acc[q][pt][it] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ks = 0; ks < N; ks += 32) {
-      const int n0 = ks + 8 * (lane / 16);
-      u32x4v hf[4], cf[2][2];
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) hf[pt] = *reinterpret_cast<const u32x4v*>(Hin + (16 * pt + lane % 16) * N + n0);
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int it = 0; it < 2; ++it) cf[q][it] = cfrag(t0 + 32 * blk[q] + 16 * it + lane % 16, n0);
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-          for (int it = 0; it < 2; ++it)
-            acc[q][pt][it] = M::run(as_vec<IO>(hf[pt]), as_vec<IO>(cf[q][it]), acc[q][pt][it]);
-    }
-    __syncthreads();  // sWp
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const float sc = exp2_hw(sCs[32 * blk[q] + 16 * it + lane % 16] * kLog2e);
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) acc[q][pt][it] *= sc;
-      }
-  }
-
-  const float* CBbase = p.ws_cb + ((b * p.nchunks + c) * p.ngroups + g) * (int64_t)(kQ * kQ);
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int i0 = 32 * blk[q];
-    const int dpiece = blk[q] / 2;  // the piece holding this block's rows
-    float csi[2];
-    const float* cbrow[2];
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      csi[it] = sCs[i0 + 16 * it + lane % 16];
-      cbrow[it] = CBbase + (i0 + 16 * it + lane % 16) * kQ;
-    }
-    for (int piece = 0; piece <= dpiece; ++piece) {
-      const int jb = 64 * piece;
-      const bool diag = piece == dpiece;
-      float ei[2];
-#pragma unroll
-      for (int it = 0; it < 2; ++it) ei[it] = exp2_hw((csi[it] - sCs[jb + 63]) * kLog2e);
-#pragma unroll
-      for (int ks = 0; ks < kJB; ks += 32) {
-        const int j0 = jb + ks + 8 * (lane / 16);
-        u32x4v xa[4];
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) xa[pt] = *reinterpret_cast<const u32x4v*>(&sXT[16 * pt + lane % 16][j0]);
-        const float4 w0 = *reinterpret_cast<const float4*>(&sWp[j0]);
-        const float4 w1 = *reinterpret_cast<const float4*>(&sWp[j0 + 4]);
-        const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-          const int i = i0 + 16 * it + lane % 16;
-          const float4 c0 = *reinterpret_cast<const float4*>(cbrow[it] + j0);
-          const float4 c1 = *reinterpret_cast<const float4*>(cbrow[it] + j0 + 4);
-          const float cb[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-          float m[8];
-          if (diag) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int j = j0 + e;
-              const float v = cb[e] * exp2_hw((csi[it] - sCs[j]) * kLog2e) * sDelta[j];
-              m[e] = j <= i ? v : 0.0f;
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) m[e] = cb[e] * (wj[e] * ei[it]);
-          }
-          u32x4v bop;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            bop[e] = (uint32_t)bits16<IO>(m[2 * e]) | ((uint32_t)bits16<IO>(m[2 * e + 1]) << 16);
-#pragma unroll
-          for (int pt = 0; pt < 4; ++pt) acc[q][pt][it] = M::run(as_vec<IO>(xa[pt]), as_vec<IO>(bop), acc[q][pt][it]);
-        }
-      }
-    }
-  }
-
-  // D skip, gate, store: lane has channels 16 pt + 4 (lane / 16) .. + 3 of step i
-  const float Dh = p.D ? p.D[h] : 0.0f;
+  u32x4v cf[2][N / 32];
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int64_t t = t0 + 32 * blk[q] + 16 * it + lane % 16;
-      if (t >= p.seqlen) continue;
+    for (int ks = 0; ks < N / 32; ++ks) cf[q][ks] = cfrag(t0 + 32 * blk[q] + 16 * half + lane % 16, 32 * ks + 8 * (lane / 16));
+
+  {  // Delta and the inclusive cumulative sum of Delta A over the chunk (threads 0..255 = steps)
+    float delta = 0.0f;
+    if (tid < kQ && t0 + tid < p.seqlen) {
+      const float xd = dt_raw + (p.dt_bias ? p.dt_bias[h] : 0.0f);
+      delta = p.softplus ? softplus_f(xd) : xd;
+    }
+    float v = delta * p.A[h];
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        const int64_t idx = ((b * p.seqlen + t) * p.nheads + h) * kP + 16 * pt + 4 * (lane / 16);
-        const uint2 xv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.x) + idx);
-        uint2 zv = make_uint2(0u, 0u);
-        if (p.z) zv = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.z) + idx);
-        const uint32_t xw[2] = {xv.x, xv.y}, zw[2] = {zv.x, zv.y};
-        uint32_t yw[2];
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(v, off, 64);
+      if (lane >= off) v += o;
+    }
+    if (tid < kQ) {
+      if (lane == 63) sWave[wave] = v;
+      sDelta[tid] = delta;
+    }
+    // x^T and H_in into LDS meanwhile
 #pragma unroll
-        for (int hw = 0; hw < 2; ++hw) {
-          float yy[2];
+    for (int e = 0; e < 8; ++e) {
+      const int q = e / 2, sh = 16 * (e % 2);
+      uint2 pk;
+      pk.x = ((xr[0][q] >> sh) & 0xffffu) | (((xr[1][q] >> sh) & 0xffffu) << 16);
+      pk.y = ((xr[2][q] >> sh) & 0xffffu) | (((xr[3][q] >> sh) & 0xffffu) << 16);
+      *reinterpret_cast<uint2*>(&sXT[8 * co + e][64 * pc + 4 * jq]) = pk;
+    }
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const float xf = bits_f32<IO>((raw_t<IO>)((xw[hw] >> (16 * s2)) & 0xffffu));
-            float yv = fmaf(Dh, xf, acc[q][pt][it][2 * hw + s2]);
-            if (p.z) yv *= silu_f(bits_f32<IO>((raw_t<IO>)((zw[hw] >> (16 * s2)) & 0xffffu)));
-            yy[s2] = yv;
+    for (int k = 0; k < kHItems; ++k) {
+      const int item = tid + kScanThreads * k;
+      if (item < kHPieces) *reinterpret_cast<u32x4v*>(&sH[item / (N / 8)][8 * (item % (N / 8))]) = hr[k];
+    }
+    __syncthreads();
+    if (tid < kQ) {
+      float base = 0.0f;
+      for (int w = 0; w < wave; ++w) base += sWave[w];
+      sCs[tid] = v + base;
+    }
+    __syncthreads();
+    if (tid < kQ) sWp[tid] = exp2_hw((sCs[tid | 63] - sCs[tid]) * kLog2e) * sDelta[tid];
+  }
+
+  // gate values for the epilogue: lane has channels 16 pt + 4 (lane / 16) .. + 3 of its step
+  uint2 zv[2][4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t t = t0 + 32 * blk[q] + 16 * half + lane % 16;
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+      zv[q][pt] = (p.z && t < p.seqlen)
+                      ? *reinterpret_cast<const uint2*>(static_cast<const char*>(p.z) + t * xrow +
+                                                        ((b * p.seqlen) * p.nheads + h) * kP * 2 +
+                                                        (16 * pt + 4 * (lane / 16)) * 2)
+                      : make_uint2(0u, 0u);
+  }
+
+  // ---- Y_off = H_in C^T, scaled by exp(cs_i)
+  f32x4 acc[2][4];  // [block][p tile]: p = 16 pt + 4 (lane / 16) + r, i = 32 blk + 16 half + lane % 16
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) acc[q][pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ks = 0; ks < N / 32; ++ks) {
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      const u32x4v hf = *reinterpret_cast<const u32x4v*>(&sH[16 * pt + lane % 16][32 * ks + 8 * (lane / 16)]);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) acc[q][pt] = M::run(as_vec<IO>(hf), as_vec<IO>(cf[q][ks]), acc[q][pt]);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const float sc = exp2_hw(sCs[32 * blk[q] + 16 * half + lane % 16] * kLog2e);
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) acc[q][pt] *= sc;
+  }
+
+  // ---- Y_diag += x^T M^T, piece by piece
+  const float* CBbase = p.ws_cb + ((b * p.nchunks + c) * p.ngroups + g) * (int64_t)(kQ * kQ);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int i = 32 * blk[q] + 16 * half + lane % 16;  // this lane's row (chunk-local)
+    const int dpiece = blk[q] / 2;                      // the piece holding the block's rows
+    const float csi = sCs[i];
+    const float* cbrow = CBbase + i * kQ + 8 * (lane / 16);
+    float4 nxt[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) nxt[k] = *reinterpret_cast<const float4*>(cbrow + 32 * (k / 2) + 4 * (k % 2));
+    for (int piece = 0; piece <= dpiece; ++piece) {
+      const int jb = 64 * piece;
+      float4 cur[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) cur[k] = nxt[k];
+      if (piece < dpiece) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          nxt[k] = *reinterpret_cast<const float4*>(cbrow + jb + 64 + 32 * (k / 2) + 4 * (k % 2));
+      }
+      const bool diag = piece == dpiece;
+      const float ei = exp2_hw((csi - sCs[jb + 63]) * kLog2e);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int j0 = jb + 32 * ks + 8 * (lane / 16);
+        const float cb[8] = {cur[2 * ks].x, cur[2 * ks].y, cur[2 * ks].z, cur[2 * ks].w,
+                             cur[2 * ks + 1].x, cur[2 * ks + 1].y, cur[2 * ks + 1].z, cur[2 * ks + 1].w};
+        float m[8];
+        if (diag) {
+          const float4 c0 = *reinterpret_cast<const float4*>(&sCs[j0]);
+          const float4 c1 = *reinterpret_cast<const float4*>(&sCs[j0 + 4]);
+          const float4 d0 = *reinterpret_cast<const float4*>(&sDelta[j0]);
+          const float4 d1 = *reinterpret_cast<const float4*>(&sDelta[j0 + 4]);
+          const float csj[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+          const float dj[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = cb[e] * exp2_hw((csi - csj[e]) * kLog2e) * dj[e];
+            m[e] = j0 + e <= i ? v : 0.0f;
           }
-          yw[hw] = (uint32_t)bits16<IO>(yy[0]) | ((uint32_t)bits16<IO>(yy[1]) << 16);
+        } else {
+          const float4 w0 = *reinterpret_cast<const float4*>(&sWp[j0]);
+          const float4 w1 = *reinterpret_cast<const float4*>(&sWp[j0 + 4]);
+          const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) m[e] = cb[e] * (wj[e] * ei);
         }
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + idx) = make_uint2(yw[0], yw[1]);
+        u32x4v bop;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          bop[e] = pack2<IO>(m[2 * e], m[2 * e + 1]);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          const u32x4v xa = *reinterpret_cast<const u32x4v*>(&sXT[16 * pt + lane % 16][j0]);
+          acc[q][pt] = M::run(as_vec<IO>(xa), as_vec<IO>(bop), acc[q][pt]);
+        }
       }
     }
+  }
+
+  // ---- D skip (x from LDS), gate, store
+  const float Dh = p.D ? p.D[h] : 0.0f;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int il = 32 * blk[q] + 16 * half + lane % 16;
+    const int64_t t = t0 + il;
+    if (t >= p.seqlen) continue;
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      const int p0 = 16 * pt + 4 * (lane / 16);
+      const uint32_t zw[2] = {zv[q][pt].x, zv[q][pt].y};
+      uint32_t yw[2];
+#pragma unroll
+      for (int hw = 0; hw < 2; ++hw) {
+        float yy[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int r = 2 * hw + s2;
+          float yv = fmaf(Dh, bits_f32<IO>((raw_t<IO>)sXT[p0 + r][il]), acc[q][pt][r]);
+          if (p.z) yv *= silu_f(bits_f32<IO>((raw_t<IO>)((zw[hw] >> (16 * s2)) & 0xffffu)));
+          yy[s2] = yv;
+        }
+        yw[hw] = pack2<IO>(yy[0], yy[1]);
+      }
+      *reinterpret_cast<uint2*>(static_cast<char*>(p.y) + t * xrow + ((b * p.seqlen) * p.nheads + h) * kP * 2 +
+                                p0 * 2) = make_uint2(yw[0], yw[1]);
+    }
+  }
 }
 
 template <int IO, int N>
@@ -431,15 +567,11 @@ hipError_t launch_ssd_n(const SsdParams& p, hipStream_t st) {
   hipLaunchKernelGGL((ssd_state_kernel<IO, N>), grid, dim3(kSsdThreads), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((ssd_cb_kernel<IO, N>), dim3((uint32_t)(p.batch * p.nchunks * p.ngroups * (kQ / 16))),
-                     dim3(kSsdThreads), 0, st, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int64_t elems = p.batch * p.nheads * kP * N;
   hipLaunchKernelGGL((ssd_pass_kernel<IO>), dim3((uint32_t)((elems + 255) / 256)), dim3(256), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((ssd_scan_kernel<IO, N>), grid, dim3(kSsdThreads), 0, st, p);
+  hipLaunchKernelGGL((ssd_scan_kernel<IO, N>), grid, dim3(kScanThreads), 0, st, p);
   return hipGetLastError();
 }
 
