@@ -269,7 +269,7 @@ ss_status check_ssd(const ss_ssd_problem* p) {
   if (p->batch > lim || p->seqlen > lim || p->nheads > lim) return SS_ERR_BAD_SHAPE;
   const double nchunks = (double)((p->seqlen + kSsdChunk - 1) / kSsdChunk);
   if ((double)p->batch * nchunks * (double)p->nheads > (double)kMaxGrid) return SS_ERR_BAD_SHAPE;
-  if ((double)p->batch * nchunks * (double)p->ngroups * (kSsdChunk / 16) > (double)kMaxGrid) return SS_ERR_BAD_SHAPE;
+  if ((double)p->batch * (double)p->nheads * (p->dstate / 32) > (double)kMaxGrid) return SS_ERR_BAD_SHAPE;
   if ((double)p->batch * (double)p->seqlen * (double)p->nheads * 64.0 > 9.0e18) return SS_ERR_BAD_SHAPE;
   return SS_OK;
 }
@@ -280,12 +280,14 @@ size_t ssd_state_elems(const ss_ssd_problem* p) {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 }  // namespace
 
+size_t ssd_cb_bytes(const ss_ssd_problem* p) {
+  const int64_t nchunks = (p->seqlen + kSsdChunk - 1) / kSsdChunk;
+  return (size_t)(p->batch * nchunks * p->ngroups) * (size_t)(kSsdChunk * kSsdChunk) * 4;
+}
+
 size_t ss_ssd_workspace_size(const ss_ssd_problem* p) {
   if (check_ssd(p) != SS_OK) return 0;
-  const size_t e = ssd_state_elems(p);
-  const int64_t nchunks = (p->seqlen + kSsdChunk - 1) / kSsdChunk;
-  return align256(e * 4) + align256(e * 2) + align256((size_t)(p->batch * nchunks * p->nheads) * 4) +
-         align256((size_t)(p->batch * nchunks * p->ngroups) * (size_t)(kSsdChunk * kSsdChunk) * 4);
+  return align256(ssd_state_elems(p) * 2) + align256(ssd_cb_bytes(p));
 }
 
 ss_status ss_ssd_fwd(const ss_ssd_problem* p, const void* x, const void* dt, const float* A, const void* Bm,
@@ -305,12 +307,8 @@ ss_status ss_ssd_fwd(const ss_ssd_problem* p, const void* x, const void* dt, con
   k.x = x; k.dt = dt; k.A = A; k.Bm = Bm; k.Cm = Cm; k.D = D; k.z = z; k.dt_bias = dt_bias; k.h0 = h0;
   k.y = y; k.final_state = final_state;
   char* ws = static_cast<char*>(workspace);
-  k.ws_state = reinterpret_cast<float*>(ws);
-  k.ws_entry = reinterpret_cast<uint16_t*>(ws + align256(e * 4));
-  k.ws_decay = reinterpret_cast<float*>(ws + align256(e * 4) + align256(e * 2));
-  k.ws_cb = reinterpret_cast<float*>(ws + align256(e * 4) + align256(e * 2) +
-                                     align256((size_t)(p->batch * ((p->seqlen + kSsdChunk - 1) / kSsdChunk) *
-                                                       p->nheads) * 4));
+  k.ws_entry = reinterpret_cast<uint16_t*>(ws);
+  k.ws_cb = reinterpret_cast<float*>(ws + align256(e * 2));
   k.batch = p->batch; k.seqlen = p->seqlen; k.nheads = p->nheads; k.ngroups = p->ngroups; k.dstate = p->dstate;
   k.nchunks = (p->seqlen + kSsdChunk - 1) / kSsdChunk;
   return from_hip(ss::launch_ssd(k, static_cast<hipStream_t>(stream)));

@@ -130,9 +130,7 @@ struct SsdParams {
   void* y;
   float* final_state;    // (batch, nheads, 64, dstate) or null
   // workspace
-  float* ws_state;       // (batch, nchunks, nheads, 64, dstate) fp32: each chunk's own state
-  uint16_t* ws_entry;    // same shape, I/O dtype bits: each chunk's entry state
-  float* ws_decay;       // (batch, nchunks, nheads)
+  uint16_t* ws_entry;    // (batch, nchunks, nheads, 64, dstate), I/O dtype bits: each chunk's entry state
   float* ws_cb;          // (batch, nchunks, ngroups, 256, 256) fp32: C B^T of each chunk
   int64_t batch, seqlen, nheads, ngroups, dstate, nchunks;
 };

@@ -13,16 +13,17 @@
 //   S_c = sum_j exp(cs_last - cs_j) Delta_j x_j B_j^T   (the chunk's own state)
 //   H_in(c + 1) = exp(cs_last(c)) H_in(c) + S_c,  H_in(0) = h0,
 //   Y_off = diag(exp(cs_i)) C H_in(c).
-// Three kernels:
-//   ssd_state_kernel  per (batch, chunk, head): S_c on MFMA (P x N, K = Q),
-//                     and the chunk decay exp(cs_last);
-//   ssd_pass_kernel   per (batch, head, state element): the chunk recurrence
-//                     in fp32, writing each chunk's entry state (as the MFMA
-//                     input dtype) and the final state;
-//   ssd_scan_kernel   per (batch, chunk, head): Y_off = C H_in, then per
-//                     64-step piece of the chunk's columns C B^T on MFMA,
-//                     the decay mask in fp32, and Y_diag += M (Delta-scaled
-//                     through the mask) x on MFMA; D skip, SiLU(z) gate, store.
+// Two kernels:
+//   ssd_state_kernel  per (batch, head, slice of 32 states), walking the
+//                     chunks in order: S_c on MFMA (K = Q) added into the
+//                     decayed state held in the accumulators, each chunk's
+//                     entry state written in the I/O dtype, the final state
+//                     in fp32; the workgroups of a group also share out its
+//                     C B^T (fp32, once per group rather than per head);
+//   ssd_scan_kernel   per (batch, chunk, head): Y_off = C H_in on MFMA, then
+//                     per 64-step piece of the chunk's columns M = the decay-
+//                     masked, Delta-scaled C B^T built in registers and
+//                     Y_diag += M x on MFMA; D skip, SiLU(z) gate, store.
 // MFMA: v_mfma_f32_16x16x32_{bf16,f16}, fp32 accumulation.  Operand lane
 // layout (checked on the chip): A[m][k] in lane m + 16 (k / 8), element k % 8;
 // B[k][n] in lane n + 16 (k / 8), element k % 8; D[m][n] in lane
@@ -80,16 +81,17 @@ __device__ __forceinline__ typename mfma_t<IO>::V as_vec(u32x4v w) {
   return __builtin_bit_cast(typename mfma_t<IO>::V, w);
 }
 
-// Delta and the inclusive cumulative sum cs of Delta * A over the chunk's
-// 256 steps (thread i = step i; steps past the sequence have Delta = 0).
+// Delta of this thread's step and the inclusive cumulative sum cs of Delta * A
+// over the chunk (threads 0..255 = steps; steps past the sequence have Delta =
+// 0).  cs goes to sCs; every thread of the workgroup must call it (it holds
+// two barriers).
 template <int IO>
-__device__ __forceinline__ void chunk_cumsum(const SsdParams& p, int64_t b, int64_t c, int64_t h, float A, float* sDelta,
-                                             float* sCs, float* sWave) {
+__device__ __forceinline__ float chunk_cumsum(const SsdParams& p, float dt_raw, bool valid, float A, float bias,
+                                              float* sCs, float* sWave) {
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-  const int64_t t = c * kQ + tid;
   float delta = 0.0f;
-  if (t < p.seqlen) {
-    const float xd = load_io<IO>(p.dt, (b * p.seqlen + t) * p.nheads + h) + (p.dt_bias ? p.dt_bias[h] : 0.0f);
+  if (tid < kQ && valid) {
+    const float xd = dt_raw + bias;
     delta = p.softplus ? softplus_f(xd) : xd;
   }
   float v = delta * A;
@@ -98,166 +100,142 @@ __device__ __forceinline__ void chunk_cumsum(const SsdParams& p, int64_t b, int6
     const float o = __shfl_up(v, off, 64);
     if (lane >= off) v += o;
   }
-  if (lane == 63) sWave[wave] = v;
-  sDelta[tid] = delta;
+  if (tid < kQ && lane == 63) sWave[wave] = v;
   __syncthreads();
-  float base = 0.0f;
-  for (int w = 0; w < wave; ++w) base += sWave[w];
-  sCs[tid] = v + base;
+  if (tid < kQ) {
+    float base = 0.0f;
+    for (int w = 0; w < wave; ++w) base += sWave[w];
+    sCs[tid] = v + base;
+  }
   __syncthreads();
+  return delta;
 }
 
-// Stage a 64-step piece of a (time x width) row-major 16-bit tensor into LDS
-// transposed, dst[col][j] (j contiguous, row stride kXR): work item (jq, co)
-// reads steps 4 jq .. 4 jq + 3 of columns 8 co .. 8 co + 7 with four 16-byte
-// loads and writes each column's 4 steps with one 8-byte store.  `scale`
-// (per step, optional) multiplies the values first.
-template <int IO, int WIDTH, int kXR>
-__device__ __forceinline__ void stage_transposed(uint16_t (*dst)[kXR], const char* base, int64_t row_stride_bytes,
-                                                 int64_t t0, int64_t seqlen, const float* scale, int item) {
-  constexpr int kOct = WIDTH / 8;
-  const int jq = item / kOct, co = item % kOct;
-  uint32_t w[4][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t t = t0 + 4 * jq + r;
-    u32x4v v = u32x4v{0u, 0u, 0u, 0u};
-    if (t < seqlen) v = *reinterpret_cast<const u32x4v*>(base + t * row_stride_bytes + co * 16);
-    if (scale) {
-      const float sc = scale[4 * jq + r];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float lo = bits_f32<IO>((raw_t<IO>)(v[q] & 0xffffu)) * sc;
-        const float hi = bits_f32<IO>((raw_t<IO>)(v[q] >> 16)) * sc;
-        v[q] = pack2<IO>(lo, hi);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) w[r][q] = v[q];
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {  // column 8 co + e: its 4 steps
-    const int q = e / 2, sh = 16 * (e % 2);
-    const uint32_t a0 = (w[0][q] >> sh) & 0xffffu, a1 = (w[1][q] >> sh) & 0xffffu;
-    const uint32_t a2 = (w[2][q] >> sh) & 0xffffu, a3 = (w[3][q] >> sh) & 0xffffu;
-    uint2 pk;
-    pk.x = a0 | (a1 << 16);
-    pk.y = a2 | (a3 << 16);
-    *reinterpret_cast<uint2*>(&dst[8 * co + e][4 * jq]) = pk;
-  }
+// ---- C B^T of a chunk, once per group -------------------------------------------
+// CB[i][j] = sum_n C_i[n] B_j[n] in fp32 for the chunk's rows i and the columns j
+// of every 64-step piece up to the one holding i (the causal half plus the rest
+// of the diagonal pieces, so the output pass never reads an unwritten value):
+// 160 tiles of 16 x 16.  Tile idx: row band R = rt / 4 holds 4 (R + 1) column
+// tiles per row tile, and the bands start at idx 0, 16, 48, 96.
+constexpr int kCbTiles = 160;
+__device__ __forceinline__ void cb_tile_of(int idx, int& rt, int& jt) {
+  const int R = idx < 16 ? 0 : idx < 48 ? 1 : idx < 96 ? 2 : 3;
+  const int local = idx - 8 * R * (R + 1), ncols = 4 * (R + 1);
+  rt = 4 * R + local / ncols;
+  jt = local % ncols;
 }
-
-// ---- pass 1: the chunk's own state S_c[p][n] = sum_j w_j x_j[p] B_j[n] ----
-// w_j = exp(cs_last - cs_j) Delta_j.  Every global operand of the chunk (x,
-// B, dt) is loaded at once into registers, then moved to LDS transposed
-// (time contiguous) two 64-step pieces at a time for the MFMAs: wave w takes
-// rows p in [16w, 16w + 16) and all states n.  The workgroups of a group's
-// heads also share out the group's C B^T: head k of the group takes the
-// 16-row tiles k, k + heads_per_group, ...
 template <int IO, int N>
-__device__ __forceinline__ void cb_row_tile(const SsdParams& p, int64_t b, int64_t c, int64_t g, int rt, int lane,
-                                            int wave) {
-  using M = mfma_t<IO>;
-  const int64_t t0 = c * kQ;
-  const int64_t crow = p.ngroups * N * 2;
-  const char* cbase = static_cast<const char*>(p.Cm) + ((b * p.seqlen) * p.ngroups + g) * N * 2;
-  const char* bbase = static_cast<const char*>(p.Bm) + ((b * p.seqlen) * p.ngroups + g) * N * 2;
-  auto frag = [&](const char* base, int64_t t, int n0) -> u32x4v {
-    if (t >= p.seqlen) return u32x4v{0u, 0u, 0u, 0u};
-    return *reinterpret_cast<const u32x4v*>(base + t * crow + n0 * 2);
-  };
-  // columns of every 64-step piece up to the one holding the row tile
-  const int last_tile = 4 * (rt / 4) + 3;
-  u32x4v af[N / 32], bf[4][N / 32];
+struct CbTile {
+  u32x4v a[N / 32], b[N / 32];  // C rows 16 rt .., B rows 16 jt .. (8 states per lane and k-step)
+  int rt, jt;
+  __device__ __forceinline__ void load(const SsdParams& p, int64_t b_, int64_t c, int64_t g, int idx, int lane) {
+    cb_tile_of(idx, rt, jt);
+    const int64_t t0 = c * kQ, crow = p.ngroups * N * 2;
+    const char* cbase = static_cast<const char*>(p.Cm) + ((b_ * p.seqlen) * p.ngroups + g) * N * 2;
+    const char* bbase = static_cast<const char*>(p.Bm) + ((b_ * p.seqlen) * p.ngroups + g) * N * 2;
+    const int64_t ti = t0 + 16 * rt + lane % 16, tj = t0 + 16 * jt + lane % 16;
 #pragma unroll
-  for (int ks = 0; ks < N / 32; ++ks) af[ks] = frag(cbase, t0 + 16 * rt + lane % 16, 32 * ks + 8 * (lane / 16));
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int jt = wave + 4 * u;
-#pragma unroll
-    for (int ks = 0; ks < N / 32; ++ks)
-      bf[u][ks] = jt <= last_tile ? frag(bbase, t0 + 16 * jt + lane % 16, 32 * ks + 8 * (lane / 16))
-                                  : u32x4v{0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < N / 32; ++ks) {
+      const int n0 = 32 * ks + 8 * (lane / 16);
+      a[ks] = ti < p.seqlen ? *reinterpret_cast<const u32x4v*>(cbase + ti * crow + n0 * 2) : u32x4v{0u, 0u, 0u, 0u};
+      b[ks] = tj < p.seqlen ? *reinterpret_cast<const u32x4v*>(bbase + tj * crow + n0 * 2) : u32x4v{0u, 0u, 0u, 0u};
+    }
   }
-  float* CB = p.ws_cb + ((b * p.nchunks + c) * p.ngroups + g) * (int64_t)(kQ * kQ);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int jt = wave + 4 * u;
-    if (jt > last_tile) break;
+  __device__ __forceinline__ void finish(const SsdParams& p, int64_t b_, int64_t c, int64_t g, int lane) {
     f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int ks = 0; ks < N / 32; ++ks) acc = M::run(as_vec<IO>(af[ks]), as_vec<IO>(bf[u][ks]), acc);
+    for (int ks = 0; ks < N / 32; ++ks) acc = mfma_t<IO>::run(as_vec<IO>(a[ks]), as_vec<IO>(b[ks]), acc);
     // lane holds rows i = 16 rt + 4 (lane / 16) + r of column j = 16 jt + lane % 16
+    float* CB = p.ws_cb + ((b_ * p.nchunks + c) * p.ngroups + g) * (int64_t)(kQ * kQ);
 #pragma unroll
     for (int r = 0; r < 4; ++r) CB[(16 * rt + 4 * (lane / 16) + r) * kQ + 16 * jt + lane % 16] = acc[r];
   }
-}
+};
 
+// ---- pass 1: chunk states and the state passed between chunks ---------------------
+// Workgroup = (batch row, head, slice of 32 states).  It walks the chunks in
+// order with its slice of the state H[p][n] (64 x 32) in the accumulators:
+//   entry(c) = H   (stored in the I/O dtype for the output pass)
+//   H <- exp(cs_last) H + sum_j exp(cs_last - cs_j) Delta_j x_j B_j^T
+// The j-sum runs on the matrix cores with both operands staged transposed in
+// LDS (time contiguous); wave w holds rows p in [16w, 16w + 16).  The next
+// chunk's x, B and dt are loaded once this chunk's are in LDS, while it is
+// being multiplied.  The
+// waves of a group's workgroups (heads x slices x 4) also share out its C B^T
+// tiles, one per wave and chunk while there are waves enough; the first
+// tile's operands are loaded at the top of the chunk's iteration.
+constexpr int kNS = 32;  // states per slice
 template <int IO, int N>
-__global__ void __launch_bounds__(kSsdThreads) ssd_state_kernel(SsdParams p) {
+__global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) {
   using M = mfma_t<IO>;
-  constexpr int kXR = 2 * kJB + 8;  // LDS row: two pieces of time, padded (272 B keeps 16-byte reads aligned)
+  constexpr int kXR = kQ + 8;  // LDS row: the chunk's 256 steps, padded (528 B keeps 16-byte reads aligned)
+  constexpr int kSlices = N / kNS;
   __shared__ __attribute__((aligned(16))) float sW[kQ];
-  __shared__ float sDelta[kQ], sCs[kQ], sWave[4];
-  __shared__ __attribute__((aligned(16))) uint16_t sXT[kP][kXR];  // (x * w)^T of two pieces: [p][j]
-  __shared__ __attribute__((aligned(16))) uint16_t sBT[N][kXR];   // B^T of two pieces: [n][j]
+  __shared__ float sCs[kQ], sWave[4];
+  __shared__ __attribute__((aligned(16))) uint16_t sXT[kP][kXR];   // (x * w)^T: [p][j]
+  __shared__ __attribute__((aligned(16))) uint16_t sBT[kNS][kXR];  // B^T of the slice: [n][j]
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-  const int64_t lb = xcd_logical_block();  // the heads of one chunk run on one XCD and share its B, C in L2
-  const int64_t h = lb % p.nheads;
-  const int64_t c = (lb / p.nheads) % p.nchunks;
-  const int64_t b = lb / (p.nheads * p.nchunks);
-  const int64_t hpg = p.nheads / p.ngroups;
-  const int64_t g = h / hpg;
-  const int64_t t0 = c * kQ;
+  const int64_t lb = xcd_logical_block();  // the workgroups of one row's group share B in an XCD's L2
+  const int s = (int)(lb % kSlices);
+  const int64_t h = (lb / kSlices) % p.nheads;
+  const int64_t b = lb / (kSlices * p.nheads);
+  const int64_t hpg = p.nheads / p.ngroups, g = h / hpg;
   const int64_t xrow = p.nheads * kP * 2, brow = p.ngroups * N * 2;
   const char* xbase = static_cast<const char*>(p.x) + ((b * p.seqlen) * p.nheads + h) * kP * 2;
-  const char* bbase = static_cast<const char*>(p.Bm) + ((b * p.seqlen) * p.ngroups + g) * N * 2;
+  const char* bbase = static_cast<const char*>(p.Bm) + ((b * p.seqlen) * p.ngroups + g) * N * 2 + s * kNS * 2;
+  const float A = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
 
-  // x: 512 items (4 steps x 8 channels); item = tid + 256 k, piece 2 k + tid / 128
-  u32x4v xr[2][4];
+  // x: 512 items of 4 steps x 8 channels (two per thread), B: 256 items of 4 steps x 8 states
+  const int xj[2] = {tid / 8, (tid + kSsdThreads) / 8}, xc = tid % 8;
+  const int bj = tid / 4, bc = tid % 4;
+  u32x4v xr[2][4], br[4];
+  float dtr = 0.0f;
+  auto load_chunk = [&](int64_t c) {
+    const int64_t t0 = c * kQ;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int item = tid + kSsdThreads * k, pc = item / 128, jq = (item % 128) / 8, co = item % 8;
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t t = t0 + 4 * xj[k] + r;
+        xr[k][r] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(xbase + t * xrow + xc * 16) : u32x4v{0u, 0u, 0u, 0u};
+      }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t t = t0 + 64 * pc + 4 * jq + r;
-      xr[k][r] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(xbase + t * xrow + co * 16) : u32x4v{0u, 0u, 0u, 0u};
+      const int64_t t = t0 + 4 * bj + r;
+      br[r] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(bbase + t * brow + bc * 16) : u32x4v{0u, 0u, 0u, 0u};
     }
-  }
-  // B: 8 N items (4 steps x 8 states), N / 32 per thread; item = tid + 256 k
-  constexpr int kBI = N / 32;
-  u32x4v br[kBI][4];
-#pragma unroll
-  for (int k = 0; k < kBI; ++k) {
-    const int item = tid + kSsdThreads * k, pc = item / (2 * N), rem = item % (2 * N);
-    const int jq = rem / (N / 8), co = rem % (N / 8);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t t = t0 + 64 * pc + 4 * jq + r;
-      br[k][r] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(bbase + t * brow + co * 16) : u32x4v{0u, 0u, 0u, 0u};
-    }
-  }
-  chunk_cumsum<IO>(p, b, c, h, p.A[h], sDelta, sCs, sWave);  // ends with a barrier
-  sW[tid] = exp2_hw((sCs[kQ - 1] - sCs[tid]) * kLog2e) * sDelta[tid];  // 0 past the sequence (Delta = 0)
-  __syncthreads();
+    dtr = t0 + tid < p.seqlen ? load_io<IO>(p.dt, (b * p.seqlen + t0 + tid) * p.nheads + h) : 0.0f;
+  };
 
-  f32x4 acc[N / 16];
+  // the state slice: lane holds p = 16 w + 4 (lane / 16) + r, n = 32 s + 16 nt + lane % 16
+  f32x4 acc[2];
+  const int64_t hbase = (b * p.nheads + h) * (int64_t)(kP * N);
 #pragma unroll
-  for (int i = 0; i < N / 16; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    {  // x * w, transposed
-      const int item = tid + kSsdThreads * round, pc = item / 128, jq = (item % 128) / 8, co = item % 8;
+    for (int r = 0; r < 4; ++r)
+      acc[nt][r] = p.h0 ? p.h0[hbase + (16 * wave + 4 * (lane / 16) + r) * N + kNS * s + 16 * nt + lane % 16] : 0.0f;
+  const int cb_slot = (int)(((h % hpg) * kSlices + s) * 4 + wave), cb_slots = (int)(hpg * kSlices * 4);
+
+  load_chunk(0);
+  for (int64_t c = 0; c < p.nchunks; ++c) {
+    const int64_t t0 = c * kQ;
+    CbTile<IO, N> cbt;
+    if (cb_slot < kCbTiles) cbt.load(p, b, c, g, cb_slot, lane);
+    const float delta = chunk_cumsum<IO>(p, dtr, t0 + tid < p.seqlen, A, bias, sCs, sWave);  // barriers
+    const float cs_last = sCs[kQ - 1];
+    sW[tid] = exp2_hw((cs_last - sCs[tid]) * kLog2e) * delta;  // 0 past the sequence (Delta = 0)
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {  // (x * w)^T
       uint32_t v[4][4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float sc = sW[64 * pc + 4 * jq + r];
+        const float sc = sW[4 * xj[k] + r];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float lo = bits_f32<IO>((raw_t<IO>)(xr[round][r][q] & 0xffffu)) * sc;
-          const float hi = bits_f32<IO>((raw_t<IO>)(xr[round][r][q] >> 16)) * sc;
-          v[r][q] = pack2<IO>(lo, hi);
-        }
+        for (int q = 0; q < 4; ++q)
+          v[r][q] = pack2<IO>(bits_f32<IO>((raw_t<IO>)(xr[k][r][q] & 0xffffu)) * sc,
+                              bits_f32<IO>((raw_t<IO>)(xr[k][r][q] >> 16)) * sc);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -265,63 +243,54 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_state_kernel(SsdParams p) {
         uint2 pk;
         pk.x = ((v[0][q] >> sh) & 0xffffu) | (((v[1][q] >> sh) & 0xffffu) << 16);
         pk.y = ((v[2][q] >> sh) & 0xffffu) | (((v[3][q] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<uint2*>(&sXT[8 * co + e][64 * (pc % 2) + 4 * jq]) = pk;
+        *reinterpret_cast<uint2*>(&sXT[8 * xc + e][4 * xj[k]]) = pk;
       }
     }
 #pragma unroll
-    for (int k = 0; k < kBI; ++k) {  // B, transposed
-      const int item = tid + kSsdThreads * k, pc = item / (2 * N), rem = item % (2 * N);
-      if (pc / 2 != round) continue;
-      const int jq = rem / (N / 8), co = rem % (N / 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int q = e / 2, sh = 16 * (e % 2);
-        uint2 pk;
-        pk.x = ((br[k][0][q] >> sh) & 0xffffu) | (((br[k][1][q] >> sh) & 0xffffu) << 16);
-        pk.y = ((br[k][2][q] >> sh) & 0xffffu) | (((br[k][3][q] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<uint2*>(&sBT[8 * co + e][64 * (pc % 2) + 4 * jq]) = pk;
-      }
+    for (int e = 0; e < 8; ++e) {  // B^T
+      const int q = e / 2, sh = 16 * (e % 2);
+      uint2 pk;
+      pk.x = ((br[0][q] >> sh) & 0xffffu) | (((br[1][q] >> sh) & 0xffffu) << 16);
+      pk.y = ((br[2][q] >> sh) & 0xffffu) | (((br[3][q] >> sh) & 0xffffu) << 16);
+      *reinterpret_cast<uint2*>(&sBT[8 * bc + e][4 * bj]) = pk;
     }
     __syncthreads();
+    if (c + 1 < p.nchunks) load_chunk(c + 1);  // lands while chunk c is multiplied
+
+    // entry state of chunk c, then H <- decay H + S_c
+    uint16_t* E = p.ws_entry + ((b * p.nchunks + c) * p.nheads + h) * (int64_t)(kP * N);
 #pragma unroll
-    for (int ks = 0; ks < 2 * kJB; ks += 32) {
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        E[(16 * wave + 4 * (lane / 16) + r) * N + kNS * s + 16 * nt + lane % 16] = bits16<IO>(acc[nt][r]);
+    const float decay = exp2_hw(cs_last * kLog2e);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) acc[nt] *= decay;
+#pragma unroll
+    for (int ks = 0; ks < kQ; ks += 32) {
       const int k0 = ks + 8 * (lane / 16);
       const u32x4v a = *reinterpret_cast<const u32x4v*>(&sXT[16 * wave + lane % 16][k0]);
 #pragma unroll
-      for (int nt = 0; nt < N / 16; ++nt) {
+      for (int nt = 0; nt < 2; ++nt) {
         const u32x4v bb = *reinterpret_cast<const u32x4v*>(&sBT[16 * nt + lane % 16][k0]);
         acc[nt] = M::run(as_vec<IO>(a), as_vec<IO>(bb), acc[nt]);
       }
     }
+    if (cb_slot < kCbTiles) cbt.finish(p, b, c, g, lane);
+    for (int idx = cb_slot + cb_slots; idx < kCbTiles; idx += cb_slots) {  // few waves per group: the rest in turn
+      cbt.load(p, b, c, g, idx, lane);
+      cbt.finish(p, b, c, g, lane);
+    }
     __syncthreads();
   }
-  // S_c[p][n]: lane holds rows p = 16 w + 4 (lane / 16) + r, column n = 16 nt + lane % 16
-  float* S = p.ws_state + ((b * p.nchunks + c) * p.nheads + h) * (int64_t)(kP * N);
+  if (p.final_state) {
 #pragma unroll
-  for (int nt = 0; nt < N / 16; ++nt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) S[(16 * wave + 4 * (lane / 16) + r) * N + 16 * nt + lane % 16] = acc[nt][r];
-  if (tid == 0) p.ws_decay[(b * p.nchunks + c) * p.nheads + h] = exp2_hw(sCs[kQ - 1] * kLog2e);
-  // this head's share of the group's C B^T
-  for (int64_t rt = h % hpg; rt < kQ / 16; rt += hpg) cb_row_tile<IO, N>(p, b, c, g, (int)rt, lane, wave);
-}
-
-// ---- pass 2: entry state of every chunk, H_in(c + 1) = decay_c H_in(c) + S_c ----
-template <int IO>
-__global__ void __launch_bounds__(256) ssd_pass_kernel(SsdParams p) {
-  const int64_t per = (int64_t)kP * p.dstate;  // state elements per head
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= p.batch * p.nheads * per) return;
-  const int64_t bh = e / per, i = e % per;
-  const int64_t b = bh / p.nheads, h = bh % p.nheads;
-  float H = p.h0 ? p.h0[e] : 0.0f;  // h0 is (B, H, P, N): element e
-  uint16_t* Hin = p.ws_entry;
-  for (int64_t c = 0; c < p.nchunks; ++c) {
-    const int64_t s = ((b * p.nchunks + c) * p.nheads + h) * per + i;
-    Hin[s] = bits16<IO>(H);
-    H = fmaf(p.ws_decay[(b * p.nchunks + c) * p.nheads + h], H, p.ws_state[s]);
+      for (int r = 0; r < 4; ++r)
+        p.final_state[hbase + (16 * wave + 4 * (lane / 16) + r) * N + kNS * s + 16 * nt + lane % 16] = acc[nt][r];
   }
-  if (p.final_state) p.final_state[e] = H;
 }
 
 // ---- pass 3: outputs of a chunk -------------------------------------------------
@@ -340,7 +309,7 @@ __global__ void __launch_bounds__(256) ssd_pass_kernel(SsdParams p) {
 // piece's CB during the current piece, the gate z before the main loop.
 constexpr int kScanThreads = 512;
 template <int IO, int N>
-__global__ void __launch_bounds__(kScanThreads) ssd_scan_kernel(SsdParams p) {
+__global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) {
   using M = mfma_t<IO>;
   constexpr int kXR = kQ + 8;  // x^T row: 264 elements (528 B keeps 16-byte reads aligned)
   constexpr int kHR = N + 8;   // H_in row
@@ -394,44 +363,27 @@ __global__ void __launch_bounds__(kScanThreads) ssd_scan_kernel(SsdParams p) {
 #pragma unroll
     for (int ks = 0; ks < N / 32; ++ks) cf[q][ks] = cfrag(t0 + 32 * blk[q] + 16 * half + lane % 16, 32 * ks + 8 * (lane / 16));
 
-  {  // Delta and the inclusive cumulative sum of Delta A over the chunk (threads 0..255 = steps)
-    float delta = 0.0f;
-    if (tid < kQ && t0 + tid < p.seqlen) {
-      const float xd = dt_raw + (p.dt_bias ? p.dt_bias[h] : 0.0f);
-      delta = p.softplus ? softplus_f(xd) : xd;
-    }
-    float v = delta * p.A[h];
+  // x^T and H_in into LDS, then Delta and its cumulative sum (threads 0..255 = steps)
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_up(v, off, 64);
-      if (lane >= off) v += o;
-    }
+  for (int e = 0; e < 8; ++e) {
+    const int q = e / 2, sh = 16 * (e % 2);
+    uint2 pk;
+    pk.x = ((xr[0][q] >> sh) & 0xffffu) | (((xr[1][q] >> sh) & 0xffffu) << 16);
+    pk.y = ((xr[2][q] >> sh) & 0xffffu) | (((xr[3][q] >> sh) & 0xffffu) << 16);
+    *reinterpret_cast<uint2*>(&sXT[8 * co + e][64 * pc + 4 * jq]) = pk;
+  }
+#pragma unroll
+  for (int k = 0; k < kHItems; ++k) {
+    const int item = tid + kScanThreads * k;
+    if (item < kHPieces) *reinterpret_cast<u32x4v*>(&sH[item / (N / 8)][8 * (item % (N / 8))]) = hr[k];
+  }
+  {
+    const float delta = chunk_cumsum<IO>(p, dt_raw, tid < kQ && t0 + tid < p.seqlen, p.A[h],
+                                         p.dt_bias ? p.dt_bias[h] : 0.0f, sCs, sWave);
     if (tid < kQ) {
-      if (lane == 63) sWave[wave] = v;
       sDelta[tid] = delta;
+      sWp[tid] = exp2_hw((sCs[tid | 63] - sCs[tid]) * kLog2e) * delta;
     }
-    // x^T and H_in into LDS meanwhile
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int q = e / 2, sh = 16 * (e % 2);
-      uint2 pk;
-      pk.x = ((xr[0][q] >> sh) & 0xffffu) | (((xr[1][q] >> sh) & 0xffffu) << 16);
-      pk.y = ((xr[2][q] >> sh) & 0xffffu) | (((xr[3][q] >> sh) & 0xffffu) << 16);
-      *reinterpret_cast<uint2*>(&sXT[8 * co + e][64 * pc + 4 * jq]) = pk;
-    }
-#pragma unroll
-    for (int k = 0; k < kHItems; ++k) {
-      const int item = tid + kScanThreads * k;
-      if (item < kHPieces) *reinterpret_cast<u32x4v*>(&sH[item / (N / 8)][8 * (item % (N / 8))]) = hr[k];
-    }
-    __syncthreads();
-    if (tid < kQ) {
-      float base = 0.0f;
-      for (int w = 0; w < wave; ++w) base += sWave[w];
-      sCs[tid] = v + base;
-    }
-    __syncthreads();
-    if (tid < kQ) sWp[tid] = exp2_hw((sCs[tid | 63] - sCs[tid]) * kLog2e) * sDelta[tid];
   }
 
   // gate values for the epilogue: lane has channels 16 pt + 4 (lane / 16) .. + 3 of its step
@@ -469,6 +421,8 @@ __global__ void __launch_bounds__(kScanThreads) ssd_scan_kernel(SsdParams p) {
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) acc[q][pt] *= sc;
   }
+
+  __syncthreads();  // sDelta, sWp
 
   // ---- Y_diag += x^T M^T, piece by piece
   const float* CBbase = p.ws_cb + ((b * p.nchunks + c) * p.ngroups + g) * (int64_t)(kQ * kQ);
@@ -563,15 +517,12 @@ __global__ void __launch_bounds__(kScanThreads) ssd_scan_kernel(SsdParams p) {
 
 template <int IO, int N>
 hipError_t launch_ssd_n(const SsdParams& p, hipStream_t st) {
-  const dim3 grid((uint32_t)(p.batch * p.nchunks * p.nheads));
-  hipLaunchKernelGGL((ssd_state_kernel<IO, N>), grid, dim3(kSsdThreads), 0, st, p);
+  hipLaunchKernelGGL((ssd_state_kernel<IO, N>), dim3((uint32_t)(p.batch * p.nheads * (N / kNS))), dim3(kSsdThreads), 0,
+                     st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t elems = p.batch * p.nheads * kP * N;
-  hipLaunchKernelGGL((ssd_pass_kernel<IO>), dim3((uint32_t)((elems + 255) / 256)), dim3(256), 0, st, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((ssd_scan_kernel<IO, N>), grid, dim3(kScanThreads), 0, st, p);
+  hipLaunchKernelGGL((ssd_scan_kernel<IO, N>), dim3((uint32_t)(p.batch * p.nchunks * p.nheads)), dim3(kScanThreads), 0,
+                     st, p);
   return hipGetLastError();
 }
 
