@@ -311,7 +311,7 @@ def bench_ssd(stream):
     ws = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
     f = lambda i: ss.ssd_fwd(sets[i % 2]["x"], sets[i % 2]["dt"], A, sets[i % 2]["Bm"], sets[i % 2]["Cm"], D=D,
                              z=sets[i % 2]["z"], dt_bias=dt_bias, y=sets[i % 2]["y"], workspace=ws)
-    for i in range(20):
+    for i in range(800):   # ~100 ms of load: the clock settles before the timed calls
         f(i)
     ms = timed(f, 50, stream)
     nchunks = (L + Q - 1) // Q
@@ -370,6 +370,8 @@ def main():
                     help="untimed steps first: the GPU needs ~100 ms of load to reach its working clock")
     ap.add_argument("--no-rows", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--row", choices=["ssd"], help="time one secondary workload alone and print its JSON line "
+                    "(for profiling it on its own); the headline is not run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the scan shards by batch "
@@ -378,6 +380,11 @@ def main():
         sys.exit(2)
     torch.cuda.init()
     stream = torch.cuda.current_stream()
+    if args.row == "ssd":
+        out = {"row": "ssd_fwd_B8_L2048_H24_P64_N128_bf16", **bench_ssd(stream)}
+        out["copy_probe_GBps"] = copy_probe(stream)   # the counter calibration kernel, same process
+        print(json.dumps(out), flush=True)
+        return
     log("headline: %d warmup + %d timed steps" % (args.warmup, args.steps))
     ms, kernel_ms, wall, (Bsz, Dd, N, L), sets, ys = bench_headline(args.steps, args.warmup, stream)
     del sets, ys
