@@ -190,8 +190,9 @@ __device__ __forceinline__ void agg_block(float& g, const BwdOwned& o, float A2,
 // ---- MAIN: forward recompute ---------------------------------------------------
 // fwd_pass advances h through block I (and, WITH_Y, leaves the readout terms
 // C h in the sum-over-states tile); fwd_states recomputes block I's 16
-// states from its entry state into hs[0..16] just before the reverse walk
-// needs them, so that only 17 states (not 65) are live at once.
+// states from its entry state into hs[0..16], and keeps the block's 16 decays
+// in as[0..16) for the reverse walk, just before the walk needs them, so that
+// only 17 states (not 65) are live at once.
 template <int I, bool WITH_Y, bool RESET, int... J>
 __device__ __forceinline__ void fwd_pass(float& h, const BwdOwned& o, float A2, const float* sBrow,
                                          const float* sCrow, float* t1c, int n, uint64_t starts,
@@ -218,7 +219,7 @@ __device__ __forceinline__ void fwd_pass(float& h, const BwdOwned& o, float A2, 
 }
 
 template <int I, bool RESET, int... J>
-__device__ __forceinline__ void fwd_states(float (&hs)[17], float h0, const BwdOwned& o, float A2,
+__device__ __forceinline__ void fwd_states(float (&hs)[17], float (&as)[16], float h0, const BwdOwned& o, float A2,
                                            const float* sBrow, uint64_t starts, std::integer_sequence<int, J...>) {
   float4 b4;
   hs[0] = h0;
@@ -228,6 +229,7 @@ __device__ __forceinline__ void fwd_states(float (&hs)[17], float h0, const BwdO
         if constexpr (J % 4 == 0) b4 = *reinterpret_cast<const float4*>(sBrow + s);
         const float bj = (J % 4 == 0) ? b4.x : (J % 4 == 1) ? b4.y : (J % 4 == 2) ? b4.z : b4.w;
         const float a = reset_decay<RESET, s>(exp2_hw(row_bcast<J>(o.dt[I]) * A2), starts);
+        as[J] = a;
         hs[J + 1] = fmaf(a, hs[J], row_bcast<J>(o.dtu[I]) * bj);
       }(),
       ...);
@@ -239,10 +241,10 @@ __device__ __forceinline__ void fwd_states(float (&hs)[17], float h0, const BwdO
 // Per step: the per-state terms G B and A G a h_{t-1} go to the sum-over-states
 // tiles (their row sums give du and dDelta), the per-channel terms G Delta u
 // and dy0 h_t to the sum-over-channels tiles (dB and dC).
-template <int I, bool RESET, int... J>
-__device__ __forceinline__ void bwd_block(float& g, float& dA_acc, const float (&hs)[17], const BwdOwned& o,
-                                          float A2, float Anat, const float* sBrow, const float* sCrow, float* t1c,
-                                          float* t2c, float* t3w, float* t4w, int n, int cw, uint64_t starts,
+template <int I, int... J>
+__device__ __forceinline__ void bwd_block(float& g, float& dA_acc, const float (&hs)[17], const float (&as)[16],
+                                          const BwdOwned& o, float Anat, const float* sBrow, const float* sCrow, float* t1c,
+                                          float* t2c, float* t3w, float* t4w, int n, int cw,
                                           std::integer_sequence<int, J...>) {
   float4 b4, c4;
   (
@@ -257,7 +259,7 @@ __device__ __forceinline__ void bwd_block(float& g, float& dA_acc, const float (
         const float cqj = (jj % 4 == 0) ? c4.x : (jj % 4 == 1) ? c4.y : (jj % 4 == 2) ? c4.z : c4.w;
         const float dtb = row_bcast<jj>(o.dt[I]);
         const float dy0b = row_bcast<jj>(o.dy0[I]);
-        const float a = reset_decay<RESET, s>(exp2_hw(dtb * A2), starts);
+        const float a = as[jj];               // decay of step s (0 at a document start)
         const float gh = fmaf(dy0b, cqj, g);  // dLoss/dh_t
         t4w[(jj * 16 + n) * kChPerWave + cw] = dy0b * hs[jj + 1];
         t3w[(jj * 16 + n) * kChPerWave + cw] = gh * row_bcast<jj>(o.dtu[I]);
@@ -421,12 +423,12 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
       float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
 #define SS_BWD(I)                                                                                   \
   {                                                                                                 \
-    float hs[17];                                                                                   \
+    float hs[17], as[16];                                                                           \
     o.dt[I] = fresh(o.dt[I]);                                                                       \
     o.dtu[I] = fresh(o.dtu[I]);                                                                     \
     o.dy0[I] = fresh(o.dy0[I]);                                                                     \
-    fwd_states<I, SEQ>(hs, hb[I], o, A2, sBrow, starts, seq);                                       \
-    bwd_block<I, SEQ>(g, dA_acc, hs, o, A2, A, sBrow, sCrow, t1c, t2c, t3w, t4w, n, cw, starts, seq);\
+    fwd_states<I, SEQ>(hs, as, hb[I], o, A2, sBrow, starts, seq);                                   \
+    bwd_block<I>(g, dA_acc, hs, as, o, A, sBrow, sCrow, t1c, t2c, t3w, t4w, n, cw, seq);            \
     wave_lds_sync();                                                                                \
     const float sGB = row16_sum(t1c, l);                                                            \
     const float sQA = row16_sum(t2c, l);                                                            \
