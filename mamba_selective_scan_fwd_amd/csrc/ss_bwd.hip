@@ -188,13 +188,13 @@ __device__ __forceinline__ void agg_block(float& g, const BwdOwned& o, float A2,
 }
 
 // ---- MAIN: forward recompute ---------------------------------------------------
-// fwd_pass advances h through block I (and, WITH_Y, leaves the readout terms
-// C h in the sum-over-states tile); fwd_states recomputes block I's 16
-// states from its entry state into hs[0..16], and keeps the block's 16 decays
-// in as[0..16) for the reverse walk, just before the walk needs them, so that
-// only 17 states (not 65) are live at once.
+// fwd_pass advances h through block I, keeping the block's 16 decays in
+// as[0..16) (and, WITH_Y, leaving the readout terms C h in the sum-over-states
+// tile); fwd_states recomputes block I's 16 states from its entry state and
+// those decays into hs[0..16] just before the reverse walk needs them, so
+// that only 17 states (not 65) are live at once, and no decay is taken twice.
 template <int I, bool WITH_Y, bool RESET, int... J>
-__device__ __forceinline__ void fwd_pass(float& h, const BwdOwned& o, float A2, const float* sBrow,
+__device__ __forceinline__ void fwd_pass(float& h, float (&as)[16], const BwdOwned& o, float A2, const float* sBrow,
                                          const float* sCrow, float* t1c, int n, uint64_t starts,
                                          std::integer_sequence<int, J...>) {
   float4 b4, c4;
@@ -207,6 +207,7 @@ __device__ __forceinline__ void fwd_pass(float& h, const BwdOwned& o, float A2, 
         }
         const float bj = (J % 4 == 0) ? b4.x : (J % 4 == 1) ? b4.y : (J % 4 == 2) ? b4.z : b4.w;
         const float a = reset_decay<RESET, s>(exp2_hw(row_bcast<J>(o.dt[I]) * A2), starts);
+        as[J] = a;
         h = fmaf(a, h, row_bcast<J>(o.dtu[I]) * bj);
         if constexpr (WITH_Y) {
           const float cj = (J % 4 == 0) ? c4.x : (J % 4 == 1) ? c4.y : (J % 4 == 2) ? c4.z : c4.w;
@@ -218,9 +219,9 @@ __device__ __forceinline__ void fwd_pass(float& h, const BwdOwned& o, float A2, 
   __builtin_amdgcn_sched_barrier(0);  // no hoisting across blocks (registers)
 }
 
-template <int I, bool RESET, int... J>
-__device__ __forceinline__ void fwd_states(float (&hs)[17], float (&as)[16], float h0, const BwdOwned& o, float A2,
-                                           const float* sBrow, uint64_t starts, std::integer_sequence<int, J...>) {
+template <int I, int... J>
+__device__ __forceinline__ void fwd_states(float (&hs)[17], const float (&as)[16], float h0, const BwdOwned& o,
+                                           const float* sBrow, std::integer_sequence<int, J...>) {
   float4 b4;
   hs[0] = h0;
   (
@@ -228,9 +229,7 @@ __device__ __forceinline__ void fwd_states(float (&hs)[17], float (&as)[16], flo
         constexpr int s = 16 * I + J;
         if constexpr (J % 4 == 0) b4 = *reinterpret_cast<const float4*>(sBrow + s);
         const float bj = (J % 4 == 0) ? b4.x : (J % 4 == 1) ? b4.y : (J % 4 == 2) ? b4.z : b4.w;
-        const float a = reset_decay<RESET, s>(exp2_hw(row_bcast<J>(o.dt[I]) * A2), starts);
-        as[J] = a;
-        hs[J + 1] = fmaf(a, hs[J], row_bcast<J>(o.dtu[I]) * bj);
+        hs[J + 1] = fmaf(as[J], hs[J], row_bcast<J>(o.dtu[I]) * bj);
       }(),
       ...);
   hs[16] = fresh(hs[16]);
@@ -395,12 +394,12 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
       float* t3w = sm.T3[wave];
       float* t4w = sm.T4[wave];
       // first pass: entry state of each 16-step block (and y0 when gated)
-      float hb[4];
+      float hb[4], ac[4][16];  // block entry states, the chunk's decays
       float h = (ch_ok && n_ok) ? p.ckpt[(ch * K + k) * p.dstate + n] : 0.0f;
       if (need_z) {
-#define SS_FWD_Y(I)                                                        \
-  hb[I] = h;                                                               \
-  fwd_pass<I, true, SEQ>(h, o, A2, sBrow, sCrow, t1c, n, starts, seq);     \
+#define SS_FWD_Y(I)                                                          \
+  hb[I] = h;                                                                 \
+  fwd_pass<I, true, SEQ>(h, ac[I], o, A2, sBrow, sCrow, t1c, n, starts, seq); \
   wave_lds_sync();                                                         \
   o.y0[I] = fmaf(Dd, o.u[I], row16_sum(t1c, l));                           \
   wave_lds_sync();
@@ -411,24 +410,25 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
 #undef SS_FWD_Y
       } else {
         hb[0] = h;
-        fwd_pass<0, false, SEQ>(h, o, A2, sBrow, sCrow, t1c, n, starts, seq);
+        fwd_pass<0, false, SEQ>(h, ac[0], o, A2, sBrow, sCrow, t1c, n, starts, seq);
         hb[1] = h;
-        fwd_pass<1, false, SEQ>(h, o, A2, sBrow, sCrow, t1c, n, starts, seq);
+        fwd_pass<1, false, SEQ>(h, ac[1], o, A2, sBrow, sCrow, t1c, n, starts, seq);
         hb[2] = h;
-        fwd_pass<2, false, SEQ>(h, o, A2, sBrow, sCrow, t1c, n, starts, seq);
+        fwd_pass<2, false, SEQ>(h, ac[2], o, A2, sBrow, sCrow, t1c, n, starts, seq);
         hb[3] = h;
+        fwd_pass<3, false, SEQ>(h, ac[3], o, A2, sBrow, sCrow, t1c, n, starts, seq);  // its decays
       }
 
       float g = (k < K - 1 && ch_ok) ? p.gcarry[wslot] : g_last;
       float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
 #define SS_BWD(I)                                                                                   \
   {                                                                                                 \
-    float hs[17], as[16];                                                                           \
+    float hs[17];                                                                                   \
     o.dt[I] = fresh(o.dt[I]);                                                                       \
     o.dtu[I] = fresh(o.dtu[I]);                                                                     \
     o.dy0[I] = fresh(o.dy0[I]);                                                                     \
-    fwd_states<I, SEQ>(hs, as, hb[I], o, A2, sBrow, starts, seq);                                   \
-    bwd_block<I>(g, dA_acc, hs, as, o, A, sBrow, sCrow, t1c, t2c, t3w, t4w, n, cw, seq);            \
+    fwd_states<I>(hs, ac[I], hb[I], o, sBrow, seq);                                                 \
+    bwd_block<I>(g, dA_acc, hs, ac[I], o, A, sBrow, sCrow, t1c, t2c, t3w, t4w, n, cw, seq);         \
     wave_lds_sync();                                                                                \
     const float sGB = row16_sum(t1c, l);                                                            \
     const float sQA = row16_sum(t2c, l);                                                            \
