@@ -423,22 +423,23 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   }
 }
 
-// Entry value of every chunk: an exclusive scan over the chunk pairs (P, S)
-// of one channel, left to right (forward states) or right to left (the
-// backward's carried state gradient, reverse = 1: chunk c is visited as
-// K-1-c).  256 threads per channel: thread (n, g) serially combines the
-// chunks [g*per, (g+1)*per) of state n, the 16 groups of a state (one DPP
-// row) are then scanned with shuffles, and each group replays its chunks
-// from its exclusive prefix.
+// Pass 2: exclusive scan of the chunk pairs of one channel (forward: the
+// entry state of every chunk; reverse = 1, the backward's carried state
+// gradient: chunk c is visited as K-1-c).  256 threads per channel: thread
+// (g, n), state n fastest so that 16 lanes read one chunk's 64 contiguous
+// bytes, serially combines chunks [g*per, (g+1)*per) of state n; the value
+// entering each group is then combined from the groups on its left through
+// LDS, and each group replays its chunks from it.
 __global__ void __launch_bounds__(256) ss_carry_kernel(const float* __restrict__ aggP, const float* __restrict__ aggS,
                                                        float* __restrict__ carry, int64_t nch, int32_t nchunks,
                                                        int32_t reverse) {
+  __shared__ float sP[16][16], sS[16][16];
   const int tid = threadIdx.x;
-  const int n = tid / 16, g = tid % 16;
+  const int n = tid % 16, g = tid / 16;
   const int64_t ch = blockIdx.x;
-  if (ch >= nch) return;
+  if (ch >= nch) return;  // uniform per workgroup
   const int per = (nchunks + 15) / 16;
-  const int c0 = g * per;
+  const int c0 = g * per < nchunks ? g * per : nchunks;
   const int c1 = c0 + per < nchunks ? c0 + per : nchunks;
   const int64_t base = ch * nchunks;
   auto slot = [&](int c) { return (base + (reverse ? nchunks - 1 - c : c)) * kStates + n; };
@@ -446,25 +447,20 @@ __global__ void __launch_bounds__(256) ss_carry_kernel(const float* __restrict__
   // local pair over [c0, c1): applying it maps the value entering c0 to the
   // value leaving c1 - 1
   float P = 1.0f, S = 0.0f;
+#pragma unroll 4
   for (int c = c0; c < c1; ++c) {
     const float pc = aggP[slot(c)];
     const float sc = aggS[slot(c)];
     S = fmaf(pc, S, sc);
     P *= pc;
   }
-  // inclusive scan across the 16 groups (earlier groups on the left)
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) {
-    const float Pl = __shfl_up(P, off, 16);
-    const float Sl = __shfl_up(S, off, 16);
-    if (g >= off) {
-      S = fmaf(P, Sl, S);
-      P *= Pl;
-    }
-  }
-  // exclusive prefix = inclusive prefix of the group on the left
-  float E = __shfl_up(S, 1, 16);
-  if (g == 0) E = 0.0f;
+  sP[g][n] = P;
+  sS[g][n] = S;
+  __syncthreads();
+  // the value entering group g: groups 0 .. g-1 applied in order to 0
+  float E = 0.0f;
+  for (int q = 0; q < g; ++q) E = fmaf(sP[q][n], E, sS[q][n]);
+#pragma unroll 4
   for (int c = c0; c < c1; ++c) {
     carry[slot(c)] = E;
     E = fmaf(aggP[slot(c)], E, aggS[slot(c)]);
