@@ -502,10 +502,17 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
   }
 }
 
-__global__ void __launch_bounds__(256) ss_fill_kernel(float* __restrict__ dst, int64_t count, float value) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// Zero up to five float buffers in one launch (the atomic targets of the
+// backward: dB, dC, dA, dD, dbias); a null buffer has count 0.
+struct ZeroList {
+  float* ptr[5];
+  int64_t count[5];
+};
+__global__ void __launch_bounds__(256) ss_zero_kernel(ZeroList z) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (; i < count; i += stride) dst[i] = value;
+#pragma unroll
+  for (int k = 0; k < 5; ++k)
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < z.count[k]; i += stride) z.ptr[k][i] = 0.0f;
 }
 
 // dA[d, n] = sum over (batch row, chunk) partials; dD, dbias likewise.  The
@@ -539,20 +546,25 @@ __global__ void __launch_bounds__(256) ss_bwd_reduce_kernel(const float* __restr
   }
 }
 
-hipError_t fill(float* dst, int64_t count, hipStream_t st) {
-  int64_t blocks = (count + 255) / 256;
+hipError_t zero_outputs(const BwdParams& p, hipStream_t st) {
+  ZeroList z{};
+  const int64_t nbc = p.batch * p.dstate * p.seqlen;
+  z.ptr[0] = p.dB; z.count[0] = nbc;
+  z.ptr[1] = p.dC; z.count[1] = nbc;
+  z.ptr[2] = p.dA; z.count[2] = p.dim * p.dstate;
+  z.ptr[3] = p.dD; z.count[3] = p.dD ? p.dim : 0;
+  z.ptr[4] = p.dbias; z.count[4] = p.dbias ? p.dim : 0;
+  int64_t blocks = (nbc + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(ss_fill_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, dst, count, 0.0f);
+  hipLaunchKernelGGL(ss_zero_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, z);
   return hipGetLastError();
 }
 
 template <int IO, bool SEQ>
 hipError_t launch_bwd_seq(const BwdParams& p, hipStream_t st) {
   const int64_t K = p.nchunks;
-  hipError_t e = fill(p.dB, p.batch * p.dstate * p.seqlen, st);
-  if (e != hipSuccess) return e;
-  e = fill(p.dC, p.batch * p.dstate * p.seqlen, st);
+  hipError_t e = zero_outputs(p, st);  // every atomic target, before any kernel adds into it
   if (e != hipSuccess) return e;
   // MAIN: channel blocks per workgroup chosen for enough workgroups to fill
   // the chip (each workgroup adds its channel sums of dB/dC once per element)
@@ -575,10 +587,6 @@ hipError_t launch_bwd_seq(const BwdParams& p, hipStream_t st) {
   hipLaunchKernelGGL((ss_bwd_chunk_kernel<IO, true, SEQ>), grid, dim3(kThreads), 0, st, p, (int32_t)groups,
                      (int32_t)per);
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = fill(p.dA, p.dim * p.dstate, st);
-  if (e == hipSuccess && p.dD) e = fill(p.dD, p.dim, st);
-  if (e == hipSuccess && p.dbias) e = fill(p.dbias, p.dim, st);
   if (e != hipSuccess) return e;
   const int64_t threads = p.dim * kStates;
   int64_t groups_y = (bk + 31) / 32;
