@@ -532,15 +532,18 @@ __global__ void __launch_bounds__(256) ss_bwd_reduce_kernel(const float* __restr
   const int64_t bk1 = bk0 + per < nbk ? bk0 + per : nbk;
   if (bk0 >= bk1) return;
   float acc = 0.0f;
+#pragma unroll 8
   for (int64_t bk = bk0; bk < bk1; ++bk) acc += dApart[(bk * dim + d) * kStates + n];
   if (n < dstate) unsafeAtomicAdd(dA + d * dstate + n, acc);
   if (n == 0 && dD) {
     float s = 0.0f;
+#pragma unroll 8
     for (int64_t bk = bk0; bk < bk1; ++bk) s += dDpart[bk * dim + d];
     unsafeAtomicAdd(dD + d, s);
   }
   if (n == 1 && dbias) {
     float s = 0.0f;
+#pragma unroll 8
     for (int64_t bk = bk0; bk < bk1; ++bk) s += dbpart[bk * dim + d];
     unsafeAtomicAdd(dbias + d, s);
   }
