@@ -108,6 +108,15 @@ def test_prefill_in_pieces():
     assert rel_err(f64(f2), f64(fin)) <= TOL["bf16"]
 
 
+def test_long_sequence_many_chunks():
+    """64 chunks of 256 steps walked in order by the state kernel, with few waves per group
+    (2 heads x 2 state slices), so the C B^T tiles are shared out in turns."""
+    q = _data(1, 16384, 2, 1, 64, "bf16", seed=14)
+    y, fin = _run(q)
+    yr, fr = _ref(q)
+    assert rel_err(f64(y), yr) <= TOL["bf16"] and rel_err(f64(fin), fr) <= TOL["bf16"]
+
+
 def test_workspace_contents_do_not_matter():
     """A workspace full of NaN (and one left dirty by a different problem) gives the same
     output bit for bit: nothing is read before it is written."""
