@@ -382,7 +382,7 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
                                          p.dt_bias ? p.dt_bias[h] : 0.0f, sCs, sWave);
     if (tid < kQ) {
       sDelta[tid] = delta;
-      sWp[tid] = exp2_hw((sCs[tid | 63] - sCs[tid]) * kLog2e) * delta;
+      sWp[tid] = exp2_hw((sCs[tid | (kJB - 1)] - sCs[tid]) * kLog2e) * delta;
     }
   }
 
@@ -429,24 +429,24 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int i = 32 * blk[q] + 16 * half + lane % 16;  // this lane's row (chunk-local)
-    const int dpiece = blk[q] / 2;                      // the piece holding the block's rows
+    const int dpiece = 32 * blk[q] / kJB;               // the piece holding the block's rows
     const float csi = sCs[i];
     const float* cbrow = CBbase + i * kQ + 8 * (lane / 16);
     float4 nxt[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) nxt[k] = *reinterpret_cast<const float4*>(cbrow + 32 * (k / 2) + 4 * (k % 2));
     for (int piece = 0; piece <= dpiece; ++piece) {
-      const int jb = 64 * piece;
+      const int jb = kJB * piece;
       float4 cur[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) cur[k] = nxt[k];
       if (piece < dpiece) {
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          nxt[k] = *reinterpret_cast<const float4*>(cbrow + jb + 64 + 32 * (k / 2) + 4 * (k % 2));
+          nxt[k] = *reinterpret_cast<const float4*>(cbrow + jb + kJB + 32 * (k / 2) + 4 * (k % 2));
       }
       const bool diag = piece == dpiece;
-      const float ei = exp2_hw((csi - sCs[jb + 63]) * kLog2e);
+      const float ei = exp2_hw((csi - sCs[jb + kJB - 1]) * kLog2e);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int j0 = jb + 32 * ks + 8 * (lane / 16);
