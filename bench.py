@@ -214,6 +214,13 @@ def bench_rows(stream):
     fcs(0)
     ms = timed(fcs, 64, stream)
     rows["conv1d_silu_B8_D1536_L2048_W4_f16"]["decode_us_per_step_checked_call"] = ms * 1e3
+    # the serving form: preallocated token, window and output buffers, one C call per step
+    xt = xs[0][..., 0].contiguous()
+    ot = torch.empty_like(xt)
+    ccs = ss.ConvStepCall(xt, wcv, win, ot, bias=bcv, stream=stream)
+    ccs()
+    ms = timed(lambda i: ccs(), 256, stream)
+    rows["conv1d_silu_B8_D1536_L2048_W4_f16"]["decode_us_per_step"] = ms * 1e3
     del xs, outs, win
     # Mamba-2 SSD chunked scan on the matrix cores: d_model 768, expand 2 -> 24 heads of 64,
     # d_state 128, one group, chunk 256 (the "niverel-mamba" README's V3 configuration), B=8,

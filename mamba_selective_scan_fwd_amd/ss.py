@@ -376,6 +376,45 @@ def conv1d(x, w, bias=None, silu=True, seq_idx=None, conv_init=None, return_fina
     return out
 
 
+class ConvStepCall:
+    """A decode step of the convolution validated once and replayed with one C call per launch
+    (the serving pattern of StepCall: preallocated token, window and output buffers refilled in
+    place; the tensors must stay alive and unmoved)."""
+
+    def __init__(self, x_t, w, window, out, bias=None, silu=True, window_out=None, stream=None):
+        lib = load_library()
+        io = x_t.dtype
+        if io not in _IO:
+            raise TypeError("unsupported dtype %s" % io)
+        Bsz, Dd = x_t.shape
+        W = w.shape[-1]
+        if window_out is None:
+            window_out = window
+        checks = [(x_t, io, "x_t", (Bsz, Dd)), (w, torch.float32, "w", (Dd, W)), (bias, torch.float32, "bias", (Dd,)),
+                  (out, io, "out", (Bsz, Dd))]
+        if W > 1:
+            checks += [(window, torch.float32, "window", (Bsz, Dd, W - 1)),
+                       (window_out, torch.float32, "window_out", (Bsz, Dd, W - 1))]
+        for t, dt, name, shape in checks:
+            if t is None:
+                continue
+            if not (t.is_cuda and t.dtype == dt and tuple(t.shape) == shape and t.is_contiguous()
+                    and t.data_ptr() % 16 == 0):
+                raise ValueError("%s must be a contiguous, 16-byte aligned %s device tensor of shape %s"
+                                 % (name, dt, shape))
+        self.pr = ss_conv_problem(Bsz, Dd, 1, W, _IO[io], 1 if silu else 0, 0)
+        self.keep = (x_t, w, window, out, bias, window_out)
+        st = stream if stream is not None else torch.cuda.current_stream(x_t.device)
+        self.args = (ctypes.byref(self.pr), _ptr(x_t), _ptr(w), _ptr(bias), _ptr(window) if W > 1 else None,
+                     _ptr(window_out) if W > 1 else None, _ptr(out), ctypes.c_void_p(st.cuda_stream))
+        self.fn = lib.ss_conv1d_step
+
+    def __call__(self):
+        status = self.fn(*self.args)
+        if status != 0:
+            _check(status)
+
+
 def conv1d_step(x_t, w, window, bias=None, silu=True, window_out=None, out=None):
     """One decode step of the convolution.  x_t: (B, D); window: (B, D, W-1) fp32, updated in place
     unless window_out is given.  Returns (out_t (B, D), window_out)."""

@@ -124,6 +124,26 @@ def test_decode_step_against_oracle(io):
         assert np.array_equal(f64(win_d), ref_win)
 
 
+def test_prepared_step_matches_checked_step():
+    """ConvStepCall (validated once, buffers refilled in place) gives the checked call's
+    outputs and windows bit for bit over 8 steps."""
+    ss = _ss()
+    Bsz, Dd, W = 2, 40, 4
+    x, w, bias = _data(Bsz, Dd, 8, W, "f16", 12)
+    xd, wd, bd = x.cuda(), w.cuda(), bias.cuda()
+    win_a = torch.zeros((Bsz, Dd, W - 1), dtype=torch.float32, device="cuda")
+    win_b = win_a.clone()
+    xt = torch.empty((Bsz, Dd), dtype=torch.float16, device="cuda")
+    ot = torch.empty_like(xt)
+    call = ss.ConvStepCall(xt, wd, win_b, ot, bias=bd)
+    for t in range(8):
+        oa, win_a = ss.conv1d_step(xd[..., t].contiguous(), wd, win_a, bd)
+        xt.copy_(xd[..., t])
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ot) and torch.equal(win_a, win_b)
+
+
 def test_mamba130m_layer_shape():
     """B=8, d_inner=1536, L=2048, fp16, width 4: sampled channels against the oracle."""
     ss = _ss()
