@@ -266,10 +266,12 @@ size_t ss_ssd_workspace_size(const ss_ssd_problem *p);
 
 /*
  * SSD forward.  D, z, dt_bias, h0 and final_state are optional (NULL).
- * Every pointer must be 16-byte aligned.  Returns SS_ERR_BAD_DTYPE for fp32
- * I/O (the matrix-core path takes 16-bit data), SS_ERR_UNSUPPORTED for a
+ * Every pointer must be 16-byte aligned.  y may be x or z itself (in place)
+ * and final_state may be h0 itself; any other overlap between an output or
+ * the workspace and another buffer is rejected.  Returns SS_ERR_BAD_DTYPE for
+ * fp32 I/O (the matrix-core path takes 16-bit data), SS_ERR_UNSUPPORTED for a
  * headdim other than 64, a dstate outside {32, 64, 96, 128}, ngroups not
- * dividing nheads, or a workspace missing or too small.
+ * dividing nheads, a workspace missing or too small, or overlapping buffers.
  */
 ss_status ss_ssd_fwd(const ss_ssd_problem *p, const void *x, const void *dt, const float *A,
                      const void *Bm, const void *Cm, const float *D, const void *z, const float *dt_bias,

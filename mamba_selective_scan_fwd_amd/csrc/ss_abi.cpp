@@ -301,6 +301,28 @@ ss_status ss_ssd_fwd(const ss_ssd_problem* p, const void* x, const void* dt, con
     if (q && !aligned(q)) return SS_ERR_MISALIGNED;
   const size_t need = ss_ssd_workspace_size(p);
   if (!workspace || workspace_bytes < need) return SS_ERR_UNSUPPORTED;
+  {
+    // y may be x or z itself (a workgroup reads its own rows of x and z before it writes
+    // them) and final_state may be h0 itself (each element is read and written by one
+    // thread); no other overlap between an output or the workspace and an operand
+    const size_t xb = (size_t)(p->batch * p->seqlen * p->nheads) * 64 * 2;
+    const size_t dtb = (size_t)(p->batch * p->seqlen * p->nheads) * 2;
+    const size_t bcb = (size_t)(p->batch * p->seqlen * p->ngroups * p->dstate) * 2;
+    const size_t hb = (size_t)(p->batch * p->nheads) * 64 * (size_t)p->dstate * 4;
+    const size_t vb = (size_t)p->nheads * 4;
+    struct Span { const void* ptr; size_t n; };
+    const Span in[] = {{x, xb}, {dt, dtb}, {A, vb}, {Bm, bcb}, {Cm, bcb}, {D, vb}, {z, xb}, {dt_bias, vb}, {h0, hb}};
+    for (const Span& r : in) {
+      if (!r.ptr) continue;
+      if (overlaps(r.ptr, r.n, y, xb) && !(r.ptr == y && (r.ptr == x || r.ptr == z))) return SS_ERR_UNSUPPORTED;
+      if (final_state && overlaps(r.ptr, r.n, final_state, hb) && !(r.ptr == final_state && r.ptr == h0))
+        return SS_ERR_UNSUPPORTED;
+      if (overlaps(r.ptr, r.n, workspace, need)) return SS_ERR_UNSUPPORTED;
+    }
+    if (final_state && overlaps(final_state, hb, y, xb)) return SS_ERR_UNSUPPORTED;
+    if (overlaps(workspace, need, y, xb) || (final_state && overlaps(workspace, need, final_state, hb)))
+      return SS_ERR_UNSUPPORTED;
+  }
   const size_t e = ssd_state_elems(p);
   ss::SsdParams k{};
   k.io = p->io_dtype; k.softplus = p->dt_softplus != 0;

@@ -165,3 +165,29 @@ def test_ssd_workspace_and_validation():
                           None) == 1
     assert lib.ss_ssd_fwd(ctypes.byref(p), *([FAKE] * 5), None, None, None, FAKE + 4, FAKE, None, FAKE, wsz,
                           None) == 4
+
+
+def test_ssd_rejects_overlapping_buffers():
+    """Outputs and workspace may not overlap other operands (y may only be x or z itself,
+    final_state only h0 itself).  Every case returns before any HIP call."""
+    lib = ss.load_library()
+    p = _ssd_prob()
+    wsz = lib.ss_ssd_workspace_size(ctypes.byref(p))
+    G = 1 << 32                                   # far-apart, aligned fake device addresses
+    x, dt, A, Bm, Cm, y, fin, ws, h0 = (G * k for k in range(1, 10))
+
+    def call(**kw):
+        a = dict(x=x, dt=dt, A=A, Bm=Bm, Cm=Cm, D=None, z=None, dt_bias=None, h0=h0, y=y, fin=fin, ws=ws)
+        a.update(kw)
+        return lib.ss_ssd_fwd(ctypes.byref(p), a["x"], a["dt"], a["A"], a["Bm"], a["Cm"], a["D"], a["z"],
+                              a["dt_bias"], a["h0"], a["y"], a["fin"], a["ws"], wsz, None)
+
+    assert call(y=Cm + 256) == 5          # y overlaps C
+    assert call(y=Bm) == 5                # y is B
+    assert call(y=x + 256) == 5           # y partly overlaps x
+    assert call(fin=y + 4096) == 5        # final state inside y
+    assert call(fin=dt) == 5              # final state is dt
+    assert call(ws=x + 1024) == 5         # workspace overlaps x
+    assert call(ws=h0) == 5               # workspace is h0
+    assert call(h0=fin + 256) == 5        # h0 partly overlaps the final state
+

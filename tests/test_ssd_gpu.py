@@ -117,6 +117,21 @@ def test_long_sequence_many_chunks():
     assert rel_err(f64(y), yr) <= TOL["bf16"] and rel_err(f64(fin), fr) <= TOL["bf16"]
 
 
+def test_in_place_output():
+    """y written over x (and, separately, over z) gives the out-of-place result bit for bit."""
+    ss = _ss()
+    q = _data(2, 600, 4, 2, 64, "bf16", seed=15)
+    g = {k: v.cuda() for k, v in q.items()}
+    kw = dict(D=g["D"], dt_bias=g["dt_bias"], h0=g["h0"])
+    y = ss.ssd_fwd(g["x"], g["dt"], g["A"], g["Bm"], g["Cm"], z=g["z"], **kw)
+    xi = g["x"].clone()
+    ss.ssd_fwd(xi, g["dt"], g["A"], g["Bm"], g["Cm"], z=g["z"], y=xi, **kw)
+    zi = g["z"].clone()
+    ss.ssd_fwd(g["x"], g["dt"], g["A"], g["Bm"], g["Cm"], z=zi, y=zi, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(xi, y) and torch.equal(zi, y)
+
+
 def test_workspace_contents_do_not_matter():
     """A workspace full of NaN (and one left dirty by a different problem) gives the same
     output bit for bit: nothing is read before it is written."""
