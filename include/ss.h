@@ -57,7 +57,8 @@ typedef enum ss_status {
     SS_ERR_BAD_SHAPE = 2,    /* a size is < 1 or overflows */
     SS_ERR_BAD_DTYPE = 3,    /* io_dtype is not one of ss_dtype */
     SS_ERR_MISALIGNED = 4,   /* a pointer is not 16-byte aligned */
-    SS_ERR_UNSUPPORTED = 5,  /* dstate > 16, or a workspace smaller than required */
+    SS_ERR_UNSUPPORTED = 5,  /* a size outside the supported set, a workspace missing or
+                                smaller than required, or overlapping buffers */
     SS_ERR_HIP = 6           /* the HIP runtime reported an error at launch */
 } ss_status;
 
@@ -111,6 +112,9 @@ size_t ss_fwd_workspace_size(const ss_problem *p);
  *   workspace         : device buffer of ss_fwd_workspace_size() bytes, or
  *                       NULL when that size is 0 (SS_ERR_UNSUPPORTED when it
  *                       is needed and missing or too small).
+ * y may be u, delta or z itself (in place); any other overlap between an
+ * output (y, last_state, ckpt, workspace) and another buffer returns
+ * SS_ERR_UNSUPPORTED.
  */
 ss_status ss_fwd(const ss_problem *p,
                  const void *u, const void *delta, const float *A,
@@ -165,7 +169,8 @@ size_t ss_bwd_workspace_size(const ss_problem *p);
  *   overwritten; the library clears its accumulation targets itself.
  *   workspace    : device buffer of ss_bwd_workspace_size() bytes.
  * Returns SS_ERR_NULL_ARG when a gradient output and its input are not given
- * together, SS_ERR_UNSUPPORTED when the workspace is missing or too small.
+ * together, SS_ERR_UNSUPPORTED when the workspace is missing or too small or
+ * when an output or the workspace overlaps any other buffer (no in-place).
  */
 ss_status ss_bwd(const ss_problem *p,
                  const void *u, const void *delta, const float *A,

@@ -69,6 +69,31 @@ FwdPlan plan_fwd(const ss_problem* p) {
 
 ss_status from_hip(hipError_t e) { return e == hipSuccess ? SS_OK : SS_ERR_HIP; }
 
+// A device buffer as a byte range; a null pointer or zero size is no buffer.
+struct Span {
+  const void* ptr;
+  size_t n;
+};
+bool share_bytes(const Span& a, const Span& b) {
+  if (!a.ptr || !b.ptr || !a.n || !b.n) return false;
+  const uintptr_t x = (uintptr_t)a.ptr, y = (uintptr_t)b.ptr;
+  return x < y + b.n && y < x + a.n;
+}
+// True when an output shares a byte with an input (unless it is that input
+// itself and inplace[i][j] allows it) or with another output.
+template <size_t NI, size_t NO>
+bool conflict(const Span (&in)[NI], const Span (&out)[NO], const bool (*inplace)[NI] = nullptr) {
+  for (size_t o = 0; o < NO; ++o) {
+    for (size_t i = 0; i < NI; ++i)
+      if (share_bytes(out[o], in[i]) &&
+          !(inplace && inplace[o][i] && out[o].ptr == in[i].ptr && out[o].n == in[i].n))
+        return true;
+    for (size_t o2 = o + 1; o2 < NO; ++o2)
+      if (share_bytes(out[o], out[o2])) return true;
+  }
+  return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -80,7 +105,9 @@ const char* ss_status_str(ss_status s) {
     case SS_ERR_BAD_SHAPE: return "ss: invalid problem size";
     case SS_ERR_BAD_DTYPE: return "ss: io_dtype must be SS_F32, SS_F16 or SS_BF16";
     case SS_ERR_MISALIGNED: return "ss: every tensor pointer must be 16-byte aligned";
-    case SS_ERR_UNSUPPORTED: return "ss: unsupported request (dstate > 16, or workspace missing/too small)";
+    case SS_ERR_UNSUPPORTED:
+      return "ss: unsupported request (a size outside the supported set, a workspace missing or too small, or "
+             "overlapping buffers)";
     case SS_ERR_HIP: return "ss: HIP launch failed";
   }
   return "ss: unknown status";
@@ -108,6 +135,21 @@ ss_status ss_fwd(const ss_problem* p, const void* u, const void* delta, const fl
     if (q && !aligned(q)) return SS_ERR_MISALIGNED;
   const FwdPlan pl = plan_fwd(p);
   if (pl.workspace > 0 && (!workspace || workspace_bytes < pl.workspace)) return SS_ERR_UNSUPPORTED;
+  {
+    // y may be u, delta or z itself (each wave reads a tile's inputs before it writes the
+    // tile's outputs); no other overlap between an output and any buffer
+    const size_t io = (size_t)(p->batch * p->dim * p->seqlen) * elem_size(p->io_dtype);
+    const size_t bc = (size_t)(p->batch * p->dstate * p->seqlen) * elem_size(p->io_dtype);
+    const size_t st = (size_t)(p->batch * p->dim * p->dstate) * sizeof(float);
+    const Span in[] = {{u, io}, {delta, io}, {z, io}, {Bm, bc}, {Cm, bc},
+                       {A, (size_t)(p->dim * p->dstate) * sizeof(float)}, {D, (size_t)p->dim * sizeof(float)},
+                       {delta_bias, (size_t)p->dim * sizeof(float)}, {lengths, (size_t)p->batch * 4},
+                       {seq_idx, (size_t)(p->batch * p->seqlen) * 4}, {h0, st}};
+    const Span out[] = {{y, io}, {last_state, st}, {ckpt, ss_ckpt_count(p) * sizeof(float)},
+                        {pl.workspace ? workspace : nullptr, pl.workspace}};
+    static const bool inplace[4][11] = {{true, true, true}};
+    if (conflict(in, out, inplace)) return SS_ERR_UNSUPPORTED;
+  }
 
   ss::FwdParams k{};
   k.io = p->io_dtype;
@@ -179,6 +221,20 @@ ss_status ss_bwd(const ss_problem* p, const void* u, const void* delta, const fl
     if (q && !aligned(q)) return SS_ERR_MISALIGNED;
   const size_t need = ss_bwd_workspace_size(p);
   if (!workspace || workspace_bytes < need) return SS_ERR_UNSUPPORTED;
+  {
+    // no output (or the workspace) shares a byte with any other buffer
+    const size_t io = (size_t)(p->batch * p->dim * p->seqlen) * elem_size(p->io_dtype);
+    const size_t bc = (size_t)(p->batch * p->dstate * p->seqlen) * elem_size(p->io_dtype);
+    const size_t bc32 = (size_t)(p->batch * p->dstate * p->seqlen) * sizeof(float);
+    const size_t st = (size_t)(p->batch * p->dim * p->dstate) * sizeof(float);
+    const size_t dn = (size_t)(p->dim * p->dstate) * sizeof(float), dv = (size_t)p->dim * sizeof(float);
+    const Span in[] = {{u, io}, {delta, io}, {z, io}, {Bm, bc}, {Cm, bc}, {A, dn}, {D, dv}, {delta_bias, dv},
+                       {seq_idx, (size_t)(p->batch * p->seqlen) * 4}, {ckpt, ss_ckpt_count(p) * sizeof(float)},
+                       {dy, io}, {dlast, st}};
+    const Span out[] = {{du, io}, {ddelta, io}, {dz, io}, {dA, dn}, {dB, bc32}, {dC, bc32},
+                        {dD, dv}, {dbias, dv}, {dh0, st}, {workspace, need}};
+    if (conflict(in, out)) return SS_ERR_UNSUPPORTED;
+  }
 
   ss::BwdParams k{};
   k.io = p->io_dtype;

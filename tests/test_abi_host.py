@@ -191,3 +191,32 @@ def test_ssd_rejects_overlapping_buffers():
     assert call(ws=h0) == 5               # workspace is h0
     assert call(h0=fin + 256) == 5        # h0 partly overlaps the final state
 
+
+def test_fwd_bwd_reject_overlapping_buffers():
+    """ss_fwd: y may only be u, delta or z itself, other outputs overlap nothing; ss_bwd: no
+    output or workspace overlaps any buffer.  Every case returns before any HIP call."""
+    lib = ss.load_library()
+    p = _prob(batch=2, dim=40, seqlen=300)
+    G = 1 << 32
+    u, dl, A, Bm, Cm, y, last, ck, h0 = (G * k for k in range(1, 10))
+    assert _fwd(p, u=u, delta=dl, A=A, Bm=Bm, Cm=Cm, y=Bm) == 5              # y is B
+    assert _fwd(p, u=u, delta=dl, A=A, Bm=Bm, Cm=Cm, y=u + 16) == 5          # y partly overlaps u
+    assert _fwd(p, u=u, delta=dl, A=A, Bm=Bm, Cm=Cm, y=y, h0=h0, last=h0) == 5   # final state over h0
+    assert _fwd(p, u=u, delta=dl, A=A, Bm=Bm, Cm=Cm, y=y, ckpt=y + 64) == 5  # checkpoints inside y
+    wsz = lib.ss_bwd_workspace_size(ctypes.byref(p))
+    names = ["u", "delta", "A", "Bm", "Cm", "D", "z", "bias", "seq_idx", "ckpt", "dy", "dlast", "du", "ddelta",
+             "dz", "dA", "dB", "dC", "dD", "dbias", "dh0", "ws"]
+    base = dict(zip(names, [G * (k + 1) for k in range(len(names))]))
+    for opt in ("D", "z", "bias", "seq_idx", "dlast", "dz", "dD", "dbias", "dh0"):
+        base[opt] = None
+
+    def bwd(**kw):
+        a = dict(base)
+        a.update(kw)
+        return lib.ss_bwd(ctypes.byref(p), *[a[k] for k in names], wsz, None)
+
+    assert bwd(du=base["u"]) == 5                  # no in-place gradient
+    assert bwd(dC=base["dB"] + 64) == 5            # dB and dC overlap
+    assert bwd(ws=base["dy"] + 1024) == 5          # workspace overlaps dy
+    assert bwd(dA=base["A"]) == 5                  # dA over A
+
