@@ -217,7 +217,8 @@ typedef struct ss_conv_problem {
  *                precede the row without conv_init): the window that
  *                ss_conv1d_step continues from ("mamba-metal" README: the
  *                conv1d sliding window is carried across calls).
- * Errors as ss_fwd; SS_ERR_UNSUPPORTED when W is outside 1..4 or out overlaps x.
+ * Errors as ss_fwd; SS_ERR_UNSUPPORTED when W is outside 1..4 or when out or
+ * conv_final overlaps another buffer.
  */
 ss_status ss_conv1d_fwd(const ss_conv_problem *p, const void *x, const float *w, const float *bias,
                         const int32_t *seq_idx, const float *conv_init, void *out, float *conv_final,

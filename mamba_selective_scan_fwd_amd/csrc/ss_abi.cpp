@@ -285,7 +285,16 @@ ss_status ss_conv1d_fwd(const ss_conv_problem* p, const void* x, const float* w,
   for (const void* q : ptrs)
     if (q && !aligned(q)) return SS_ERR_MISALIGNED;
   const size_t bytes = (size_t)(p->batch * p->dim * p->seqlen * elem_size(p->io_dtype));
-  if (overlaps(x, bytes, out, bytes)) return SS_ERR_UNSUPPORTED;
+  {
+    // no output shares a byte with an input or the other output (the window going out is
+    // written by a row's last time block while its first reads the window coming in)
+    const size_t win = (size_t)(p->batch * p->dim * (p->width - 1)) * sizeof(float);
+    const Span in[] = {{x, bytes}, {w, (size_t)(p->dim * p->width) * sizeof(float)},
+                       {bias, (size_t)p->dim * sizeof(float)}, {seq_idx, (size_t)(p->batch * p->seqlen) * 4},
+                       {conv_init, win}};
+    const Span outs[] = {{out, bytes}, {conv_final, win}};
+    if (conflict(in, outs)) return SS_ERR_UNSUPPORTED;
+  }
   ss::ConvParams k{};
   k.io = p->io_dtype; k.width = p->width; k.silu = p->silu != 0;
   k.x = x; k.w = w; k.bias = bias; k.seq_idx = seq_idx; k.conv_init = conv_init;

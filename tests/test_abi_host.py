@@ -220,3 +220,17 @@ def test_fwd_bwd_reject_overlapping_buffers():
     assert bwd(ws=base["dy"] + 1024) == 5          # workspace overlaps dy
     assert bwd(dA=base["A"]) == 5                  # dA over A
 
+
+def test_conv_rejects_overlapping_outputs():
+    """The window going out may not be the window coming in, nor overlap x or out."""
+    lib = ss.load_library()
+    p = ss.ss_conv_problem(2, 40, 300, 4, 0, 1, 0)
+    G = 1 << 32
+    x, w, out, win_in, win_out = (G * k for k in range(1, 6))
+    f = lambda **kw: lib.ss_conv1d_fwd(ctypes.byref(p), kw.get("x", x), w, None, None, kw.get("init", win_in),
+                                       kw.get("out", out), kw.get("final", win_out), None)
+    assert f(final=win_in) == 5          # in place: rejected (first and last time blocks race)
+    assert f(final=out + 256) == 5       # final window inside out
+    assert f(final=x) == 5               # final window over x
+    assert f(out=x + 4096) == 5          # out partly over x
+
