@@ -35,6 +35,7 @@
 // whose 4-channel sums each lane accumulates in registers over the
 // workgroup's channel loop, then one cross-wave sum and one global atomic per
 // element per workgroup (LDS float atomics serialise on gfx950).
+#include <atomic>
 #include <type_traits>
 
 #include "ss_device.h"
@@ -549,6 +550,25 @@ __global__ void __launch_bounds__(256) ss_bwd_reduce_kernel(const float* __restr
   }
 }
 
+// MAIN workgroups resident per CU: 76 KB of LDS and 232 VGPRs per lane
+// (2 waves per SIMD) each allow two.
+constexpr int64_t kMainPerCu = 2;
+
+// Compute units of the current device, asked once per device (256 if the
+// runtime cannot say).
+int64_t device_cus() {
+  static std::atomic<int64_t> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int64_t v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int n = 0;
+    v = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
 hipError_t zero_outputs(const BwdParams& p, hipStream_t st) {
   ZeroList z{};
   const int64_t nbc = p.batch * p.dstate * p.seqlen;
@@ -569,12 +589,24 @@ hipError_t launch_bwd_seq(const BwdParams& p, hipStream_t st) {
   const int64_t K = p.nchunks;
   hipError_t e = zero_outputs(p, st);  // every atomic target, before any kernel adds into it
   if (e != hipSuccess) return e;
-  // MAIN: channel blocks per workgroup chosen for enough workgroups to fill
-  // the chip (each workgroup adds its channel sums of dB/dC once per element)
+  // MAIN: the channel blocks of a (batch row, chunk) are split into `groups`
+  // workgroups.  All workgroups take the same time, so the kernel lasts
+  // ceil(workgroups / resident) rounds of `per` channel blocks each; each
+  // workgroup also adds its dB/dC channel sums atomically once per element, so
+  // more groups cost atomics.  Take the smallest group count (up to 16) whose
+  // round count x per is within 5% of the best.
   const int64_t bk = p.batch * K;
-  int64_t groups = (1024 + bk - 1) / bk;
-  if (groups > p.ch_blocks) groups = p.ch_blocks;
-  if (groups < 1) groups = 1;
+  const int64_t resident = kMainPerCu * device_cus();
+  auto makespan = [&](int64_t g) {
+    const int64_t per_g = (p.ch_blocks + g - 1) / g;
+    const int64_t g_eff = (p.ch_blocks + per_g - 1) / per_g;
+    return ((bk * g_eff + resident - 1) / resident) * per_g;
+  };
+  const int64_t gmax = p.ch_blocks < 16 ? p.ch_blocks : 16;
+  int64_t best = makespan(1);
+  for (int64_t g = 2; g <= gmax; ++g) best = makespan(g) < best ? makespan(g) : best;
+  int64_t groups = 1;
+  while (groups < gmax && makespan(groups) * 100 > best * 105) ++groups;
   const int64_t per = (p.ch_blocks + groups - 1) / groups;
   groups = (p.ch_blocks + per - 1) / per;
   const dim3 grid((uint32_t)(bk * groups));
