@@ -81,6 +81,37 @@ __device__ __forceinline__ typename mfma_t<IO>::V as_vec(u32x4v w) {
   return __builtin_bit_cast(typename mfma_t<IO>::V, w);
 }
 
+// Time-major tiles in LDS (row = step, W 16-bit columns, 16-byte chunks of a
+// row rotated by (row / 4) so that both the row writes and the transposing
+// reads below are free of bank conflicts).  Element offset of (row, col):
+template <int W>
+__device__ __forceinline__ int tm_off(int row, int col) {
+  return row * W + 8 * ((col >> 3) ^ ((row >> 2) & (W / 8 - 1))) + (col & 7);
+}
+// An MFMA operand fragment whose k axis is time, read from a time-major
+// tile with ds_read_b64_tr_b16 (gfx950; lane layout checked on the chip: in
+// each group of 16 lanes, lane i receives element i % 4 of the 4-element
+// reads of lanes i / 4 + 4q, q = 0..3).  Lane j of group g reads 4 columns
+// c0 + 4 (j % 4) .. + 3 of row r0 + 8 g + 4 h + j / 4 (h = 0, 1), so lane i
+// ends with column c0 + i at the 8 steps r0 + 8 g .. + 7: A[m = i][k] or
+// B[k][n = i] of v_mfma_f32_16x16x32.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+// For r0 a multiple of 32 the rotation does not depend on r0, so a lane's
+// read address is r0 * W plus a per-lane offset: tm_lane_off gives it (h = 0
+// for steps r0 + 8 g .. + 3, h = 1 for the next 4) and tm_frag reads the
+// fragment at tile + r0 * W.
+template <int W>
+__device__ __forceinline__ int tm_lane_off(int c0, int h, int lane) {
+  const int j = lane % 16, g = lane / 16;
+  return tm_off<W>(8 * g + 4 * h + j / 4, c0 + 4 * (j % 4));
+}
+__device__ __forceinline__ u32x4v tm_frag(const uint16_t* at, int off_lo, int off_hi) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(at + off_lo));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(at + off_hi));
+  return __builtin_bit_cast(u32x4v, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Delta of this thread's step and the inclusive cumulative sum cs of Delta * A
 // over the chunk (threads 0..255 = steps; steps past the sequence have Delta =
 // 0).  cs goes to sCs; every thread of the workgroup must call it (it holds
@@ -157,10 +188,10 @@ struct CbTile {
 // order with its slice of the state H[p][n] (64 x 32) in the accumulators:
 //   entry(c) = H   (stored in the I/O dtype for the output pass)
 //   H <- exp(cs_last) H + sum_j exp(cs_last - cs_j) Delta_j x_j B_j^T
-// The j-sum runs on the matrix cores with both operands staged transposed in
-// LDS (time contiguous); wave w holds rows p in [16w, 16w + 16).  The next
-// chunk's x, B and dt are loaded once this chunk's are in LDS, while it is
-// being multiplied.  The
+// The j-sum runs on the matrix cores: x * w and B are copied to LDS as
+// time-major rows and read back as operand fragments with the transposing LDS
+// read; wave w holds rows p in [16w, 16w + 16).  The next chunk's x, B and dt
+// are loaded once this chunk's are in LDS, while it is being multiplied.  The
 // waves of a group's workgroups (heads x slices x 4) also share out its C B^T
 // tiles, one per wave and chunk while there are waves enough; the first
 // tile's operands are loaded at the top of the chunk's iteration.
@@ -168,12 +199,11 @@ constexpr int kNS = 32;  // states per slice
 template <int IO, int N>
 __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) {
   using M = mfma_t<IO>;
-  constexpr int kXR = kQ + 8;  // LDS row: the chunk's 256 steps, padded (528 B keeps 16-byte reads aligned)
   constexpr int kSlices = N / kNS;
   __shared__ __attribute__((aligned(16))) float sW[kQ];
   __shared__ float sCs[kQ], sWave[4];
-  __shared__ __attribute__((aligned(16))) uint16_t sXT[kP][kXR];   // (x * w)^T: [p][j]
-  __shared__ __attribute__((aligned(16))) uint16_t sBT[kNS][kXR];  // B^T of the slice: [n][j]
+  __shared__ __attribute__((aligned(16))) uint16_t sX[kQ * kP];   // x * w, time-major (tm_off<64>)
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kQ * kNS];  // B of the slice, time-major (tm_off<32>)
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const int64_t lb = xcd_logical_block();  // the workgroups of one row's group share B in an XCD's L2
   const int s = (int)(lb % kSlices);
@@ -185,24 +215,21 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
   const char* bbase = static_cast<const char*>(p.Bm) + ((b * p.seqlen) * p.ngroups + g) * N * 2 + s * kNS * 2;
   const float A = p.A[h], bias = p.dt_bias ? p.dt_bias[h] : 0.0f;
 
-  // x: 512 items of 4 steps x 8 channels (two per thread), B: 256 items of 4 steps x 8 states
-  const int xj[2] = {tid / 8, (tid + kSsdThreads) / 8}, xc = tid % 8;
-  const int bj = tid / 4, bc = tid % 4;
-  u32x4v xr[2][4], br[4];
+  // x: 2048 16-byte pieces (step tid / 8 + 32 k, channels 8 (tid % 8) ..), eight per thread;
+  // B: 1024 pieces (step tid / 4 + 64 k, states 8 (tid % 4) ..), four per thread
+  u32x4v xr[8], br[4];
   float dtr = 0.0f;
   auto load_chunk = [&](int64_t c) {
     const int64_t t0 = c * kQ;
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < 8; ++k) {
+      const int64_t t = t0 + tid / 8 + 32 * k;
+      xr[k] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(xbase + t * xrow + (tid % 8) * 16) : u32x4v{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t t = t0 + 4 * xj[k] + r;
-        xr[k][r] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(xbase + t * xrow + xc * 16) : u32x4v{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t t = t0 + 4 * bj + r;
-      br[r] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(bbase + t * brow + bc * 16) : u32x4v{0u, 0u, 0u, 0u};
+    for (int k = 0; k < 4; ++k) {
+      const int64_t t = t0 + tid / 4 + 64 * k;
+      br[k] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(bbase + t * brow + (tid % 4) * 16) : u32x4v{0u, 0u, 0u, 0u};
     }
     dtr = t0 + tid < p.seqlen ? load_io<IO>(p.dt, (b * p.seqlen + t0 + tid) * p.nheads + h) : 0.0f;
   };
@@ -216,6 +243,10 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
     for (int r = 0; r < 4; ++r)
       acc[nt][r] = p.h0 ? p.h0[hbase + (16 * wave + 4 * (lane / 16) + r) * N + kNS * s + 16 * nt + lane % 16] : 0.0f;
   const int cb_slot = (int)(((h % hpg) * kSlices + s) * 4 + wave), cb_slots = (int)(hpg * kSlices * 4);
+  // per-lane offsets of the fragment reads: x at channels 16 w .., B at states 16 nt ..
+  const int xo0 = tm_lane_off<kP>(16 * wave, 0, lane), xo1 = tm_lane_off<kP>(16 * wave, 1, lane);
+  const int bo[2][2] = {{tm_lane_off<kNS>(0, 0, lane), tm_lane_off<kNS>(0, 1, lane)},
+                        {tm_lane_off<kNS>(16, 0, lane), tm_lane_off<kNS>(16, 1, lane)}};
 
   load_chunk(0);
   for (int64_t c = 0; c < p.nchunks; ++c) {
@@ -227,33 +258,19 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
     sW[tid] = exp2_hw((cs_last - sCs[tid]) * kLog2e) * delta;  // 0 past the sequence (Delta = 0)
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {  // (x * w)^T
-      uint32_t v[4][4];
+    for (int k = 0; k < 8; ++k) {  // x * w, one step per piece
+      const int row = tid / 8 + 32 * k;
+      const float sc = sW[row];
+      u32x4v v;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float sc = sW[4 * xj[k] + r];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          v[r][q] = pack2<IO>(bits_f32<IO>((raw_t<IO>)(xr[k][r][q] & 0xffffu)) * sc,
-                              bits_f32<IO>((raw_t<IO>)(xr[k][r][q] >> 16)) * sc);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int q = e / 2, sh = 16 * (e % 2);
-        uint2 pk;
-        pk.x = ((v[0][q] >> sh) & 0xffffu) | (((v[1][q] >> sh) & 0xffffu) << 16);
-        pk.y = ((v[2][q] >> sh) & 0xffffu) | (((v[3][q] >> sh) & 0xffffu) << 16);
-        *reinterpret_cast<uint2*>(&sXT[8 * xc + e][4 * xj[k]]) = pk;
-      }
+      for (int q = 0; q < 4; ++q)
+        v[q] = pack2<IO>(bits_f32<IO>((raw_t<IO>)(xr[k][q] & 0xffffu)) * sc,
+                         bits_f32<IO>((raw_t<IO>)(xr[k][q] >> 16)) * sc);
+      *reinterpret_cast<u32x4v*>(&sX[tm_off<kP>(row, 8 * (tid % 8))]) = v;
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {  // B^T
-      const int q = e / 2, sh = 16 * (e % 2);
-      uint2 pk;
-      pk.x = ((br[0][q] >> sh) & 0xffffu) | (((br[1][q] >> sh) & 0xffffu) << 16);
-      pk.y = ((br[2][q] >> sh) & 0xffffu) | (((br[3][q] >> sh) & 0xffffu) << 16);
-      *reinterpret_cast<uint2*>(&sBT[8 * bc + e][4 * bj]) = pk;
-    }
+    for (int k = 0; k < 4; ++k)
+      *reinterpret_cast<u32x4v*>(&sB[tm_off<kNS>(tid / 4 + 64 * k, 8 * (tid % 4))]) = br[k];
     __syncthreads();
     if (c + 1 < p.nchunks) load_chunk(c + 1);  // lands while chunk c is multiplied
 
@@ -269,11 +286,10 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
     for (int nt = 0; nt < 2; ++nt) acc[nt] *= decay;
 #pragma unroll
     for (int ks = 0; ks < kQ; ks += 32) {
-      const int k0 = ks + 8 * (lane / 16);
-      const u32x4v a = *reinterpret_cast<const u32x4v*>(&sXT[16 * wave + lane % 16][k0]);
+      const u32x4v a = tm_frag(sX + ks * kP, xo0, xo1);  // A[m = p][k = step]
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const u32x4v bb = *reinterpret_cast<const u32x4v*>(&sBT[16 * nt + lane % 16][k0]);
+        const u32x4v bb = tm_frag(sB + ks * kNS, bo[nt][0], bo[nt][1]);  // B[k = step][n]
         acc[nt] = M::run(as_vec<IO>(a), as_vec<IO>(bb), acc[nt]);
       }
     }
