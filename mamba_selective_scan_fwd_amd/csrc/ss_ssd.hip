@@ -327,13 +327,12 @@ constexpr int kScanThreads = 512;
 template <int IO, int N>
 __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) {
   using M = mfma_t<IO>;
-  constexpr int kXR = kQ + 8;  // x^T row: 264 elements (528 B keeps 16-byte reads aligned)
   constexpr int kHR = N + 8;   // H_in row
   __shared__ __attribute__((aligned(16))) float sDelta[kQ];
   __shared__ __attribute__((aligned(16))) float sCs[kQ];
   __shared__ __attribute__((aligned(16))) float sWp[kQ];           // exp(cs_e - cs_j) Delta_j, e = end of j's piece
   __shared__ float sWave[4];
-  __shared__ __attribute__((aligned(16))) uint16_t sXT[kP][kXR];   // x^T of the chunk: [p][j]
+  __shared__ __attribute__((aligned(16))) uint16_t sX[kQ * kP];    // x of the chunk, time-major (tm_off<64>)
   __shared__ __attribute__((aligned(16))) uint16_t sH[kP][kHR];    // entry state H_in[p][n]
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const int64_t lb = xcd_logical_block();  // the heads of one chunk run on one XCD and share its C, CB in L2
@@ -351,12 +350,11 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
   const uint16_t* Hin = p.ws_entry + ((b * p.nchunks + c) * p.nheads + h) * (int64_t)(kP * N);
 
   // ---- prologue: issue every operand load, then scan Delta A and fill LDS
-  const int pc = tid / 128, jq = (tid % 128) / 8, co = tid % 8;  // x item: steps 64 pc + 4 jq .. + 3, channels 8 co ..
-  u32x4v xr[4];
+  u32x4v xr[4];  // 16-byte pieces of x: step tid / 8 + 64 k, channels 8 (tid % 8) ..
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t t = t0 + 64 * pc + 4 * jq + r;
-    xr[r] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(xbase + t * xrow + co * 16) : u32x4v{0u, 0u, 0u, 0u};
+  for (int k = 0; k < 4; ++k) {
+    const int64_t t = t0 + tid / 8 + 64 * k;
+    xr[k] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(xbase + t * xrow + (tid % 8) * 16) : u32x4v{0u, 0u, 0u, 0u};
   }
   constexpr int kHPieces = kP * (N / 8);  // 16-byte pieces of H_in
   constexpr int kHItems = (kHPieces + kScanThreads - 1) / kScanThreads;
@@ -379,15 +377,9 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
 #pragma unroll
     for (int ks = 0; ks < N / 32; ++ks) cf[q][ks] = cfrag(t0 + 32 * blk[q] + 16 * half + lane % 16, 32 * ks + 8 * (lane / 16));
 
-  // x^T and H_in into LDS, then Delta and its cumulative sum (threads 0..255 = steps)
+  // x and H_in into LDS, then Delta and its cumulative sum (threads 0..255 = steps)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int q = e / 2, sh = 16 * (e % 2);
-    uint2 pk;
-    pk.x = ((xr[0][q] >> sh) & 0xffffu) | (((xr[1][q] >> sh) & 0xffffu) << 16);
-    pk.y = ((xr[2][q] >> sh) & 0xffffu) | (((xr[3][q] >> sh) & 0xffffu) << 16);
-    *reinterpret_cast<uint2*>(&sXT[8 * co + e][64 * pc + 4 * jq]) = pk;
-  }
+  for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4v*>(&sX[tm_off<kP>(tid / 8 + 64 * k, 8 * (tid % 8))]) = xr[k];
 #pragma unroll
   for (int k = 0; k < kHItems; ++k) {
     const int item = tid + kScanThreads * k;
@@ -493,8 +485,9 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
         for (int e = 0; e < 4; ++e)
           bop[e] = pack2<IO>(m[2 * e], m[2 * e + 1]);
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          const u32x4v xa = *reinterpret_cast<const u32x4v*>(&sXT[16 * pt + lane % 16][j0]);
+        for (int pt = 0; pt < 4; ++pt) {  // A[m = p][k = step] = x^T, from the time-major tile
+          const u32x4v xa = tm_frag(sX + (jb + 32 * ks) * kP, tm_lane_off<kP>(16 * pt, 0, lane),
+                                    tm_lane_off<kP>(16 * pt, 1, lane));
           acc[q][pt] = M::run(as_vec<IO>(xa), as_vec<IO>(bop), acc[q][pt]);
         }
       }
@@ -512,6 +505,8 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
     for (int pt = 0; pt < 4; ++pt) {
       const int p0 = 16 * pt + 4 * (lane / 16);
       const uint32_t zw[2] = {zv[q][pt].x, zv[q][pt].y};
+      const uint2 xv = *reinterpret_cast<const uint2*>(&sX[tm_off<kP>(il, p0)]);  // x of channels p0 .. p0 + 3
+      const uint32_t xw[2] = {xv.x, xv.y};
       uint32_t yw[2];
 #pragma unroll
       for (int hw = 0; hw < 2; ++hw) {
@@ -519,7 +514,7 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           const int r = 2 * hw + s2;
-          float yv = fmaf(Dh, bits_f32<IO>((raw_t<IO>)sXT[p0 + r][il]), acc[q][pt][r]);
+          float yv = fmaf(Dh, bits_f32<IO>((raw_t<IO>)((xw[hw] >> (16 * s2)) & 0xffffu)), acc[q][pt][r]);
           if (p.z) yv *= silu_f(bits_f32<IO>((raw_t<IO>)((zw[hw] >> (16 * s2)) & 0xffffu)));
           yy[s2] = yv;
         }
