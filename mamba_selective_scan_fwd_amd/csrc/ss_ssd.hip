@@ -27,8 +27,9 @@
 // MFMA: v_mfma_f32_16x16x32_{bf16,f16}, fp32 accumulation.  Operand lane
 // layout (checked on the chip): A[m][k] in lane m + 16 (k / 8), element k % 8;
 // B[k][n] in lane n + 16 (k / 8), element k % 8; D[m][n] in lane
-// n + 16 (m / 4), element m % 4.  Operands whose k axis is time are staged
-// transposed in LDS (time is the slow axis in memory).
+// n + 16 (m / 4), element m % 4.  Operands whose k axis is time (x, B) are
+// copied to LDS as time-major rows, the layout they have in memory, and read
+// back as fragments with the transposing LDS read (tm_frag).
 #include "ss_device.h"
 #include "ss_internal.h"
 
