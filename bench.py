@@ -91,10 +91,19 @@ def recorded_traffic():
     return float(m_bytes.group(1))
 
 
-def timed(fn, reps, stream):
-    """Average ms per call of fn() over reps calls, HIP events on the launch stream."""
+def timed(fn, reps, stream, warm_s=0.12):
+    """Average ms per call of fn() over reps calls, HIP events on the launch stream, after
+    ~warm_s of untimed calls: the GPU needs ~100 ms of load to reach its working clock, and
+    it idles while the host prepares the next workload."""
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while n < 2 or time.perf_counter() - t0 < warm_s:
+        fn(n)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(reps):
