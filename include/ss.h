@@ -7,7 +7,10 @@
  * call validates its arguments on the host first and returns an error code
  * without touching the GPU when they are invalid; otherwise it enqueues its
  * kernels on `stream` (a hipStream_t, NULL = the null stream) and returns
- * without synchronising.  A failed launch returns SS_ERR_HIP.
+ * without synchronising.  A failed launch returns SS_ERR_HIP.  Beside the
+ * scan (forward, decode step, backward) it exports the depthwise causal
+ * conv1d + SiLU that feeds the scan, and the Mamba-2 SSD chunked scan on the
+ * matrix cores, each declared below with its own layouts.
  *
  * Problem (page "Mamba", Part IV Stage 5, the selective_scan_fn interface):
  *   per batch row b, channel d (d < dim = d_inner) and state n (n < dstate):
@@ -23,7 +26,8 @@
  *   README, "seq_idx strict reset") the state is zero before every step t >= 1
  *   whose document id seq_idx[b,t] differs from seq_idx[b,t-1].
  *
- * Layouts: every tensor is C-contiguous with the time axis innermost:
+ * Layouts of the scan (the SSD below keeps Mamba-2's time-major ones): every
+ * tensor is C-contiguous with the time axis innermost:
  *   u, delta, z, y, dy, du, ddelta, dz : (batch, dim, seqlen)   io dtype
  *   Bm, Cm, dB, dC                     : (batch, dstate, seqlen) io dtype (dB, dC: fp32)
  *   A, dA                              : (dim, dstate)  fp32
