@@ -143,6 +143,36 @@ __device__ __forceinline__ float chunk_cumsum(const SsdParams& p, float dt_raw, 
   return delta;
 }
 
+// cs for the whole chunk in every wave from the chunk's Delta (sDelta, one
+// value per step): lane l takes steps 4 l .. 4 l + 3, sums them in order, and
+// an inclusive scan of the lane totals (DPP row shifts 1, 2, 4, 8, then row
+// broadcasts 15 and 31) gives each lane the sum of the steps before its own.
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ float dpp_scan_step(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, BOUND_ZERO));
+}
+__device__ __forceinline__ void wave_chunk_cumsum(const float* sDelta, float A, float (&delta)[4], float (&cs)[4]) {
+  const int lane = threadIdx.x % 64;
+  const float4 d4 = *reinterpret_cast<const float4*>(&sDelta[4 * lane]);
+  delta[0] = d4.x; delta[1] = d4.y; delta[2] = d4.z; delta[3] = d4.w;
+  float run = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    run = fmaf(delta[e], A, run);
+    cs[e] = run;
+  }
+  float v = run;
+  v += dpp_scan_step<0x111, 0xf, true>(v);   // row_shr:1
+  v += dpp_scan_step<0x112, 0xf, true>(v);   // row_shr:2
+  v += dpp_scan_step<0x114, 0xf, true>(v);   // row_shr:4
+  v += dpp_scan_step<0x118, 0xf, true>(v);   // row_shr:8
+  v += dpp_scan_step<0x142, 0xa, false>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_scan_step<0x143, 0xc, false>(v);  // row_bcast:31 into rows 2 and 3
+  const float before = v - run;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) cs[e] += before;
+}
+
 // ---- C B^T of a chunk, once per group -------------------------------------------
 // CB[i][j] = sum_n C_i[n] B_j[n] in fp32 for the chunk's rows i and the columns j
 // of every 64-step piece up to the one holding i (the causal half plus the rest
@@ -202,7 +232,7 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
   using M = mfma_t<IO>;
   constexpr int kSlices = N / kNS;
   __shared__ __attribute__((aligned(16))) float sW[kQ];
-  __shared__ float sCs[kQ], sWave[4];
+  __shared__ __attribute__((aligned(16))) float sDelta[kQ];
   __shared__ __attribute__((aligned(16))) uint16_t sX[kQ * kP];   // x * w, time-major (tm_off<64>)
   __shared__ __attribute__((aligned(16))) uint16_t sB[kQ * kNS];  // B of the slice, time-major (tm_off<32>)
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
@@ -219,7 +249,7 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
   // x: 2048 16-byte pieces (step tid / 8 + 32 k, channels 8 (tid % 8) ..), eight per thread;
   // B: 1024 pieces (step tid / 4 + 64 k, states 8 (tid % 4) ..), four per thread
   u32x4v xr[8], br[4];
-  float dtr = 0.0f;
+  float dtr = 0.0f;  // dt of step tid
   auto load_chunk = [&](int64_t c) {
     const int64_t t0 = c * kQ;
 #pragma unroll
@@ -254,9 +284,26 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
     const int64_t t0 = c * kQ;
     CbTile<IO, N> cbt;
     if (cb_slot < kCbTiles) cbt.load(p, b, c, g, cb_slot, lane);
-    const float delta = chunk_cumsum<IO>(p, dtr, t0 + tid < p.seqlen, A, bias, sCs, sWave);  // barriers
-    const float cs_last = sCs[kQ - 1];
-    sW[tid] = exp2_hw((cs_last - sCs[tid]) * kLog2e) * delta;  // 0 past the sequence (Delta = 0)
+    {  // Delta of step tid (0 past the sequence)
+      float d = 0.0f;
+      if (t0 + tid < p.seqlen) {
+        const float xd = dtr + bias;
+        d = p.softplus ? softplus_f(xd) : xd;
+      }
+      sDelta[tid] = d;
+    }
+    __syncthreads();
+    float delta[4], cs[4];
+    wave_chunk_cumsum(sDelta, A, delta, cs);
+    const float cs_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs[3]), 63));
+    if (lane / 16 == wave) {  // this wave's quarter of the chunk: steps 4 lane .. 4 lane + 3
+      float4 w;
+      w.x = exp2_hw((cs_last - cs[0]) * kLog2e) * delta[0];  // 0 past the sequence (Delta = 0)
+      w.y = exp2_hw((cs_last - cs[1]) * kLog2e) * delta[1];
+      w.z = exp2_hw((cs_last - cs[2]) * kLog2e) * delta[2];
+      w.w = exp2_hw((cs_last - cs[3]) * kLog2e) * delta[3];
+      *reinterpret_cast<float4*>(&sW[4 * lane]) = w;
+    }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < 8; ++k) {  // x * w, one step per piece
