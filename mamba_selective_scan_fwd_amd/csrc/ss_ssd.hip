@@ -323,12 +323,12 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
     if (c + 1 < p.nchunks) load_chunk(c + 1);  // lands while chunk c is multiplied
 
     // entry state of chunk c, then H <- decay H + S_c
+    // stored [n][p]: the lane's 4 consecutive channels p of state n in one 8-byte store
     uint16_t* E = p.ws_entry + ((b * p.nchunks + c) * p.nheads + h) * (int64_t)(kP * N);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        E[(16 * wave + 4 * (lane / 16) + r) * N + kNS * s + 16 * nt + lane % 16] = bits16<IO>(acc[nt][r]);
+      *reinterpret_cast<uint2*>(&E[(kNS * s + 16 * nt + lane % 16) * kP + 16 * wave + 4 * (lane / 16)]) =
+          make_uint2(pack2<IO>(acc[nt][0], acc[nt][1]), pack2<IO>(acc[nt][2], acc[nt][3]));
     const float decay = exp2_hw(cs_last * kLog2e);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[nt] *= decay;
@@ -375,13 +375,12 @@ constexpr int kScanThreads = 512;
 template <int IO, int N>
 __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) {
   using M = mfma_t<IO>;
-  constexpr int kHR = N + 8;   // H_in row
   __shared__ __attribute__((aligned(16))) float sDelta[kQ];
   __shared__ __attribute__((aligned(16))) float sCs[kQ];
   __shared__ __attribute__((aligned(16))) float sWp[kQ];           // exp(cs_e - cs_j) Delta_j, e = end of j's piece
   __shared__ float sWave[4];
   __shared__ __attribute__((aligned(16))) uint16_t sX[kQ * kP];    // x of the chunk, time-major (tm_off<64>)
-  __shared__ __attribute__((aligned(16))) uint16_t sH[kP][kHR];    // entry state H_in[p][n]
+  __shared__ __attribute__((aligned(16))) uint16_t sH[N * kP];     // entry state H_in, rows n of 64 p (tm_off<64>)
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const int64_t lb = xcd_logical_block();  // the heads of one chunk run on one XCD and share its C, CB in L2
   const int64_t h = lb % p.nheads;
@@ -404,14 +403,13 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
     const int64_t t = t0 + tid / 8 + 64 * k;
     xr[k] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(xbase + t * xrow + (tid % 8) * 16) : u32x4v{0u, 0u, 0u, 0u};
   }
-  constexpr int kHPieces = kP * (N / 8);  // 16-byte pieces of H_in
+  constexpr int kHPieces = N * (kP / 8);  // 16-byte pieces of H_in (stored [n][p])
   constexpr int kHItems = (kHPieces + kScanThreads - 1) / kScanThreads;
   u32x4v hr[kHItems];
 #pragma unroll
   for (int k = 0; k < kHItems; ++k) {
     const int item = tid + kScanThreads * k;
-    hr[k] = item < kHPieces ? *reinterpret_cast<const u32x4v*>(Hin + (item / (N / 8)) * N + 8 * (item % (N / 8)))
-                            : u32x4v{0u, 0u, 0u, 0u};
+    hr[k] = item < kHPieces ? *reinterpret_cast<const u32x4v*>(Hin + item * 8) : u32x4v{0u, 0u, 0u, 0u};
   }
   float dt_raw = 0.0f;
   if (tid < kQ && t0 + tid < p.seqlen) dt_raw = load_io<IO>(p.dt, (b * p.seqlen + t0 + tid) * p.nheads + h);
@@ -431,7 +429,7 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
 #pragma unroll
   for (int k = 0; k < kHItems; ++k) {
     const int item = tid + kScanThreads * k;
-    if (item < kHPieces) *reinterpret_cast<u32x4v*>(&sH[item / (N / 8)][8 * (item % (N / 8))]) = hr[k];
+    if (item < kHPieces) *reinterpret_cast<u32x4v*>(&sH[tm_off<kP>(item / 8, 8 * (item % 8))]) = hr[k];
   }
   {
     const float delta = chunk_cumsum<IO>(p, dt_raw, tid < kQ && t0 + tid < p.seqlen, p.A[h],
@@ -465,8 +463,8 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
 #pragma unroll
   for (int ks = 0; ks < N / 32; ++ks) {
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      const u32x4v hf = *reinterpret_cast<const u32x4v*>(&sH[16 * pt + lane % 16][32 * ks + 8 * (lane / 16)]);
+    for (int pt = 0; pt < 4; ++pt) {  // A[m = p][k = n] from the [n][p] tile
+      const u32x4v hf = tm_frag(sH + 32 * ks * kP, tm_lane_off<kP>(16 * pt, 0, lane), tm_lane_off<kP>(16 * pt, 1, lane));
 #pragma unroll
       for (int q = 0; q < 2; ++q) acc[q][pt] = M::run(as_vec<IO>(hf), as_vec<IO>(cf[q][ks]), acc[q][pt]);
     }
