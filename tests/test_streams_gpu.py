@@ -1,0 +1,99 @@
+"""Every entry point enqueues on the caller's stream: the same calls made on a side stream
+(default priority) give bit-identical results to the default stream's, and FwdCall /
+StepCall / ConvStepCall honour an explicit stream."""
+import pytest
+import torch
+
+from _util import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _ss():
+    from mamba_selective_scan_fwd_amd import ss
+    ss.load_library()
+    return ss
+
+
+def _scan_inputs(seed=21, Bsz=2, Dd=40, N=16, L=700):
+    g = torch.Generator().manual_seed(seed)
+    r = lambda *s: torch.randn(s, generator=g)
+    return dict(u=r(Bsz, Dd, L).cuda(), delta=(r(Bsz, Dd, L) * 0.5).cuda(), A=(-torch.rand(Dd, N, generator=g) * 4).cuda(),
+                Bm=r(Bsz, N, L).cuda(), Cm=r(Bsz, N, L).cuda(), D=r(Dd).cuda(), z=r(Bsz, Dd, L).cuda(),
+                bias=(r(Dd) * 0.1).cuda(), dy=r(Bsz, Dd, L).cuda())
+
+
+def test_forward_backward_on_side_stream():
+    ss = _ss()
+    q = _scan_inputs()
+    kw = dict(D=q["D"], z=q["z"], delta_bias=q["bias"])
+    y0, l0, c0 = ss.fwd(q["u"], q["delta"], q["A"], q["Bm"], q["Cm"], return_ckpt=True, **kw)
+    g0 = ss.bwd(q["u"], q["delta"], q["A"], q["Bm"], q["Cm"], c0, q["dy"], **kw)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        y1, l1, c1 = ss.fwd(q["u"], q["delta"], q["A"], q["Bm"], q["Cm"], return_ckpt=True, **kw)
+        g1 = ss.bwd(q["u"], q["delta"], q["A"], q["Bm"], q["Cm"], c1, q["dy"], **kw)
+    side.synchronize()
+    say("side-stream forward/backward")
+    assert torch.equal(y0, y1) and torch.equal(l0, l1) and torch.equal(c0, c1)
+    for k in g0:
+        assert torch.allclose(g0[k], g1[k], rtol=1e-5, atol=1e-6), k   # float atomics: order may differ
+
+
+def test_prepared_calls_on_explicit_stream():
+    ss = _ss()
+    q = _scan_inputs(seed=22)
+    side = torch.cuda.Stream()
+    y0 = torch.empty_like(q["u"])
+    y1 = torch.empty_like(q["u"])
+    ss.FwdCall(q["u"], q["delta"], q["A"], q["Bm"], q["Cm"], D=q["D"], z=q["z"], delta_bias=q["bias"], y=y0)()
+    torch.cuda.synchronize()
+    call = ss.FwdCall(q["u"], q["delta"], q["A"], q["Bm"], q["Cm"], D=q["D"], z=q["z"], delta_bias=q["bias"], y=y1,
+                      stream=side)
+    call()
+    side.synchronize()
+    assert torch.equal(y0, y1)
+    # decode step and conv step, prepared on the side stream
+    Bsz, Dd, N = 2, 40, 16
+    st_a = torch.randn(Bsz, Dd, N, device="cuda")
+    st_b = st_a.clone()
+    u_t, d_t, z_t = (q[k][..., 0].contiguous() for k in ("u", "delta", "z"))
+    B_t, C_t = q["Bm"][..., 0].contiguous(), q["Cm"][..., 0].contiguous()
+    ya, _ = ss.step(u_t, d_t, q["A"], B_t, C_t, st_a, D=q["D"], z_t=z_t, delta_bias=q["bias"], state_out=st_a)
+    yb = torch.empty_like(u_t)
+    torch.cuda.synchronize()
+    ss.StepCall(u_t, d_t, q["A"], B_t, C_t, st_b, D=q["D"], z_t=z_t, delta_bias=q["bias"], y=yb, stream=side)()
+    side.synchronize()
+    assert torch.equal(ya, yb) and torch.equal(st_a, st_b)
+    w = torch.randn(Dd, 4, device="cuda") * 0.5
+    win_a = torch.randn(Bsz, Dd, 3, device="cuda")
+    win_b = win_a.clone()
+    oa, _ = ss.conv1d_step(u_t, w, win_a)
+    ob = torch.empty_like(u_t)
+    torch.cuda.synchronize()
+    ss.ConvStepCall(u_t, w, win_b, ob, stream=side)()
+    side.synchronize()
+    assert torch.equal(oa, ob) and torch.equal(win_a, win_b)
+
+
+def test_conv_and_ssd_on_side_stream():
+    ss = _ss()
+    g = torch.Generator().manual_seed(23)
+    x = torch.randn(2, 40, 900, generator=g).half().cuda()
+    w = (torch.randn(40, 4, generator=g) * 0.5).cuda()
+    o0 = ss.conv1d(x, w)
+    sx = torch.randn(1, 600, 4, 64, generator=g).bfloat16().cuda()
+    sdt = (torch.randn(1, 600, 4, generator=g) * 0.5).bfloat16().cuda()
+    sB = torch.randn(1, 600, 2, 64, generator=g).bfloat16().cuda()
+    sC = torch.randn(1, 600, 2, 64, generator=g).bfloat16().cuda()
+    sA = -torch.rand(4, generator=g).cuda() * 4
+    s0 = ss.ssd_fwd(sx, sdt, sA, sB, sC)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        o1 = ss.conv1d(x, w)
+        s1 = ss.ssd_fwd(sx, sdt, sA, sB, sC)
+    side.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(s0, s1)
