@@ -97,3 +97,56 @@ def test_conv_and_ssd_on_side_stream():
         s1 = ss.ssd_fwd(sx, sdt, sA, sB, sC)
     side.synchronize()
     assert torch.equal(o0, o1) and torch.equal(s0, s1)
+
+
+def test_graph_replays_match_eager():
+    """Decode steps and a forward captured in a HIP graph (the serving pattern) and replayed
+    three times, with eager work and a state reset between replays: every replay equals
+    the eager results bit for bit (no memset node is ever recorded)."""
+    ss = _ss()
+    q = _scan_inputs(seed=24)
+    Bsz, Dd, N = 2, 40, 16
+    toks = [{k: q[k][..., t].contiguous() for k in ("u", "delta", "z")} for t in range(8)]
+    for t, tok in enumerate(toks):
+        tok["B"], tok["C"] = q["Bm"][..., t].contiguous(), q["Cm"][..., t].contiguous()
+    st0 = torch.randn(Bsz, Dd, N, device="cuda")
+    st_e = st0.clone()
+    ys_e = []
+    for tok in toks:
+        y, _ = ss.step(tok["u"], tok["delta"], q["A"], tok["B"], tok["C"], st_e, D=q["D"], z_t=tok["z"],
+                       delta_bias=q["bias"], state_out=st_e)
+        ys_e.append(y.clone())
+    yf_e = ss.fwd(q["u"], q["delta"], q["A"], q["Bm"], q["Cm"], D=q["D"], z=q["z"], delta_bias=q["bias"])[0]
+    torch.cuda.synchronize()
+
+    st = st0.clone()
+    ys = [torch.empty_like(toks[0]["u"]) for _ in toks]
+    yf = torch.empty_like(q["u"])
+
+    def steps():
+        for tok, y in zip(toks, ys):
+            ss.step(tok["u"], tok["delta"], q["A"], tok["B"], tok["C"], st, D=q["D"], z_t=tok["z"],
+                    delta_bias=q["bias"], state_out=st, y=y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        steps()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps()
+        ss.FwdCall(q["u"], q["delta"], q["A"], q["Bm"], q["Cm"], D=q["D"], z=q["z"], delta_bias=q["bias"], y=yf,
+                   stream=torch.cuda.current_stream())()
+    for rep in range(3):
+        st.copy_(st0)
+        yf.zero_()
+        junk = torch.randn(1 << 16, device="cuda").mul_(2.0).sum()  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        say("graph replay %d" % rep)
+        for y, ye in zip(ys, ys_e):
+            assert torch.equal(y, ye)
+        assert torch.equal(st, st_e) and torch.equal(yf, yf_e)
