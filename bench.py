@@ -149,8 +149,21 @@ def bench_headline(steps, warmup, stream):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = starts[0].elapsed_time(stops[-1]) / steps
-    kernel_ms = sum(a.elapsed_time(b) for a, b in zip(starts, stops)) / steps
-    return ms, kernel_ms, wall, (Bsz, Dd, N, L), sets, ys
+    per_launch = sorted(a.elapsed_time(b) for a, b in zip(starts, stops))
+    kernel_ms = sum(per_launch) / steps
+    stats = {"kernel_ms_median": per_launch[steps // 2], "kernel_ms_min": per_launch[0],
+             "kernel_ms_max": per_launch[-1]}
+    # warm figure, labelled as such: one input set called back to back, so the
+    # MALL can hold part of it; never the reported value
+    warm = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    reps = max(10, steps // 4)
+    warm[0].record(stream)
+    for _ in range(reps):
+        calls[0]()
+    warm[1].record(stream)
+    torch.cuda.synchronize()
+    stats["warm_single_set_kernel_ms"] = warm[0].elapsed_time(warm[1]) / reps
+    return ms, kernel_ms, stats, wall, (Bsz, Dd, N, L), sets, ys
 
 
 def bench_rows(stream):
@@ -407,7 +420,7 @@ def main():
         print(json.dumps(out), flush=True)
         return
     log("headline: %d warmup + %d timed steps" % (args.warmup, args.steps))
-    ms, kernel_ms, wall, (Bsz, Dd, N, L), sets, ys = bench_headline(args.steps, args.warmup, stream)
+    ms, kernel_ms, stats, wall, (Bsz, Dd, N, L), sets, ys = bench_headline(args.steps, args.warmup, stream)
     del sets, ys
     torch.cuda.empty_cache()
     tc = Bsz * Dd * L
@@ -438,6 +451,7 @@ def main():
                      "traffic": traffic,
                      "kernel": "ss_fwd_chunk_kernel<f16, FINAL>",
                      "kernel_ms": kernel_ms,
+                     **stats,
                      "alg_slots_per_launch": alg_slots},
         "hbm": {"alg_bytes_per_launch": alg_bytes, "achieved_GBps": alg_bytes / (kernel_ms * 1e-3) / 1e9,
                 "peak_GBps": PEAK_HBM_GBPS, "frac": alg_bytes / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
@@ -446,6 +460,7 @@ def main():
     }
     try:
         result["copy_probe_GBps"] = copy_probe(stream)
+        result["hbm"]["frac_of_copy_probe"] = result["hbm"]["achieved_GBps"] / result["copy_probe_GBps"]
     except Exception as e:
         result["copy_probe_error"] = str(e)[:200]
     if not args.no_rows:
