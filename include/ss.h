@@ -269,7 +269,8 @@ typedef struct ss_ssd_problem {
 
 /* Bytes of device workspace ss_ssd_fwd needs: per 256-step chunk of every
  * (batch row, head), the state entering the chunk (headdim x dstate, io
- * dtype); per chunk of every (batch row, group), C B^T (256 x 256 fp32).  The
+ * dtype); per chunk of every (batch row, group), C B^T (256 x 256, fp32 sums
+ * stored as bf16).  The
  * caller owns it; its contents on entry do not matter.  Returns 0 for an
  * invalid problem. */
 size_t ss_ssd_workspace_size(const ss_ssd_problem *p);

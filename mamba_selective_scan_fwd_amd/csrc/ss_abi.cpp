@@ -347,7 +347,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 size_t ssd_cb_bytes(const ss_ssd_problem* p) {
   const int64_t nchunks = (p->seqlen + kSsdChunk - 1) / kSsdChunk;
-  return (size_t)(p->batch * nchunks * p->ngroups) * (size_t)(kSsdChunk * kSsdChunk) * 4;
+  return (size_t)(p->batch * nchunks * p->ngroups) * (size_t)(kSsdChunk * kSsdChunk) * 2;
 }
 
 size_t ss_ssd_workspace_size(const ss_ssd_problem* p) {
@@ -395,7 +395,7 @@ ss_status ss_ssd_fwd(const ss_ssd_problem* p, const void* x, const void* dt, con
   k.y = y; k.final_state = final_state;
   char* ws = static_cast<char*>(workspace);
   k.ws_entry = reinterpret_cast<uint16_t*>(ws);
-  k.ws_cb = reinterpret_cast<float*>(ws + align256(e * 2));
+  k.ws_cb = reinterpret_cast<uint16_t*>(ws + align256(e * 2));
   k.batch = p->batch; k.seqlen = p->seqlen; k.nheads = p->nheads; k.ngroups = p->ngroups; k.dstate = p->dstate;
   k.nchunks = (p->seqlen + kSsdChunk - 1) / kSsdChunk;
   return from_hip(ss::launch_ssd(k, static_cast<hipStream_t>(stream)));

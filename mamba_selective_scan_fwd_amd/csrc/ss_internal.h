@@ -131,7 +131,7 @@ struct SsdParams {
   float* final_state;    // (batch, nheads, 64, dstate) or null
   // workspace
   uint16_t* ws_entry;    // (batch, nchunks, nheads, dstate, 64), I/O dtype bits: each chunk's entry state, [n][p]
-  float* ws_cb;          // (batch, nchunks, ngroups, 256, 256) fp32: C B^T of each chunk
+  uint16_t* ws_cb;       // (batch, nchunks, ngroups, 256, 256) bf16: C B^T of each chunk
   int64_t batch, seqlen, nheads, ngroups, dstate, nchunks;
 };
 

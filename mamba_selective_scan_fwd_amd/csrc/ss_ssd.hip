@@ -174,7 +174,7 @@ __device__ __forceinline__ void wave_chunk_cumsum(const float* sDelta, float A, 
 }
 
 // ---- C B^T of a chunk, once per group -------------------------------------------
-// CB[i][j] = sum_n C_i[n] B_j[n] in fp32 for the chunk's rows i and the columns j
+// CB[i][j] = sum_n C_i[n] B_j[n] (fp32 sums, stored as bf16) for the chunk's rows i and the columns j
 // of every 64-step piece up to the one holding i (the causal half plus the rest
 // of the diagonal pieces, so the output pass never reads an unwritten value):
 // 160 tiles of 16 x 16.  Tile idx: row band R = rt / 4 holds 4 (R + 1) column
@@ -204,13 +204,15 @@ struct CbTile {
     }
   }
   __device__ __forceinline__ void finish(const SsdParams& p, int64_t b_, int64_t c, int64_t g, int lane) {
+    // the tile transposed, (B C^T)[j][i], so that a lane holds 4 consecutive
+    // columns j = 16 jt + 4 (lane / 16) + r of one row i = 16 rt + lane % 16:
+    // one 8-byte bf16 store per lane
     f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int ks = 0; ks < N / 32; ++ks) acc = mfma_t<IO>::run(as_vec<IO>(a[ks]), as_vec<IO>(b[ks]), acc);
-    // lane holds rows i = 16 rt + 4 (lane / 16) + r of column j = 16 jt + lane % 16
-    float* CB = p.ws_cb + ((b_ * p.nchunks + c) * p.ngroups + g) * (int64_t)(kQ * kQ);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) CB[(16 * rt + 4 * (lane / 16) + r) * kQ + 16 * jt + lane % 16] = acc[r];
+    for (int ks = 0; ks < N / 32; ++ks) acc = mfma_t<IO>::run(as_vec<IO>(b[ks]), as_vec<IO>(a[ks]), acc);
+    uint16_t* CB = p.ws_cb + ((b_ * p.nchunks + c) * p.ngroups + g) * (int64_t)(kQ * kQ);
+    *reinterpret_cast<uint2*>(CB + (16 * rt + lane % 16) * kQ + 16 * jt + 4 * (lane / 16)) =
+        make_uint2(pack2<SS_BF16>(acc[0], acc[1]), pack2<SS_BF16>(acc[2], acc[3]));
   }
 };
 
@@ -479,33 +481,40 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
   __syncthreads();  // sDelta, sWp
 
   // ---- Y_diag += x^T M^T, piece by piece
-  const float* CBbase = p.ws_cb + ((b * p.nchunks + c) * p.ngroups + g) * (int64_t)(kQ * kQ);
+  const uint16_t* CBbase = p.ws_cb + ((b * p.nchunks + c) * p.ngroups + g) * (int64_t)(kQ * kQ);
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int i = 32 * blk[q] + 16 * half + lane % 16;  // this lane's row (chunk-local)
-    const int dpiece = 32 * blk[q] / kJB;               // the piece holding the block's rows
+    const int dpiece = 32 * blk[q] / kJB;               // the piece holding the block's rows (at most 3)
     const float csi = sCs[i];
-    const float* cbrow = CBbase + i * kQ + 8 * (lane / 16);
-    float4 nxt[4];
+    const uint16_t* cbrow = CBbase + i * kQ + 8 * (lane / 16);
+    // CB of each piece (8 bf16 columns per lane and k-step), loaded two pieces ahead
+    u32x4v cbv[kQ / kJB][2];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) nxt[k] = *reinterpret_cast<const float4*>(cbrow + 32 * (k / 2) + 4 * (k % 2));
-    for (int piece = 0; piece <= dpiece; ++piece) {
+    for (int pc = 0; pc < 2; ++pc)
+      if (pc <= dpiece)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) cbv[pc][ks] = *reinterpret_cast<const u32x4v*>(cbrow + kJB * pc + 32 * ks);
+#pragma unroll
+    for (int piece = 0; piece < kQ / kJB; ++piece) {
+      if (piece > dpiece) break;
       const int jb = kJB * piece;
-      float4 cur[4];
+      if (piece + 2 < kQ / kJB && piece + 2 <= dpiece) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) cur[k] = nxt[k];
-      if (piece < dpiece) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          nxt[k] = *reinterpret_cast<const float4*>(cbrow + jb + kJB + 32 * (k / 2) + 4 * (k % 2));
+        for (int ks = 0; ks < 2; ++ks)
+          cbv[piece + 2][ks] = *reinterpret_cast<const u32x4v*>(cbrow + jb + 2 * kJB + 32 * ks);
       }
       const bool diag = piece == dpiece;
       const float ei = exp2_hw((csi - sCs[jb + kJB - 1]) * kLog2e);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const int j0 = jb + 32 * ks + 8 * (lane / 16);
-        const float cb[8] = {cur[2 * ks].x, cur[2 * ks].y, cur[2 * ks].z, cur[2 * ks].w,
-                             cur[2 * ks + 1].x, cur[2 * ks + 1].y, cur[2 * ks + 1].z, cur[2 * ks + 1].w};
+        float cb[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {  // bf16 -> fp32: the high half of a 32-bit float
+          cb[2 * e] = __builtin_bit_cast(float, cbv[piece][ks][e] << 16);
+          cb[2 * e + 1] = __builtin_bit_cast(float, cbv[piece][ks][e] & 0xffff0000u);
+        }
         float m[8];
         if (diag) {
           const float4 c0 = *reinterpret_cast<const float4*>(&sCs[j0]);

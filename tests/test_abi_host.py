@@ -156,9 +156,9 @@ def test_ssd_workspace_and_validation():
     p = _ssd_prob()
     wsz = lib.ss_ssd_workspace_size(ctypes.byref(p))
     # 2 chunks of 256 steps x 2 rows x 4 heads: entry states (64 x 64) 16-bit;
-    # 2 chunks x 2 rows x 2 groups: C B^T (256 x 256) fp32
+    # 2 chunks x 2 rows x 2 groups: C B^T (256 x 256) bf16
     assert p.ngroups == 2
-    assert wsz == 16 * 4096 * 2 + 8 * 256 * 256 * 4
+    assert wsz == 16 * 4096 * 2 + 8 * 256 * 256 * 2
     assert lib.ss_ssd_fwd(ctypes.byref(p), *([FAKE] * 5), None, None, None, None, FAKE, None, FAKE, wsz - 1,
                           None) == 5
     assert lib.ss_ssd_fwd(ctypes.byref(p), None, *([FAKE] * 4), None, None, None, None, FAKE, None, FAKE, wsz,
