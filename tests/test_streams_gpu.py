@@ -150,3 +150,53 @@ def test_graph_replays_match_eager():
         for y, ye in zip(ys, ys_e):
             assert torch.equal(y, ye)
         assert torch.equal(st, st_e) and torch.equal(yf, yf_e)
+
+
+def test_graph_replays_conv_ssd_bwd():
+    """The conv, the SSD layer and the backward captured in one HIP graph and replayed three
+    times, with eager work between the replays: every replay equals the eager results (the
+    backward's float atomics to within rounding, everything else bit for bit)."""
+    ss = _ss()
+    q = _scan_inputs(seed=25)
+    kw = dict(D=q["D"], z=q["z"], delta_bias=q["bias"])
+    g = torch.Generator().manual_seed(26)
+    x = torch.randn(2, 40, 900, generator=g).half().cuda()
+    w = (torch.randn(40, 4, generator=g) * 0.5).cuda()
+    sx = torch.randn(1, 600, 4, 64, generator=g).bfloat16().cuda()
+    sdt = (torch.randn(1, 600, 4, generator=g) * 0.5).bfloat16().cuda()
+    sB = torch.randn(1, 600, 2, 64, generator=g).bfloat16().cuda()
+    sC = torch.randn(1, 600, 2, 64, generator=g).bfloat16().cuda()
+    sA = -torch.rand(4, generator=g).cuda() * 4
+    _, _, ck = ss.fwd(q["u"], q["delta"], q["A"], q["Bm"], q["Cm"], return_ckpt=True, **kw)
+
+    def work():
+        o = ss.conv1d(x, w)
+        s = ss.ssd_fwd(sx, sdt, sA, sB, sC, z=sx, D=sA)
+        gr = ss.bwd(q["u"], q["delta"], q["A"], q["Bm"], q["Cm"], ck, q["dy"], **kw)
+        return o, s, gr
+
+    o_e, s_e, g_e = work()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        work()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        o_g, s_g, g_g = work()
+    for rep in range(3):
+        for t in (o_g, s_g, *g_g.values()):
+            t.fill_(float("nan"))
+        junk = torch.randn(1 << 16, device="cuda").mul_(3.0).sum()  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        say("graph replay %d (conv, ssd, bwd)" % rep)
+        assert torch.equal(o_g, o_e) and torch.equal(s_g, s_e)
+        for k in g_e:
+            if k in ("du", "ddelta", "dz"):
+                assert torch.equal(g_g[k], g_e[k]), k
+            else:
+                assert torch.allclose(g_g[k], g_e[k], rtol=1e-5, atol=1e-6), k
