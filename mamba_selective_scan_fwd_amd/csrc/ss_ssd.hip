@@ -442,20 +442,6 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
     }
   }
 
-  // gate values for the epilogue: lane has channels 16 pt + 4 (lane / 16) .. + 3 of its step
-  uint2 zv[2][4];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int64_t t = t0 + 32 * blk[q] + 16 * half + lane % 16;
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
-      zv[q][pt] = (p.z && t < p.seqlen)
-                      ? *reinterpret_cast<const uint2*>(static_cast<const char*>(p.z) + t * xrow +
-                                                        ((b * p.seqlen) * p.nheads + h) * kP * 2 +
-                                                        (16 * pt + 4 * (lane / 16)) * 2)
-                      : make_uint2(0u, 0u);
-  }
-
   // ---- Y_off = H_in C^T, scaled by exp(cs_i)
   f32x4 acc[2][4];  // [block][p tile]: p = 16 pt + 4 (lane / 16) + r, i = 32 blk + 16 half + lane % 16
 #pragma unroll
@@ -476,6 +462,20 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
     const float sc = exp2_hw(sCs[32 * blk[q] + 16 * half + lane % 16] * kLog2e);
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) acc[q][pt] *= sc;
+  }
+
+  // gate values for the epilogue: lane has channels 16 pt + 4 (lane / 16) .. + 3 of its step
+  uint2 zv[2][4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t t = t0 + 32 * blk[q] + 16 * half + lane % 16;
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+      zv[q][pt] = (p.z && t < p.seqlen)
+                      ? *reinterpret_cast<const uint2*>(static_cast<const char*>(p.z) + t * xrow +
+                                                        ((b * p.seqlen) * p.nheads + h) * kP * 2 +
+                                                        (16 * pt + 4 * (lane / 16)) * 2)
+                      : make_uint2(0u, 0u);
   }
 
   __syncthreads();  // sDelta, sWp
