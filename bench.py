@@ -418,8 +418,8 @@ def main():
                     "(for profiling it on its own); the headline is not run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the scan shards by batch "
-              "row or channel with no communication in the forward; see the design notes). Run with --gpus 1.",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the scan shards by batch "
+              "row or channel with no communication in the forward). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     torch.cuda.init()

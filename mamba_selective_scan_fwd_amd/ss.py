@@ -52,8 +52,8 @@ def load_library(path: str = LIB_PATH):
     if _lib is not None:
         return _lib
     if not os.path.exists(path):
-        raise RuntimeError("libss.so is not built (%s); run `python -m mamba_selective_scan_fwd_amd.build` "
-                           "or __graft_entry__.build()" % path)
+        raise RuntimeError("libss.so is not built (%s); run `python -m mamba_selective_scan_fwd_amd.build`"
+                           % path)
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER(ss_problem)
     lib.ss_status_str.restype = ctypes.c_char_p
