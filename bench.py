@@ -227,33 +227,7 @@ def bench_rows(stream):
         "ms": ms, "documents": docs, "token_channel_per_s": 8 * 1536 * 2048 / (ms * 1e-3),
         "alu_frac": fwd_alg_slots(8, 1536, 16, 2048, 2) / (ms * 1e-3) / PEAK_SLOTS}
     del g2p, c2p, y2p, s2p, seq, h0
-    # the step before the scan: depthwise causal conv1d (width 4) + SiLU on the mamba-130m
-    # layer's x branch (fp16), three rotated input sets (the 256 MB MALL cannot hold them)
-    gcv = torch.Generator(device="cuda")
-    gcv.manual_seed(9)
-    xs = [torch.randn((8, 1536, 2048), device="cuda", generator=gcv).half() for _ in range(3)]
-    outs = [torch.empty_like(xs[0]) for _ in range(3)]
-    wcv = torch.randn((1536, 4), device="cuda", generator=gcv) * 0.5
-    bcv = torch.randn((1536,), device="cuda", generator=gcv) * 0.1
-    fc = lambda i: ss.conv1d(xs[i % 3], wcv, bcv, out=outs[i % 3])
-    fc(0)
-    ms = timed(fc, 30, stream)
-    cbytes = 2 * 8 * 1536 * 2048 * 2 + 1536 * 5 * 4
-    rows["conv1d_silu_B8_D1536_L2048_W4_f16"] = {
-        "ms": ms, "alg_GBps": cbytes / (ms * 1e-3) / 1e9, "hbm_frac": cbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
-    win = torch.zeros((8, 1536, 3), dtype=torch.float32, device="cuda")
-    fcs = lambda i: ss.conv1d_step(xs[0][..., i % 2048].contiguous(), wcv, win, bcv)
-    fcs(0)
-    ms = timed(fcs, 64, stream)
-    rows["conv1d_silu_B8_D1536_L2048_W4_f16"]["decode_us_per_step_checked_call"] = ms * 1e3
-    # the serving form: preallocated token, window and output buffers, one C call per step
-    xt = xs[0][..., 0].contiguous()
-    ot = torch.empty_like(xt)
-    ccs = ss.ConvStepCall(xt, wcv, win, ot, bias=bcv, stream=stream)
-    ccs()
-    ms = timed(lambda i: ccs(), 256, stream)
-    rows["conv1d_silu_B8_D1536_L2048_W4_f16"]["decode_us_per_step"] = ms * 1e3
-    del xs, outs, win
+    rows["conv1d_silu_B8_D1536_L2048_W4_f16"] = bench_conv(stream)
     # Mamba-2 SSD chunked scan on the matrix cores: d_model 768, expand 2 -> 24 heads of 64,
     # d_state 128, one group, chunk 256 (the "niverel-mamba" README's V3 configuration), B=8,
     # L=2048, bf16, with D, z gate and dt_bias; two rotated input sets
@@ -300,6 +274,44 @@ def bench_rows(stream):
     except Exception as e:  # graph capture is a measurement extra, never the headline
         rows["decode_step_B8_D1536_f16"]["graph_error"] = str(e)[:200]
     del g2, toks
+    rows.update(bench_bwd(stream))
+    torch.cuda.empty_cache()
+    return rows
+
+
+def bench_conv(stream):
+    # the step before the scan: depthwise causal conv1d (width 4) + SiLU on the mamba-130m
+    # layer's x branch (fp16), three rotated input sets (the 256 MB MALL cannot hold them)
+    gcv = torch.Generator(device="cuda")
+    gcv.manual_seed(9)
+    xs = [torch.randn((8, 1536, 2048), device="cuda", generator=gcv).half() for _ in range(3)]
+    outs = [torch.empty_like(xs[0]) for _ in range(3)]
+    wcv = torch.randn((1536, 4), device="cuda", generator=gcv) * 0.5
+    bcv = torch.randn((1536,), device="cuda", generator=gcv) * 0.1
+    fc = lambda i: ss.conv1d(xs[i % 3], wcv, bcv, out=outs[i % 3])
+    fc(0)
+    ms = timed(fc, 30, stream)
+    cbytes = 2 * 8 * 1536 * 2048 * 2 + 1536 * 5 * 4
+    row = {
+        "ms": ms, "alg_GBps": cbytes / (ms * 1e-3) / 1e9, "hbm_frac": cbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    win = torch.zeros((8, 1536, 3), dtype=torch.float32, device="cuda")
+    fcs = lambda i: ss.conv1d_step(xs[0][..., i % 2048].contiguous(), wcv, win, bcv)
+    fcs(0)
+    ms = timed(fcs, 64, stream)
+    row["decode_us_per_step_checked_call"] = ms * 1e3
+    # the serving form: preallocated token, window and output buffers, one C call per step
+    xt = xs[0][..., 0].contiguous()
+    ot = torch.empty_like(xt)
+    ccs = ss.ConvStepCall(xt, wcv, win, ot, bias=bcv, stream=stream)
+    ccs()
+    ms = timed(lambda i: ccs(), 256, stream)
+    row["decode_us_per_step"] = ms * 1e3
+    del xs, outs, win
+    return row
+
+
+def bench_bwd(stream):
+    rows = {}
     # backward, fp32
     try:
         prob4 = inputs.make_config(4)
@@ -329,7 +341,6 @@ def bench_rows(stream):
         del p4, ck, ck2, seq, dlast
     except RuntimeError as e:
         rows["bwd_B4_D1536_L4097_f32"] = {"error": str(e)[:200]}
-    torch.cuda.empty_cache()
     return rows
 
 
@@ -414,7 +425,7 @@ def main():
                     help="untimed steps first: the GPU needs ~100 ms of load to reach its working clock")
     ap.add_argument("--no-rows", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    ap.add_argument("--row", choices=["ssd"], help="time one secondary workload alone and print its JSON line "
+    ap.add_argument("--row", choices=["ssd", "conv", "bwd"], help="time one secondary workload alone and print its JSON line "
                     "(for profiling it on its own); the headline is not run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -424,8 +435,13 @@ def main():
         sys.exit(2)
     torch.cuda.init()
     stream = torch.cuda.current_stream()
-    if args.row == "ssd":
-        out = {"row": "ssd_fwd_B8_L2048_H24_P64_N128_bf16", **bench_ssd(stream)}
+    if args.row:
+        if args.row == "ssd":
+            out = {"ssd_fwd_B8_L2048_H24_P64_N128_bf16": bench_ssd(stream)}
+        elif args.row == "conv":
+            out = {"conv1d_silu_B8_D1536_L2048_W4_f16": bench_conv(stream)}
+        else:
+            out = bench_bwd(stream)
         out["copy_probe_GBps"] = copy_probe(stream)   # the counter calibration kernel, same process
         print(json.dumps(out), flush=True)
         return
