@@ -417,6 +417,97 @@ def cpu_baseline(sets_cpu_seed=2, target_s=12.0):
                       "workload, %d pass(es) (%d token*channel), %.2f s wall" % (nd2, L, reps, tc, t2)}
 
 
+def cpu_rows(rows, target_s=1.0):
+    """The float64 oracle beside each other workload, on a bounded sample of it (the whole
+    workload where it is small, else a block of channels or one head over the full sequence,
+    drawn from the same distributions), scaled to the row's unit."""
+    import oracle
+    threads = oracle.default_threads()
+    f64 = inputs.to_f64
+    out = {}
+
+    def per_call(fn):
+        t0 = time.perf_counter()
+        fn()
+        t = time.perf_counter() - t0
+        reps = max(1, int(target_s / max(t, 1e-4)))
+        if reps > 1:
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                fn()
+            t = (time.perf_counter() - t0) / reps
+        return t, reps + 1
+
+    def rec(value, unit, cores, sample):
+        log("  oracle: %s" % sample)
+        return {"value": value, "unit": unit, "cores": cores, "kind": "oracle", "sample": sample}
+
+    def scan_args(p):
+        return {k: f64(p[k]) for k in ("u", "delta", "A", "Bm", "Cm", "D", "z", "bias")}
+
+    if "fwd_long_B1_D16_L32768_f32" in rows:
+        a = scan_args(inputs.make_config(1))
+        t, n = per_call(lambda: oracle.fwd(**a, threads=threads))
+        out["fwd_long_B1_D16_L32768_f32"] = rec(16 * 32768 / t, "(token*channel)/s", min(threads, 16),
+                                                "the whole workload, %d passes" % n)
+    lens = rows.get("fwd_ragged_B4_D5120_L8192_bf16", {}).get("lengths")
+    if lens:
+        nd = 64
+        a = scan_args(inputs.make_problem(4, nd, 16, 8192, io="bf16", seed=3))
+        ln = np.asarray(lens, dtype=np.int64)
+        t, n = per_call(lambda: oracle.fwd(**a, lengths=ln, threads=threads))
+        out["fwd_ragged_B4_D5120_L8192_bf16"] = rec(sum(lens) * nd / t, "(token*channel)/s", threads,
+                                                    "%d of 5120 channels, the row's lengths %s, %d passes" % (nd, lens, n))
+    if "fwd_packed_docs_h0_B8_D1536_L2048_f16" in rows:
+        nd = 64
+        a = scan_args(inputs.make_problem(8, nd, 16, 2048, io="f16", seed=2, A_mode="a_log"))
+        seq = inputs.packed_documents(2048, 8, 512, seed=7).numpy()
+        h0 = np.random.default_rng(7).standard_normal((8, nd, 16))
+        t, n = per_call(lambda: oracle.fwd(**a, seq_idx=seq, h0=h0, threads=threads))
+        out["fwd_packed_docs_h0_B8_D1536_L2048_f16"] = rec(8 * nd * 2048 / t, "(token*channel)/s", threads,
+                                                           "%d of 1536 channels, the row's documents, %d passes" % (nd, n))
+    if "conv1d_silu_B8_D1536_L2048_W4_f16" in rows:
+        nd = 128
+        rng = np.random.default_rng(9)
+        x = f64(torch.from_numpy(rng.standard_normal((8, nd, 2048))).half())
+        w = rng.standard_normal((nd, 4)) * 0.5
+        bc = rng.standard_normal(nd) * 0.1
+        t, n = per_call(lambda: oracle.conv1d_fwd(x, w, bc))
+        out["conv1d_silu_B8_D1536_L2048_W4_f16"] = rec(8 * nd * 2048 / t, "(token*channel)/s", 1,
+                                                       "%d of 1536 channels (single-threaded oracle), %d passes" % (nd, n))
+    if "ssd_fwd_B8_L2048_H24_P64_N128_bf16" in rows:
+        rng = np.random.default_rng(11)
+        bf = lambda *sh: f64(torch.from_numpy(rng.standard_normal(sh)).bfloat16())
+        x, z = bf(8, 2048, 1, 64), bf(8, 2048, 1, 64)
+        dt = f64(torch.from_numpy(rng.standard_normal((8, 2048, 1)) * 0.5).bfloat16())
+        Bm, Cm = bf(8, 2048, 1, 128), bf(8, 2048, 1, 128)
+        A = -np.exp(rng.uniform(0, 2.77, 1))
+        D = rng.standard_normal(1)
+        db = np.log(np.expm1(np.exp(rng.uniform(-6.9, -2.3, 1))))
+        t, n = per_call(lambda: oracle.ssd_fwd(x, dt, A, Bm, Cm, D=D, z=z, dt_bias=db))
+        out["ssd_fwd_B8_L2048_H24_P64_N128_bf16"] = rec(8 * 2048 * 64 / t, "(token*channel)/s", 1,
+                                                        "1 of 24 heads (single-threaded oracle), %d passes" % n)
+    if "decode_step_B8_D1536_f16" in rows:
+        p = inputs.make_problem(8, 1536, 16, 1, io="f16", seed=2, A_mode="a_log", decode_steps=1)
+        tok = {k: f64(v) for k, v in p["decode"][0].items()}
+        st = np.zeros((8, 1536, 16))
+        a = {k: f64(p[k]) for k in ("A", "D", "bias")}
+        t, n = per_call(lambda: oracle.step(tok["u_t"], tok["delta_t"], a["A"], tok["B_t"], tok["C_t"], st,
+                                            D=a["D"], z_t=tok["z_t"], bias=a["bias"]))
+        out["decode_step_B8_D1536_f16"] = rec(t * 1e6, "us/step", 1,
+                                              "one step of the whole state (single-threaded oracle), %d steps" % n)
+    if "bwd_B4_D1536_L4097_f32" in rows and "ms" in rows["bwd_B4_D1536_L4097_f32"]:
+        nd = 32
+        p = inputs.make_problem(4, nd, 16, 4097, io="f32", seed=4, with_dy=True)
+        a = scan_args(p)
+        dy = f64(p["dy"])
+        t, n = per_call(lambda: oracle.bwd(a["u"], a["delta"], a["A"], a["Bm"], a["Cm"], dy, D=a["D"], z=a["z"],
+                                           bias=a["bias"], threads=threads))
+        out["bwd_B4_D1536_L4097_f32"] = rec(4 * nd * 4097 / t, "(token*channel)/s", threads,
+                                            "%d of 1536 channels, %d passes" % (nd, n))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -495,6 +586,10 @@ def main():
     if not args.no_cpu:
         log("cpu baseline (float64 oracle)")
         result["cpu_baseline"] = cpu_baseline()
+        if "rows" in result:
+            log("float64 oracle beside the other workloads")
+            for k, v in cpu_rows(result["rows"]).items():
+                result["rows"][k]["cpu_oracle"] = v
     print(json.dumps(result), flush=True)
 
 
