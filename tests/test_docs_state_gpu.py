@@ -95,6 +95,29 @@ def test_forward_resets_long_rows():
             assert rel_err(f64(last[:, ds.cuda()]), lr) <= 1e-5
 
 
+def test_packed_documents_h0_mamba130m_layer():
+    """The benchmarked packed-document workload: the mamba-130m layer (B=8, d_inner=1536,
+    L=2048, fp16) with documents of U[1, 512] steps and an initial state, in the launch
+    configuration the bench times; 64 sampled channels against the oracle."""
+    ss = _ss()
+    prob = inputs.make_config(2, decode_steps=0)
+    seq = inputs.packed_documents(2048, 8, 512, seed=7)
+    h0 = torch.from_numpy(np.random.default_rng(17).standard_normal((8, 1536, 16))).float()
+    g = to_dev(prob)
+    y, last, _ = ss.fwd(g["u"], g["delta"], g["A"], g["Bm"], g["Cm"], D=g["D"], z=g["z"], delta_bias=g["bias"],
+                        seq_idx=seq.to("cuda"), h0=h0.to("cuda"))
+    torch.cuda.synchronize()
+    ds = torch.tensor(sorted(set(np.random.default_rng(18).choice(1536, 60, replace=False).tolist()) | {0, 1535}))
+    sl = lambda t: f64(t[:, ds])
+    yr, lr = oracle.fwd(sl(prob["u"]), sl(prob["delta"]), f64(prob["A"][ds]), f64(prob["Bm"]), f64(prob["Cm"]),
+                        D=f64(prob["D"][ds]), z=sl(prob["z"]), bias=f64(prob["bias"][ds]), seq_idx=seq.numpy(),
+                        h0=f64(h0[:, ds]))
+    ey, el = rel_err(f64(y[:, ds.cuda()]), yr), rel_err(f64(last[:, ds.cuda()]), lr)
+    say("  mamba-130m packed documents + h0: %d documents, errors y=%.2e last=%.2e"
+        % (int((seq[:, 1:] != seq[:, :-1]).sum()) + 8, ey, el))
+    assert ey <= TOL["f16"] and el <= TOL["f16"]
+
+
 def test_packed_equals_documents_on_device():
     """model(x, seq_idx) == concat(model(doc_i)) with both sides on the GPU."""
     ss = _ss()
