@@ -212,11 +212,13 @@ def test_backward_initial_and_final_state(L):
 
 
 def test_backward_resets_workload_shape():
-    """The backward workload's shape (B=4, d_inner=1536, L=4097) with packed documents."""
+    """The backward workload's shape (B=4, d_inner=1536, L=4097) with packed documents and a
+    final-state gradient, dh0 out: the benchmarked configuration."""
     prob = inputs.make_config(4)
     seq = inputs.packed_documents(4097, 4, 600, seed=118)
-    say("bwd workload shape with packed documents")
-    _bwd_check(prob, seq=seq)
+    dlast = torch.from_numpy(np.random.default_rng(119).standard_normal((4, 1536, 16))).float()
+    say("bwd workload shape with packed documents and dlast")
+    _bwd_check(prob, seq=seq, dlast=dlast)
 
 
 def test_autograd_initial_and_last_state():
