@@ -488,12 +488,16 @@ __global__ void __launch_bounds__(kThreads) ss_step_kernel(StepParams p) {
   const float Bn = (ok && n_ok) ? load_io<IO>(p.Bt, b * p.dstate + n) : 0.0f;
   const float Cn = (ok && n_ok) ? load_io<IO>(p.Ct, b * p.dstate + n) : 0.0f;
   const float h0 = (ok && n_ok) ? p.state_in[ch * p.dstate + n] : 0.0f;
+  // the skip weight and the gate are loaded with everything else, so the
+  // step waits on one round of loads, not two
+  const float Dd = (ok && p.D) ? p.D[d] : 0.0f;
+  const float zv = (ok && p.z) ? load_io<IO>(p.z, ch) : 0.0f;
   const float h = fmaf(exp2_hw(dt * A2), h0, dt * u * Bn);
   const float y0 = row_sum(Cn * h);
   if (ok && n_ok) p.state_out[ch * p.dstate + n] = h;
   if (ok && n == 0) {
-    float yv = y0 + (p.D ? p.D[d] * u : 0.0f);
-    if (p.z) yv *= silu_f(load_io<IO>(p.z, ch));
+    float yv = y0 + (p.D ? Dd * u : 0.0f);
+    if (p.z) yv *= silu_f(zv);
     store_io<IO>(p.y, ch, yv);
   }
 }
