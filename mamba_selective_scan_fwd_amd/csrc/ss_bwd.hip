@@ -290,6 +290,25 @@ __device__ __forceinline__ void collect_block(float (&accB)[4][4], float (&accC)
   }
 }
 
+// The per-lane scalars of one channel block (lane: channel d, state n).
+struct BlockScalars {
+  float A, bias, Dd, g_last, h_ck, g_in;
+};
+template <bool MAIN>
+__device__ __forceinline__ void load_scalars(BlockScalars& s, const BwdParams& p, int64_t b, int64_t d, int64_t k,
+                                             int64_t K, int n) {
+  const bool ch_ok = d < p.dim, n_ok = n < p.dstate;
+  const int64_t ch = b * p.dim + d;
+  s.A = (ch_ok && n_ok) ? p.A[d * p.dstate + n] : 0.0f;
+  s.bias = (ch_ok && p.bias) ? p.bias[d] : 0.0f;
+  s.Dd = (ch_ok && p.D) ? p.D[d] : 0.0f;
+  // gradient entering the chunk from the right with a zero carry; the last
+  // chunk also receives the caller's gradient of the final state
+  s.g_last = (k == K - 1 && p.dlast && ch_ok && n_ok) ? p.dlast[ch * p.dstate + n] : 0.0f;
+  s.h_ck = (MAIN && ch_ok && n_ok) ? p.ckpt[(ch * K + k) * p.dstate + n] : 0.0f;
+  s.g_in = (MAIN && k < K - 1 && ch_ok) ? p.gcarry[(ch * K + k) * kStates + n] : 0.0f;
+}
+
 template <int IO, bool MAIN, bool SEQ>
 __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int32_t groups, int32_t per_group) {
   __shared__ BwdSmem<MAIN> sm;
@@ -353,31 +372,39 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
   int64_t cb_end = cb_begin + per_group;
   if (cb_end > p.ch_blocks) cb_end = p.ch_blocks;
 
+  // Every load of a channel block is issued one block ahead, while the
+  // previous block is computed: its inputs, its weights and (MAIN) its
+  // checkpoint and carried gradient.  Loads complete in issue order for the
+  // wait counter, so nothing else is loaded between two blocks' prefetches.
+  const bool n_ok = n < p.dstate;
+  const uint32_t lane_elem0 = (uint32_t)cw * L;
+  BwdRaw<IO> raw;
+  BlockScalars cur, nxt;
+  if (cb_begin < cb_end) {
+    load_scalars<MAIN>(cur, p, b, cb_begin * kChPerBlock + wave * kChPerWave + cw, k, K, n);
+    load_raw<IO>(raw, make_views<IO>(p, b, cb_begin * kChPerBlock + wave * kChPerWave, need_z), lane_elem0, t0, l);
+  }
   for (int64_t cb = cb_begin; cb < cb_end; ++cb) {
     const int64_t d0 = cb * kChPerBlock + wave * kChPerWave;
     const int64_t d = d0 + cw;
     const bool ch_ok = d < p.dim;
-    const bool n_ok = n < p.dstate;
     const int64_t ch = b * p.dim + d;
     const BwdViews v = make_views<IO>(p, b, d0, need_z);
-    const uint32_t lane_elem0 = (uint32_t)cw * L;
 
-    const float A = (ch_ok && n_ok) ? p.A[d * p.dstate + n] : 0.0f;
+    const float A = cur.A;
     const float A2 = A * kLog2e;
-    const float bias = (ch_ok && p.bias) ? p.bias[d] : 0.0f;
-    const float Dd = (ch_ok && p.D) ? p.D[d] : 0.0f;
-
+    const float bias = cur.bias;
+    const float Dd = cur.Dd;
     BwdOwned o;
-    {
-      BwdRaw<IO> raw;
-      load_raw<IO>(raw, v, lane_elem0, t0, l);
-      prep<IO>(o, raw, t0, l, t_end, bias, softplus, need_z);
+    prep<IO>(o, raw, t0, l, t_end, bias, softplus, need_z);
+    __builtin_amdgcn_sched_barrier(0);
+    if (cb + 1 < cb_end) {
+      load_scalars<MAIN>(nxt, p, b, d + kChPerBlock, k, K, n);
+      load_raw<IO>(raw, make_views<IO>(p, b, d0 + kChPerBlock, need_z), lane_elem0, t0, l);
     }
+    __builtin_amdgcn_sched_barrier(0);
     const int64_t wslot = ((ch * K + k) * kStates + n);
-
-    // gradient entering the chunk from the right with a zero carry; the last
-    // chunk also receives the caller's gradient of the final state
-    const float g_last = (k == K - 1 && p.dlast && ch_ok && n_ok) ? p.dlast[ch * p.dstate + n] : 0.0f;
+    const float g_last = cur.g_last;
     if constexpr (!MAIN) {
       float g = g_last;
       agg_block<3, SEQ>(g, o, A2, sCrow, starts, seq);
@@ -396,7 +423,7 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
       float* t4w = sm.T4[wave];
       // first pass: entry state of each 16-step block (and y0 when gated)
       float hb[4], ac[4][16];  // block entry states, the chunk's decays
-      float h = (ch_ok && n_ok) ? p.ckpt[(ch * K + k) * p.dstate + n] : 0.0f;
+      float h = cur.h_ck;
       if (need_z) {
 #define SS_FWD_Y(I)                                                          \
   hb[I] = h;                                                                 \
@@ -420,7 +447,7 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
         fwd_pass<3, false, SEQ>(h, ac[3], o, A2, sBrow, sCrow, t1c, n, starts, seq);  // its decays
       }
 
-      float g = (k < K - 1 && ch_ok) ? p.gcarry[wslot] : g_last;
+      float g = (k < K - 1 && ch_ok) ? cur.g_in : g_last;
       float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
 #define SS_BWD(I)                                                                                   \
   {                                                                                                 \
@@ -468,6 +495,7 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
         p.aggG[p.batch * K * p.dim + bk * p.dim + d] = dbs;
       }
     }
+    cur = nxt;
   }
 
   if constexpr (MAIN) {
