@@ -464,20 +464,7 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
     for (int pt = 0; pt < 4; ++pt) acc[q][pt] *= sc;
   }
 
-  // gate values for the epilogue: lane has channels 16 pt + 4 (lane / 16) .. + 3 of its step
   uint2 zv[2][4];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int64_t t = t0 + 32 * blk[q] + 16 * half + lane % 16;
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
-      zv[q][pt] = (p.z && t < p.seqlen)
-                      ? *reinterpret_cast<const uint2*>(static_cast<const char*>(p.z) + t * xrow +
-                                                        ((b * p.seqlen) * p.nheads + h) * kP * 2 +
-                                                        (16 * pt + 4 * (lane / 16)) * 2)
-                      : make_uint2(0u, 0u);
-  }
-
   __syncthreads();  // sDelta, sWp
 
   // ---- Y_diag += x^T M^T, piece by piece
@@ -495,6 +482,20 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
       if (pc <= dpiece)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) cbv[pc][ks] = *reinterpret_cast<const u32x4v*>(cbrow + kJB * pc + 32 * ks);
+    if (q == 0) {  // the gate, loaded once the first pieces' C B^T are on their way
+    // gate values for the epilogue: lane has channels 16 pt + 4 (lane / 16) .. + 3 of its step
+  #pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const int64_t t = t0 + 32 * blk[qq] + 16 * half + lane % 16;
+  #pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+        zv[qq][pt] = (p.z && t < p.seqlen)
+                        ? *reinterpret_cast<const uint2*>(static_cast<const char*>(p.z) + t * xrow +
+                                                          ((b * p.seqlen) * p.nheads + h) * kP * 2 +
+                                                          (16 * pt + 4 * (lane / 16)) * 2)
+                        : make_uint2(0u, 0u);
+    }
+    }
 #pragma unroll
     for (int piece = 0; piece < kQ / kJB; ++piece) {
       if (piece > dpiece) break;
