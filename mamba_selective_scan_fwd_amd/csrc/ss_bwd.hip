@@ -247,6 +247,9 @@ __device__ __forceinline__ void bwd_block(float& g, float& dA_acc, const float (
                                           float* t2c, float* t3w, float* t4w, int n, int cw,
                                           std::integer_sequence<int, J...>) {
   float4 b4, c4;
+  // a copy of Delta u of its own, so that the broadcast folds into this block's
+  // multiply instead of being shared (as a separate move) with the state recompute
+  const float dtu_f = fresh(o.dtu[I]);
   (
       [&] {
         constexpr int jj = 15 - J;
@@ -262,7 +265,7 @@ __device__ __forceinline__ void bwd_block(float& g, float& dA_acc, const float (
         const float a = as[jj];               // decay of step s (0 at a document start)
         const float gh = fmaf(dy0b, cqj, g);  // dLoss/dh_t
         t4w[(jj * 16 + n) * kChPerWave + cw] = dy0b * hs[jj + 1];
-        t3w[(jj * 16 + n) * kChPerWave + cw] = gh * row_bcast<jj>(o.dtu[I]);
+        t3w[(jj * 16 + n) * kChPerWave + cw] = gh * row_bcast<jj>(dtu_f);
         t1c[swz(jj, n)] = gh * bqj;
         g = gh * a;                                 // to h_{t-1}
         const float q = g * hs[jj];                 // gh * a * h_{t-1}
