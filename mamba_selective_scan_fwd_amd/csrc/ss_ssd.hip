@@ -19,7 +19,8 @@
 //                     decayed state held in the accumulators, each chunk's
 //                     entry state written in the I/O dtype, the final state
 //                     in fp32; the workgroups of a group also share out its
-//                     C B^T (fp32, once per group rather than per head);
+//                     C B^T (summed in fp32, kept as bf16; once per group
+//                     rather than per head);
 //   ssd_scan_kernel   per (batch, chunk, head): Y_off = C H_in on MFMA, then
 //                     per 64-step piece of the chunk's columns M = the decay-
 //                     masked, Delta-scaled C B^T built in registers and
@@ -174,7 +175,7 @@ __device__ __forceinline__ void wave_chunk_cumsum(const float* sDelta, float A, 
 }
 
 // ---- C B^T of a chunk, once per group -------------------------------------------
-// CB[i][j] = sum_n C_i[n] B_j[n] (fp32 sums, stored as bf16) for the chunk's rows i and the columns j
+// CB[i][j] = sum_n C_i[n] B_j[n] (summed in fp32, stored as bf16) for the chunk's rows i and the columns j
 // of every 64-step piece up to the one holding i (the causal half plus the rest
 // of the diagonal pieces, so the output pass never reads an unwritten value):
 // 160 tiles of 16 x 16.  Tile idx: row band R = rt / 4 holds 4 (R + 1) column
@@ -371,8 +372,10 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
 // diagonal piece the decay factors through the piece's last step e:
 // exp(cs_i - cs_e) * exp(cs_e - cs_j), both at most 1 there, so one exp per
 // lane is enough; the diagonal piece takes the exp per element.  Global loads
-// are issued ahead of their use: all prologue operands at once, the next
-// piece's CB during the current piece, the gate z before the main loop.
+// are issued ahead of their use: all prologue operands at once, each piece's
+// CB two pieces ahead, the gate z right after the first block's first CB
+// pieces (loads complete in issue order for the wait counter, so a load
+// issued earlier than those would delay the first piece).
 constexpr int kScanThreads = 512;
 template <int IO, int N>
 __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) {
