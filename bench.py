@@ -450,6 +450,8 @@ def cpu_rows(rows, target_s=1.0):
         t, n = per_call(lambda: oracle.fwd(**a, threads=threads))
         out["fwd_long_B1_D16_L32768_f32"] = rec(16 * 32768 / t, "(token*channel)/s", min(threads, 16),
                                                 "the whole workload, %d passes" % n)
+        t1, n1 = per_call(lambda: oracle.fwd(**a, threads=1))
+        out["fwd_long_B1_D16_L32768_f32"]["value_single_core"] = 16 * 32768 / t1
     lens = rows.get("fwd_ragged_B4_D5120_L8192_bf16", {}).get("lengths")
     if lens:
         nd = 64
