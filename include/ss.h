@@ -58,7 +58,9 @@ extern "C" {
 typedef enum ss_status {
     SS_OK = 0,
     SS_ERR_NULL_ARG = 1,     /* a required pointer is NULL, or an optional pair is half given */
-    SS_ERR_BAD_SHAPE = 2,    /* a size is < 1 or overflows */
+    SS_ERR_BAD_SHAPE = 2,    /* a size is < 1 or overflows (also: a launch grid beyond
+                                2^23 workgroups, so that every dispatch stays within
+                                2^32 work-items) */
     SS_ERR_BAD_DTYPE = 3,    /* io_dtype is not one of ss_dtype */
     SS_ERR_MISALIGNED = 4,   /* a pointer is not 16-byte aligned */
     SS_ERR_UNSUPPORTED = 5,  /* a size outside the supported set, a workspace missing or

@@ -16,7 +16,9 @@ constexpr int64_t kMaxDstate = 16;
 constexpr int64_t kChPerBlock = 16;
 // below this many wavefronts a forward splits the time axis into chunks
 constexpr int64_t kTargetWaves = 1024;
-constexpr int64_t kMaxGrid = (int64_t)1 << 31;
+// the largest grid, in workgroups of up to 512 threads, whose work-item count
+// fits the 32-bit grid size of a dispatch
+constexpr int64_t kMaxGrid = ((int64_t)1 << 23) - 1;
 constexpr int64_t kMaxSeqlen = (int64_t)1 << 24;
 
 bool aligned(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
@@ -29,7 +31,7 @@ ss_status check_problem(const ss_problem* p, bool need_seqlen) {
   if (need_seqlen && p->seqlen < 1) return SS_ERR_BAD_SHAPE;
   if (p->dstate > kMaxDstate) return SS_ERR_UNSUPPORTED;
   if (p->io_dtype != SS_F32 && p->io_dtype != SS_F16 && p->io_dtype != SS_BF16) return SS_ERR_BAD_DTYPE;
-  // keep every element index far from int64 overflow and grids within 2^31 blocks
+  // keep every element index far from int64 overflow and every grid within kMaxGrid
   const int64_t lim = (int64_t)1 << 40;
   if (p->batch > lim || p->dim > lim) return SS_ERR_BAD_SHAPE;
   // kernels address a row with 32-bit offsets
@@ -197,8 +199,23 @@ ss_status ss_fwd_step(const ss_problem* p, const void* u_t, const void* delta_t,
   return from_hip(ss::launch_step(k, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+// The backward's own grids: a workgroup per (batch row, 64-step chunk,
+// channel block) for the chunk aggregates, one per channel for the carry scan
+// (which runs only when there is more than one chunk).
+ss_status check_bwd(const ss_problem* p) {
+  const ss_status s = check_problem(p, true);
+  if (s != SS_OK) return s;
+  const double chunks = (double)((p->seqlen + kTile - 1) / kTile);
+  const double cblocks = (double)((p->dim + kChPerBlock - 1) / kChPerBlock);
+  if ((double)p->batch * chunks * cblocks > (double)kMaxGrid) return SS_ERR_BAD_SHAPE;
+  if (chunks > 1 && (double)p->batch * (double)p->dim > (double)kMaxGrid) return SS_ERR_BAD_SHAPE;
+  return SS_OK;
+}
+}  // namespace
+
 size_t ss_bwd_workspace_size(const ss_problem* p) {
-  if (check_problem(p, true) != SS_OK) return 0;
+  if (check_bwd(p) != SS_OK) return 0;
   const int64_t nchunks = (p->seqlen + kTile - 1) / kTile;
   return (size_t)3 * (size_t)(p->batch * p->dim * nchunks * 16) * sizeof(float);
 }
@@ -208,7 +225,7 @@ ss_status ss_bwd(const ss_problem* p, const void* u, const void* delta, const fl
                  const float* ckpt, const void* dy, const float* dlast, void* du, void* ddelta, void* dz, float* dA,
                  float* dB, float* dC, float* dD, float* dbias, float* dh0, void* workspace, size_t workspace_bytes,
                  void* stream) {
-  ss_status s = check_problem(p, true);
+  ss_status s = check_bwd(p);
   if (s != SS_OK) return s;
   if (!u || !delta || !A || !Bm || !Cm || !ckpt || !dy || !du || !ddelta || !dA || !dB || !dC)
     return SS_ERR_NULL_ARG;

@@ -62,6 +62,18 @@ def test_sizes():
     assert lib.ss_ckpt_count(ctypes.byref(_prob(seqlen=0))) == 0
 
 
+def test_bwd_rejects_grids_beyond_the_dispatch_limit():
+    """A backward whose per-chunk grid (batch x 64-step chunks x channel blocks) or carry grid
+    (one workgroup per channel) would pass 2^23 workgroups is rejected on the host."""
+    lib = ss.load_library()
+    args = [FAKE] * 5 + [None, None, None] + [None, FAKE, FAKE, None] + [FAKE, FAKE, None] + [FAKE] * 3 + [None] * 3
+    for p in (_prob(batch=1 << 20, dim=16, seqlen=1 << 14),      # 2^28 chunk workgroups
+              _prob(batch=1 << 12, dim=1 << 12, seqlen=65)):      # 2^24 channels for the carry scan
+        assert lib.ss_bwd_workspace_size(ctypes.byref(p)) == 0
+        assert lib.ss_bwd(ctypes.byref(p), *args, FAKE, 1 << 30, None) == 2
+    for ok in (_prob(batch=4, dim=1536, seqlen=4097), _prob(batch=1 << 12, dim=1 << 12, seqlen=64)):
+        assert lib.ss_bwd_workspace_size(ctypes.byref(ok)) > 0
+
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), 2), (dict(dim=-1), 2), (dict(seqlen=0), 2), (dict(dstate=0), 2),
     (dict(dstate=17), 5), (dict(io_dtype=3), 3)])
