@@ -75,8 +75,8 @@ def test_bwd_rejects_grids_beyond_the_dispatch_limit():
         assert lib.ss_bwd_workspace_size(ctypes.byref(ok)) > 0
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(batch=0), 2), (dict(dim=-1), 2), (dict(seqlen=0), 2), (dict(dstate=0), 2),
-    (dict(dstate=17), 5), (dict(io_dtype=3), 3)])
+    (dict(batch=0), 2), (dict(dim=-1), 2), (dict(seqlen=0), 2), (dict(seqlen=(1 << 24) + 1), 2),
+    (dict(dstate=0), 2), (dict(dstate=17), 5), (dict(io_dtype=3), 3)])
 def test_fwd_rejects_bad_problem(kw, code):
     assert _fwd(_prob(**kw)) == code
 

@@ -116,6 +116,12 @@ def test_edge_shapes(Bsz, Dd, N, L):
     _check(inputs.make_problem(Bsz, Dd, N, L, "f32", seed=7 * L + Dd, with_dy=True))
 
 
+def test_max_seqlen():
+    """The longest sequence the ABI accepts, L = 2^24, on one channel: 2^18 checkpoints,
+    the reverse carry over 2^18 chunks and the dA/dD/dbias sums over all of them."""
+    _check(inputs.make_problem(1, 1, 16, 1 << 24, "f32", seed=2425, with_dy=True))
+
+
 def test_invariants_and_repeatability():
     """On device results: sum of ddelta over (b, t) equals dbias; u.du = dy.y per channel;
     two runs agree within the tolerance (channel sums use atomics)."""

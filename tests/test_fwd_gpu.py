@@ -139,6 +139,15 @@ def test_edge_shapes(Bsz, Dd, N, L):
         _check_full(prob)
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_max_seqlen(io):
+    """The longest sequence the ABI accepts, L = 2^24 (one step past it is rejected on
+    the host): two channels of one row, so the time-chunked path runs with 2^18 tiles
+    per row and the 32-bit buffer offsets at their largest; whole y and final state
+    against the oracle."""
+    _check_full(inputs.make_problem(1, 2, 16, 1 << 24, io, seed=2424))
+
+
 @pytest.mark.parametrize("io", ["f32", "f16"])
 def test_ragged_lengths_edges(io):
     """Row lengths on and around tile edges, a length-1 row, a full row, and clamped values."""
