@@ -148,6 +148,31 @@ def test_max_seqlen(io):
     _check_full(inputs.make_problem(1, 2, 16, 1 << 24, io, seed=2424))
 
 
+def test_max_channels():
+    """2^24 channels (two rows of d_inner = 2^23) at L = 2: 2^20 workgroups for the scan
+    and for the decode step, with 64-bit channel and weight indices; y and the final
+    state against the oracle, then one decode step from the device's final state."""
+    Bsz, Dd, N, L = 2, 1 << 23, 16, 2
+    prob = inputs.make_problem(Bsz, Dd, N, L, "f16", seed=2426, decode_steps=1)
+    say("max channels B=%d D=%d L=%d" % (Bsz, Dd, L))
+    ss = _ss()
+    y, last, _ = _run(prob)
+    yr, lr = oracle.fwd(**oracle_args(prob))
+    assert rel_err(f64(y), yr) <= TOL["f16"]
+    assert rel_err(f64(last), lr) <= TOL["f16"]
+    del y, yr
+    g = to_dev(prob)
+    tok = prob["decode"][0]
+    gt = {key: v.to("cuda") for key, v in tok.items()}
+    yt, st = ss.step(gt["u_t"], gt["delta_t"], g["A"], gt["B_t"], gt["C_t"], last, D=g["D"], z_t=gt["z_t"],
+                     delta_bias=g["bias"])
+    torch.cuda.synchronize()
+    ytr, str_ = oracle.step(f64(tok["u_t"]), f64(tok["delta_t"]), f64(prob["A"]), f64(tok["B_t"]), f64(tok["C_t"]),
+                            f64(last), D=f64(prob["D"]), z_t=f64(tok["z_t"]), bias=f64(prob["bias"]))
+    assert rel_err(f64(yt), ytr) <= TOL["f16"]
+    assert rel_err(f64(st), str_) <= TOL["f16"]
+
+
 @pytest.mark.parametrize("io", ["f32", "f16"])
 def test_ragged_lengths_edges(io):
     """Row lengths on and around tile edges, a length-1 row, a full row, and clamped values."""
