@@ -312,8 +312,15 @@ __device__ __forceinline__ void load_scalars(BlockScalars& s, const BwdParams& p
   s.g_in = (MAIN && k < K - 1 && ch_ok) ? p.gcarry[(ch * K + k) * kStates + n] : 0.0f;
 }
 
+// Work units are channel blocks in (batch row, chunk, block) order, block
+// fastest.  Workgroup w takes the contiguous units [w U / W, (w + 1) U / W)
+// of the U units over W workgroups, as segments that share a (batch row,
+// chunk): each segment stages that chunk's B and C once, walks its channel
+// blocks, and (MAIN) adds its dB/dC channel sums into the outputs.  AGG runs
+// one unit per workgroup; MAIN runs one workgroup per resident slot, so every
+// slot gets the same number of units (to within one).
 template <int IO, bool MAIN, bool SEQ>
-__global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int32_t groups, int32_t per_group) {
+__global__ void __launch_bounds__(kThreads, MAIN ? 2 : 7) ss_bwd_chunk_kernel(BwdParams p) {
   __shared__ BwdSmem<MAIN> sm;
   constexpr uint32_t s = io_bytes<IO>();
   const int tid = threadIdx.x;
@@ -321,19 +328,33 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
   const int lane = tid % 64;
   const int cw = lane / 16, n = lane % 16, l = n;
 
-  uint32_t lb = xcd_logical_block();
-  const int64_t grp = lb % groups;
-  lb /= groups;
-  const int64_t k = lb % p.nchunks;
-  const int64_t b = lb / p.nchunks;
   const int64_t K = p.nchunks;
-
-  const int64_t t0 = k * kTile;
-  const int64_t t_end = t0 + kTile < p.seqlen ? t0 + kTile : p.seqlen;
+  const int64_t U = p.batch * K * p.ch_blocks;
+  const int64_t W = gridDim.x;
+  const int64_t w = xcd_logical_block();
+  // AGG: exactly unit w (its grid is U workgroups)
+  const int64_t u_begin = MAIN ? w * U / W : w;
+  const int64_t u_end = MAIN ? (w + 1) * U / W : w + 1;
   const bool need_z = p.z != nullptr;
   const bool softplus = p.softplus != 0;
   const uint32_t L = (uint32_t)p.seqlen;
+  const float* sBrow = &sm.B[n][0];
+  const float* sCrow = &sm.C[n][0];
+  constexpr auto seq = std::make_integer_sequence<int, 16>{};
 
+  for (int64_t unit = u_begin; unit < u_end;) {
+  const int64_t bk = unit / p.ch_blocks;
+  const int64_t k = bk % K;
+  const int64_t b = bk / K;
+  const int64_t cb_begin = unit % p.ch_blocks;
+  const int64_t cb_end =
+      !MAIN ? cb_begin + 1 : (cb_begin + (u_end - unit) < p.ch_blocks ? cb_begin + (u_end - unit) : p.ch_blocks);
+  unit += cb_end - cb_begin;
+
+  const int64_t t0 = k * kTile;
+  const int64_t t_end = t0 + kTile < p.seqlen ? t0 + kTile : p.seqlen;
+
+  __syncthreads();  // the previous segment is done with the B/C and staging tiles
   // stage the chunk's B and C (shared by every channel of this batch row)
   {
     const uint32_t bc_bytes = (uint32_t)(p.dstate * p.seqlen) * s;
@@ -362,18 +383,11 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
   }
   __syncthreads();
 
-  const float* sBrow = &sm.B[n][0];
-  const float* sCrow = &sm.C[n][0];
-  constexpr auto seq = std::make_integer_sequence<int, 16>{};
   float accB[4][4], accC[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q) accB[i][q] = accC[i][q] = 0.0f;
-
-  const int64_t cb_begin = grp * per_group;
-  int64_t cb_end = cb_begin + per_group;
-  if (cb_end > p.ch_blocks) cb_end = p.ch_blocks;
 
   // Every load of a channel block is issued one block ahead, while the
   // previous block is computed: its inputs, its weights and (MAIN) its
@@ -532,6 +546,7 @@ __global__ void __launch_bounds__(kThreads) ss_bwd_chunk_kernel(BwdParams p, int
       }
     }
   }
+  }  // segment
 }
 
 // Zero up to five float buffers in one launch (the atomic targets of the
@@ -581,8 +596,9 @@ __global__ void __launch_bounds__(256) ss_bwd_reduce_kernel(const float* __restr
   }
 }
 
-// MAIN workgroups resident per CU: 76 KB of LDS and 232 VGPRs per lane
-// (2 waves per SIMD) each allow two.
+// MAIN workgroups resident per CU: 76 KB of LDS and at most 256 registers per
+// lane (2 waves per SIMD, held there by the kernel's launch bounds) each allow
+// two.
 constexpr int64_t kMainPerCu = 2;
 
 // Compute units of the current device, asked once per device (256 if the
@@ -620,38 +636,23 @@ hipError_t launch_bwd_seq(const BwdParams& p, hipStream_t st) {
   const int64_t K = p.nchunks;
   hipError_t e = zero_outputs(p, st);  // every atomic target, before any kernel adds into it
   if (e != hipSuccess) return e;
-  // MAIN: the channel blocks of a (batch row, chunk) are split into `groups`
-  // workgroups.  All workgroups take the same time, so the kernel lasts
-  // ceil(workgroups / resident) rounds of `per` channel blocks each; each
-  // workgroup also adds its dB/dC channel sums atomically once per element, so
-  // more groups cost atomics.  Take the smallest group count (up to 16) whose
-  // round count x per is within 5% of the best.
+  // MAIN: one workgroup per resident slot, each over an equal share of the
+  // channel-block units (to within one), so that every slot finishes at about
+  // the same time; a workgroup adds its dB/dC channel sums atomically once
+  // per (batch row, chunk) it touches.
   const int64_t bk = p.batch * K;
+  const int64_t units = bk * p.ch_blocks;
   const int64_t resident = kMainPerCu * device_cus();
-  auto makespan = [&](int64_t g) {
-    const int64_t per_g = (p.ch_blocks + g - 1) / g;
-    const int64_t g_eff = (p.ch_blocks + per_g - 1) / per_g;
-    return ((bk * g_eff + resident - 1) / resident) * per_g;
-  };
-  const int64_t gmax = p.ch_blocks < 16 ? p.ch_blocks : 16;
-  int64_t best = makespan(1);
-  for (int64_t g = 2; g <= gmax; ++g) best = makespan(g) < best ? makespan(g) : best;
-  int64_t groups = 1;
-  while (groups < gmax && makespan(groups) * 100 > best * 105) ++groups;
-  const int64_t per = (p.ch_blocks + groups - 1) / groups;
-  groups = (p.ch_blocks + per - 1) / per;
-  const dim3 grid((uint32_t)(bk * groups));
+  const dim3 grid((uint32_t)(units < resident ? units : resident));
   if (K > 1) {
     // AGG has nothing to reduce over channels: one channel block per workgroup
-    hipLaunchKernelGGL((ss_bwd_chunk_kernel<IO, false, SEQ>), dim3((uint32_t)(bk * p.ch_blocks)), dim3(kThreads), 0,
-                       st, p, (int32_t)p.ch_blocks, 1);
+    hipLaunchKernelGGL((ss_bwd_chunk_kernel<IO, false, SEQ>), dim3((uint32_t)units), dim3(kThreads), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_carry(p.aggP, p.aggG, p.gcarry, p.batch * p.dim, (int32_t)K, true, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((ss_bwd_chunk_kernel<IO, true, SEQ>), grid, dim3(kThreads), 0, st, p, (int32_t)groups,
-                     (int32_t)per);
+  hipLaunchKernelGGL((ss_bwd_chunk_kernel<IO, true, SEQ>), grid, dim3(kThreads), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t threads = p.dim * kStates;
