@@ -3,7 +3,9 @@
  *
  * The library (libss.so) runs the selective scan of Mamba-1 as hand-written
  * HIP kernels.  All tensor arguments are DEVICE pointers allocated by the
- * caller; the library allocates nothing and keeps no global state.  Every
+ * caller; the library allocates nothing, and its only global state is a
+ * per-device cache of the compute-unit count (read once from the runtime, to
+ * size the backward's launch to the resident workgroup slots).  Every
  * call validates its arguments on the host first and returns an error code
  * without touching the GPU when they are invalid; otherwise it enqueues its
  * kernels on `stream` (a hipStream_t, NULL = the null stream) and returns
