@@ -656,7 +656,7 @@ hipError_t launch_bwd_seq(const BwdParams& p, hipStream_t st) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t threads = p.dim * kStates;
-  int64_t groups_y = (bk + 31) / 32;
+  int64_t groups_y = (bk + 7) / 8;
   if (groups_y > 64) groups_y = 64;
   hipLaunchKernelGGL(ss_bwd_reduce_kernel, dim3((uint32_t)((threads + 255) / 256), (uint32_t)groups_y), dim3(256), 0,
                      st, p.aggP, p.aggG, p.aggG + p.batch * K * p.dim, p.dA, p.dD, p.dbias, p.dim, p.dstate, bk);
