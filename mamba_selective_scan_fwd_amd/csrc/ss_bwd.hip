@@ -422,12 +422,19 @@ __global__ void __launch_bounds__(kThreads, MAIN ? 2 : 7) ss_bwd_chunk_kernel(Bw
     __builtin_amdgcn_sched_barrier(0);
     const int64_t wslot = ((ch * K + k) * kStates + n);
     const float g_last = cur.g_last;
+    // chunks in which no document starts take the copy without the resets
+    const bool reset = SEQ && starts != 0;
     if constexpr (!MAIN) {
       float g = g_last;
-      agg_block<3, SEQ>(g, o, A2, sCrow, starts, seq);
-      agg_block<2, SEQ>(g, o, A2, sCrow, starts, seq);
-      agg_block<1, SEQ>(g, o, A2, sCrow, starts, seq);
-      agg_block<0, SEQ>(g, o, A2, sCrow, starts, seq);
+      auto walk = [&](auto reset_tag) {
+        constexpr bool R = decltype(reset_tag)::value;
+        agg_block<3, R>(g, o, A2, sCrow, starts, seq);
+        agg_block<2, R>(g, o, A2, sCrow, starts, seq);
+        agg_block<1, R>(g, o, A2, sCrow, starts, seq);
+        agg_block<0, R>(g, o, A2, sCrow, starts, seq);
+      };
+      if (reset) walk(std::bool_constant<SEQ>{});
+      else walk(std::false_type{});
       const float dsum = row_sum((o.dt[0] + o.dt[1]) + (o.dt[2] + o.dt[3]));
       if (ch_ok) {
         p.aggP[wslot] = starts != 0 ? 0.0f : exp2_hw(A2 * dsum);
@@ -441,28 +448,33 @@ __global__ void __launch_bounds__(kThreads, MAIN ? 2 : 7) ss_bwd_chunk_kernel(Bw
       // first pass: entry state of each 16-step block (and y0 when gated)
       float hb[4], ac[4][16];  // block entry states, the chunk's decays
       float h = cur.h_ck;
-      if (need_z) {
-#define SS_FWD_Y(I)                                                          \
-  hb[I] = h;                                                                 \
-  fwd_pass<I, true, SEQ>(h, ac[I], o, A2, sBrow, sCrow, t1c, n, starts, seq); \
-  wave_lds_sync();                                                         \
-  o.y0[I] = fmaf(Dd, o.u[I], row16_sum(t1c, l));                           \
+      auto recompute = [&](auto reset_tag) {
+        constexpr bool R = decltype(reset_tag)::value;
+        if (need_z) {
+#define SS_FWD_Y(I)                                                         \
+  hb[I] = h;                                                                \
+  fwd_pass<I, true, R>(h, ac[I], o, A2, sBrow, sCrow, t1c, n, starts, seq); \
+  wave_lds_sync();                                                        \
+  o.y0[I] = fmaf(Dd, o.u[I], row16_sum(t1c, l));                          \
   wave_lds_sync();
-        SS_FWD_Y(0)
-        SS_FWD_Y(1)
-        SS_FWD_Y(2)
-        SS_FWD_Y(3)
+          SS_FWD_Y(0)
+          SS_FWD_Y(1)
+          SS_FWD_Y(2)
+          SS_FWD_Y(3)
 #undef SS_FWD_Y
-      } else {
-        hb[0] = h;
-        fwd_pass<0, false, SEQ>(h, ac[0], o, A2, sBrow, sCrow, t1c, n, starts, seq);
-        hb[1] = h;
-        fwd_pass<1, false, SEQ>(h, ac[1], o, A2, sBrow, sCrow, t1c, n, starts, seq);
-        hb[2] = h;
-        fwd_pass<2, false, SEQ>(h, ac[2], o, A2, sBrow, sCrow, t1c, n, starts, seq);
-        hb[3] = h;
-        fwd_pass<3, false, SEQ>(h, ac[3], o, A2, sBrow, sCrow, t1c, n, starts, seq);  // its decays
-      }
+        } else {
+          hb[0] = h;
+          fwd_pass<0, false, R>(h, ac[0], o, A2, sBrow, sCrow, t1c, n, starts, seq);
+          hb[1] = h;
+          fwd_pass<1, false, R>(h, ac[1], o, A2, sBrow, sCrow, t1c, n, starts, seq);
+          hb[2] = h;
+          fwd_pass<2, false, R>(h, ac[2], o, A2, sBrow, sCrow, t1c, n, starts, seq);
+          hb[3] = h;
+          fwd_pass<3, false, R>(h, ac[3], o, A2, sBrow, sCrow, t1c, n, starts, seq);  // its decays
+        }
+      };
+      if (reset) recompute(std::bool_constant<SEQ>{});
+      else recompute(std::false_type{});
 
       float g = (k < K - 1 && ch_ok) ? cur.g_in : g_last;
       float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
