@@ -343,221 +343,221 @@ __global__ void __launch_bounds__(kThreads, MAIN ? 2 : 7) ss_bwd_chunk_kernel(Bw
   constexpr auto seq = std::make_integer_sequence<int, 16>{};
 
   for (int64_t unit = u_begin; unit < u_end;) {
-  const int64_t bk = unit / p.ch_blocks;
-  const int64_t k = bk % K;
-  const int64_t b = bk / K;
-  const int64_t cb_begin = unit % p.ch_blocks;
-  const int64_t cb_end =
-      !MAIN ? cb_begin + 1 : (cb_begin + (u_end - unit) < p.ch_blocks ? cb_begin + (u_end - unit) : p.ch_blocks);
-  unit += cb_end - cb_begin;
+    const int64_t bk = unit / p.ch_blocks;
+    const int64_t k = bk % K;
+    const int64_t b = bk / K;
+    const int64_t cb_begin = unit % p.ch_blocks;
+    const int64_t cb_end =
+        !MAIN ? cb_begin + 1 : (cb_begin + (u_end - unit) < p.ch_blocks ? cb_begin + (u_end - unit) : p.ch_blocks);
+    unit += cb_end - cb_begin;
 
-  const int64_t t0 = k * kTile;
-  const int64_t t_end = t0 + kTile < p.seqlen ? t0 + kTile : p.seqlen;
+    const int64_t t0 = k * kTile;
+    const int64_t t_end = t0 + kTile < p.seqlen ? t0 + kTile : p.seqlen;
 
-  __syncthreads();  // the previous segment is done with the B/C and staging tiles
-  // stage the chunk's B and C (shared by every channel of this batch row)
-  {
-    const uint32_t bc_bytes = (uint32_t)(p.dstate * p.seqlen) * s;
-    const char* bbase = static_cast<const char*>(p.Bm) + b * p.dstate * p.seqlen * s;
-    const char* cbase = static_cast<const char*>(p.Cm) + b * p.dstate * p.seqlen * s;
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(bbase, bc_bytes), rC = make_rsrc(cbase, bc_bytes);
-    const int sn = tid / 16, j = tid % 16;
+    __syncthreads();  // the previous segment is done with the B/C and staging tiles
+    // stage the chunk's B and C (shared by every channel of this batch row)
+    {
+      const uint32_t bc_bytes = (uint32_t)(p.dstate * p.seqlen) * s;
+      const char* bbase = static_cast<const char*>(p.Bm) + b * p.dstate * p.seqlen * s;
+      const char* cbase = static_cast<const char*>(p.Cm) + b * p.dstate * p.seqlen * s;
+      const __amdgpu_buffer_rsrc_t rB = make_rsrc(bbase, bc_bytes), rC = make_rsrc(cbase, bc_bytes);
+      const int sn = tid / 16, j = tid % 16;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = j + 16 * q;
-      const bool ok = sn < p.dstate && t0 + e < t_end;
-      const uint32_t off = ((uint32_t)sn * L + (uint32_t)(t0 + e)) * s;
-      const float bv = bits_f32<IO>(bload<IO>(rB, off));
-      const float cv = bits_f32<IO>(bload<IO>(rC, off));
-      sm.B[sn][e] = ok ? bv : 0.0f;
-      sm.C[sn][e] = ok ? cv : 0.0f;
-    }
-  }
-  // document starts among the chunk's steps (every wave computes the mask)
-  uint64_t starts = 0;
-  if constexpr (SEQ) {
-    const __amdgpu_buffer_rsrc_t ids = make_rsrc(p.seq_idx + b * p.seqlen, L * 4u);
-    uint32_t id_t, id_prev;
-    load_doc_ids(ids, (int)t0 + lane, id_t, id_prev);
-    starts = doc_starts(id_t, id_prev, (int)t0 + lane, (int)t_end);
-  }
-  __syncthreads();
-
-  float accB[4][4], accC[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) accB[i][q] = accC[i][q] = 0.0f;
-
-  // Every load of a channel block is issued one block ahead, while the
-  // previous block is computed: its inputs, its weights and (MAIN) its
-  // checkpoint and carried gradient.  Loads complete in issue order for the
-  // wait counter, so nothing else is loaded between two blocks' prefetches.
-  const bool n_ok = n < p.dstate;
-  const uint32_t lane_elem0 = (uint32_t)cw * L;
-  BwdRaw<IO> raw;
-  BlockScalars cur, nxt;
-  if (cb_begin < cb_end) {
-    load_scalars<MAIN>(cur, p, b, cb_begin * kChPerBlock + wave * kChPerWave + cw, k, K, n);
-    load_raw<IO>(raw, make_views<IO>(p, b, cb_begin * kChPerBlock + wave * kChPerWave, need_z), lane_elem0, t0, l);
-  }
-  for (int64_t cb = cb_begin; cb < cb_end; ++cb) {
-    const int64_t d0 = cb * kChPerBlock + wave * kChPerWave;
-    const int64_t d = d0 + cw;
-    const bool ch_ok = d < p.dim;
-    const int64_t ch = b * p.dim + d;
-    const BwdViews v = make_views<IO>(p, b, d0, need_z);
-
-    const float A = cur.A;
-    const float A2 = A * kLog2e;
-    const float bias = cur.bias;
-    const float Dd = cur.Dd;
-    BwdOwned o;
-    prep<IO>(o, raw, t0, l, t_end, bias, softplus, need_z);
-    __builtin_amdgcn_sched_barrier(0);
-    if (cb + 1 < cb_end) {
-      load_scalars<MAIN>(nxt, p, b, d + kChPerBlock, k, K, n);
-      load_raw<IO>(raw, make_views<IO>(p, b, d0 + kChPerBlock, need_z), lane_elem0, t0, l);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    const int64_t wslot = ((ch * K + k) * kStates + n);
-    const float g_last = cur.g_last;
-    // chunks in which no document starts take the copy without the resets
-    const bool reset = SEQ && starts != 0;
-    if constexpr (!MAIN) {
-      float g = g_last;
-      auto walk = [&](auto reset_tag) {
-        constexpr bool R = decltype(reset_tag)::value;
-        agg_block<3, R>(g, o, A2, sCrow, starts, seq);
-        agg_block<2, R>(g, o, A2, sCrow, starts, seq);
-        agg_block<1, R>(g, o, A2, sCrow, starts, seq);
-        agg_block<0, R>(g, o, A2, sCrow, starts, seq);
-      };
-      if (reset) walk(std::bool_constant<SEQ>{});
-      else walk(std::false_type{});
-      const float dsum = row_sum((o.dt[0] + o.dt[1]) + (o.dt[2] + o.dt[3]));
-      if (ch_ok) {
-        p.aggP[wslot] = starts != 0 ? 0.0f : exp2_hw(A2 * dsum);
-        p.aggG[wslot] = g;
-      }
-    } else {
-      float* t1c = sm.T1[wave] + cw * kSChan;  // this channel's sum-over-states tiles
-      float* t2c = sm.T2[wave] + cw * kSChan;
-      float* t3w = sm.T3[wave];
-      float* t4w = sm.T4[wave];
-      // first pass: entry state of each 16-step block (and y0 when gated)
-      float hb[4], ac[4][16];  // block entry states, the chunk's decays
-      float h = cur.h_ck;
-      auto recompute = [&](auto reset_tag) {
-        constexpr bool R = decltype(reset_tag)::value;
-        if (need_z) {
-#define SS_FWD_Y(I)                                                         \
-  hb[I] = h;                                                                \
-  fwd_pass<I, true, R>(h, ac[I], o, A2, sBrow, sCrow, t1c, n, starts, seq); \
-  wave_lds_sync();                                                        \
-  o.y0[I] = fmaf(Dd, o.u[I], row16_sum(t1c, l));                          \
-  wave_lds_sync();
-          SS_FWD_Y(0)
-          SS_FWD_Y(1)
-          SS_FWD_Y(2)
-          SS_FWD_Y(3)
-#undef SS_FWD_Y
-        } else {
-          hb[0] = h;
-          fwd_pass<0, false, R>(h, ac[0], o, A2, sBrow, sCrow, t1c, n, starts, seq);
-          hb[1] = h;
-          fwd_pass<1, false, R>(h, ac[1], o, A2, sBrow, sCrow, t1c, n, starts, seq);
-          hb[2] = h;
-          fwd_pass<2, false, R>(h, ac[2], o, A2, sBrow, sCrow, t1c, n, starts, seq);
-          hb[3] = h;
-          fwd_pass<3, false, R>(h, ac[3], o, A2, sBrow, sCrow, t1c, n, starts, seq);  // its decays
-        }
-      };
-      if (reset) recompute(std::bool_constant<SEQ>{});
-      else recompute(std::false_type{});
-
-      float g = (k < K - 1 && ch_ok) ? cur.g_in : g_last;
-      float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
-#define SS_BWD(I)                                                                                   \
-  {                                                                                                 \
-    float hs[17];                                                                                   \
-    o.dt[I] = fresh(o.dt[I]);                                                                       \
-    o.dtu[I] = fresh(o.dtu[I]);                                                                     \
-    o.dy0[I] = fresh(o.dy0[I]);                                                                     \
-    fwd_states<I>(hs, ac[I], hb[I], o, sBrow, seq);                                                 \
-    bwd_block<I>(g, dA_acc, hs, ac[I], o, A, sBrow, sCrow, t1c, t2c, t3w, t4w, n, cw, seq);         \
-    wave_lds_sync();                                                                                \
-    const float sGB = row16_sum(t1c, l);                                                            \
-    const float sQA = row16_sum(t2c, l);                                                            \
-    collect_block<I>(accB, accC, t3w, t4w, lane);                                                   \
-    const float du = fmaf(o.dt[I], sGB, o.dy0[I] * Dd);                                             \
-    const float dD = fmaf(o.u[I], sGB, sQA);                                                        \
-    float dx = softplus ? dD * sigmoid_f(o.x[I]) : dD;                                              \
-    dx = o.valid[I] ? dx : 0.0f;                                                                    \
-    const int64_t t = t0 + 16 * (I) + l;                                                            \
-    const uint32_t off = (o.valid[I] && ch_ok) ? (lane_elem0 + (uint32_t)t) * s : kOffNone;         \
-    bstore<IO>(v.du, off, o.valid[I] ? du : 0.0f);                                                  \
-    bstore<IO>(v.ddl, off, dx);                                                                     \
-    if (need_z) {                                                                                   \
-      const float sz = sigmoid_f(o.z[I]);                                                           \
-      const float dz = o.dy[I] * o.y0[I] * sz * fmaf(o.z[I], 1.0f - sz, 1.0f);                      \
-      bstore<IO>(v.dz, off, o.valid[I] ? dz : 0.0f);                                                \
-    }                                                                                               \
-    dD_acc = fmaf(o.dy0[I], o.u[I], dD_acc);                                                        \
-    db_acc += dx;                                                                                   \
-    wave_lds_sync();                                                                                \
-  }
-      SS_BWD(3)
-      SS_BWD(2)
-      SS_BWD(1)
-      SS_BWD(0)
-#undef SS_BWD
-      // the gradient left after step 0 is the gradient w.r.t. the initial state
-      if (k == 0 && p.dh0 && ch_ok && n_ok) p.dh0[ch * p.dstate + n] = g;
-      // partial sums of this (batch row, chunk) for the reduction pass
-      const int64_t bk = b * K + k;
-      if (ch_ok) p.aggP[(bk * p.dim + d) * kStates + n] = dA_acc;
-      const float dDs = row_sum(dD_acc);
-      const float dbs = row_sum(db_acc);
-      if (ch_ok && n == 0) {
-        p.aggG[bk * p.dim + d] = dDs;
-        p.aggG[p.batch * K * p.dim + bk * p.dim + d] = dbs;
+      for (int q = 0; q < 4; ++q) {
+        const int e = j + 16 * q;
+        const bool ok = sn < p.dstate && t0 + e < t_end;
+        const uint32_t off = ((uint32_t)sn * L + (uint32_t)(t0 + e)) * s;
+        const float bv = bits_f32<IO>(bload<IO>(rB, off));
+        const float cv = bits_f32<IO>(bload<IO>(rC, off));
+        sm.B[sn][e] = ok ? bv : 0.0f;
+        sm.C[sn][e] = ok ? cv : 0.0f;
       }
     }
-    cur = nxt;
-  }
-
-  if constexpr (MAIN) {
-    // sum the four waves' channel sums, then one global add per element
+    // document starts among the chunk's steps (every wave computes the mask)
+    uint64_t starts = 0;
+    if constexpr (SEQ) {
+      const __amdgpu_buffer_rsrc_t ids = make_rsrc(p.seq_idx + b * p.seqlen, L * 4u);
+      uint32_t id_t, id_prev;
+      load_doc_ids(ids, (int)t0 + lane, id_t, id_prev);
+      starts = doc_starts(id_t, id_prev, (int)t0 + lane, (int)t_end);
+    }
     __syncthreads();
-    float* stB = &sm.T1[0][0];                      // [wave][64 steps][16 states]
-    float* stC = stB + kWaves * kTile * kStates;
+
+    float accB[4][4], accC[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int st = 16 * i + (lane >> 4) + 4 * q, sn = lane & 15;
-        stB[(wave * kTile + st) * kStates + sn] = accB[i][q];
-        stC[(wave * kTile + st) * kStates + sn] = accC[i][q];
+      for (int q = 0; q < 4; ++q) accB[i][q] = accC[i][q] = 0.0f;
+
+    // Every load of a channel block is issued one block ahead, while the
+    // previous block is computed: its inputs, its weights and (MAIN) its
+    // checkpoint and carried gradient.  Loads complete in issue order for the
+    // wait counter, so nothing else is loaded between two blocks' prefetches.
+    const bool n_ok = n < p.dstate;
+    const uint32_t lane_elem0 = (uint32_t)cw * L;
+    BwdRaw<IO> raw;
+    BlockScalars cur, nxt;
+    if (cb_begin < cb_end) {
+      load_scalars<MAIN>(cur, p, b, cb_begin * kChPerBlock + wave * kChPerWave + cw, k, K, n);
+      load_raw<IO>(raw, make_views<IO>(p, b, cb_begin * kChPerBlock + wave * kChPerWave, need_z), lane_elem0, t0, l);
+    }
+    for (int64_t cb = cb_begin; cb < cb_end; ++cb) {
+      const int64_t d0 = cb * kChPerBlock + wave * kChPerWave;
+      const int64_t d = d0 + cw;
+      const bool ch_ok = d < p.dim;
+      const int64_t ch = b * p.dim + d;
+      const BwdViews v = make_views<IO>(p, b, d0, need_z);
+
+      const float A = cur.A;
+      const float A2 = A * kLog2e;
+      const float bias = cur.bias;
+      const float Dd = cur.Dd;
+      BwdOwned o;
+      prep<IO>(o, raw, t0, l, t_end, bias, softplus, need_z);
+      __builtin_amdgcn_sched_barrier(0);
+      if (cb + 1 < cb_end) {
+        load_scalars<MAIN>(nxt, p, b, d + kChPerBlock, k, K, n);
+        load_raw<IO>(raw, make_views<IO>(p, b, d0 + kChPerBlock, need_z), lane_elem0, t0, l);
       }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int idx = tid + kThreads * r;  // (step, state) pair
-      const int st = idx / kStates, sn = idx % kStates;
-      float vb = 0.0f, vc = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        vb += stB[(w * kTile + st) * kStates + sn];
-        vc += stC[(w * kTile + st) * kStates + sn];
+      __builtin_amdgcn_sched_barrier(0);
+      const int64_t wslot = ((ch * K + k) * kStates + n);
+      const float g_last = cur.g_last;
+      // chunks in which no document starts take the copy without the resets
+      const bool reset = SEQ && starts != 0;
+      if constexpr (!MAIN) {
+        float g = g_last;
+        auto walk = [&](auto reset_tag) {
+          constexpr bool R = decltype(reset_tag)::value;
+          agg_block<3, R>(g, o, A2, sCrow, starts, seq);
+          agg_block<2, R>(g, o, A2, sCrow, starts, seq);
+          agg_block<1, R>(g, o, A2, sCrow, starts, seq);
+          agg_block<0, R>(g, o, A2, sCrow, starts, seq);
+        };
+        if (reset) walk(std::bool_constant<SEQ>{});
+        else walk(std::false_type{});
+        const float dsum = row_sum((o.dt[0] + o.dt[1]) + (o.dt[2] + o.dt[3]));
+        if (ch_ok) {
+          p.aggP[wslot] = starts != 0 ? 0.0f : exp2_hw(A2 * dsum);
+          p.aggG[wslot] = g;
+        }
+      } else {
+        float* t1c = sm.T1[wave] + cw * kSChan;  // this channel's sum-over-states tiles
+        float* t2c = sm.T2[wave] + cw * kSChan;
+        float* t3w = sm.T3[wave];
+        float* t4w = sm.T4[wave];
+        // first pass: entry state of each 16-step block (and y0 when gated)
+        float hb[4], ac[4][16];  // block entry states, the chunk's decays
+        float h = cur.h_ck;
+        auto recompute = [&](auto reset_tag) {
+          constexpr bool R = decltype(reset_tag)::value;
+          if (need_z) {
+#define SS_FWD_Y(I)                                                         \
+    hb[I] = h;                                                                \
+    fwd_pass<I, true, R>(h, ac[I], o, A2, sBrow, sCrow, t1c, n, starts, seq); \
+    wave_lds_sync();                                                        \
+    o.y0[I] = fmaf(Dd, o.u[I], row16_sum(t1c, l));                          \
+    wave_lds_sync();
+            SS_FWD_Y(0)
+            SS_FWD_Y(1)
+            SS_FWD_Y(2)
+            SS_FWD_Y(3)
+#undef SS_FWD_Y
+          } else {
+            hb[0] = h;
+            fwd_pass<0, false, R>(h, ac[0], o, A2, sBrow, sCrow, t1c, n, starts, seq);
+            hb[1] = h;
+            fwd_pass<1, false, R>(h, ac[1], o, A2, sBrow, sCrow, t1c, n, starts, seq);
+            hb[2] = h;
+            fwd_pass<2, false, R>(h, ac[2], o, A2, sBrow, sCrow, t1c, n, starts, seq);
+            hb[3] = h;
+            fwd_pass<3, false, R>(h, ac[3], o, A2, sBrow, sCrow, t1c, n, starts, seq);  // its decays
+          }
+        };
+        if (reset) recompute(std::bool_constant<SEQ>{});
+        else recompute(std::false_type{});
+
+        float g = (k < K - 1 && ch_ok) ? cur.g_in : g_last;
+        float dA_acc = 0.0f, dD_acc = 0.0f, db_acc = 0.0f;
+#define SS_BWD(I)                                                                                   \
+    {                                                                                                 \
+      float hs[17];                                                                                   \
+      o.dt[I] = fresh(o.dt[I]);                                                                       \
+      o.dtu[I] = fresh(o.dtu[I]);                                                                     \
+      o.dy0[I] = fresh(o.dy0[I]);                                                                     \
+      fwd_states<I>(hs, ac[I], hb[I], o, sBrow, seq);                                                 \
+      bwd_block<I>(g, dA_acc, hs, ac[I], o, A, sBrow, sCrow, t1c, t2c, t3w, t4w, n, cw, seq);         \
+      wave_lds_sync();                                                                                \
+      const float sGB = row16_sum(t1c, l);                                                            \
+      const float sQA = row16_sum(t2c, l);                                                            \
+      collect_block<I>(accB, accC, t3w, t4w, lane);                                                   \
+      const float du = fmaf(o.dt[I], sGB, o.dy0[I] * Dd);                                             \
+      const float dD = fmaf(o.u[I], sGB, sQA);                                                        \
+      float dx = softplus ? dD * sigmoid_f(o.x[I]) : dD;                                              \
+      dx = o.valid[I] ? dx : 0.0f;                                                                    \
+      const int64_t t = t0 + 16 * (I) + l;                                                            \
+      const uint32_t off = (o.valid[I] && ch_ok) ? (lane_elem0 + (uint32_t)t) * s : kOffNone;         \
+      bstore<IO>(v.du, off, o.valid[I] ? du : 0.0f);                                                  \
+      bstore<IO>(v.ddl, off, dx);                                                                     \
+      if (need_z) {                                                                                   \
+        const float sz = sigmoid_f(o.z[I]);                                                           \
+        const float dz = o.dy[I] * o.y0[I] * sz * fmaf(o.z[I], 1.0f - sz, 1.0f);                      \
+        bstore<IO>(v.dz, off, o.valid[I] ? dz : 0.0f);                                                \
+      }                                                                                               \
+      dD_acc = fmaf(o.dy0[I], o.u[I], dD_acc);                                                        \
+      db_acc += dx;                                                                                   \
+      wave_lds_sync();                                                                                \
+    }
+        SS_BWD(3)
+        SS_BWD(2)
+        SS_BWD(1)
+        SS_BWD(0)
+#undef SS_BWD
+        // the gradient left after step 0 is the gradient w.r.t. the initial state
+        if (k == 0 && p.dh0 && ch_ok && n_ok) p.dh0[ch * p.dstate + n] = g;
+        // partial sums of this (batch row, chunk) for the reduction pass
+        const int64_t bk = b * K + k;
+        if (ch_ok) p.aggP[(bk * p.dim + d) * kStates + n] = dA_acc;
+        const float dDs = row_sum(dD_acc);
+        const float dbs = row_sum(db_acc);
+        if (ch_ok && n == 0) {
+          p.aggG[bk * p.dim + d] = dDs;
+          p.aggG[p.batch * K * p.dim + bk * p.dim + d] = dbs;
+        }
       }
-      if (sn < p.dstate && t0 + st < t_end) {
-        const int64_t gi = (b * p.dstate + sn) * p.seqlen + t0 + st;
-        unsafeAtomicAdd(p.dB + gi, vb);
-        unsafeAtomicAdd(p.dC + gi, vc);
+      cur = nxt;
+    }
+
+    if constexpr (MAIN) {
+      // sum the four waves' channel sums, then one global add per element
+      __syncthreads();
+      float* stB = &sm.T1[0][0];                      // [wave][64 steps][16 states]
+      float* stC = stB + kWaves * kTile * kStates;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int st = 16 * i + (lane >> 4) + 4 * q, sn = lane & 15;
+          stB[(wave * kTile + st) * kStates + sn] = accB[i][q];
+          stC[(wave * kTile + st) * kStates + sn] = accC[i][q];
+        }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int idx = tid + kThreads * r;  // (step, state) pair
+        const int st = idx / kStates, sn = idx % kStates;
+        float vb = 0.0f, vc = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          vb += stB[(w * kTile + st) * kStates + sn];
+          vc += stC[(w * kTile + st) * kStates + sn];
+        }
+        if (sn < p.dstate && t0 + st < t_end) {
+          const int64_t gi = (b * p.dstate + sn) * p.seqlen + t0 + st;
+          unsafeAtomicAdd(p.dB + gi, vb);
+          unsafeAtomicAdd(p.dC + gi, vc);
+        }
       }
     }
-  }
   }  // segment
 }
 
