@@ -318,7 +318,9 @@ __device__ __forceinline__ void load_scalars(BlockScalars& s, const BwdParams& p
 // chunk): each segment stages that chunk's B and C once, walks its channel
 // blocks, and (MAIN) adds its dB/dC channel sums into the outputs.  AGG runs
 // one unit per workgroup; MAIN runs one workgroup per resident slot, so every
-// slot gets the same number of units (to within one).
+// slot gets the same number of units (to within one).  The launch bounds ask
+// for at least 2 (MAIN) or 7 (AGG) waves per SIMD: left free, the compiler
+// takes MAIN past 256 registers, which leaves one wave per SIMD.
 template <int IO, bool MAIN, bool SEQ>
 __global__ void __launch_bounds__(kThreads, MAIN ? 2 : 7) ss_bwd_chunk_kernel(BwdParams p) {
   __shared__ BwdSmem<MAIN> sm;
