@@ -211,6 +211,15 @@ def test_backward_initial_and_final_state(L):
         _bwd_check(prob, seq=inputs.make_seq_idx("misaligned_rows", Bsz, L, seed=117), h0=h0, dlast=dlast)
 
 
+def test_backward_resets_many_segments_per_workgroup():
+    """One channel block over 1100 chunks: each backward workgroup walks two or three
+    (batch row, chunk) segments, chunks with and without document starts mixed."""
+    Bsz, Dd, L = 1, 16, 64 * 1100
+    prob = inputs.make_problem(Bsz, Dd, 16, L, "f32", seed=120, with_dy=True)
+    say("bwd many segments B=%d D=%d L=%d" % (Bsz, Dd, L))
+    _bwd_check(prob, seq=inputs.packed_documents(L, Bsz, 600, seed=121))
+
+
 def test_backward_resets_workload_shape():
     """The backward workload's shape (B=4, d_inner=1536, L=4097) with packed documents and a
     final-state gradient, dh0 out: the benchmarked configuration."""
