@@ -88,20 +88,20 @@ def test_resets_and_h0_match_unrolled_form(with_h0):
 
 # ------------------------------------------------------------- backward pins
 
-def _loss(p, dy, seq, dlast, **over):
+def _loss(p, dy, seq, dlast, lengths=None, **over):
     q = dict(p)
     q.update(over)
     y, last = oracle.fwd(q["u"], q["delta"], q["A"], q["Bm"], q["Cm"], D=q["D"], z=q["z"], bias=q["bias"],
-                         seq_idx=seq, h0=q.get("h0"), threads=1)
+                         seq_idx=seq, h0=q.get("h0"), lengths=lengths, threads=1)
     out = float(np.sum(dy * y))
     if dlast is not None:
         out += float(np.sum(dlast * last))
     return out
 
 
-def _fd(p, dy, seq, h0, dlast, names, tol):
+def _fd(p, dy, seq, h0, dlast, names, tol, lengths=None):
     g = oracle.bwd(p["u"], p["delta"], p["A"], p["Bm"], p["Cm"], dy, D=p["D"], z=p["z"], bias=p["bias"],
-                   seq_idx=seq, h0=h0, dlast=dlast, want_dh0=True, threads=1)
+                   seq_idx=seq, h0=h0, dlast=dlast, want_dh0=True, lengths=lengths, threads=1)
     q0 = dict(p)
     if h0 is not None:
         q0["h0"] = h0
@@ -114,7 +114,7 @@ def _fd(p, dy, seq, h0, dlast, names, tol):
             for k in (-2, -1, 1, 2):
                 q = base.copy()
                 q[idx] += k * h
-                f[k] = _loss(q0, dy, seq, dlast, **{name: q})
+                f[k] = _loss(q0, dy, seq, dlast, lengths=lengths, **{name: q})
             fd[idx] = (8.0 * (f[1] - f[-1]) - (f[2] - f[-2])) / (12.0 * h)
         assert _rel(g[gname], fd) < tol, (gname, _rel(g[gname], fd))
     return g
@@ -184,5 +184,59 @@ def test_backward_packed_equals_documents():
             assert _rel(g[k][:, :, s0:s1], gd[k]) < 1e-12, k
         for k in acc:
             acc[k] = acc[k] + gd[k]
+    for k in acc:
+        assert _rel(g[k], acc[k]) < 1e-12, k
+
+
+# --------------------------------------------------------- ragged rows (lengths)
+
+def test_backward_fd_ragged_lengths():
+    """Ragged rows: row b runs lengths[b] steps, y is 0 past that length and the final state is
+    the state after lengths[b] steps.  The backward of that loss (dy . y + dlast . h_len) against
+    five-point differences of the forward, on rows of length 0, 1, 4 and the whole row, with an
+    initial state and a final-state gradient, with and without document resets."""
+    rng = np.random.default_rng(41)
+    Bsz, Dd, N, L = 4, 2, 3, 9
+    p = _rand(rng, Bsz, Dd, N, L)
+    dy = rng.standard_normal((Bsz, Dd, L))
+    h0 = rng.standard_normal((Bsz, Dd, N))
+    dlast = rng.standard_normal((Bsz, Dd, N))
+    lengths = np.array([0, 1, 4, L])
+    g = _fd(p, dy, None, h0, dlast, dict(ALL, h0="dh0"), 1e-7, lengths=lengths)
+    # nothing past a row's length reaches the loss
+    for b, n in enumerate(lengths):
+        for k in ("du", "ddelta", "dz"):
+            assert np.all(g[k][b, :, n:] == 0.0), (k, b)
+        assert np.all(g["dB"][b, :, n:] == 0.0) and np.all(g["dC"][b, :, n:] == 0.0), b
+    # a row of length 0: its final state is h0, so dh0 = dlast
+    assert np.array_equal(g["dh0"][0], dlast[0])
+    seq = np.array([[0, 0, 1, 1, 1, 1, 1, 1, 1]] * Bsz)
+    _fd(p, dy, seq, h0, dlast, dict(ALL, h0="dh0"), 1e-7, lengths=lengths)
+
+
+def test_backward_ragged_is_truncation():
+    """bwd with lengths[b] == bwd of the row cut to its first lengths[b] steps (dlast and h0
+    included), zeros after; the reduced gradients dA, dD, dbias are the sums over the cut rows."""
+    rng = np.random.default_rng(42)
+    Bsz, Dd, N, L = 4, 3, 4, 70
+    p = _rand(rng, Bsz, Dd, N, L)
+    dy = rng.standard_normal((Bsz, Dd, L))
+    h0 = rng.standard_normal((Bsz, Dd, N))
+    dlast = rng.standard_normal((Bsz, Dd, N))
+    lengths = np.array([1, 64, 70, 33])
+    g = oracle.bwd(p["u"], p["delta"], p["A"], p["Bm"], p["Cm"], dy, D=p["D"], z=p["z"], bias=p["bias"],
+                   h0=h0, dlast=dlast, want_dh0=True, lengths=lengths, threads=1)
+    acc = {k: 0.0 for k in ("dA", "dD", "dbias")}
+    for b, n in enumerate(lengths):
+        sl = lambda a: np.ascontiguousarray(a[b:b + 1, :, :n])
+        gb = oracle.bwd(sl(p["u"]), sl(p["delta"]), p["A"], sl(p["Bm"]), sl(p["Cm"]), sl(dy), D=p["D"],
+                        z=sl(p["z"]), bias=p["bias"], h0=h0[b:b + 1], dlast=dlast[b:b + 1], want_dh0=True,
+                        threads=1)
+        for k in ("du", "ddelta", "dz", "dB", "dC"):
+            assert _rel(g[k][b:b + 1, :, :n], gb[k]) < 1e-12, (k, b)
+            assert np.all(g[k][b, :, n:] == 0.0), (k, b)
+        assert _rel(g["dh0"][b:b + 1], gb["dh0"]) < 1e-12, b
+        for k in acc:
+            acc[k] = acc[k] + gb[k]
     for k in acc:
         assert _rel(g[k], acc[k]) < 1e-12, k
