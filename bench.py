@@ -30,17 +30,16 @@ sys.path.insert(0, ROOT)
 from mamba_selective_scan_fwd_amd import inputs, ss  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0
-# VALU lane-slots per second: the fp32 vector peak, 157.3 TFLOP/s, is
-# 256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz FMA slots (no packed math).
-PEAK_SLOTS = 256 * 4 * 32 * 2.4e9
-# Algorithmic ALU work in lane-slots; a transcendental (exp2, log2, rcp) runs at
-# quarter rate and counts 4 slots:
-#   per (t, d, n): exp-argument mul, Bbar*u mul, recurrence fma, readout fma (4) + exp (4) = 8
-#   per (t, d):    softplus (exp + log: 8, 4 VALU), Delta*u, skip fma, SiLU (exp + rcp: 8, 2 VALU),
-#                  gate mul = 9 VALU + 16 = 25; plus 4 conversions when the I/O is 16-bit
-SLOTS_PER_TDN = 8
-SLOTS_PER_TD = 25
-SLOTS_PER_TD_CVT16 = 4
+# Algorithmic vector work of the forward, in lane-operations (one lane of one
+# wave64 instruction), priced below at the issue rates the library's probe
+# measures on the chip (not at a datasheet rate):
+#   per (t, d, n): one exp (the decay) and four plain operations (the exp's
+#                  argument Delta*A, Delta*u*B, the recurrence FMA, the readout FMA)
+#   per (t, d):    four transcendentals (softplus: exp + log; SiLU: exp + rcp) and
+#                  ten plain operations (softplus' other steps, Delta*u, skip, gate),
+#                  plus four conversions when the I/O is 16-bit
+TRANS_PER_TDN, PLAIN_PER_TDN = 1, 4
+TRANS_PER_TD, PLAIN_PER_TD, CVT16_PER_TD = 4, 10, 4
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["mamba_selective_scan_fwd_amd/csrc/ss_fwd.hip", "mamba_selective_scan_fwd_amd/csrc/ss_device.h"]
 
@@ -63,10 +62,33 @@ def fwd_alg_bytes(Bsz, Dd, N, L, s, lengths=None, ckpt=False):
     return byt
 
 
-def fwd_alg_slots(Bsz, Dd, N, L, s, lengths=None):
-    valid = int(sum(lengths)) if lengths is not None else Bsz * L
-    per_td = SLOTS_PER_TDN * N + SLOTS_PER_TD + (SLOTS_PER_TD_CVT16 if s == 2 else 0)
-    return valid * Dd * per_td
+def fwd_alg_ops(Bsz, Dd, N, L, s, lengths=None):
+    """(transcendental, plain) lane-operations of one forward."""
+    td = (int(sum(lengths)) if lengths is not None else Bsz * L) * Dd
+    trans = td * (TRANS_PER_TDN * N + TRANS_PER_TD)
+    plain = td * (PLAIN_PER_TDN * N + PLAIN_PER_TD + (CVT16_PER_TD if s == 2 else 0))
+    return trans, plain
+
+
+def alu_floor_ms(ops, rates):
+    """Shortest time the vector units can do `ops` in at the measured rates: every SIMD busy,
+    each wave64 instruction costing its measured cycles, at the measured clock."""
+    trans, plain = ops
+    cycles = (trans * rates["exp"]["cycles_per_unit"] + plain * rates["fma"]["cycles_per_unit"]) / 64.0
+    return cycles / rates["simds"] / (rates["clock_GHz"] * 1e9) * 1e3
+
+
+def measure_alu_rates(waves_per_simd=3):
+    """Issue rates of the scan's instructions on this chip at the headline's occupancy (three waves
+    per SIMD), from the library's probe: cycles per wave64 instruction and the clock under load."""
+    out = {}
+    for kind in ("fma", "exp", "dpp_mul", "scan_step"):
+        ss.alu_probe(kind, waves_per_simd, iters=256)        # warm
+        out[kind] = ss.alu_probe(kind, waves_per_simd, iters=8192)
+    props = torch.cuda.get_device_properties(0)
+    out["simds"] = props.multi_processor_count * 4
+    out["clock_GHz"] = out["scan_step"]["clock_GHz"]   # the mix closest to the kernel's
+    return out
 
 
 def kernel_source_hash():
@@ -118,7 +140,7 @@ def dev_problem(prob):
     return {k: (None if prob.get(k) is None else prob[k].to("cuda")) for k in keys}
 
 
-def bench_headline(steps, warmup, stream):
+def bench_headline(steps, warmup, stream, prewarm_s=0.3):
     sets = []
     for r in range(3):
         prob = inputs.make_config(2, seed=2 + 100 * r, decode_steps=0)
@@ -134,6 +156,17 @@ def bench_headline(steps, warmup, stream):
     def step(i):
         calls[i % 3]()
 
+    # untimed calls until the clock has settled (the GPU needs ~100 ms of load; a cold
+    # clock reads 15-25% slow), then the requested warm-up steps
+    torch.cuda.synchronize()
+    t_pre, n_pre = time.perf_counter(), 0
+    while time.perf_counter() - t_pre < prewarm_s:
+        step(n_pre)
+        n_pre += 1
+        if n_pre % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    prewarm = {"prewarm_s": time.perf_counter() - t_pre, "prewarm_calls": n_pre}
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -173,6 +206,7 @@ def bench_headline(steps, warmup, stream):
     warm[1].record(stream)
     torch.cuda.synchronize()
     stats["warm_single_set_kernel_ms"] = warm[0].elapsed_time(warm[1]) / reps
+    stats.update(prewarm)
     return ms, kernel_ms, stats, wall, (Bsz, Dd, N, L), sets, ys
 
 
@@ -207,7 +241,7 @@ def bench_rows(stream):
     rows["fwd_ragged_B4_D5120_L8192_bf16"] = {
         "ms": ms, "lengths": lens, "token_channel_per_s": sum(lens) * 5120 / (ms * 1e-3),
         "alg_GBps": byt / (ms * 1e-3) / 1e9, "hbm_frac": byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-        "alu_frac": fwd_alg_slots(4, 5120, 16, 8192, 2, lens) / (ms * 1e-3) / PEAK_SLOTS}
+        "alu_ops": fwd_alg_ops(4, 5120, 16, 8192, 2, lens)}
     del p3, c3, y3
     # packed documents (lengths U[1, 512]) and an initial state on the mamba-130m layer
     prob2p = inputs.make_config(2, decode_steps=0)
@@ -225,7 +259,7 @@ def bench_rows(stream):
     docs = int((seq[:, 1:] != seq[:, :-1]).sum().item()) + 8
     rows["fwd_packed_docs_h0_B8_D1536_L2048_f16"] = {
         "ms": ms, "documents": docs, "token_channel_per_s": 8 * 1536 * 2048 / (ms * 1e-3),
-        "alu_frac": fwd_alg_slots(8, 1536, 16, 2048, 2) / (ms * 1e-3) / PEAK_SLOTS}
+        "hbm_frac": fwd_alg_bytes(8, 1536, 16, 2048, 2) / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
     del g2p, c2p, y2p, s2p, seq, h0
     rows["conv1d_silu_B8_D1536_L2048_W4_f16"] = bench_conv(stream)
     # Mamba-2 SSD chunked scan on the matrix cores: d_model 768, expand 2 -> 24 heads of 64,
@@ -545,9 +579,8 @@ def main():
     tc = Bsz * Dd * L
     value = tc / (ms * 1e-3)
     alg_bytes = fwd_alg_bytes(Bsz, Dd, N, L, 2)
-    alg_slots = fwd_alg_slots(Bsz, Dd, N, L, 2)
-    achieved_slots = alg_slots / (kernel_ms * 1e-3)
     traffic = recorded_traffic()
+    achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
     result = {
         "metric": "selective-scan fwd (token*channel)/s and HBM GB/s as % of MI355X peak",
         "value": value,
@@ -560,31 +593,56 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "io_dtype": "f16",
         "data": "synthetic",
         "config": {"workload": "mamba-130m layer selective-scan forward: B=8, d_inner=1536, d_state=16, "
                                "L=2048, fp16 I/O, softplus+bias, D skip, SiLU gate, final state",
-                   "io_dtype": "f16", "batch": Bsz, "d_inner": Dd, "d_state": N, "seq_len": L,
-                   "input_sets_rotated": 3},
-        "roofline": {"bound": "alu", "achieved": achieved_slots / 1e12, "peak": PEAK_SLOTS / 1e12,
-                     "unit": "T VALU-slot/s", "frac": achieved_slots / PEAK_SLOTS,
-                     "traffic": traffic,
+                   "io_dtype": "f16", "compute_dtype": "f32", "batch": Bsz, "d_inner": Dd, "d_state": N,
+                   "seq_len": L, "input_sets_rotated": 3},
+        # the HBM roofline of the one kernel of a step: algorithmic bytes per launch over the
+        # launch's duration (HIP events around K back-to-back launches on the launch stream,
+        # divided by K), against MI355X's 8 TB/s
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "kernel": "ss_fwd_chunk_kernel<f16, FINAL>",
-                     "kernel_ms": kernel_ms,
-                     **stats,
-                     "alg_slots_per_launch": alg_slots},
-        "hbm": {"alg_bytes_per_launch": alg_bytes, "achieved_GBps": alg_bytes / (kernel_ms * 1e-3) / 1e9,
-                "peak_GBps": PEAK_HBM_GBPS, "frac": alg_bytes / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                "whole_job_GBps": alg_bytes / (ms * 1e-3) / 1e9},
+                     "alg_bytes_per_launch": alg_bytes,
+                     "kernel_ms_event_region": kernel_ms,
+                     **stats},
         "wall_s_timed_region": wall,
     }
+    # the vector-ALU ceiling, measured: the algorithm's instruction mix priced at the issue
+    # rates the library's probe measures on this chip at the kernel's occupancy
+    try:
+        rates = measure_alu_rates(3)
+        ops = fwd_alg_ops(Bsz, Dd, N, L, 2)
+        floor = alu_floor_ms(ops, rates)
+        step_cycles = rates["scan_step"]["cycles_per_unit"]
+        # the scan core alone as this kernel maps it: one step per lane per (t, d, n), on
+        # 16 lanes per channel
+        core = tc * N / 64.0 * step_cycles / rates["simds"] / (rates["clock_GHz"] * 1e9) * 1e3
+        result["alu"] = {
+            "clock_GHz_under_load": rates["clock_GHz"],
+            "cycles_per_wave64_instr": {k: rates[k]["cycles_per_unit"] for k in ("fma", "exp", "dpp_mul")},
+            "cycles_per_scan_step": step_cycles,
+            "alg_trans_lane_ops": ops[0], "alg_plain_lane_ops": ops[1],
+            "floor_ms": floor, "frac": floor / kernel_ms,
+            "scan_core_floor_ms": core, "scan_core_frac": core / kernel_ms,
+            "probe": {k: rates[k] for k in ("fma", "exp", "dpp_mul", "scan_step")}}
+    except Exception as e:
+        rates = None
+        result["alu_error"] = str(e)[:200]
     try:
         result["copy_probe_GBps"] = copy_probe(stream)
-        result["hbm"]["frac_of_copy_probe"] = result["hbm"]["achieved_GBps"] / result["copy_probe_GBps"]
+        result["roofline"]["frac_of_copy_probe"] = achieved / result["copy_probe_GBps"]
     except Exception as e:
         result["copy_probe_error"] = str(e)[:200]
     if not args.no_rows:
         log("other workloads")
         result["rows"] = bench_rows(stream)
+        for row in result["rows"].values():
+            if rates is not None and "alu_ops" in row:
+                row["alu_floor_ms"] = alu_floor_ms(row["alu_ops"], rates)
+                row["alu_frac"] = row["alu_floor_ms"] / row["ms"]
     if not args.no_cpu:
         log("cpu baseline (float64 oracle)")
         result["cpu_baseline"] = cpu_baseline()

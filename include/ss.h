@@ -307,6 +307,33 @@ const char *ss_status_str(ss_status s);
  */
 ss_status ss_copy_probe(const void *src, void *dst, size_t bytes, void *stream);
 
+/*
+ * Measurement utility, not part of the scan: the issue rate of the vector
+ * instructions the scan is made of, so that its ALU ceiling is measured on
+ * the chip rather than taken from a datasheet.  Launches `workgroups`
+ * workgroups of 256 threads (4 waves), each with `lds_bytes` of LDS it does
+ * not use (0..65536: it limits how many workgroups share a CU, as a kernel's
+ * own LDS does); every wave runs `iters` iterations of 16 instructions of
+ * `kind` (SS_PROBE_SCAN_STEP: 16 steps of the scan's per-lane state update,
+ * each two DPP-broadcast multiplies, one exp2 and one FMA) between two reads
+ * of the shader clock (s_memtime) and of the constant 100 MHz clock
+ * (s_memrealtime), and writes to `out`, a device int64 array of 6 entries per
+ * wave: [clock0, clock1, real0, real1, place, 0], where place holds the
+ * hardware wave-id register (bits 0..31: SIMD, CU, shader engine) and the XCD
+ * (bits 32..63), so that the host can count the waves each SIMD held.
+ * SS_ERR_BAD_SHAPE unless 1 <= workgroups <= 2^20, 1 <= iters <= 2^20 and
+ * 0 <= lds_bytes <= 65536; SS_ERR_UNSUPPORTED for an unknown kind.
+ */
+typedef enum ss_probe_kind {
+    SS_PROBE_FMA = 0,        /* v_fma_f32, 16 independent chains */
+    SS_PROBE_EXP = 1,        /* v_exp_f32, 16 independent chains */
+    SS_PROBE_DPP_MUL = 2,    /* v_mul_f32 with a DPP row broadcast, 16 chains */
+    SS_PROBE_SCAN_STEP = 3   /* the scan's per-lane step (4 instructions) */
+} ss_probe_kind;
+
+ss_status ss_alu_probe(int32_t kind, int32_t workgroups, int32_t iters, int32_t lds_bytes, int64_t *out,
+                       void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -129,6 +129,20 @@ ss_status ss_fwd(const ss_problem* p, const void* u, const void* delta, const fl
                  const void* Cm, const float* D, const void* z, const float* delta_bias, const int32_t* lengths,
                  const int32_t* seq_idx, const float* h0, void* y, float* last_state, float* ckpt, void* workspace,
                  size_t workspace_bytes, void* stream) {
+  return ss::fwd_checked(p, u, delta, A, Bm, Cm, D, z, delta_bias, lengths, seq_idx, h0, y, last_state, ckpt,
+                         workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace ss {
+
+size_t fwd_workspace_bytes(const ss_problem* p) { return ss_fwd_workspace_size(p); }
+
+ss_status fwd_checked(const ss_problem* p, const void* u, const void* delta, const float* A, const void* Bm,
+                      const void* Cm, const float* D, const void* z, const float* delta_bias, const int32_t* lengths,
+                      const int32_t* seq_idx, const float* h0, void* y, float* last_state, float* ckpt,
+                      void* workspace, size_t workspace_bytes, void* stream) {
   ss_status s = check_problem(p, true);
   if (s != SS_OK) return s;
   if (!u || !delta || !A || !Bm || !Cm || !y) return SS_ERR_NULL_ARG;
@@ -174,6 +188,10 @@ ss_status ss_fwd(const ss_problem* p, const void* u, const void* delta, const fl
   }
   return from_hip(ss::launch_fwd(k, pl.nchunks, static_cast<hipStream_t>(stream)));
 }
+
+}  // namespace ss
+
+extern "C" {
 
 ss_status ss_fwd_step(const ss_problem* p, const void* u_t, const void* delta_t, const float* A, const void* B_t,
                       const void* C_t, const float* D, const void* z_t, const float* delta_bias,
@@ -423,6 +441,16 @@ ss_status ss_copy_probe(const void* src, void* dst, size_t bytes, void* stream) 
   if (!aligned(src) || !aligned(dst)) return SS_ERR_MISALIGNED;
   if (bytes % 16 != 0 || bytes == 0) return SS_ERR_BAD_SHAPE;
   return from_hip(ss::launch_copy(src, dst, (int64_t)bytes, static_cast<hipStream_t>(stream)));
+}
+
+ss_status ss_alu_probe(int32_t kind, int32_t workgroups, int32_t iters, int32_t lds_bytes, int64_t* out,
+                       void* stream) {
+  if (!out) return SS_ERR_NULL_ARG;
+  if (!aligned(out)) return SS_ERR_MISALIGNED;
+  if (kind < SS_PROBE_FMA || kind > SS_PROBE_SCAN_STEP) return SS_ERR_UNSUPPORTED;
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 20)) return SS_ERR_BAD_SHAPE;
+  if (lds_bytes < 0 || lds_bytes > 65536) return SS_ERR_BAD_SHAPE;
+  return from_hip(ss::launch_alu_probe(kind, workgroups, iters, lds_bytes, out, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

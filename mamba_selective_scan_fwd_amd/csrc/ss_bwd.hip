@@ -44,7 +44,7 @@
 namespace ss {
 
 hipError_t launch_carry(const float* aggP, const float* aggS, float* carry, int64_t nch, int32_t nchunks,
-                        bool reverse, hipStream_t st);
+                        int32_t npairs, bool reverse, hipStream_t st);
 
 namespace {
 
@@ -663,7 +663,7 @@ hipError_t launch_bwd_seq(const BwdParams& p, hipStream_t st) {
     hipLaunchKernelGGL((ss_bwd_chunk_kernel<IO, false, SEQ>), dim3((uint32_t)units), dim3(kThreads), 0, st, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_carry(p.aggP, p.aggG, p.gcarry, p.batch * p.dim, (int32_t)K, true, st);
+    e = launch_carry(p.aggP, p.aggG, p.gcarry, p.batch * p.dim, (int32_t)K, (int32_t)K, true, st);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((ss_bwd_chunk_kernel<IO, true, SEQ>), grid, dim3(kThreads), 0, st, p);

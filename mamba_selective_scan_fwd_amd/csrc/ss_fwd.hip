@@ -42,7 +42,7 @@
 namespace ss {
 
 hipError_t launch_carry(const float* aggP, const float* aggS, float* carry, int64_t nch, int32_t nchunks,
-                        bool reverse, hipStream_t st);
+                        int32_t npairs, bool reverse, hipStream_t st);
 
 namespace {
 
@@ -429,10 +429,12 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
 // (g, n), state n fastest so that 16 lanes read one chunk's 64 contiguous
 // bytes, serially combines chunks [g*per, (g+1)*per) of state n; the value
 // entering each group is then combined from the groups on its left through
-// LDS, and each group replays its chunks from it.
+// LDS, and each group replays its chunks from it.  Only the first npairs
+// visited chunks have a pair (the forward's last chunk has none: nothing
+// follows it); no other pair is read.
 __global__ void __launch_bounds__(256) ss_carry_kernel(const float* __restrict__ aggP, const float* __restrict__ aggS,
                                                        float* __restrict__ carry, int64_t nch, int32_t nchunks,
-                                                       int32_t reverse) {
+                                                       int32_t npairs, int32_t reverse) {
   __shared__ float sP[16][16], sS[16][16];
   const int tid = threadIdx.x;
   const int n = tid % 16, g = tid / 16;
@@ -447,8 +449,9 @@ __global__ void __launch_bounds__(256) ss_carry_kernel(const float* __restrict__
   // local pair over [c0, c1): applying it maps the value entering c0 to the
   // value leaving c1 - 1
   float P = 1.0f, S = 0.0f;
+  const int c1p = c1 < npairs ? c1 : npairs;
 #pragma unroll 4
-  for (int c = c0; c < c1; ++c) {
+  for (int c = c0; c < c1p; ++c) {
     const float pc = aggP[slot(c)];
     const float sc = aggS[slot(c)];
     S = fmaf(pc, S, sc);
@@ -463,7 +466,7 @@ __global__ void __launch_bounds__(256) ss_carry_kernel(const float* __restrict__
 #pragma unroll 4
   for (int c = c0; c < c1; ++c) {
     carry[slot(c)] = E;
-    E = fmaf(aggP[slot(c)], E, aggS[slot(c)]);
+    if (c < c1p) E = fmaf(aggP[slot(c)], E, aggS[slot(c)]);
   }
 }
 
@@ -502,15 +505,6 @@ __global__ void __launch_bounds__(kThreads) ss_step_kernel(StepParams p) {
   }
 }
 
-// Plain device copy, 16 bytes per lane per iteration: the reference kernel
-// for HBM bandwidth and for calibrating traffic counters.
-__global__ void __launch_bounds__(256) ss_copy_kernel(const float4* __restrict__ src, float4* __restrict__ dst,
-                                                      int64_t n16) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (; i < n16; i += stride) dst[i] = src[i];
-}
-
 template <int IO, bool PAIR, bool SEQ>
 hipError_t launch_fwd_variant(const FwdParams& p, int64_t nchunks, hipStream_t st) {
   const int64_t blocks_per_chunk = p.batch * p.ch_blocks;
@@ -522,8 +516,8 @@ hipError_t launch_fwd_variant(const FwdParams& p, int64_t nchunks, hipStream_t s
                        dim3((uint32_t)(blocks_per_chunk * (nchunks - 1))), dim3(kThreads), 0, st, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // pass 2: entry states
-    e = launch_carry(p.aggP, p.aggS, p.carry, p.batch * p.dim, p.nchunks, false, st);
+    // pass 2: entry states (pairs of chunks 0 .. K-2 only)
+    e = launch_carry(p.aggP, p.aggS, p.carry, p.batch * p.dim, p.nchunks, p.nchunks - 1, false, st);
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, true, PAIR, SEQ>), dim3((uint32_t)(blocks_per_chunk * nchunks)),
@@ -571,19 +565,9 @@ hipError_t launch_step(const StepParams& p, hipStream_t st) {
 }
 
 hipError_t launch_carry(const float* aggP, const float* aggS, float* carry, int64_t nch, int32_t nchunks,
-                        bool reverse, hipStream_t st) {
+                        int32_t npairs, bool reverse, hipStream_t st) {
   hipLaunchKernelGGL(ss_carry_kernel, dim3((uint32_t)nch), dim3(256), 0, st, aggP, aggS, carry, nch, nchunks,
-                     (int32_t)(reverse ? 1 : 0));
-  return hipGetLastError();
-}
-
-hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st) {
-  const int64_t n16 = bytes / 16;
-  int64_t blocks = (n16 + 255) / 256;
-  if (blocks > 256 * 16) blocks = 256 * 16;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(ss_copy_kernel, dim3((uint32_t)blocks), dim3(256), 0, st,
-                     reinterpret_cast<const float4*>(src), reinterpret_cast<float4*>(dst), n16);
+                     npairs, (int32_t)(reverse ? 1 : 0));
   return hipGetLastError();
 }
 

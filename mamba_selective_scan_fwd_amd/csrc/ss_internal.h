@@ -7,7 +7,17 @@
 
 #include <utility>
 
+#include "../../include/ss.h"
+
 namespace ss {
+
+// ss_fwd's validation and dispatch, with the workspace given explicitly (the
+// C entry points ss_fwd and ss_fwd_noalloc both go through it).
+ss_status fwd_checked(const ss_problem* p, const void* u, const void* delta, const float* A, const void* Bm,
+                      const void* Cm, const float* D, const void* z, const float* delta_bias, const int32_t* lengths,
+                      const int32_t* seq_idx, const float* h0, void* y, float* last_state, float* ckpt,
+                      void* workspace, size_t workspace_bytes, void* stream);
+size_t fwd_workspace_bytes(const ss_problem* p);
 
 struct FwdParams {
   int32_t io;
@@ -143,5 +153,7 @@ int64_t conv_tblocks(int64_t seqlen);
 hipError_t launch_step(const StepParams& p, hipStream_t st);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t st);
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
+hipError_t launch_alu_probe(int32_t kind, int32_t workgroups, int32_t iters, int32_t lds_bytes, int64_t* out,
+                            hipStream_t st);
 
 }  // namespace ss

@@ -42,8 +42,9 @@ _lib = None
 
 # every symbol declared in include/ss.h
 EXPORTS = ("ss_fwd", "ss_fwd_step", "ss_bwd", "ss_fwd_workspace_size", "ss_bwd_workspace_size",
-           "ss_ckpt_count", "ss_status_str", "ss_copy_probe", "ss_conv1d_fwd", "ss_conv1d_step",
+           "ss_ckpt_count", "ss_status_str", "ss_copy_probe", "ss_alu_probe", "ss_conv1d_fwd", "ss_conv1d_step",
            "ss_ssd_fwd", "ss_ssd_workspace_size")
+PROBE_KINDS = {"fma": 0, "exp": 1, "dpp_mul": 2, "scan_step": 3}
 
 
 def load_library(path: str = LIB_PATH):
@@ -82,6 +83,8 @@ def load_library(path: str = LIB_PATH):
     lib.ss_ssd_fwd.argtypes = [SP] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]
     lib.ss_copy_probe.restype = ctypes.c_int
     lib.ss_copy_probe.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
+    lib.ss_alu_probe.restype = ctypes.c_int
+    lib.ss_alu_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, _vp]
     _lib = lib
     return lib
 
@@ -482,6 +485,42 @@ def copy_probe(src, dst):
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("dst too small")
     _check(lib.ss_copy_probe(_ptr(src), _ptr(dst), nbytes, _stream(src.device)))
+
+
+def alu_probe(kind, waves_per_simd=3, iters=2048, lds_bytes=0, workgroups=None, device=None):
+    """Issue rate of one kind of vector instruction ("fma", "exp", "dpp_mul", "scan_step").
+    Launches workgroups (default waves_per_simd * CUs) of 4 waves, each with lds_bytes of unused
+    LDS.  Every wave records where it ran, so the rate is taken per SIMD: the span from the first
+    of its waves to start to the last to finish (the SIMD's arbiter favours older waves, so single
+    waves finish at very different times), over all the instructions its waves issued.  Returns a
+    dict: shader cycles per unit on one SIMD (a wave64 instruction; for "scan_step" a step of 4
+    instructions), median over SIMDs; the shader clock over those spans (GHz, median); the
+    histogram of waves per SIMD."""
+    lib = load_library()
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    wg = workgroups if workgroups is not None else cus * waves_per_simd
+    out = torch.zeros(wg * 4 * 6, dtype=torch.int64, device=dev)
+    _check(lib.ss_alu_probe(PROBE_KINDS[kind], wg, iters, lds_bytes, _ptr(out), _stream(dev)))
+    torch.cuda.synchronize(dev)
+    a = out.view(-1, 6).cpu()
+    place = (a[:, 4] >> 32) * 65536 + (a[:, 4] & 0xFFF0)       # XCD, shader engine, CU, SIMD
+    keys, inv, counts = torch.unique(place, return_inverse=True, return_counts=True)
+    n = keys.numel()
+    big = torch.iinfo(torch.int64).max
+    c0 = torch.full((n,), big, dtype=torch.int64).scatter_reduce(0, inv, a[:, 0], "amin")
+    c1 = torch.zeros(n, dtype=torch.int64).scatter_reduce(0, inv, a[:, 1], "amax")
+    r0 = torch.full((n,), big, dtype=torch.int64).scatter_reduce(0, inv, a[:, 2], "amin")
+    r1 = torch.zeros(n, dtype=torch.int64).scatter_reduce(0, inv, a[:, 3], "amax")
+    span = (c1 - c0).double()
+    secs = (r1 - r0).double() / 100e6
+    per_instr = span / (iters * 16.0 * counts.double())
+    hist = {int(k): int(v) for k, v in zip(*torch.unique(counts, return_counts=True))}
+    return {"kind": kind, "unit": "step of 4 instructions" if kind == "scan_step" else "wave64 instruction",
+            "workgroups": wg, "lds_bytes": lds_bytes, "cycles_per_unit": float(per_instr.median()),
+            "clock_GHz": float((span / secs).median()) / 1e9, "waves_per_simd_hist": hist,
+            "simds_used": int(n), "span_cycles_median": float(span.median()),
+            "span_seconds_median": float(secs.median())}
 
 
 class SelectiveScanFn(torch.autograd.Function):

@@ -117,6 +117,20 @@ def test_step_and_bwd_validation():
     assert lib.ss_copy_probe(FAKE, FAKE, 15, None) == 2
 
 
+def test_alu_probe_rejects_bad_arguments():
+    lib = ss.load_library()
+    assert lib.ss_alu_probe(0, 4, 16, 0, None, None) == 1          # no output
+    assert lib.ss_alu_probe(0, 4, 16, 0, FAKE + 8, None) == 4      # misaligned output
+    assert lib.ss_alu_probe(4, 4, 16, 0, FAKE, None) == 5          # unknown kind
+    assert lib.ss_alu_probe(-1, 4, 16, 0, FAKE, None) == 5
+    assert lib.ss_alu_probe(0, 0, 16, 0, FAKE, None) == 2          # empty grid
+    assert lib.ss_alu_probe(0, (1 << 20) + 1, 16, 0, FAKE, None) == 2
+    assert lib.ss_alu_probe(0, 4, 0, 0, FAKE, None) == 2           # no iterations
+    assert lib.ss_alu_probe(0, 4, (1 << 20) + 1, 0, FAKE, None) == 2
+    assert lib.ss_alu_probe(0, 4, 16, -1, FAKE, None) == 2         # LDS outside 0..65536
+    assert lib.ss_alu_probe(0, 4, 16, 65537, FAKE, None) == 2
+
+
 def _conv_prob(**kw):
     d = dict(batch=2, dim=3, seqlen=10, width=4, io_dtype=0, silu=1, reserved=0)
     d.update(kw)
