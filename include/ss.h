@@ -134,6 +134,33 @@ ss_status ss_fwd(const ss_problem *p,
                  void *stream);
 
 /*
+ * ss_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, results and errors as ss_fwd, without the workspace: the
+ * time-chunked scan keeps its chunk pairs and carries in a fixed array of
+ * ss_fwd_noalloc_max_workspace() bytes (2 MiB) of device memory that the
+ * library holds on every GPU it runs on until the process ends.  No call
+ * allocates or frees memory.  The array is shared by every call on one GPU
+ * and keeps the last call's contents (nothing in it needs clearing): calls
+ * that overlap in time on one GPU, e.g. on two streams, race on it and must
+ * be ordered by the caller.  `stream` must belong to the current device.
+ * Returns SS_ERR_UNSUPPORTED for a problem whose workspace would exceed the
+ * array (no valid problem does: the scan splits time only for problems with
+ * fewer than 1024 wavefronts, which bounds the workspace at 1.6 MB), and
+ * SS_ERR_HIP when the array's device address cannot be obtained.
+ */
+ss_status ss_fwd_noalloc(const ss_problem *p,
+                         const void *u, const void *delta, const float *A,
+                         const void *Bm, const void *Cm,
+                         const float *D, const void *z, const float *delta_bias,
+                         const int32_t *lengths, const int32_t *seq_idx, const float *h0,
+                         void *y, float *last_state, float *ckpt,
+                         void *stream);
+
+/* Bytes of the fixed device array ss_fwd_noalloc uses as its workspace. */
+size_t ss_fwd_noalloc_max_workspace(void);
+
+/*
  * One decode step from a carried state ("mamba-metal" README, "O(1) per
  * token via state caching"; page "Mamba", Part IV Stage 7, single-step
  * decoding updates the cached state in place).  p->seqlen is ignored.

@@ -7,7 +7,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libss.so")
-SOURCES = ["ss_fwd.hip", "ss_bwd.hip", "ss_conv.hip", "ss_ssd.hip", "ss_probe.hip", "ss_abi.cpp"]
+SOURCES = ["ss_fwd.hip", "ss_bwd.hip", "ss_conv.hip", "ss_ssd.hip", "ss_probe.hip", "ss_noalloc.hip", "ss_abi.cpp"]
 HEADERS = ["ss_device.h", "ss_internal.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,0 +1,71 @@
+// ss_noalloc.hip -- ss_fwd_noalloc: the forward scan for callers that cannot
+// allocate device memory (code under HIP graph capture, tight serving loops,
+// harnesses that forbid allocation).  It is ss_fwd with the time-chunked
+// scan's workspace taken from a fixed array in device memory instead of from
+// the caller.
+//
+// The array lives for the life of the process, one copy per GPU that the
+// library runs on.  Every call on a GPU uses that GPU's copy: calls that
+// overlap in time on one GPU (on different streams) race on it.  Nothing in
+// it needs clearing between calls: the chunk pairs and carries of a call are
+// written before that call reads them.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "../../include/ss.h"
+#include "ss_internal.h"
+
+namespace {
+
+// Largest forward workspace any valid problem needs: the scan splits time only
+// while the problem has fewer than 1024 wavefronts (4 per 16 channels), into
+// at most ceil(1024 / waves) chunks, so batch * dim * chunks <= 8188 and the
+// three per-chunk arrays of 16 floats take at most 1.57 MB.
+constexpr size_t kScratchBytes = (size_t)2 << 20;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+void* g_ptr[kMaxDevices] = {};
+
+// The device address of this GPU's copy of `scratch`, looked up once per
+// device with that device current (in host code the array's name is only a
+// stand-in for it).  Null when the runtime cannot give it.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_ptr[dev] = p;
+  }
+  return g_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ss_fwd_noalloc_max_workspace(void) { return kScratchBytes; }
+
+ss_status ss_fwd_noalloc(const ss_problem* p, const void* u, const void* delta, const float* A, const void* Bm,
+                         const void* Cm, const float* D, const void* z, const float* delta_bias,
+                         const int32_t* lengths, const int32_t* seq_idx, const float* h0, void* y,
+                         float* last_state, float* ckpt, void* stream) {
+  // validation of the problem itself happens in fwd_checked; an invalid
+  // problem needs no workspace and is rejected there
+  const size_t need = ss::fwd_workspace_bytes(p);
+  if (need > kScratchBytes) return SS_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (need > 0) {
+    ws = scratch_ptr();
+    if (!ws) return SS_ERR_HIP;
+  }
+  return ss::fwd_checked(p, u, delta, A, Bm, Cm, D, z, delta_bias, lengths, seq_idx, h0, y, last_state, ckpt,
+                         ws, need > 0 ? kScratchBytes : 0, stream);
+}
+
+}  // extern "C"

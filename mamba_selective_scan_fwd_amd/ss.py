@@ -43,7 +43,7 @@ _lib = None
 # every symbol declared in include/ss.h
 EXPORTS = ("ss_fwd", "ss_fwd_step", "ss_bwd", "ss_fwd_workspace_size", "ss_bwd_workspace_size",
            "ss_ckpt_count", "ss_status_str", "ss_copy_probe", "ss_alu_probe", "ss_conv1d_fwd", "ss_conv1d_step",
-           "ss_ssd_fwd", "ss_ssd_workspace_size")
+           "ss_ssd_fwd", "ss_ssd_workspace_size", "ss_fwd_noalloc", "ss_fwd_noalloc_max_workspace")
 PROBE_KINDS = {"fma": 0, "exp": 1, "dpp_mul": 2, "scan_step": 3}
 
 
@@ -67,6 +67,10 @@ def load_library(path: str = LIB_PATH):
     lib.ss_bwd_workspace_size.argtypes = [P]
     lib.ss_fwd.restype = ctypes.c_int
     lib.ss_fwd.argtypes = [P] + [_vp] * 14 + [_vp, ctypes.c_size_t, _vp]
+    lib.ss_fwd_noalloc.restype = ctypes.c_int
+    lib.ss_fwd_noalloc.argtypes = [P] + [_vp] * 14 + [_vp]
+    lib.ss_fwd_noalloc_max_workspace.restype = ctypes.c_size_t
+    lib.ss_fwd_noalloc_max_workspace.argtypes = []
     lib.ss_fwd_step.restype = ctypes.c_int
     lib.ss_fwd_step.argtypes = [P] + [_vp] * 11 + [_vp]
     lib.ss_bwd.restype = ctypes.c_int
