@@ -167,6 +167,22 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
+// The SIMD's issue arbiter serves the oldest of equally ranked waves first, so
+// of the waves that share a SIMD the first to arrive races ahead and the last
+// one finishes alone, with the SIMD idle between its instructions.  A wave
+// that walks a sequence therefore lowers its own rank as its work proceeds:
+// 3 in the first half, 2 to three quarters, 1 to seven eighths, 0 after.
+// Whenever a wave passes a mark the waves behind it are served first until
+// they pass it too, so they all reach the last eighth close together and only
+// that stretch is served oldest first.
+__device__ __forceinline__ void rank_by_progress(int done, int total) {
+  const int e = total > 0 ? (int)(((int64_t)done * 8) / total) : 0;
+  if (e < 4) __builtin_amdgcn_s_setprio(3);
+  else if (e < 6) __builtin_amdgcn_s_setprio(2);
+  else if (e < 7) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Workgroup index remapped so that consecutive logical blocks share an XCD
 // (MI355X dispatches workgroups round-robin over its 8 XCDs, each with its
 // own L2): logical blocks that read the same B/C rows then hit one L2.

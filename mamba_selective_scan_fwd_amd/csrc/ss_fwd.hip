@@ -46,6 +46,16 @@ hipError_t launch_carry(const float* aggP, const float* aggS, float* carry, int6
 
 namespace {
 
+// flags of a forward launch, fixed at compile time
+constexpr int kFlSoftplus = 1;  // Delta = softplus(delta + bias)
+constexpr int kFlGate = 2;      // y *= SiLU(z)
+
+// A byte offset that puts every access of a tile out of range: added to a
+// lane's offset inside its view (< 2^30: a view spans at most 16 rows of
+// 2^24 four-byte elements) it stays below 2^32 and above every view's size,
+// so loads return 0 and no branch is needed around the last tile's prefetch.
+constexpr uint32_t kTileNone = 0x7fff0000u;
+
 constexpr int kBCStride = kTile + 4;     // padded LDS row of the B tile (floats)
 constexpr int kCTRow = 20;               // padded LDS row of the transposed C tile
 constexpr int kPRow = 20;                // padded LDS row of the state tile (16 states + 4)
@@ -98,15 +108,16 @@ struct Views {
   __amdgpu_buffer_rsrc_t u, dl, z, y, B, C;
 };
 
-template <int IO>
-__device__ __forceinline__ void load_owned(RawOwned<IO>& r, const Views& v, uint32_t lane_elem0, int t0, int l) {
+template <int IO, bool GATE>
+__device__ __forceinline__ void load_owned(RawOwned<IO>& r, const Views& v, uint32_t lane_off, uint32_t tile_off) {
   constexpr uint32_t s = io_bytes<IO>();
+  const uint32_t base = lane_off + tile_off;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t off = (lane_elem0 + (uint32_t)(t0 + 16 * i + l)) * s;
+    const uint32_t off = base + (uint32_t)(16 * i) * s;
     r.u[i] = bload<IO>(v.u, off);
     r.dl[i] = bload<IO>(v.dl, off);
-    r.z[i] = bload<IO>(v.z, off);  // a zero-size view when there is no gate
+    if constexpr (GATE) r.z[i] = bload<IO>(v.z, off);
   }
 }
 
@@ -123,18 +134,24 @@ struct BCRaw {
 };
 
 template <int IO, bool PAIR>
-__device__ __forceinline__ void load_bc(BCRaw<IO, PAIR>& r, const Views& v, uint32_t seqlen, int t0, int tid,
+__device__ __forceinline__ uint32_t bc_lane_off(uint32_t seqlen, int tid) {
+  const int n = tid / 16, j = tid % 16;
+  return ((uint32_t)n * seqlen + (uint32_t)(PAIR ? 2 * j : j)) * io_bytes<IO>();
+}
+
+template <int IO, bool PAIR>
+__device__ __forceinline__ void load_bc(BCRaw<IO, PAIR>& r, const Views& v, uint32_t lane_off, uint32_t tile_off,
                                         bool need_c) {
   constexpr uint32_t s = io_bytes<IO>();
-  const int n = tid / 16, j = tid % 16;
+  const uint32_t base = lane_off + tile_off;
 #pragma unroll
   for (int k = 0; k < BCRaw<IO, PAIR>::kN; ++k) {
     if constexpr (PAIR) {
-      const uint32_t off = ((uint32_t)n * seqlen + (uint32_t)(t0 + 32 * k + 2 * j)) * s;
+      const uint32_t off = base + (uint32_t)(32 * k) * s;
       r.b[k] = __builtin_amdgcn_raw_buffer_load_b32(v.B, off, 0, 0);
       r.c[k] = need_c ? __builtin_amdgcn_raw_buffer_load_b32(v.C, off, 0, 0) : 0u;
     } else {
-      const uint32_t off = ((uint32_t)n * seqlen + (uint32_t)(t0 + j + 16 * k)) * s;
+      const uint32_t off = base + (uint32_t)(16 * k) * s;
       r.b[k] = bload<IO>(v.B, off);
       r.c[k] = need_c ? bload<IO>(v.C, off) : raw_t<IO>(0);
     }
@@ -169,21 +186,26 @@ __device__ __forceinline__ void store_bc(FwdSmem<FINAL>& sm, int buf, const BCRa
   }
 }
 
-// Per-(t, d) work of the four owned steps: Delta, Delta*u (zero when masked).
-template <int IO>
+// Per-(t, d) work of the four owned steps: Delta, Delta*u (zero when masked;
+// a FULL tile has no masked step).
+template <int IO, int FL, bool FULL>
 __device__ __forceinline__ void prep_owned(Owned& o, const RawOwned<IO>& r, int l, int nvalid, float bias,
-                                           bool softplus, float& dt_sum) {
+                                           float& dt_sum) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const bool v = 16 * i + l < nvalid;
     const float u = bits_f32<IO>(r.u[i]);
     const float x = bits_f32<IO>(r.dl[i]) + bias;
-    float dt = softplus ? softplus_f(x) : x;
-    dt = v ? dt : 0.0f;
+    float dt = (FL & kFlSoftplus) ? softplus_f(x) : x;
+    float dtu = dt * u;
+    if constexpr (!FULL) {
+      const bool ok = 16 * i + l < nvalid;
+      dt = ok ? dt : 0.0f;
+      dtu = ok ? dtu : 0.0f;
+    }
     o.dt[i] = dt;
-    o.dtu[i] = v ? dt * u : 0.0f;
+    o.dtu[i] = dtu;
     o.u[i] = u;
-    o.z[i] = bits_f32<IO>(r.z[i]);
+    if constexpr ((FL & kFlGate) != 0) o.z[i] = bits_f32<IO>(r.z[i]);
     dt_sum += dt;
   }
 }
@@ -233,28 +255,36 @@ __device__ __forceinline__ CRow load_crow(const float* crow) {
 }
 
 // Readout, skip, gate and store of the owned step 16 I + l of the tile:
-// y0 = sum_n C[t][n] h_t[n] (four independent FMA chains).
-template <int IO, int I>
+// y = sum_n C[t][n] h_t[n] + D u in two FMA chains (the skip starts the first).
+// ybase is the byte offset of the lane's step 0 of the tile in its y row.
+template <int IO, int I, int FL, bool FULL>
 __device__ __forceinline__ void finish_block(const Owned& o, const float* prow, const CRow& c, float Dd,
-                                             bool need_z, const Views& v, uint32_t elem, int l, int nvalid,
-                                             int nstop) {
+                                             const Views& v, uint32_t ybase, int l, int nvalid, int nstop) {
   const float4 h0 = *reinterpret_cast<const float4*>(prow + 0);
   const float4 h1 = *reinterpret_cast<const float4*>(prow + 4);
   const float4 h2 = *reinterpret_cast<const float4*>(prow + 8);
   const float4 h3 = *reinterpret_cast<const float4*>(prow + 12);
-  float y0 = c.c0.x * h0.x, y1 = c.c0.y * h0.y, y2 = c.c0.z * h0.z, y3 = c.c0.w * h0.w;
-  y0 = fmaf(c.c1.x, h1.x, y0); y1 = fmaf(c.c1.y, h1.y, y1); y2 = fmaf(c.c1.z, h1.z, y2); y3 = fmaf(c.c1.w, h1.w, y3);
-  y0 = fmaf(c.c2.x, h2.x, y0); y1 = fmaf(c.c2.y, h2.y, y1); y2 = fmaf(c.c2.z, h2.z, y2); y3 = fmaf(c.c2.w, h2.w, y3);
-  y0 = fmaf(c.c3.x, h3.x, y0); y1 = fmaf(c.c3.y, h3.y, y1); y2 = fmaf(c.c3.z, h3.z, y2); y3 = fmaf(c.c3.w, h3.w, y3);
-  float yv = fmaf(Dd, o.u[I], (y0 + y1) + (y2 + y3));
-  if (need_z) yv *= silu_f(o.z[I]);
-  const int tr = 16 * I + l;
-  yv = tr < nvalid ? yv : 0.0f;
-  const uint32_t off = tr < nstop ? (elem + (uint32_t)tr) * io_bytes<IO>() : kOffNone;
+  float ya = fmaf(c.c0.x, h0.x, Dd * o.u[I]);
+  float yb = c.c0.y * h0.y;
+  ya = fmaf(c.c0.z, h0.z, ya); yb = fmaf(c.c0.w, h0.w, yb);
+  ya = fmaf(c.c1.x, h1.x, ya); yb = fmaf(c.c1.y, h1.y, yb);
+  ya = fmaf(c.c1.z, h1.z, ya); yb = fmaf(c.c1.w, h1.w, yb);
+  ya = fmaf(c.c2.x, h2.x, ya); yb = fmaf(c.c2.y, h2.y, yb);
+  ya = fmaf(c.c2.z, h2.z, ya); yb = fmaf(c.c2.w, h2.w, yb);
+  ya = fmaf(c.c3.x, h3.x, ya); yb = fmaf(c.c3.y, h3.y, yb);
+  ya = fmaf(c.c3.z, h3.z, ya); yb = fmaf(c.c3.w, h3.w, yb);
+  float yv = ya + yb;
+  if constexpr ((FL & kFlGate) != 0) yv *= silu_f(o.z[I]);
+  uint32_t off = ybase + (uint32_t)(16 * I) * io_bytes<IO>();
+  if constexpr (!FULL) {
+    const int tr = 16 * I + l;
+    yv = tr < nvalid ? yv : 0.0f;
+    off = tr < nstop ? off : kOffNone;
+  }
   bstore<IO>(v.y, off, yv);
 }
 
-template <int IO, bool FINAL, bool PAIR, bool SEQ>
+template <int IO, bool FINAL, bool PAIR, bool SEQ, int FL>
 __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   __shared__ FwdSmem<FINAL> sm;
   constexpr uint32_t s = io_bytes<IO>();
@@ -296,22 +326,22 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   const int t_tile_end =
       t_valid_end > t_begin ? t_begin + ((t_valid_end - t_begin + kTile - 1) / kTile) * kTile : t_begin;
 
-  const bool need_z = p.z != nullptr;
-  const bool softplus = p.softplus != 0;
+  constexpr bool GATE = FINAL && (FL & kFlGate) != 0;
   const int64_t row0 = (b * p.dim + d0) * p.seqlen;  // element offset of the wave's first row
   const uint32_t wave_bytes = (uint32_t)(nch_w * p.seqlen) * s;
   Views v;
   v.u = make_rsrc(static_cast<const char*>(p.u) + row0 * s, wave_bytes);
   v.dl = make_rsrc(static_cast<const char*>(p.delta) + row0 * s, wave_bytes);
-  const bool load_z = FINAL && need_z;
-  v.z = make_rsrc(load_z ? static_cast<const char*>(p.z) + row0 * s : static_cast<const char*>(p.u),
-                  load_z ? wave_bytes : 0u);
+  v.z = make_rsrc(GATE ? static_cast<const char*>(p.z) + row0 * s : static_cast<const char*>(p.u),
+                  GATE ? wave_bytes : 0u);
   v.y = make_rsrc(FINAL ? static_cast<const char*>(p.y) + row0 * s : static_cast<const char*>(p.u),
                   FINAL ? wave_bytes : 0u);
   const uint32_t bc_bytes = (uint32_t)(p.dstate * p.seqlen) * s;
   v.B = make_rsrc(static_cast<const char*>(p.Bm) + b * p.dstate * p.seqlen * s, bc_bytes);
   v.C = make_rsrc(static_cast<const char*>(p.Cm) + b * p.dstate * p.seqlen * s, bc_bytes);
   const uint32_t lane_elem0 = (uint32_t)cw * (uint32_t)L;
+  const uint32_t lane_off = (lane_elem0 + (uint32_t)l) * s;  // byte offset of the lane's owned step 0
+  const uint32_t bc_off = bc_lane_off<IO, PAIR>((uint32_t)L, tid);
   const bool stage_n_ok = tid / 16 < p.dstate;
 
   const float A2 = (ch_ok && n_ok) ? p.A[d * p.dstate + n] * kLog2e : 0.0f;
@@ -342,8 +372,8 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   BCRaw<IO, PAIR> bcr;
   if (t_begin < t_tile_end) {
     if constexpr (SEQ) load_doc_ids(ids, t_begin + lane, id_t, id_prev);
-    load_owned<IO>(raw, v, lane_elem0, t_begin, l);
-    load_bc<IO, PAIR>(bcr, v, (uint32_t)L, t_begin, tid, FINAL);
+    load_owned<IO, GATE>(raw, v, lane_off, (uint32_t)t_begin * s);
+    load_bc<IO, PAIR>(bcr, v, bc_off, (uint32_t)t_begin * s, FINAL);
     store_bc<IO, PAIR, FINAL>(sm, 0, bcr, tid, t_valid_end - t_begin, stage_n_ok);
   }
   __syncthreads();
@@ -352,8 +382,7 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   for (int t0 = t_begin; t0 < t_tile_end; t0 += kTile) {
     const int nvalid = t_valid_end - t0;  // steps of this tile that advance the state
     const int nstop = t_stop - t0;        // steps of this tile that exist in the chunk
-    Owned o;
-    prep_owned<IO>(o, raw, l, nvalid, bias, softplus, dt_sum);
+    rank_by_progress(t0 - t_begin, t_tile_end - t_begin);
     if (FINAL && p.ckpt && ch_ok && n_ok) p.ckpt[(ch * p.ckpt_per_row + t0 / kTile) * p.dstate + n] = h;
 
     uint64_t starts = 0;
@@ -364,20 +393,27 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
 
     const int t1 = t0 + kTile;
     const bool more = t1 < t_tile_end;
-    if (more) {
-      if constexpr (SEQ) load_doc_ids(ids, t1 + lane, id_t, id_prev);
-      load_owned<IO>(raw, v, lane_elem0, t1, l);
-      load_bc<IO, PAIR>(bcr, v, (uint32_t)L, t1, tid, FINAL);
+    // the next tile's operands are loaded whether or not there is one: past
+    // the last tile the offset is out of range and the loads return 0
+    const uint32_t next_off = more ? (uint32_t)t1 * s : kTileNone;
+    if constexpr (SEQ) {
+      if (more) load_doc_ids(ids, t1 + lane, id_t, id_prev);
     }
 
     const float* sBrow = &sm.B[buf][n][0];
     const float* sCT = ct_row<FINAL>(sm, buf, l);
-    const uint32_t elem = lane_elem0 + (uint32_t)t0;
+    const uint32_t ybase = lane_off + (uint32_t)t0 * s;
     constexpr auto seq = std::make_integer_sequence<int, 16>{};
-    // the 64 steps of the tile; tiles in which a document starts take the
-    // copy with the resets
-    auto run_tile = [&](auto reset_tag) {
+    // the 64 steps of the tile: a tile whose steps all advance the state takes
+    // the copy without masks, a tile in which a document starts the copy with
+    // the resets
+    auto run_tile = [&](auto reset_tag, auto full_tag) {
       constexpr bool RESET = decltype(reset_tag)::value;
+      constexpr bool FULL = decltype(full_tag)::value;
+      Owned o;
+      prep_owned<IO, FL, FULL>(o, raw, l, nvalid, bias, dt_sum);
+      load_owned<IO, GATE>(raw, v, lane_off, next_off);
+      load_bc<IO, PAIR>(bcr, v, bc_off, next_off, FINAL);
 #define SS_BLOCK(I)                                                                          \
       {                                                                                      \
         CRow cr;                                                                             \
@@ -385,7 +421,7 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
         scan_block<I, FINAL, RESET>(h, o, A2, sBrow, pcol, starts, seq);                     \
         if constexpr (FINAL) {                                                               \
           wave_lds_sync();                                                                   \
-          finish_block<IO, I>(o, prow, cr, Dd, need_z, v, elem, l, nvalid, nstop);           \
+          finish_block<IO, I, FL, FULL>(o, prow, cr, Dd, v, ybase, l, nvalid, nstop);        \
           wave_lds_sync();                                                                   \
         }                                                                                    \
       }
@@ -395,11 +431,18 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
       SS_BLOCK(3)
 #undef SS_BLOCK
     };
+    const bool full = t0 + kTile <= t_valid_end;
     if constexpr (SEQ) {
-      if (starts != 0) run_tile(std::true_type{});
-      else run_tile(std::false_type{});
+      if (starts != 0) {
+        if (full) run_tile(std::true_type{}, std::true_type{});
+        else run_tile(std::true_type{}, std::false_type{});
+      } else {
+        if (full) run_tile(std::false_type{}, std::true_type{});
+        else run_tile(std::false_type{}, std::false_type{});
+      }
     } else {
-      run_tile(std::false_type{});
+      if (full) run_tile(std::false_type{}, std::true_type{});
+      else run_tile(std::false_type{}, std::false_type{});
     }
 
     if (more) store_bc<IO, PAIR, FINAL>(sm, buf ^ 1, bcr, tid, t_valid_end - t1, stage_n_ok);
@@ -505,14 +548,15 @@ __global__ void __launch_bounds__(kThreads) ss_step_kernel(StepParams p) {
   }
 }
 
-template <int IO, bool PAIR, bool SEQ>
-hipError_t launch_fwd_variant(const FwdParams& p, int64_t nchunks, hipStream_t st) {
+template <int IO, bool PAIR, bool SEQ, int FL>
+hipError_t launch_fwd_flags(const FwdParams& p, int64_t nchunks, hipStream_t st) {
   const int64_t blocks_per_chunk = p.batch * p.ch_blocks;
   if (nchunks > 1) {
     FwdParams q = p;
     q.chunk_base = 0;
-    // pass 1: summaries of chunks 0 .. K-2 (the last chunk's summary is never needed)
-    hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, false, PAIR, SEQ>),
+    // pass 1: summaries of chunks 0 .. K-2 (the last chunk's summary is never
+    // needed; the gate plays no part in them)
+    hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, false, PAIR, SEQ, FL & kFlSoftplus>),
                        dim3((uint32_t)(blocks_per_chunk * (nchunks - 1))), dim3(kThreads), 0, st, q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -520,9 +564,20 @@ hipError_t launch_fwd_variant(const FwdParams& p, int64_t nchunks, hipStream_t s
     e = launch_carry(p.aggP, p.aggS, p.carry, p.batch * p.dim, p.nchunks, p.nchunks - 1, false, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, true, PAIR, SEQ>), dim3((uint32_t)(blocks_per_chunk * nchunks)),
+  hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, true, PAIR, SEQ, FL>), dim3((uint32_t)(blocks_per_chunk * nchunks)),
                      dim3(kThreads), 0, st, p);
   return hipGetLastError();
+}
+
+template <int IO, bool PAIR, bool SEQ>
+hipError_t launch_fwd_variant(const FwdParams& p, int64_t nchunks, hipStream_t st) {
+  const int fl = (p.softplus ? kFlSoftplus : 0) | (p.z ? kFlGate : 0);
+  switch (fl) {
+    case 0: return launch_fwd_flags<IO, PAIR, SEQ, 0>(p, nchunks, st);
+    case kFlSoftplus: return launch_fwd_flags<IO, PAIR, SEQ, kFlSoftplus>(p, nchunks, st);
+    case kFlGate: return launch_fwd_flags<IO, PAIR, SEQ, kFlGate>(p, nchunks, st);
+    default: return launch_fwd_flags<IO, PAIR, SEQ, kFlSoftplus | kFlGate>(p, nchunks, st);
+  }
 }
 
 template <int IO, bool SEQ>
