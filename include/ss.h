@@ -82,14 +82,29 @@ typedef struct ss_problem {
 } ss_problem;
 
 /*
- * Bytes of device workspace ss_fwd needs for this problem (0 when the
- * problem has enough channels to fill the GPU without splitting time).  The
+ * Bytes of device workspace ss_fwd runs fastest with for this problem.  A
+ * problem with too few channels to fill the GPU splits time, and its
  * workspace holds per-chunk partial states of the time-parallel scan: for a
  * time chunk c of a channel, the decay product over the chunk and the state
  * reached from zero (the associative pair of the page "Mamba", Part V
- * "S6 ... forbids the convolution").  Returns 0 for an invalid problem.
+ * "S6 ... forbids the convolution").  Any other problem (batch <= 256) can
+ * use a work queue, which ss_fwd takes for ragged rows (`lengths` given) and
+ * for more 16-channel row blocks than the GPU holds at once when they do not
+ * fill it evenly: units of 512 steps of a 16-channel block, handed out
+ * longest row first, each continuing from the state its block reached at the
+ * end of the previous unit; its workspace holds a control block, a flag per
+ * unit and that state per (channel, unit).  Returns 0 for an invalid problem.
  */
 size_t ss_fwd_workspace_size(const ss_problem *p);
+
+/*
+ * The least workspace ss_fwd accepts for this problem: the time-chunked
+ * scan's (0 when time is not split).  Between this and
+ * ss_fwd_workspace_size() bytes (or with no workspace at all when this is 0)
+ * ss_fwd runs without the work queue: the same results, a slower schedule for
+ * ragged or uneven problems.  Returns 0 for an invalid problem.
+ */
+size_t ss_fwd_workspace_min(const ss_problem *p);
 
 /*
  * Forward scan (the op of page "Mamba", Part IV Stage 5, with the final
@@ -117,9 +132,14 @@ size_t ss_fwd_workspace_size(const ss_problem *p);
  *                       steps (entry 0 is h0, or zero), the checkpoints of page
  *                       "Mamba, on a laptop GPU", "The state lives in
  *                       registers", used by ss_bwd.
- *   workspace         : device buffer of ss_fwd_workspace_size() bytes, or
- *                       NULL when that size is 0 (SS_ERR_UNSUPPORTED when it
- *                       is needed and missing or too small).
+ *   workspace         : device buffer of ss_fwd_workspace_size() bytes (at
+ *                       least ss_fwd_workspace_min(); NULL when that is 0;
+ *                       SS_ERR_UNSUPPORTED when it is smaller).  Its contents
+ *                       on entry do not matter.  Ragged problems that use
+ *                       the work queue record in its second 32-bit word a
+ *                       nonzero value if a wait between units ever gave up
+ *                       (it never should: the wait is bounded only so that
+ *                       every kernel ends).
  * y may be u, delta or z itself (in place); any other overlap between an
  * output (y, last_state, ckpt, workspace) and another buffer returns
  * SS_ERR_UNSUPPORTED.
@@ -137,16 +157,18 @@ ss_status ss_fwd(const ss_problem *p,
  * ss_fwd for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.  Same
  * arguments, results and errors as ss_fwd, without the workspace: the
- * time-chunked scan keeps its chunk pairs and carries in a fixed array of
+ * time-chunked scan keeps its chunk pairs and carries (and a ragged problem
+ * its work queue, when that fits) in a fixed array of
  * ss_fwd_noalloc_max_workspace() bytes (2 MiB) of device memory that the
  * library holds on every GPU it runs on until the process ends.  No call
  * allocates or frees memory.  The array is shared by every call on one GPU
  * and keeps the last call's contents (nothing in it needs clearing): calls
  * that overlap in time on one GPU, e.g. on two streams, race on it and must
  * be ordered by the caller.  `stream` must belong to the current device.
- * Returns SS_ERR_UNSUPPORTED for a problem whose workspace would exceed the
- * array (no valid problem does: the scan splits time only for problems with
- * fewer than 1024 wavefronts, which bounds the workspace at 1.6 MB), and
+ * Returns SS_ERR_UNSUPPORTED for a problem whose least workspace
+ * (ss_fwd_workspace_min) would exceed the array (no valid problem's does: the
+ * scan splits time only for problems with fewer than 1024 wavefronts, which
+ * bounds that workspace at 1.6 MB), and
  * SS_ERR_HIP when the array's device address cannot be obtained.
  */
 ss_status ss_fwd_noalloc(const ss_problem *p,

@@ -48,6 +48,28 @@ struct FwdPlan {
   size_t workspace;
 };
 
+// The forward's persistent work queue (problems that do not split time): units
+// of kQueueChunk steps of a 16-channel block, for ragged rows or for more row
+// blocks than the GPU holds at once.  Workspace: a control block, one flag per
+// unit, one carried state per (channel, chunk).
+constexpr int64_t kQueueChunk = 512;
+constexpr int64_t kQueueMaxRows = 256;
+constexpr int64_t kFinalPerCu = 3;  // readout workgroups resident per CU (the headline's launch)
+struct QueueLayout {
+  int64_t chunks;
+  size_t flags, carry, total;  // byte offsets and size
+};
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+QueueLayout queue_layout(const ss_problem* p) {
+  QueueLayout q;
+  q.chunks = (p->seqlen + kQueueChunk - 1) / kQueueChunk;
+  const int64_t ch_blocks = (p->dim + kChPerBlock - 1) / kChPerBlock;
+  q.flags = 256;
+  q.carry = q.flags + align256((size_t)(p->batch * ch_blocks * q.chunks) * 4);
+  q.total = q.carry + (size_t)(p->batch * p->dim * q.chunks) * 16 * sizeof(float);
+  return q;
+}
+
 FwdPlan plan_fwd(const ss_problem* p) {
   FwdPlan pl;
   const int64_t tiles = (p->seqlen + kTile - 1) / kTile;
@@ -122,6 +144,13 @@ size_t ss_ckpt_count(const ss_problem* p) {
 
 size_t ss_fwd_workspace_size(const ss_problem* p) {
   if (check_problem(p, true) != SS_OK) return 0;
+  const FwdPlan pl = plan_fwd(p);
+  if (pl.nchunks > 1 || p->batch > kQueueMaxRows) return pl.workspace;
+  return queue_layout(p).total;
+}
+
+size_t ss_fwd_workspace_min(const ss_problem* p) {
+  if (check_problem(p, true) != SS_OK) return 0;
   return plan_fwd(p).workspace;
 }
 
@@ -137,7 +166,8 @@ ss_status ss_fwd(const ss_problem* p, const void* u, const void* delta, const fl
 
 namespace ss {
 
-size_t fwd_workspace_bytes(const ss_problem* p) { return ss_fwd_workspace_size(p); }
+size_t fwd_workspace_bytes(const ss_problem* p) { return ss_fwd_workspace_min(p); }
+ss_status fwd_check_problem(const ss_problem* p) { return check_problem(p, true); }
 
 ss_status fwd_checked(const ss_problem* p, const void* u, const void* delta, const float* A, const void* Bm,
                       const void* Cm, const float* D, const void* z, const float* delta_bias, const int32_t* lengths,
@@ -151,6 +181,18 @@ ss_status fwd_checked(const ss_problem* p, const void* u, const void* delta, con
     if (q && !aligned(q)) return SS_ERR_MISALIGNED;
   const FwdPlan pl = plan_fwd(p);
   if (pl.workspace > 0 && (!workspace || workspace_bytes < pl.workspace)) return SS_ERR_UNSUPPORTED;
+  // the work queue: for ragged rows, or for more 16-channel row blocks than the
+  // GPU holds at once when they do not fill its slots evenly; only with a
+  // workspace that holds it (without one the same scan runs without the queue)
+  bool queue = false;
+  const QueueLayout ql = queue_layout(p);
+  const int64_t ch_blocks = (p->dim + kChPerBlock - 1) / kChPerBlock;
+  const int64_t slots = kFinalPerCu * ss::device_cus();
+  if (pl.nchunks == 1 && p->batch <= kQueueMaxRows && workspace && workspace_bytes >= ql.total) {
+    const int64_t G = p->batch * ch_blocks;
+    queue = lengths != nullptr || (G > slots && G % slots != 0);
+  }
+  const size_t ws_used = queue ? ql.total : pl.workspace;
   {
     // y may be u, delta or z itself (each wave reads a tile's inputs before it writes the
     // tile's outputs); no other overlap between an output and any buffer
@@ -162,7 +204,7 @@ ss_status fwd_checked(const ss_problem* p, const void* u, const void* delta, con
                        {delta_bias, (size_t)p->dim * sizeof(float)}, {lengths, (size_t)p->batch * 4},
                        {seq_idx, (size_t)(p->batch * p->seqlen) * 4}, {h0, st}};
     const Span out[] = {{y, io}, {last_state, st}, {ckpt, ss_ckpt_count(p) * sizeof(float)},
-                        {pl.workspace ? workspace : nullptr, pl.workspace}};
+                        {ws_used ? workspace : nullptr, ws_used}};
     static const bool inplace[4][11] = {{true, true, true}};
     if (conflict(in, out, inplace)) return SS_ERR_UNSUPPORTED;
   }
@@ -185,6 +227,17 @@ ss_status fwd_checked(const ss_problem* p, const void* u, const void* delta, con
     k.aggP = ws;
     k.aggS = ws + per;
     k.carry = ws + 2 * per;
+  }
+  if (queue) {
+    char* ws = static_cast<char*>(workspace);
+    k.q_ctrl = reinterpret_cast<int32_t*>(ws);
+    k.q_flags = reinterpret_cast<int32_t*>(ws + ql.flags);
+    k.q_carry = reinterpret_cast<float*>(ws + ql.carry);
+    k.q_chunks = ql.chunks;
+    k.chunk_len = kQueueChunk;
+    k.nchunks = (int32_t)ql.chunks;
+    const int64_t units = ql.chunks * p->batch * ch_blocks;
+    k.q_grid = units < slots ? units : slots;
   }
   return from_hip(ss::launch_fwd(k, pl.nchunks, static_cast<hipStream_t>(stream)));
 }
@@ -377,7 +430,6 @@ size_t ssd_state_elems(const ss_ssd_problem* p) {
   const int64_t nchunks = (p->seqlen + kSsdChunk - 1) / kSsdChunk;
   return (size_t)(p->batch * nchunks * p->nheads) * (size_t)(64 * p->dstate);
 }
-size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 }  // namespace
 
 size_t ssd_cb_bytes(const ss_ssd_problem* p) {

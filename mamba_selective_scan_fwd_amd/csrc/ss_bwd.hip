@@ -615,21 +615,6 @@ __global__ void __launch_bounds__(256) ss_bwd_reduce_kernel(const float* __restr
 // two.
 constexpr int64_t kMainPerCu = 2;
 
-// Compute units of the current device, asked once per device (256 if the
-// runtime cannot say).
-int64_t device_cus() {
-  static std::atomic<int64_t> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int64_t v = cached[dev].load(std::memory_order_relaxed);
-  if (v == 0) {
-    int n = 0;
-    v = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
-    cached[dev].store(v, std::memory_order_relaxed);
-  }
-  return v;
-}
-
 hipError_t zero_outputs(const BwdParams& p, hipStream_t st) {
   ZeroList z{};
   const int64_t nbc = p.batch * p.dstate * p.seqlen;
@@ -683,6 +668,21 @@ hipError_t launch_bwd_io(const BwdParams& p, hipStream_t st) {
 }
 
 }  // namespace
+
+// Compute units of the current device, asked once per device (256 if the
+// runtime cannot say).
+int64_t device_cus() {
+  static std::atomic<int64_t> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int64_t v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int n = 0;
+    v = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t st) {
   switch (p.io) {

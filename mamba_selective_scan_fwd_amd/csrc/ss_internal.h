@@ -17,7 +17,8 @@ ss_status fwd_checked(const ss_problem* p, const void* u, const void* delta, con
                       const void* Cm, const float* D, const void* z, const float* delta_bias, const int32_t* lengths,
                       const int32_t* seq_idx, const float* h0, void* y, float* last_state, float* ckpt,
                       void* workspace, size_t workspace_bytes, void* stream);
-size_t fwd_workspace_bytes(const ss_problem* p);
+size_t fwd_workspace_bytes(const ss_problem* p);  // the least workspace ss_fwd needs
+ss_status fwd_check_problem(const ss_problem* p);
 
 struct FwdParams {
   int32_t io;
@@ -46,6 +47,13 @@ struct FwdParams {
   int64_t ch_blocks;     // ceil(dim / 16)
   int64_t ckpt_per_row;  // ceil(seqlen / 64)
   int32_t nchunks;
+  // persistent work queue over (chunk, batch row, channel block) units (ragged
+  // rows, or more row blocks than fit the GPU at once): null q_ctrl = off
+  int32_t* q_ctrl;   // [0] next unit, [1] set when a wait gave up
+  int32_t* q_flags;  // per (batch row, channel block, chunk): its final state is published
+  float* q_carry;    // per (channel, chunk, state): the state after the chunk
+  int64_t q_chunks;  // chunks per row (chunk_len steps each)
+  int64_t q_grid;    // persistent workgroups
 };
 
 struct StepParams {
@@ -146,6 +154,7 @@ struct SsdParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, int64_t nchunks, hipStream_t st);
+int64_t device_cus();
 hipError_t launch_ssd(const SsdParams& p, hipStream_t st);
 hipError_t launch_conv(const ConvParams& p, hipStream_t st);
 hipError_t launch_conv_step(const ConvStepParams& p, hipStream_t st);

@@ -1,14 +1,16 @@
 // ss_noalloc.hip -- ss_fwd_noalloc: the forward scan for callers that cannot
 // allocate device memory (code under HIP graph capture, tight serving loops,
-// harnesses that forbid allocation).  It is ss_fwd with the time-chunked
-// scan's workspace taken from a fixed array in device memory instead of from
-// the caller.
+// harnesses that forbid allocation).  It is ss_fwd with its workspace (the
+// time-chunked scan's chunk pairs and carries, or the work queue of a ragged
+// problem when it fits) taken from a fixed array in device memory instead of
+// from the caller.
 //
 // The array lives for the life of the process, one copy per GPU that the
 // library runs on.  Every call on a GPU uses that GPU's copy: calls that
 // overlap in time on one GPU (on different streams) race on it.  Nothing in
-// it needs clearing between calls: the chunk pairs and carries of a call are
-// written before that call reads them.
+// it needs clearing by the caller: the chunk pairs and carries of a call are
+// written before that call reads them, and the queue's counter and flags are
+// cleared by a kernel at the start of every call that uses them.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -55,17 +57,15 @@ ss_status ss_fwd_noalloc(const ss_problem* p, const void* u, const void* delta, 
                          const void* Cm, const float* D, const void* z, const float* delta_bias,
                          const int32_t* lengths, const int32_t* seq_idx, const float* h0, void* y,
                          float* last_state, float* ckpt, void* stream) {
-  // validation of the problem itself happens in fwd_checked; an invalid
-  // problem needs no workspace and is rejected there
-  const size_t need = ss::fwd_workspace_bytes(p);
-  if (need > kScratchBytes) return SS_ERR_UNSUPPORTED;
-  void* ws = nullptr;
-  if (need > 0) {
-    ws = scratch_ptr();
-    if (!ws) return SS_ERR_HIP;
-  }
+  const ss_status bad = ss::fwd_check_problem(p);
+  if (bad != SS_OK) return bad;
+  if (ss::fwd_workspace_bytes(p) > kScratchBytes) return SS_ERR_UNSUPPORTED;  // the least the scan needs
+  // the whole array is offered: a problem whose optional work queue fits it
+  // uses the queue, others run without it (same results)
+  void* ws = scratch_ptr();
+  if (!ws) return SS_ERR_HIP;
   return ss::fwd_checked(p, u, delta, A, Bm, Cm, D, z, delta_bias, lengths, seq_idx, h0, y, last_state, ckpt,
-                         ws, need > 0 ? kScratchBytes : 0, stream);
+                         ws, kScratchBytes, stream);
 }
 
 }  // extern "C"

@@ -41,7 +41,7 @@ _vp = ctypes.c_void_p
 _lib = None
 
 # every symbol declared in include/ss.h
-EXPORTS = ("ss_fwd", "ss_fwd_step", "ss_bwd", "ss_fwd_workspace_size", "ss_bwd_workspace_size",
+EXPORTS = ("ss_fwd", "ss_fwd_step", "ss_bwd", "ss_fwd_workspace_size", "ss_fwd_workspace_min", "ss_bwd_workspace_size",
            "ss_ckpt_count", "ss_status_str", "ss_copy_probe", "ss_alu_probe", "ss_conv1d_fwd", "ss_conv1d_step",
            "ss_ssd_fwd", "ss_ssd_workspace_size", "ss_fwd_noalloc", "ss_fwd_noalloc_max_workspace")
 PROBE_KINDS = {"fma": 0, "exp": 1, "dpp_mul": 2, "scan_step": 3}
@@ -63,6 +63,8 @@ def load_library(path: str = LIB_PATH):
     lib.ss_ckpt_count.argtypes = [P]
     lib.ss_fwd_workspace_size.restype = ctypes.c_size_t
     lib.ss_fwd_workspace_size.argtypes = [P]
+    lib.ss_fwd_workspace_min.restype = ctypes.c_size_t
+    lib.ss_fwd_workspace_min.argtypes = [P]
     lib.ss_bwd_workspace_size.restype = ctypes.c_size_t
     lib.ss_bwd_workspace_size.argtypes = [P]
     lib.ss_fwd.restype = ctypes.c_int
@@ -166,13 +168,13 @@ def fwd(u, delta, A, Bm, Cm, D=None, z=None, delta_bias=None, delta_softplus=Tru
     ck = None
     if return_ckpt:
         ck = torch.empty((Bsz, Dd, ckpt_chunks(L), N), dtype=torch.float32, device=dev)
-    wsz = lib.ss_fwd_workspace_size(ctypes.byref(pr))
-    ws = None
-    if wsz:
-        if workspace is not None and workspace.numel() * workspace.element_size() >= wsz:
-            ws = workspace
-        else:
-            ws = torch.empty((wsz + 3) // 4, dtype=torch.float32, device=dev)
+    # a given workspace is passed as it is (the library checks it against its least size and
+    # uses the work queue only if it holds it); otherwise one of the full size is allocated
+    if workspace is not None:
+        ws, wsz = workspace, workspace.numel() * workspace.element_size()
+    else:
+        wsz = lib.ss_fwd_workspace_size(ctypes.byref(pr))
+        ws = torch.empty((wsz + 3) // 4, dtype=torch.float32, device=dev) if wsz else None
     _check(lib.ss_fwd(ctypes.byref(pr), _ptr(u), _ptr(delta), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z),
                       _ptr(delta_bias), _ptr(lengths), _ptr(seq_idx), _ptr(h0), _ptr(y), _ptr(last), _ptr(ck),
                       _ptr(ws), wsz, _stream(dev)))

@@ -99,3 +99,30 @@ def gather_rows(t, rows):
     flat = t.reshape(Bsz * Dd, *t.shape[2:])
     idx = torch.as_tensor(np.asarray(rows, dtype=np.int64), device=t.device)
     return f64(flat.index_select(0, idx))
+
+
+def full_compare(prob, y, last, softplus=True):
+    """max|err| / max|ref| over the WHOLE y and last_state tensors of a device forward, against
+    the oracle run one batch row at a time (so that only one row is ever widened to float64).
+    Also returns the oracle's final state (B, D, N) for continuing with decode steps."""
+    import oracle
+    Bsz, Dd, L = prob["u"].shape
+    N = prob["A"].shape[1]
+    lengths = prob.get("lengths")
+    ey = ry = el = rl = 0.0
+    last_ref = np.empty((Bsz, Dd, N))
+    for b in range(Bsz):
+        sl = lambda t: None if t is None else f64(t[b:b + 1])
+        lens = None if lengths is None else [int(lengths[b])]
+        yr, lr = oracle.fwd(sl(prob["u"]), sl(prob["delta"]), f64(prob["A"]), sl(prob["Bm"]), sl(prob["Cm"]),
+                            D=None if prob["D"] is None else f64(prob["D"]), z=sl(prob["z"]),
+                            bias=None if prob["bias"] is None else f64(prob["bias"]), softplus=softplus,
+                            lengths=lens)
+        yg, lg = f64(y[b:b + 1]), f64(last[b:b + 1])
+        assert np.all(np.isfinite(yg)) and np.all(np.isfinite(lg)), "non-finite values in the device result"
+        ey = max(ey, float(np.max(np.abs(yg - yr))))
+        ry = max(ry, float(np.max(np.abs(yr))))
+        el = max(el, float(np.max(np.abs(lg - lr))))
+        rl = max(rl, float(np.max(np.abs(lr))))
+        last_ref[b] = lr[0]
+    return ey / ry, el / rl, last_ref

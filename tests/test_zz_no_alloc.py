@@ -23,8 +23,8 @@ def _ss():
 
 
 def test_every_plan_fits_the_array():
-    """Host only: the workspace of every forward plan up to the sizes where time stops being
-    split is within the fixed array."""
+    """Host only: the least workspace of every forward plan (the time-chunked scan's) up to the
+    sizes where time stops being split is within the fixed array."""
     ss = _ss()
     lib = ss.load_library()
     cap = lib.ss_fwd_noalloc_max_workspace()
@@ -33,7 +33,7 @@ def test_every_plan_fits_the_array():
         for D in (1, 15, 16, 17, 48, 63, 64, 100, 255, 256, 1000, 1023, 1024, 4096):
             for L in (1, 63, 64, 65, 2048, 1 << 20, 1 << 24):
                 pr = ss.problem(B, D, 16, L, torch.float16)
-                worst = max(worst, lib.ss_fwd_workspace_size(ctypes.byref(pr)))
+                worst = max(worst, lib.ss_fwd_workspace_min(ctypes.byref(pr)))
     assert 0 < worst <= cap, (worst, cap)
 
 
@@ -53,7 +53,7 @@ def _compare(ss, prob, seq=None, h0=None):
     Bsz, Dd, L = prob["u"].shape
     N = prob["A"].shape[1]
     pr = ss.problem(Bsz, Dd, N, L, g["u"].dtype)
-    assert ss.load_library().ss_fwd_workspace_size(ctypes.byref(pr)) > 0, "not a time-chunked problem"
+    assert ss.load_library().ss_fwd_workspace_min(ctypes.byref(pr)) > 0, "not a time-chunked problem"
     y_ref, last_ref, _ = ss.fwd(g["u"], g["delta"], g["A"], g["Bm"], g["Cm"], D=g["D"], z=g["z"],
                                 delta_bias=g["bias"], lengths=g["lengths"], seq_idx=seq, h0=h0)
     y = torch.full_like(y_ref, float("nan"))
@@ -87,7 +87,7 @@ def test_noalloc_without_time_split_needs_no_array():
     prob = inputs.make_problem(4, 1024, 16, 300, "bf16", seed=9)
     g = to_dev(prob)
     pr = ss.problem(4, 1024, 16, 300, torch.bfloat16)
-    assert ss.load_library().ss_fwd_workspace_size(ctypes.byref(pr)) == 0
+    assert ss.load_library().ss_fwd_workspace_min(ctypes.byref(pr)) == 0
     y_ref, last_ref, _ = ss.fwd(g["u"], g["delta"], g["A"], g["Bm"], g["Cm"], D=g["D"], z=g["z"],
                                 delta_bias=g["bias"])
     y = torch.empty_like(y_ref)
