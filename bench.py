@@ -210,9 +210,8 @@ def bench_headline(steps, warmup, stream, prewarm_s=0.3):
     return ms, kernel_ms, stats, wall, (Bsz, Dd, N, L), sets, ys
 
 
-def bench_rows(stream):
-    rows = {}
-    # long sequence, few channels (time-chunked), fp32
+def bench_long(stream):
+    """Long sequence, few channels (the time-chunked scan), fp32: B=1, D=16, L=32768."""
     p1 = dev_problem(inputs.make_config(1))
     y1 = torch.empty_like(p1["u"])
     s1 = torch.empty((1, 16, 16), dtype=torch.float32, device="cuda")
@@ -222,9 +221,12 @@ def bench_rows(stream):
     f1(0)
     ms = timed(f1, 20, stream)
     tc = 1 * 16 * 32768
-    rows["fwd_long_B1_D16_L32768_f32"] = {"ms": ms, "token_channel_per_s": tc / (ms * 1e-3),
-                                          "tokens_per_s": 32768 / (ms * 1e-3)}
-    del p1, c1, y1
+    return {"ms": ms, "token_channel_per_s": tc / (ms * 1e-3), "tokens_per_s": 32768 / (ms * 1e-3)}
+
+
+def bench_rows(stream):
+    rows = {}
+    rows["fwd_long_B1_D16_L32768_f32"] = bench_long(stream)
     # ragged mamba-2.8b layer, bf16
     prob3 = inputs.make_config(3)
     lens = prob3["lengths"].tolist()
@@ -552,7 +554,7 @@ def main():
                     help="untimed steps first: the GPU needs ~100 ms of load to reach its working clock")
     ap.add_argument("--no-rows", action="store_true", help="headline only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
-    ap.add_argument("--row", choices=["ssd", "conv", "bwd"], help="time one secondary workload alone and print its JSON line "
+    ap.add_argument("--row", choices=["ssd", "conv", "bwd", "long"], help="time one secondary workload alone and print its JSON line "
                     "(for profiling it on its own); the headline is not run")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -567,6 +569,8 @@ def main():
             out = {"ssd_fwd_B8_L2048_H24_P64_N128_bf16": bench_ssd(stream)}
         elif args.row == "conv":
             out = {"conv1d_silu_B8_D1536_L2048_W4_f16": bench_conv(stream)}
+        elif args.row == "long":
+            out = {"fwd_long_B1_D16_L32768_f32": bench_long(stream)}
         else:
             out = bench_bwd(stream)
         out["copy_probe_GBps"] = copy_probe(stream)   # the counter calibration kernel, same process
@@ -604,7 +608,7 @@ def main():
         # divided by K), against MI355X's 8 TB/s
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "kernel": "ss_fwd_chunk_kernel<f16, FINAL>",
+                     "kernel": "ss_fwd_chunk_kernel<f16, pairs, no documents, softplus+gate>",
                      "alg_bytes_per_launch": alg_bytes,
                      "kernel_ms_event_region": kernel_ms,
                      **stats},

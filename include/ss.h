@@ -84,10 +84,11 @@ typedef struct ss_problem {
 /*
  * Bytes of device workspace ss_fwd runs fastest with for this problem.  A
  * problem with too few channels to fill the GPU splits time, and its
- * workspace holds per-chunk partial states of the time-parallel scan: for a
- * time chunk c of a channel, the decay product over the chunk and the state
- * reached from zero (the associative pair of the page "Mamba", Part V
- * "S6 ... forbids the convolution").  Any other problem (batch <= 256) can
+ * workspace holds a control block and per-chunk partial states of the
+ * time-parallel scan: for a time chunk c of a channel, the decay product over
+ * the chunk and the state reached from zero (the associative pair of the page
+ * "Mamba", Part V "S6 ... forbids the convolution"), and the same pair for
+ * groups of consecutive chunks.  Any other problem (batch <= 256) can
  * use a work queue, which ss_fwd takes for ragged rows (`lengths` given) and
  * for more 16-channel row blocks than the GPU holds at once when they do not
  * fill it evenly: units of 512 steps of a 16-channel block, handed out
@@ -135,11 +136,11 @@ size_t ss_fwd_workspace_min(const ss_problem *p);
  *   workspace         : device buffer of ss_fwd_workspace_size() bytes (at
  *                       least ss_fwd_workspace_min(); NULL when that is 0;
  *                       SS_ERR_UNSUPPORTED when it is smaller).  Its contents
- *                       on entry do not matter.  Ragged problems that use
- *                       the work queue record in its second 32-bit word a
- *                       nonzero value if a wait between units ever gave up
- *                       (it never should: the wait is bounded only so that
- *                       every kernel ends).
+ *                       on entry do not matter.  Time-chunked problems, and
+ *                       ragged problems that use the work queue, record in
+ *                       its second 32-bit word a nonzero value if a wait
+ *                       between workgroups ever gave up (it never should:
+ *                       the wait is bounded only so that every kernel ends).
  * y may be u, delta or z itself (in place); any other overlap between an
  * output (y, last_state, ckpt, workspace) and another buffer returns
  * SS_ERR_UNSUPPORTED.
@@ -157,8 +158,8 @@ ss_status ss_fwd(const ss_problem *p,
  * ss_fwd for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation.  Same
  * arguments, results and errors as ss_fwd, without the workspace: the
- * time-chunked scan keeps its chunk pairs and carries (and a ragged problem
- * its work queue, when that fits) in a fixed array of
+ * time-chunked scan keeps its chunk pairs (and a ragged problem its work
+ * queue, when that fits) in a fixed array of
  * ss_fwd_noalloc_max_workspace() bytes (2 MiB) of device memory that the
  * library holds on every GPU it runs on until the process ends.  No call
  * allocates or frees memory.  The array is shared by every call on one GPU
@@ -168,7 +169,7 @@ ss_status ss_fwd(const ss_problem *p,
  * Returns SS_ERR_UNSUPPORTED for a problem whose least workspace
  * (ss_fwd_workspace_min) would exceed the array (no valid problem's does: the
  * scan splits time only for problems with fewer than 1024 wavefronts, which
- * bounds that workspace at 1.6 MB), and
+ * bounds that workspace at 1.05 MB), and
  * SS_ERR_HIP when the array's device address cannot be obtained.
  */
 ss_status ss_fwd_noalloc(const ss_problem *p,

@@ -70,6 +70,27 @@ QueueLayout queue_layout(const ss_problem* p) {
   return q;
 }
 
+// The time-chunked scan's workspace (one launch): a control block (unit
+// counter, error word), then per (channel, chunk, state) the chunk pairs
+// (P, S) and per (channel, group but the last, state) the group pairs, one
+// 64-bit word each.  Groups hold G chunks, G the least power of two with
+// G * G >= K, so that a chunk's entry state composes at most G - 1 chunk
+// pairs and K / G group pairs.
+struct ChunkLayout {
+  int64_t group, ngroups;
+  size_t pairs, gpairs, total;  // byte offsets and size
+};
+ChunkLayout chunk_layout(const ss_problem* p, int64_t nchunks) {
+  ChunkLayout c;
+  c.group = 1;
+  while (c.group * c.group < nchunks) c.group *= 2;
+  c.ngroups = (nchunks + c.group - 1) / c.group;
+  c.pairs = 256;
+  c.gpairs = c.pairs + (size_t)(p->batch * p->dim * nchunks) * 16 * sizeof(uint64_t);
+  c.total = c.gpairs + (size_t)(p->batch * p->dim * (c.ngroups - 1)) * 16 * sizeof(uint64_t);
+  return c;
+}
+
 FwdPlan plan_fwd(const ss_problem* p) {
   FwdPlan pl;
   const int64_t tiles = (p->seqlen + kTile - 1) / kTile;
@@ -77,17 +98,13 @@ FwdPlan plan_fwd(const ss_problem* p) {
   const int64_t waves = p->batch * ch_blocks * 4;
   int64_t k = 1;
   if (waves < kTargetWaves) {
-    k = (kTargetWaves + waves - 1) / waves;
+    k = (kTargetWaves + waves - 1) / waves;  // at most kTargetWaves / 4 chunks
     if (k > tiles) k = tiles;
   }
   const int64_t tiles_per_chunk = (tiles + k - 1) / k;
   pl.chunk_len = tiles_per_chunk * kTile;
   pl.nchunks = (p->seqlen + pl.chunk_len - 1) / pl.chunk_len;
-  if (p->batch * ch_blocks * pl.nchunks > kMaxGrid) {  // keep the grid legal
-    pl.nchunks = 1;
-    pl.chunk_len = tiles * kTile;
-  }
-  pl.workspace = pl.nchunks > 1 ? (size_t)3 * (size_t)(p->batch * p->dim * pl.nchunks * 16) * sizeof(float) : 0;
+  pl.workspace = pl.nchunks > 1 ? chunk_layout(p, pl.nchunks).total : 0;
   return pl;
 }
 
@@ -217,16 +234,18 @@ ss_status fwd_checked(const ss_problem* p, const void* u, const void* delta, con
   k.y = y; k.last_state = last_state; k.ckpt = ckpt;
   k.batch = p->batch; k.dim = p->dim; k.dstate = p->dstate; k.seqlen = p->seqlen;
   k.chunk_len = pl.chunk_len;
-  k.chunk_base = 0;
   k.ch_blocks = (p->dim + kChPerBlock - 1) / kChPerBlock;
   k.ckpt_per_row = (p->seqlen + kTile - 1) / kTile;
   k.nchunks = (int32_t)pl.nchunks;
   if (pl.nchunks > 1) {
-    const size_t per = (size_t)(p->batch * p->dim * pl.nchunks * 16);
-    float* ws = static_cast<float*>(workspace);
-    k.aggP = ws;
-    k.aggS = ws + per;
-    k.carry = ws + 2 * per;
+    const ChunkLayout cl = chunk_layout(p, pl.nchunks);
+    char* ws = static_cast<char*>(workspace);
+    k.q_ctrl = reinterpret_cast<int32_t*>(ws);
+    k.pairs = reinterpret_cast<uint64_t*>(ws + cl.pairs);
+    k.gpairs = reinterpret_cast<uint64_t*>(ws + cl.gpairs);
+    k.nslots = (int64_t)((cl.total - cl.pairs) / sizeof(uint64_t));
+    k.group = (int32_t)cl.group;
+    k.ngroups = (int32_t)cl.ngroups;
   }
   if (queue) {
     char* ws = static_cast<char*>(workspace);

@@ -43,10 +43,62 @@
 
 namespace ss {
 
-hipError_t launch_carry(const float* aggP, const float* aggS, float* carry, int64_t nch, int32_t nchunks,
-                        int32_t npairs, bool reverse, hipStream_t st);
-
 namespace {
+
+// The carry pass: exclusive scan of the chunk pairs of one channel with the
+// associative pair operator (page "Mamba", Part V, the combine for
+// h_t = a_t h_{t-1} + b_t); reverse = 1, as the backward's carried state
+// gradient runs, visits chunk c as K-1-c.  256 threads per channel: thread
+// (g, n), state n fastest so that 16 lanes read one chunk's 64 contiguous
+// bytes, serially combines chunks [g*per, (g+1)*per) of state n; the value
+// entering each group is then combined from the groups on its left through
+// LDS, and each group replays its chunks from it.  Only the first npairs
+// visited chunks have a pair; no other pair is read.
+__global__ void __launch_bounds__(256) ss_carry_kernel(const float* __restrict__ aggP, const float* __restrict__ aggS,
+                                                       float* __restrict__ carry, int64_t nch, int32_t nchunks,
+                                                       int32_t npairs, int32_t reverse) {
+  __shared__ float sP[16][16], sS[16][16];
+  const int tid = threadIdx.x;
+  const int n = tid % 16, g = tid / 16;
+  const int64_t ch = blockIdx.x;
+  if (ch >= nch) return;  // uniform per workgroup
+  const int per = (nchunks + 15) / 16;
+  const int c0 = g * per < nchunks ? g * per : nchunks;
+  const int c1 = c0 + per < nchunks ? c0 + per : nchunks;
+  const int64_t base = ch * nchunks;
+  auto slot = [&](int c) { return (base + (reverse ? nchunks - 1 - c : c)) * kStates + n; };
+
+  // local pair over [c0, c1): applying it maps the value entering c0 to the
+  // value leaving c1 - 1
+  float P = 1.0f, S = 0.0f;
+  const int c1p = c1 < npairs ? c1 : npairs;
+#pragma unroll 4
+  for (int c = c0; c < c1p; ++c) {
+    const float pc = aggP[slot(c)];
+    const float sc = aggS[slot(c)];
+    S = fmaf(pc, S, sc);
+    P *= pc;
+  }
+  sP[g][n] = P;
+  sS[g][n] = S;
+  __syncthreads();
+  // the value entering group g: groups 0 .. g-1 applied in order to 0
+  float E = 0.0f;
+  for (int q = 0; q < g; ++q) E = fmaf(sP[q][n], E, sS[q][n]);
+#pragma unroll 4
+  for (int c = c0; c < c1; ++c) {
+    carry[slot(c)] = E;
+    if (c < c1p) E = fmaf(aggP[slot(c)], E, aggS[slot(c)]);
+  }
+}
+
+hipError_t launch_carry(const float* aggP, const float* aggS, float* carry, int64_t nch, int32_t nchunks,
+                        int32_t npairs, bool reverse, hipStream_t st) {
+  hipLaunchKernelGGL(ss_carry_kernel, dim3((uint32_t)nch), dim3(256), 0, st, aggP, aggS, carry, nch, nchunks,
+                     npairs, (int32_t)(reverse ? 1 : 0));
+  return hipGetLastError();
+}
+
 
 constexpr int kBCStride = kTile + 4;
 // Sum-over-states tiles: per channel 16 steps x 16 states, element (j, n) at

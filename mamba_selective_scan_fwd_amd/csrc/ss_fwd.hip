@@ -19,16 +19,21 @@
 // 16-wide reduction, not a contraction.
 //
 // Time chunking (for problems with too few channels to fill 256 CUs): the
-// sequence is cut into K chunks of a multiple of 64 steps.  Pass 1
-// (ss_fwd_chunk_kernel<AGG>) computes for each chunk the pair (P, S) =
-// (prod of exp(Delta A) over the chunk, state reached from the chunk's start
-// with a zero carry; the first chunk starts from the caller's initial state), pass 2
-// (ss_carry_kernel) scans the pairs with the associative operator
-// (P1,S1) then (P2,S2) = (P2 P1, P2 S1 + S2) (page "Mamba", Part V, the
-// combine for h_t = a_t h_{t-1} + b_t) to get each chunk's entry state, and
-// pass 3 (ss_fwd_chunk_kernel<FINAL>) reruns every chunk from its entry state
-// and writes y.  With K = 1 only pass 3 runs, from the initial state (zero
-// unless given).
+// sequence is cut into K chunks of a multiple of 64 steps, one workgroup per
+// (chunk, 16-channel block), all in one launch (ss_fwd_lookback_kernel).
+// Each workgroup first scans its chunk from a zero state (the first chunk
+// from the caller's initial state) to get the chunk's pair (P, S) = (prod of
+// exp(Delta A) over the chunk, state reached); pairs compose with the
+// associative operator (P1,S1) then (P2,S2) = (P2 P1, P2 S1 + S2) (page
+// "Mamba", Part V, the combine for h_t = a_t h_{t-1} + b_t).  The pairs are
+// published to the other workgroups in two levels: chunks form groups of G
+// consecutive chunks; a workgroup composes the pairs of the chunks before it
+// in its group, the last one of a group also publishes the group's pair, and
+// every workgroup composes the pairs of the groups before its own.  That
+// gives its chunk's entry state after two waits, whatever K; it then reruns
+// its chunk from that state and writes y.  With K = 1 one workgroup per
+// 16-channel block runs the whole row from the initial state (zero unless
+// given) in ss_fwd_chunk_kernel.
 //
 // Packed documents ("niverel-mamba" README, "seq_idx strict reset"): where
 // the row's document id changes the state restarts from zero; the decay of
@@ -40,9 +45,6 @@
 #include "ss_internal.h"
 
 namespace ss {
-
-hipError_t launch_carry(const float* aggP, const float* aggS, float* carry, int64_t nch, int32_t nchunks,
-                        int32_t npairs, bool reverse, hipStream_t st);
 
 namespace {
 
@@ -452,51 +454,28 @@ __device__ __forceinline__ void scan_chunk(const FwdParams& p, FwdSmem<FINAL>& s
   }
 }
 
-// One workgroup per (time chunk, batch row, channel block).  FINAL: the
-// readout pass, from the caller's initial state (first chunk) or the chunk's
-// carried entry state; otherwise the chunk-summary pass of the time-chunked
-// scan.
-template <int IO, bool FINAL, bool PAIR, bool SEQ, int FL>
+// One workgroup per (batch row, channel block): the whole row, from the
+// caller's initial state, when time is not split.
+template <int IO, bool PAIR, bool SEQ, int FL>
 __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
-  __shared__ FwdSmem<FINAL> sm;
+  __shared__ FwdSmem<true> sm;
   const int n = threadIdx.x % 16;
   const int64_t d = ss_lane_channel(threadIdx.x, 0);
-  // logical block -> (chunk, batch row, channel block).  Channel blocks vary
+  // logical block -> (batch row, channel block).  Channel blocks vary
   // fastest: the blocks that share one batch row's B and C tiles run on one
   // XCD, so each row's B and C come from HBM about once.
-  uint32_t lb = xcd_logical_block();
+  const uint32_t lb = xcd_logical_block();
   const int64_t cb = lb % p.ch_blocks;
-  lb /= p.ch_blocks;
-  const int64_t b = lb % p.batch;
-  const int64_t chunk = lb / p.batch + p.chunk_base;
+  const int64_t b = lb / p.ch_blocks;
   const int64_t dd = cb * kChPerBlock + d;
   const bool ch_ok = dd < p.dim, n_ok = n < p.dstate;
   const int64_t ch = b * p.dim + dd;
 
-  // entry state: the caller's initial state for the first chunk (both
-  // passes), the carried state for later chunks of the readout pass
-  float h = 0.0f;
-  if (chunk == 0) {
-    if (p.h0 && ch_ok && n_ok) h = p.h0[ch * p.dstate + n];
-  } else if (FINAL && p.carry && ch_ok) {
-    h = p.carry[(ch * p.nchunks + chunk) * kStates + n];
-  }
-  const int L = (int)p.seqlen;
-  const int t_stop = (int)((chunk + 1) * p.chunk_len) < L ? (int)((chunk + 1) * p.chunk_len) : L;
+  float h = (p.h0 && ch_ok && n_ok) ? p.h0[ch * p.dstate + n] : 0.0f;
   float dt_sum = 0.0f;
   bool any_start = false;
-  scan_chunk<IO, FINAL, PAIR, SEQ, FL, true>(p, sm, b, cb, chunk, t_stop, h, dt_sum, any_start);
-
-  if constexpr (FINAL) {
-    if (p.last_state && ch_ok && n_ok && chunk == p.nchunks - 1) p.last_state[ch * p.dstate + n] = h;
-  } else if (ch_ok) {
-    // chunk summary: P = exp(A * sum Delta) (= prod of the step decays), S = h
-    const float A2 = n_ok ? p.A[dd * p.dstate + n] * kLog2e : 0.0f;
-    const float dsum = row_sum(dt_sum);
-    const int64_t k = (ch * p.nchunks + chunk) * kStates + n;
-    p.aggP[k] = any_start ? 0.0f : exp2_hw(A2 * dsum);
-    p.aggS[k] = h;
-  }
+  scan_chunk<IO, true, PAIR, SEQ, FL, true>(p, sm, b, cb, 0, (int)p.seqlen, h, dt_sum, any_start);
+  if (p.last_state && ch_ok && n_ok) p.last_state[ch * p.dstate + n] = h;
 }
 
 // ---- persistent work queue (ragged rows, or more row blocks than fit) -------
@@ -616,51 +595,129 @@ __global__ void __launch_bounds__(256) ss_queue_clear_kernel(int32_t* ctrl, int3
   for (int64_t j = i; j < nflags; j += (int64_t)gridDim.x * blockDim.x) flags[j] = 0;
 }
 
-// Pass 2: exclusive scan of the chunk pairs of one channel (forward: the
-// entry state of every chunk; reverse = 1, the backward's carried state
-// gradient: chunk c is visited as K-1-c).  256 threads per channel: thread
-// (g, n), state n fastest so that 16 lanes read one chunk's 64 contiguous
-// bytes, serially combines chunks [g*per, (g+1)*per) of state n; the value
-// entering each group is then combined from the groups on its left through
-// LDS, and each group replays its chunks from it.  Only the first npairs
-// visited chunks have a pair (the forward's last chunk has none: nothing
-// follows it); no other pair is read.
-__global__ void __launch_bounds__(256) ss_carry_kernel(const float* __restrict__ aggP, const float* __restrict__ aggS,
-                                                       float* __restrict__ carry, int64_t nch, int32_t nchunks,
-                                                       int32_t npairs, int32_t reverse) {
-  __shared__ float sP[16][16], sS[16][16];
-  const int tid = threadIdx.x;
-  const int n = tid % 16, g = tid / 16;
-  const int64_t ch = blockIdx.x;
-  if (ch >= nch) return;  // uniform per workgroup
-  const int per = (nchunks + 15) / 16;
-  const int c0 = g * per < nchunks ? g * per : nchunks;
-  const int c1 = c0 + per < nchunks ? c0 + per : nchunks;
-  const int64_t base = ch * nchunks;
-  auto slot = [&](int c) { return (base + (reverse ? nchunks - 1 - c : c)) * kStates + n; };
+// ---- time-chunked scan in one launch ----------------------------------------
+// Units (chunk, batch row, channel block) are taken in that order from an
+// atomic counter, so every unit a workgroup waits for (an earlier chunk of
+// its block) was taken before it by a workgroup that is running or done.
+//
+// A pair crosses workgroups (and XCDs, whose L2 caches are not coherent with
+// one another) as one 64-bit word, P in the low half and S in the high half,
+// stored and loaded with device-scope atomics, so the word is its own flag:
+// before the launch every slot is set to kPairEmpty (both halves a NaN with
+// every bit set, which the arithmetic does not produce), and a reader polls
+// the slots it needs until none holds kPairEmpty (bounded: kSpinLimit polls,
+// then the error word q_ctrl[1] is set and the wait ends).  No fence, no
+// separate flag: one write and one read per hop.
 
-  // local pair over [c0, c1): applying it maps the value entering c0 to the
-  // value leaving c1 - 1
-  float P = 1.0f, S = 0.0f;
-  const int c1p = c1 < npairs ? c1 : npairs;
-#pragma unroll 4
-  for (int c = c0; c < c1p; ++c) {
-    const float pc = aggP[slot(c)];
-    const float sc = aggS[slot(c)];
-    S = fmaf(pc, S, sc);
-    P *= pc;
+constexpr uint64_t kPairEmpty = ~(uint64_t)0;
+constexpr int kMaxGroup = 32;  // chunks per group, and groups, at most
+
+__device__ __forceinline__ void publish_pair(uint64_t* slot, bool ok, float P, float S) {
+  const uint64_t w = (uint64_t)__float_as_uint(P) | ((uint64_t)__float_as_uint(S) << 32);
+  if (ok) __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Composes, in order, the m (<= kMaxGroup) pairs at slot[k * stride] into
+// (Pc, Sc) (one lane's own slots; nothing when !ok), waiting for each to be
+// published; all m loads are in flight at once.
+__device__ __forceinline__ void compose_published(const uint64_t* slot, int64_t stride, int m, bool ok, int32_t* err,
+                                                  float& Pc, float& Sc) {
+  if (!ok) return;
+  uint64_t v[kMaxGroup];
+#pragma unroll
+  for (int k = 0; k < kMaxGroup; ++k)
+    if (k < m) v[k] = __hip_atomic_load(slot + k * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int it = 0;; ++it) {
+    bool pending = false;
+#pragma unroll
+    for (int k = 0; k < kMaxGroup; ++k) pending |= k < m && v[k] == kPairEmpty;
+    if (!pending) break;
+    if (it == kSpinLimit) {
+      __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+    for (int k = 0; k < kMaxGroup; ++k)
+      if (k < m && v[k] == kPairEmpty)
+        v[k] = __hip_atomic_load(slot + k * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  sP[g][n] = P;
-  sS[g][n] = S;
+#pragma unroll
+  for (int k = 0; k < kMaxGroup; ++k) {
+    if (k < m) {
+      const float pk = __uint_as_float((uint32_t)v[k]), sk = __uint_as_float((uint32_t)(v[k] >> 32));
+      Sc = fmaf(pk, Sc, sk);
+      Pc *= pk;
+    }
+  }
+}
+
+template <int IO, bool PAIR, bool SEQ, int FL>
+__global__ void __launch_bounds__(kThreads) ss_fwd_lookback_kernel(FwdParams p) {
+  __shared__ FwdSmem<true> sm;
+  __shared__ int64_t s_unit;
+  const int tid = threadIdx.x;
+  const int n = tid % 16;
+  if (tid == 0) s_unit = (int64_t)atomicAdd(reinterpret_cast<unsigned int*>(p.q_ctrl), 1u);
   __syncthreads();
-  // the value entering group g: groups 0 .. g-1 applied in order to 0
-  float E = 0.0f;
-  for (int q = 0; q < g; ++q) E = fmaf(sP[q][n], E, sS[q][n]);
-#pragma unroll 4
-  for (int c = c0; c < c1; ++c) {
-    carry[slot(c)] = E;
-    if (c < c1p) E = fmaf(aggP[slot(c)], E, aggS[slot(c)]);
+  const int64_t nrb = p.batch * p.ch_blocks;  // (batch row, channel block) pairs
+  const int64_t K = p.nchunks, G = p.group, NG = p.ngroups;
+  const int64_t c = s_unit / nrb, rb = s_unit % nrb;
+  const int64_t b = rb / p.ch_blocks, cb = rb % p.ch_blocks;
+  const int64_t d = ss_lane_channel(tid, cb * kChPerBlock);
+  const bool ch_ok = d < p.dim, n_ok = n < p.dstate;
+  const int64_t ch = b * p.dim + d;
+  const int64_t g = c / G, i = c % G;
+  const int L = (int)p.seqlen;
+  const int t_stop = (int)((c + 1) * p.chunk_len) < L ? (int)((c + 1) * p.chunk_len) : L;
+  const float h_init = (c == 0 && p.h0 && ch_ok && n_ok) ? p.h0[ch * p.dstate + n] : 0.0f;
+  uint64_t* const pairs = p.pairs + ch * K * kStates + n;                 // this lane's chunk slots
+  uint64_t* const gpairs = p.gpairs + ch * (NG - 1) * kStates + n;       // and group slots
+
+  // 1. the chunk's own pair (the last chunk's is never needed).  The first
+  // chunk's pair absorbs the initial state: P = 0, S = the state it reaches.
+  float P = 0.0f, S = 0.0f;
+  if (c < K - 1) {
+    float h = h_init, dt_sum = 0.0f;
+    bool any_start = false;
+    scan_chunk<IO, false, PAIR, SEQ, FL & kFlSoftplus, false>(p, reinterpret_cast<FwdSmem<false>&>(sm), b, cb, c,
+                                                              t_stop, h, dt_sum, any_start);
+    const float A2 = (ch_ok && n_ok) ? p.A[d * p.dstate + n] * kLog2e : 0.0f;
+    const float dsum = row_sum(dt_sum);
+    P = (c == 0 || any_start) ? 0.0f : exp2_hw(A2 * dsum);
+    S = h;
+    publish_pair(pairs + c * kStates, ch_ok, P, S);
+    __syncthreads();  // the shared tiles are free for the readout
   }
+
+  // 2. the map from the group's entry to this chunk's entry: the pairs of the
+  // group's chunks before this one
+  float Pe = 1.0f, Se = 0.0f;
+  if (i > 0) compose_published(pairs + g * G * kStates, kStates, (int)i, ch_ok, p.q_ctrl + 1, Pe, Se);
+
+  // 3. the last chunk of a group that has a successor publishes the group's
+  // pair (so the last group never does: ngroups - 1 group pairs)
+  if (i == G - 1 && c < K - 1) publish_pair(gpairs + g * kStates, ch_ok, P * Pe, fmaf(P, Se, S));
+
+  // 4. the state entering the group: the pairs of the groups before it,
+  // applied to zero (the first chunk's pair holds the initial state)
+  float Pg = 1.0f, H = 0.0f;
+  if (g > 0) compose_published(gpairs, kStates, (int)g, ch_ok, p.q_ctrl + 1, Pg, H);
+
+  // 5. rerun the chunk from its entry state and write y
+  float h = c == 0 ? h_init : fmaf(Pe, H, Se);
+  float dt_sum = 0.0f;
+  bool any_start = false;
+  scan_chunk<IO, true, PAIR, SEQ, FL, false>(p, sm, b, cb, c, t_stop, h, dt_sum, any_start);
+  if (p.last_state && ch_ok && n_ok && c == K - 1) p.last_state[ch * p.dstate + n] = h;
+}
+
+// Before a launch of the one-launch time-chunked scan: the unit counter and
+// error word to zero, every pair slot to kPairEmpty.
+__global__ void __launch_bounds__(256) ss_pairs_clear_kernel(int32_t* ctrl, uint64_t* slots, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < 2) ctrl[i] = 0;
+  for (int64_t j = i; j < n; j += (int64_t)gridDim.x * blockDim.x) slots[j] = kPairEmpty;
 }
 
 // One decode step.  Lane (c, n) of the wave updates state n of channel c;
@@ -701,31 +758,28 @@ __global__ void __launch_bounds__(kThreads) ss_step_kernel(StepParams p) {
 template <int IO, bool PAIR, bool SEQ, int FL>
 hipError_t launch_fwd_flags(const FwdParams& p, int64_t nchunks, hipStream_t st) {
   const int64_t blocks_per_chunk = p.batch * p.ch_blocks;
+  if (nchunks > 1) {
+    int64_t blocks = (p.nslots + 1023) / 1024;
+    blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
+    hipLaunchKernelGGL(ss_pairs_clear_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, p.q_ctrl, p.pairs, p.nslots);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((ss_fwd_lookback_kernel<IO, PAIR, SEQ, FL>), dim3((uint32_t)(blocks_per_chunk * nchunks)),
+                       dim3(kThreads), 0, st, p);
+    return hipGetLastError();
+  }
   if (p.q_ctrl) {
     const int64_t nflags = blocks_per_chunk * p.q_chunks;
-    int64_t cb = (nflags + 255) / 256;
-    cb = cb < 1 ? 1 : (cb > 1024 ? 1024 : cb);
-    hipLaunchKernelGGL(ss_queue_clear_kernel, dim3((uint32_t)cb), dim3(256), 0, st, p.q_ctrl, p.q_flags, nflags);
+    int64_t blocks = (nflags + 255) / 256;
+    blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
+    hipLaunchKernelGGL(ss_queue_clear_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, p.q_ctrl, p.q_flags, nflags);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((ss_fwd_queue_kernel<IO, PAIR, SEQ, FL>), dim3((uint32_t)p.q_grid), dim3(kThreads), 0, st, p);
     return hipGetLastError();
   }
-  if (nchunks > 1) {
-    FwdParams q = p;
-    q.chunk_base = 0;
-    // pass 1: summaries of chunks 0 .. K-2 (the last chunk's summary is never
-    // needed; the gate plays no part in them)
-    hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, false, PAIR, SEQ, FL & kFlSoftplus>),
-                       dim3((uint32_t)(blocks_per_chunk * (nchunks - 1))), dim3(kThreads), 0, st, q);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // pass 2: entry states (pairs of chunks 0 .. K-2 only)
-    e = launch_carry(p.aggP, p.aggS, p.carry, p.batch * p.dim, p.nchunks, p.nchunks - 1, false, st);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, true, PAIR, SEQ, FL>), dim3((uint32_t)(blocks_per_chunk * nchunks)),
-                     dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((ss_fwd_chunk_kernel<IO, PAIR, SEQ, FL>), dim3((uint32_t)blocks_per_chunk), dim3(kThreads), 0,
+                     st, p);
   return hipGetLastError();
 }
 
@@ -779,11 +833,5 @@ hipError_t launch_step(const StepParams& p, hipStream_t st) {
   }
 }
 
-hipError_t launch_carry(const float* aggP, const float* aggS, float* carry, int64_t nch, int32_t nchunks,
-                        int32_t npairs, bool reverse, hipStream_t st) {
-  hipLaunchKernelGGL(ss_carry_kernel, dim3((uint32_t)nch), dim3(256), 0, st, aggP, aggS, carry, nch, nchunks,
-                     npairs, (int32_t)(reverse ? 1 : 0));
-  return hipGetLastError();
-}
 
 }  // namespace ss

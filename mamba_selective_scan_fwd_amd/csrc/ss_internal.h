@@ -37,19 +37,24 @@ struct FwdParams {
   void* y;
   float* last_state;
   float* ckpt;
-  // time-chunked scan workspace, each (batch*dim*nchunks*16) floats
-  float* aggP;
-  float* aggS;
-  float* carry;
+  // time-chunked scan (one launch): per (channel, chunk, state) the chunk's
+  // pair (P, S) as one 64-bit word (P low), per (channel, group but the last,
+  // state) the pair of a group of `group` consecutive chunks; nslots words
+  // from `pairs` (through the group slots) are set to all ones, "not yet
+  // published", before the launch; the unit counter and error word in q_ctrl
+  uint64_t* pairs;
+  uint64_t* gpairs;
+  int64_t nslots;
+  int32_t group;
+  int32_t ngroups;
   int64_t batch, dim, dstate, seqlen;
   int64_t chunk_len;     // multiple of 64
-  int64_t chunk_base;    // first chunk index covered by the launch
   int64_t ch_blocks;     // ceil(dim / 16)
   int64_t ckpt_per_row;  // ceil(seqlen / 64)
   int32_t nchunks;
   // persistent work queue over (chunk, batch row, channel block) units (ragged
   // rows, or more row blocks than fit the GPU at once): null q_ctrl = off
-  int32_t* q_ctrl;   // [0] next unit, [1] set when a wait gave up
+  int32_t* q_ctrl;   // [0] next unit, [1] set when a wait gave up (also the time-chunked scan's)
   int32_t* q_flags;  // per (batch row, channel block, chunk): its final state is published
   float* q_carry;    // per (channel, chunk, state): the state after the chunk
   int64_t q_chunks;  // chunks per row (chunk_len steps each)

@@ -1,16 +1,16 @@
 // ss_noalloc.hip -- ss_fwd_noalloc: the forward scan for callers that cannot
 // allocate device memory (code under HIP graph capture, tight serving loops,
 // harnesses that forbid allocation).  It is ss_fwd with its workspace (the
-// time-chunked scan's chunk pairs and carries, or the work queue of a ragged
+// time-chunked scan's chunk and group pairs, or the work queue of a ragged
 // problem when it fits) taken from a fixed array in device memory instead of
 // from the caller.
 //
 // The array lives for the life of the process, one copy per GPU that the
 // library runs on.  Every call on a GPU uses that GPU's copy: calls that
 // overlap in time on one GPU (on different streams) race on it.  Nothing in
-// it needs clearing by the caller: the chunk pairs and carries of a call are
-// written before that call reads them, and the queue's counter and flags are
-// cleared by a kernel at the start of every call that uses them.
+// it needs clearing by the caller: a kernel at the start of every call that
+// uses it clears what that call polls (the time-chunked scan's pair slots and
+// counter, the queue's counter and flags).
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -23,7 +23,8 @@ namespace {
 // Largest forward workspace any valid problem needs: the scan splits time only
 // while the problem has fewer than 1024 wavefronts (4 per 16 channels), into
 // at most ceil(1024 / waves) chunks, so batch * dim * chunks <= 8188 and the
-// three per-chunk arrays of 16 floats take at most 1.57 MB.
+// 64-bit pair slots of every (channel, chunk or group, state) take at most
+// 1.05 MB.
 constexpr size_t kScratchBytes = (size_t)2 << 20;
 
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
