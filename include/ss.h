@@ -336,7 +336,8 @@ size_t ss_ssd_workspace_size(const ss_ssd_problem *p);
  * the workspace and another buffer is rejected.  Returns SS_ERR_BAD_DTYPE for
  * fp32 I/O (the matrix-core path takes 16-bit data), SS_ERR_UNSUPPORTED for a
  * headdim other than 64, a dstate outside {32, 64, 96, 128}, ngroups not
- * dividing nheads, a workspace missing or too small, or overlapping buffers.
+ * dividing nheads, more than 32768 heads, a workspace missing or too small,
+ * or overlapping buffers.
  */
 ss_status ss_ssd_fwd(const ss_ssd_problem *p, const void *x, const void *dt, const float *A,
                      const void *Bm, const void *Cm, const float *D, const void *z, const float *dt_bias,

@@ -437,6 +437,9 @@ ss_status check_ssd(const ss_ssd_problem* p) {
   if (p->headdim != 64) return SS_ERR_UNSUPPORTED;
   if (p->dstate != 32 && p->dstate != 64 && p->dstate != 96 && p->dstate != 128) return SS_ERR_UNSUPPORTED;
   if (p->nheads % p->ngroups != 0) return SS_ERR_UNSUPPORTED;
+  // the kernels address a 256-step chunk of x or z (256 * nheads * 64 * 2
+  // bytes) with 32-bit offsets; at most 2^30 bytes
+  if (p->nheads > 32768) return SS_ERR_UNSUPPORTED;
   const int64_t lim = (int64_t)1 << 31;
   if (p->batch > lim || p->seqlen > lim || p->nheads > lim) return SS_ERR_BAD_SHAPE;
   const double nchunks = (double)((p->seqlen + kSsdChunk - 1) / kSsdChunk);

@@ -83,6 +83,23 @@ __device__ __forceinline__ typename mfma_t<IO>::V as_vec(u32x4v w) {
   return __builtin_bit_cast(typename mfma_t<IO>::V, w);
 }
 
+// A range-checked view of the steps [t0, t0 + kQ) of one batch row: `at`
+// points at step t0 (wave-uniform), `row` is the byte distance between
+// steps, and steps at or past seqlen read as zeros through the hardware's
+// range check.  No load is predicated, so none forces an early wait (a load
+// under a branch must complete before the branch joins).  The host keeps a
+// chunk of any operand below 2^31 bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_view(const void* at, int64_t row, int64_t t0, int64_t seqlen) {
+  const int64_t n = seqlen - t0 < kQ ? seqlen - t0 : kQ;
+  return make_rsrc(at, at ? (uint32_t)(n * row) : 0u);
+}
+__device__ __forceinline__ u32x4v vload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 vload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 // Time-major tiles in LDS (row = step, W 16-bit columns, 16-byte chunks of a
 // row rotated by (row / 4) so that both the row writes and the transposing
 // reads below are free of bank conflicts).  Element offset of (row, col):
@@ -194,14 +211,15 @@ struct CbTile {
   __device__ __forceinline__ void load(const SsdParams& p, int64_t b_, int64_t c, int64_t g, int idx, int lane) {
     cb_tile_of(idx, rt, jt);
     const int64_t t0 = c * kQ, crow = p.ngroups * N * 2;
-    const char* cbase = static_cast<const char*>(p.Cm) + ((b_ * p.seqlen) * p.ngroups + g) * N * 2;
-    const char* bbase = static_cast<const char*>(p.Bm) + ((b_ * p.seqlen) * p.ngroups + g) * N * 2;
-    const int64_t ti = t0 + 16 * rt + lane % 16, tj = t0 + 16 * jt + lane % 16;
+    const int64_t at = ((b_ * p.seqlen + t0) * p.ngroups + g) * N * 2;
+    const auto cv = chunk_view(static_cast<const char*>(p.Cm) + at, crow, t0, p.seqlen);
+    const auto bv = chunk_view(static_cast<const char*>(p.Bm) + at, crow, t0, p.seqlen);
+    const uint32_t ri = (uint32_t)((16 * rt + lane % 16) * crow), rj = (uint32_t)((16 * jt + lane % 16) * crow);
 #pragma unroll
     for (int ks = 0; ks < N / 32; ++ks) {
-      const int n0 = 32 * ks + 8 * (lane / 16);
-      a[ks] = ti < p.seqlen ? *reinterpret_cast<const u32x4v*>(cbase + ti * crow + n0 * 2) : u32x4v{0u, 0u, 0u, 0u};
-      b[ks] = tj < p.seqlen ? *reinterpret_cast<const u32x4v*>(bbase + tj * crow + n0 * 2) : u32x4v{0u, 0u, 0u, 0u};
+      const uint32_t n0 = (uint32_t)(32 * ks + 8 * (lane / 16)) * 2u;
+      a[ks] = vload16(cv, ri + n0);
+      b[ks] = vload16(bv, rj + n0);
     }
   }
   __device__ __forceinline__ void finish(const SsdParams& p, int64_t b_, int64_t c, int64_t g, int lane) {
@@ -251,21 +269,19 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
 
   // x: 2048 16-byte pieces (step tid / 8 + 32 k, channels 8 (tid % 8) ..), eight per thread;
   // B: 1024 pieces (step tid / 4 + 64 k, states 8 (tid % 4) ..), four per thread
+  const char* dtbase = static_cast<const char*>(p.dt) + (b * p.seqlen * p.nheads + h) * 2;
   u32x4v xr[8], br[4];
-  float dtr = 0.0f;  // dt of step tid
+  raw_t<IO> dtr = 0;  // dt of step tid (raw bits)
   auto load_chunk = [&](int64_t c) {
     const int64_t t0 = c * kQ;
+    const auto xv = chunk_view(xbase + t0 * xrow, xrow, t0, p.seqlen);
+    const auto bv = chunk_view(bbase + t0 * brow, brow, t0, p.seqlen);
+    const auto dv = chunk_view(dtbase + t0 * p.nheads * 2, p.nheads * 2, t0, p.seqlen);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int64_t t = t0 + tid / 8 + 32 * k;
-      xr[k] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(xbase + t * xrow + (tid % 8) * 16) : u32x4v{0u, 0u, 0u, 0u};
-    }
+    for (int k = 0; k < 8; ++k) xr[k] = vload16(xv, (uint32_t)((tid / 8 + 32 * k) * xrow + (tid % 8) * 16));
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t t = t0 + tid / 4 + 64 * k;
-      br[k] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(bbase + t * brow + (tid % 4) * 16) : u32x4v{0u, 0u, 0u, 0u};
-    }
-    dtr = t0 + tid < p.seqlen ? load_io<IO>(p.dt, (b * p.seqlen + t0 + tid) * p.nheads + h) : 0.0f;
+    for (int k = 0; k < 4; ++k) br[k] = vload16(bv, (uint32_t)((tid / 4 + 64 * k) * brow + (tid % 4) * 16));
+    dtr = bload<IO>(dv, (uint32_t)(tid * p.nheads * 2));
   };
 
   // the state slice: lane holds p = 16 w + 4 (lane / 16) + r, n = 32 s + 16 nt + lane % 16
@@ -290,7 +306,7 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
     {  // Delta of step tid (0 past the sequence)
       float d = 0.0f;
       if (t0 + tid < p.seqlen) {
-        const float xd = dtr + bias;
+        const float xd = bits_f32<IO>(dtr) + bias;
         d = p.softplus ? softplus_f(xd) : xd;
       }
       sDelta[tid] = d;
@@ -402,12 +418,10 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
   const uint16_t* Hin = p.ws_entry + ((b * p.nchunks + c) * p.nheads + h) * (int64_t)(kP * N);
 
   // ---- prologue: issue every operand load, then scan Delta A and fill LDS
+  const auto xv = chunk_view(xbase + t0 * xrow, xrow, t0, p.seqlen);
   u32x4v xr[4];  // 16-byte pieces of x: step tid / 8 + 64 k, channels 8 (tid % 8) ..
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int64_t t = t0 + tid / 8 + 64 * k;
-    xr[k] = t < p.seqlen ? *reinterpret_cast<const u32x4v*>(xbase + t * xrow + (tid % 8) * 16) : u32x4v{0u, 0u, 0u, 0u};
-  }
+  for (int k = 0; k < 4; ++k) xr[k] = vload16(xv, (uint32_t)((tid / 8 + 64 * k) * xrow + (tid % 8) * 16));
   constexpr int kHPieces = N * (kP / 8);  // 16-byte pieces of H_in (stored [n][p])
   constexpr int kHItems = (kHPieces + kScanThreads - 1) / kScanThreads;
   u32x4v hr[kHItems];
@@ -416,17 +430,16 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
     const int item = tid + kScanThreads * k;
     hr[k] = item < kHPieces ? *reinterpret_cast<const u32x4v*>(Hin + item * 8) : u32x4v{0u, 0u, 0u, 0u};
   }
-  float dt_raw = 0.0f;
-  if (tid < kQ && t0 + tid < p.seqlen) dt_raw = load_io<IO>(p.dt, (b * p.seqlen + t0 + tid) * p.nheads + h);
-  auto cfrag = [&](int64_t t, int n0) -> u32x4v {
-    if (t >= p.seqlen) return u32x4v{0u, 0u, 0u, 0u};
-    return *reinterpret_cast<const u32x4v*>(cbase + t * crow + n0 * 2);
-  };
+  const auto dv = chunk_view(static_cast<const char*>(p.dt) + ((b * p.seqlen + t0) * p.nheads + h) * 2, p.nheads * 2,
+                             t0, p.seqlen);
+  const raw_t<IO> dt_bits = bload<IO>(dv, tid < kQ ? (uint32_t)(tid * p.nheads * 2) : kOffNone);
+  const auto cv = chunk_view(cbase + t0 * crow, crow, t0, p.seqlen);
   u32x4v cf[2][N / 32];
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int ks = 0; ks < N / 32; ++ks) cf[q][ks] = cfrag(t0 + 32 * blk[q] + 16 * half + lane % 16, 32 * ks + 8 * (lane / 16));
+    for (int ks = 0; ks < N / 32; ++ks)
+      cf[q][ks] = vload16(cv, (uint32_t)((32 * blk[q] + 16 * half + lane % 16) * crow + (32 * ks + 8 * (lane / 16)) * 2));
 
   // x and H_in into LDS, then Delta and its cumulative sum (threads 0..255 = steps)
 #pragma unroll
@@ -437,7 +450,7 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
     if (item < kHPieces) *reinterpret_cast<u32x4v*>(&sH[tm_off<kP>(item / 8, 8 * (item % 8))]) = hr[k];
   }
   {
-    const float delta = chunk_cumsum<IO>(p, dt_raw, tid < kQ && t0 + tid < p.seqlen, p.A[h],
+    const float delta = chunk_cumsum<IO>(p, bits_f32<IO>(dt_bits), tid < kQ && t0 + tid < p.seqlen, p.A[h],
                                          p.dt_bias ? p.dt_bias[h] : 0.0f, sCs, sWave);
     if (tid < kQ) {
       sDelta[tid] = delta;
@@ -486,18 +499,15 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) cbv[pc][ks] = *reinterpret_cast<const u32x4v*>(cbrow + kJB * pc + 32 * ks);
     if (q == 0) {  // the gate, loaded once the first pieces' C B^T are on their way
-    // gate values for the epilogue: lane has channels 16 pt + 4 (lane / 16) .. + 3 of its step
-  #pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      const int64_t t = t0 + 32 * blk[qq] + 16 * half + lane % 16;
-  #pragma unroll
-      for (int pt = 0; pt < 4; ++pt)
-        zv[qq][pt] = (p.z && t < p.seqlen)
-                        ? *reinterpret_cast<const uint2*>(static_cast<const char*>(p.z) + t * xrow +
-                                                          ((b * p.seqlen) * p.nheads + h) * kP * 2 +
-                                                          (16 * pt + 4 * (lane / 16)) * 2)
-                        : make_uint2(0u, 0u);
-    }
+      // gate values for the epilogue: lane has channels 16 pt + 4 (lane / 16) .. + 3 of its step
+      const auto zw = chunk_view(p.z ? static_cast<const char*>(p.z) + ((b * p.seqlen + t0) * p.nheads + h) * kP * 2
+                                     : nullptr,
+                                 xrow, t0, p.seqlen);
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+          zv[qq][pt] = vload8(zw, (uint32_t)((32 * blk[qq] + 16 * half + lane % 16) * xrow + (16 * pt + 4 * (lane / 16)) * 2));
     }
 #pragma unroll
     for (int piece = 0; piece < kQ / kJB; ++piece) {
