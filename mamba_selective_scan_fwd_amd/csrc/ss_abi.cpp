@@ -70,8 +70,8 @@ QueueLayout queue_layout(const ss_problem* p) {
   return q;
 }
 
-// The time-chunked scan's workspace (one launch): a control block (unit
-// counter, error word), then per (channel, chunk, state) the chunk pairs
+// The time-chunked scan's workspace (one launch): a control block (its second
+// word is the error word), then per (channel, chunk, state) the chunk pairs
 // (P, S) and per (channel, group but the last, state) the group pairs, one
 // 64-bit word each.  Groups hold G chunks, G the least power of two with
 // G * G >= K, so that a chunk's entry state composes at most G - 1 chunk

@@ -596,9 +596,14 @@ __global__ void __launch_bounds__(256) ss_queue_clear_kernel(int32_t* ctrl, int3
 }
 
 // ---- time-chunked scan in one launch ----------------------------------------
-// Units (chunk, batch row, channel block) are taken in that order from an
-// atomic counter, so every unit a workgroup waits for (an earlier chunk of
-// its block) was taken before it by a workgroup that is running or done.
+// Workgroup i runs unit i of the order (chunk, batch row, channel block), so
+// a workgroup waits only on workgroups numbered below it.  Those are running
+// or done: the launch has at most 2 x 256 - 2 workgroups of 40 KB of LDS (four
+// fit per CU), all resident at once on an otherwise idle GPU, and the hardware
+// hands out workgroups in order of their number.  (An atomic counter handing
+// out units would not need either fact, but its atomics serialise: the last
+// unit of the long-sequence workload started 2.9 us after the first.)  Every
+// wait is bounded all the same, so no launch can hang.
 //
 // A pair crosses workgroups (and XCDs, whose L2 caches are not coherent with
 // one another) as one 64-bit word, P in the low half and S in the high half,
@@ -655,14 +660,11 @@ __device__ __forceinline__ void compose_published(const uint64_t* slot, int64_t 
 template <int IO, bool PAIR, bool SEQ, int FL>
 __global__ void __launch_bounds__(kThreads) ss_fwd_lookback_kernel(FwdParams p) {
   __shared__ FwdSmem<true> sm;
-  __shared__ int64_t s_unit;
   const int tid = threadIdx.x;
   const int n = tid % 16;
-  if (tid == 0) s_unit = (int64_t)atomicAdd(reinterpret_cast<unsigned int*>(p.q_ctrl), 1u);
-  __syncthreads();
   const int64_t nrb = p.batch * p.ch_blocks;  // (batch row, channel block) pairs
   const int64_t K = p.nchunks, G = p.group, NG = p.ngroups;
-  const int64_t c = s_unit / nrb, rb = s_unit % nrb;
+  const int64_t c = blockIdx.x / nrb, rb = blockIdx.x % nrb;
   const int64_t b = rb / p.ch_blocks, cb = rb % p.ch_blocks;
   const int64_t d = ss_lane_channel(tid, cb * kChPerBlock);
   const bool ch_ok = d < p.dim, n_ok = n < p.dstate;
@@ -712,8 +714,8 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_lookback_kernel(FwdParams p) 
   if (p.last_state && ch_ok && n_ok && c == K - 1) p.last_state[ch * p.dstate + n] = h;
 }
 
-// Before a launch of the one-launch time-chunked scan: the unit counter and
-// error word to zero, every pair slot to kPairEmpty.
+// Before a launch of the one-launch time-chunked scan: the error word to zero,
+// every pair slot to kPairEmpty.
 __global__ void __launch_bounds__(256) ss_pairs_clear_kernel(int32_t* ctrl, uint64_t* slots, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < 2) ctrl[i] = 0;

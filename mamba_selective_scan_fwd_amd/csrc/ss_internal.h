@@ -41,7 +41,7 @@ struct FwdParams {
   // pair (P, S) as one 64-bit word (P low), per (channel, group but the last,
   // state) the pair of a group of `group` consecutive chunks; nslots words
   // from `pairs` (through the group slots) are set to all ones, "not yet
-  // published", before the launch; the unit counter and error word in q_ctrl
+  // published", before the launch; the error word in q_ctrl[1]
   uint64_t* pairs;
   uint64_t* gpairs;
   int64_t nslots;

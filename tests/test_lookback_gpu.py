@@ -103,20 +103,45 @@ def test_dstate_below_16_and_h0():
     _check(prob, h0=h0)
 
 
-def test_dirty_workspace_and_reuse():
-    """The workspace's contents on entry do not matter (its flags and counter are cleared
-    by the call itself), one workspace serves two problems in a row, and no wait gave up."""
+def test_dirty_workspace_reused_across_paths():
+    """The workspace's contents on entry do not matter (a kernel at the start of each call
+    resets what the call polls), so one workspace, dirty to begin with, serves a sequence of
+    calls: two time-chunked problems of different plans, a ragged problem through the work
+    queue, then a time-chunked one again, each over what the previous one left.  No wait
+    gave up."""
     ss = _ss()
     lib = ss.load_library()
-    big = (1, 16, 8192)
-    wsz = lib.ss_fwd_workspace_size(ctypes.byref(ss.problem(big[0], big[1], 16, big[2], torch.float32)))
+    shapes = [((1, 16, 8192), None, 307), ((2, 24, 700), None, 308), ((3, 2048, 600), [600, 1, 333], 309),
+              ((1, 40, 5000), None, 310)]
+    wsz = 0
+    for (Bsz, Dd, L), lens, _ in shapes:
+        wsz = max(wsz, lib.ss_fwd_workspace_size(ctypes.byref(ss.problem(Bsz, Dd, 16, L, torch.float32))))
     ws = torch.full((wsz // 4 + 64,), -1, dtype=torch.int32, device="cuda")
-    for shape, seed in [(big, 307), ((2, 24, 700), 308)]:
-        say("lookback reuse shape=%s plan=%s" % (shape, plan(*shape)))
-        Bsz, Dd, L = shape
-        _check(inputs.make_problem(Bsz, Dd, 16, L, "f32", seed=seed), workspace=ws)
+    for (Bsz, Dd, L), lens, seed in shapes:
+        say("lookback reuse shape=%s lengths=%s plan=%s" % ((Bsz, Dd, L), lens, plan(Bsz, Dd, L)))
+        prob = inputs.make_problem(Bsz, Dd, 16, L, "f32", seed=seed)
+        if lens is not None:
+            prob["lengths"] = torch.tensor(lens, dtype=torch.int32)
+        if Dd > 1000:  # the queue problem: a few sampled channels are enough here
+            _check_sampled(prob, workspace=ws)
+        else:
+            _check(prob, workspace=ws)
         assert int(ws[1].item()) == 0, "a wait between workgroups gave up"
-        ws.fill_(-1)
+
+
+def _check_sampled(prob, workspace):
+    ss = _ss()
+    g = to_dev(prob)
+    Bsz, Dd, L = prob["u"].shape
+    y, last, _ = ss.fwd(g["u"], g["delta"], g["A"], g["Bm"], g["Cm"], D=g["D"], z=g["z"], delta_bias=g["bias"],
+                        lengths=g["lengths"], workspace=workspace)
+    torch.cuda.synchronize()
+    rows = np.array([0 * Dd + 5, 1 * Dd + 1000, 2 * Dd + 2047])
+    yr, lr = oracle.fwd(**oracle_args(prob), lengths=prob["lengths"].numpy(), rows=rows)
+    yg, lg = f64(y).reshape(Bsz * Dd, L), f64(last).reshape(Bsz * Dd, -1)
+    ey = rel_err(yg[rows], yr.reshape(Bsz * Dd, L)[rows])
+    el = rel_err(lg[rows], lr.reshape(Bsz * Dd, -1)[rows])
+    assert ey <= TOL["f32"] and el <= TOL["f32"], (ey, el)
 
 
 def test_repeated_calls_bit_identical():
