@@ -300,14 +300,19 @@ ss_status ss_conv1d_step(const ss_conv_problem *p, const void *x_t, const float 
  *   Delta_t  = softplus(dt[b,t,h] + dt_bias[h])     (softplus only if flagged)
  *   H_t      = exp(Delta_t A[h]) H_{t-1} + Delta_t x[b,t,h,:] B[b,t,g,:]^T
  *   y[b,t,h,p] = sum_n H_t[p][n] C[b,t,g,n] + D[h] x[b,t,h,p]   (* SiLU(z) if z)
- * from H_{-1} = h0 (or 0).  Computed by the chunked algorithm the page
- * describes (quadratic, attention-like matmuls inside 256-step chunks, one
- * state passed between chunks) on the matrix cores, fp32 accumulation.
+ * from H_{-1} = h0 (or 0).  With packed documents ("niverel-mamba" README,
+ * "seq_idx strict reset": for Mamba-2 the SSM state resets at a document
+ * boundary) H is zero before every step t >= 1 whose id seq_idx[b,t] differs
+ * from seq_idx[b,t-1], so h0 feeds only a row's first document.  Computed by
+ * the chunked algorithm the page describes (quadratic, attention-like
+ * matmuls inside 256-step chunks, one state passed between chunks) on the
+ * matrix cores, fp32 accumulation.
  * Layouts (time-major, as Mamba-2 stores them):
  *   x, z, y : (batch, seqlen, nheads, headdim)  io dtype
  *   dt      : (batch, seqlen, nheads)           io dtype
  *   Bm, Cm  : (batch, seqlen, ngroups, dstate)  io dtype
  *   A, D, dt_bias : (nheads) fp32
+ *   seq_idx : (batch, seqlen) int32 (any values; only changes matter)
  *   h0, final_state : (batch, nheads, headdim, dstate) fp32
  */
 typedef struct ss_ssd_problem {
@@ -330,18 +335,18 @@ typedef struct ss_ssd_problem {
 size_t ss_ssd_workspace_size(const ss_ssd_problem *p);
 
 /*
- * SSD forward.  D, z, dt_bias, h0 and final_state are optional (NULL).
+ * SSD forward.  D, z, dt_bias, seq_idx, h0 and final_state are optional (NULL).
  * Every pointer must be 16-byte aligned.  y may be x or z itself (in place)
  * and final_state may be h0 itself; any other overlap between an output or
  * the workspace and another buffer is rejected.  Returns SS_ERR_BAD_DTYPE for
  * fp32 I/O (the matrix-core path takes 16-bit data), SS_ERR_UNSUPPORTED for a
  * headdim other than 64, a dstate outside {32, 64, 96, 128}, ngroups not
- * dividing nheads, more than 32768 heads, a workspace missing or too small,
- * or overlapping buffers.
+ * dividing nheads, more than 32768 heads, document ids on a row longer than
+ * 2^29 steps, a workspace missing or too small, or overlapping buffers.
  */
 ss_status ss_ssd_fwd(const ss_ssd_problem *p, const void *x, const void *dt, const float *A,
                      const void *Bm, const void *Cm, const float *D, const void *z, const float *dt_bias,
-                     const float *h0, void *y, float *final_state,
+                     const int32_t *seq_idx, const float *h0, void *y, float *final_state,
                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Number of floats of the checkpoint buffer: batch*dim*ceil(seqlen/64)*dstate (0 if invalid). */

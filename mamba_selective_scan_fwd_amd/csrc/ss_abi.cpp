@@ -465,12 +465,15 @@ size_t ss_ssd_workspace_size(const ss_ssd_problem* p) {
 }
 
 ss_status ss_ssd_fwd(const ss_ssd_problem* p, const void* x, const void* dt, const float* A, const void* Bm,
-                     const void* Cm, const float* D, const void* z, const float* dt_bias, const float* h0, void* y,
-                     float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+                     const void* Cm, const float* D, const void* z, const float* dt_bias, const int32_t* seq_idx,
+                     const float* h0, void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   ss_status s = check_ssd(p);
   if (s != SS_OK) return s;
   if (!x || !dt || !A || !Bm || !Cm || !y) return SS_ERR_NULL_ARG;
-  const void* ptrs[] = {x, dt, A, Bm, Cm, D, z, dt_bias, h0, y, final_state, workspace};
+  // a row's document ids are read through one 32-bit range-checked view
+  if (seq_idx && p->seqlen > ((int64_t)1 << 29)) return SS_ERR_UNSUPPORTED;
+  const void* ptrs[] = {x, dt, A, Bm, Cm, D, z, dt_bias, seq_idx, h0, y, final_state, workspace};
   for (const void* q : ptrs)
     if (q && !aligned(q)) return SS_ERR_MISALIGNED;
   const size_t need = ss_ssd_workspace_size(p);
@@ -485,7 +488,10 @@ ss_status ss_ssd_fwd(const ss_ssd_problem* p, const void* x, const void* dt, con
     const size_t hb = (size_t)(p->batch * p->nheads) * 64 * (size_t)p->dstate * 4;
     const size_t vb = (size_t)p->nheads * 4;
     struct Span { const void* ptr; size_t n; };
-    const Span in[] = {{x, xb}, {dt, dtb}, {A, vb}, {Bm, bcb}, {Cm, bcb}, {D, vb}, {z, xb}, {dt_bias, vb}, {h0, hb}};
+    const Span in[] = {{x, xb},       {dt, dtb},      {A, vb},
+                       {Bm, bcb},     {Cm, bcb},      {D, vb},
+                       {z, xb},       {dt_bias, vb},  {seq_idx, (size_t)(p->batch * p->seqlen) * 4},
+                       {h0, hb}};
     for (const Span& r : in) {
       if (!r.ptr) continue;
       if (overlaps(r.ptr, r.n, y, xb) && !(r.ptr == y && (r.ptr == x || r.ptr == z))) return SS_ERR_UNSUPPORTED;
@@ -501,6 +507,7 @@ ss_status ss_ssd_fwd(const ss_ssd_problem* p, const void* x, const void* dt, con
   ss::SsdParams k{};
   k.io = p->io_dtype; k.softplus = p->dt_softplus != 0;
   k.x = x; k.dt = dt; k.A = A; k.Bm = Bm; k.Cm = Cm; k.D = D; k.z = z; k.dt_bias = dt_bias; k.h0 = h0;
+  k.seq_idx = seq_idx;
   k.y = y; k.final_state = final_state;
   char* ws = static_cast<char*>(workspace);
   k.ws_entry = reinterpret_cast<uint16_t*>(ws);

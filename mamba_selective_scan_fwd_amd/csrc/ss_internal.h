@@ -149,6 +149,7 @@ struct SsdParams {
   const float* D;        // (nheads) or null
   const void* z;         // like x, or null
   const float* dt_bias;  // (nheads) or null
+  const int32_t* seq_idx;  // (batch, seqlen) document ids, or null
   const float* h0;       // (batch, nheads, 64, dstate) or null
   void* y;
   float* final_state;    // (batch, nheads, 64, dstate) or null

@@ -248,7 +248,7 @@ struct CbTile {
 // tiles, one per wave and chunk while there are waves enough; the first
 // tile's operands are loaded at the top of the chunk's iteration.
 constexpr int kNS = 32;  // states per slice
-template <int IO, int N>
+template <int IO, int N, bool SEQ>
 __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) {
   using M = mfma_t<IO>;
   constexpr int kSlices = N / kNS;
@@ -256,6 +256,7 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
   __shared__ __attribute__((aligned(16))) float sDelta[kQ];
   __shared__ __attribute__((aligned(16))) uint16_t sX[kQ * kP];   // x * w, time-major (tm_off<64>)
   __shared__ __attribute__((aligned(16))) uint16_t sB[kQ * kNS];  // B of the slice, time-major (tm_off<32>)
+  __shared__ int s_lr[2];  // SEQ: the chunk's last document start (-1: none), by chunk parity
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const int64_t lb = xcd_logical_block();  // the workgroups of one row's group share B in an XCD's L2
   const int s = (int)(lb % kSlices);
@@ -270,10 +271,15 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
   // x: 2048 16-byte pieces (step tid / 8 + 32 k, channels 8 (tid % 8) ..), eight per thread;
   // B: 1024 pieces (step tid / 4 + 64 k, states 8 (tid % 4) ..), four per thread
   const char* dtbase = static_cast<const char*>(p.dt) + (b * p.seqlen * p.nheads + h) * 2;
+  // SEQ: the row's document ids through one range-checked view (step -1 and
+  // steps past the row read as 0); step tid's id and its predecessor's
+  const auto idv = make_rsrc(SEQ ? p.seq_idx + b * p.seqlen : nullptr, SEQ ? (uint32_t)(p.seqlen * 4) : 0u);
+  uint32_t idr = 0, idpr = 0;
   u32x4v xr[8], br[4];
   raw_t<IO> dtr = 0;  // dt of step tid (raw bits)
   auto load_chunk = [&](int64_t c) {
     const int64_t t0 = c * kQ;
+    if constexpr (SEQ) load_doc_ids(idv, (int)(t0 + tid), idr, idpr);
     const auto xv = chunk_view(xbase + t0 * xrow, xrow, t0, p.seqlen);
     const auto bv = chunk_view(bbase + t0 * brow, brow, t0, p.seqlen);
     const auto dv = chunk_view(dtbase + t0 * p.nheads * 2, p.nheads * 2, t0, p.seqlen);
@@ -298,6 +304,8 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
   const int bo[2][2] = {{tm_lane_off<kNS>(0, 0, lane), tm_lane_off<kNS>(0, 1, lane)},
                         {tm_lane_off<kNS>(16, 0, lane), tm_lane_off<kNS>(16, 1, lane)}};
 
+  if (SEQ && tid < 2) s_lr[tid] = -1;
+  __syncthreads();
   load_chunk(0);
   for (int64_t c = 0; c < p.nchunks; ++c) {
     const int64_t t0 = c * kQ;
@@ -310,8 +318,19 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
         d = p.softplus ? softplus_f(xd) : xd;
       }
       sDelta[tid] = d;
+      if constexpr (SEQ) {  // a document starts at step tid
+        if (t0 + tid > 0 && t0 + tid < p.seqlen && idr != idpr) atomicMax(&s_lr[c & 1], tid);
+      }
     }
     __syncthreads();
+    // documents: only the steps from the chunk's last document start on feed
+    // the state that leaves the chunk, and a start inside it drops the
+    // entering state (the state is zero before every start)
+    int lr = -1;
+    if constexpr (SEQ) {
+      lr = s_lr[c & 1];
+      if (tid == 0) s_lr[(c + 1) & 1] = -1;
+    }
     float delta[4], cs[4];
     wave_chunk_cumsum(sDelta, A, delta, cs);
     const float cs_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cs[3]), 63));
@@ -321,6 +340,13 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
       w.y = exp2_hw((cs_last - cs[1]) * kLog2e) * delta[1];
       w.z = exp2_hw((cs_last - cs[2]) * kLog2e) * delta[2];
       w.w = exp2_hw((cs_last - cs[3]) * kLog2e) * delta[3];
+      if constexpr (SEQ) {
+        const int j = 4 * lane;
+        w.x = j + 0 >= lr ? w.x : 0.0f;
+        w.y = j + 1 >= lr ? w.y : 0.0f;
+        w.z = j + 2 >= lr ? w.z : 0.0f;
+        w.w = j + 3 >= lr ? w.w : 0.0f;
+      }
       *reinterpret_cast<float4*>(&sW[4 * lane]) = w;
     }
     __syncthreads();
@@ -348,7 +374,7 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
     for (int nt = 0; nt < 2; ++nt)
       *reinterpret_cast<uint2*>(&E[(kNS * s + 16 * nt + lane % 16) * kP + 16 * wave + 4 * (lane / 16)]) =
           make_uint2(pack2<IO>(acc[nt][0], acc[nt][1]), pack2<IO>(acc[nt][2], acc[nt][3]));
-    const float decay = exp2_hw(cs_last * kLog2e);
+    const float decay = lr >= 0 ? 0.0f : exp2_hw(cs_last * kLog2e);
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) acc[nt] *= decay;
 #pragma unroll
@@ -393,13 +419,15 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
 // pieces (loads complete in issue order for the wait counter, so a load
 // issued earlier than those would delay the first piece).
 constexpr int kScanThreads = 512;
-template <int IO, int N>
+template <int IO, int N, bool SEQ>
 __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) {
   using M = mfma_t<IO>;
   __shared__ __attribute__((aligned(16))) float sDelta[kQ];
   __shared__ __attribute__((aligned(16))) float sCs[kQ];
   __shared__ __attribute__((aligned(16))) float sWp[kQ];           // exp(cs_e - cs_j) Delta_j, e = end of j's piece
   __shared__ float sWave[4];
+  __shared__ __attribute__((aligned(16))) int sSeg[kQ];            // SEQ: document starts at or before each step
+  __shared__ int sSegW[4];
   __shared__ __attribute__((aligned(16))) uint16_t sX[kQ * kP];    // x of the chunk, time-major (tm_off<64>)
   __shared__ __attribute__((aligned(16))) uint16_t sH[N * kP];     // entry state H_in, rows n of 64 p (tm_off<64>)
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
@@ -433,6 +461,11 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
   const auto dv = chunk_view(static_cast<const char*>(p.dt) + ((b * p.seqlen + t0) * p.nheads + h) * 2, p.nheads * 2,
                              t0, p.seqlen);
   const raw_t<IO> dt_bits = bload<IO>(dv, tid < kQ ? (uint32_t)(tid * p.nheads * 2) : kOffNone);
+  uint32_t idr = 0, idpr = 0;  // SEQ: document ids of step tid and of the step before it
+  if constexpr (SEQ) {
+    const auto idv = make_rsrc(p.seq_idx + b * p.seqlen, (uint32_t)(p.seqlen * 4));
+    load_doc_ids(idv, (int)(t0 + tid), idr, idpr);
+  }
   const auto cv = chunk_view(cbase + t0 * crow, crow, t0, p.seqlen);
   u32x4v cf[2][N / 32];
 #pragma unroll
@@ -449,12 +482,29 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
     const int item = tid + kScanThreads * k;
     if (item < kHPieces) *reinterpret_cast<u32x4v*>(&sH[tm_off<kP>(item / 8, 8 * (item % 8))]) = hr[k];
   }
+  // documents: step i of the chunk sees the state entering the chunk only
+  // before the chunk's first document start, and step j's input only from
+  // the same document (no start in (j, i]): sSeg[i] counts the starts at or
+  // before i (threads 0..255 = steps; per-wave counts in sSegW first)
+  uint64_t starts = 0;
+  if constexpr (SEQ) {
+    starts = __builtin_amdgcn_ballot_w64(tid < kQ && t0 + tid > 0 && t0 + tid < p.seqlen && idr != idpr);
+    if (tid < kQ && lane == 0) sSegW[wave] = (int)__builtin_popcountll(starts);
+  }
   {
     const float delta = chunk_cumsum<IO>(p, bits_f32<IO>(dt_bits), tid < kQ && t0 + tid < p.seqlen, p.A[h],
                                          p.dt_bias ? p.dt_bias[h] : 0.0f, sCs, sWave);
     if (tid < kQ) {
       sDelta[tid] = delta;
       sWp[tid] = exp2_hw((sCs[tid | (kJB - 1)] - sCs[tid]) * kLog2e) * delta;
+    }
+  }
+  if constexpr (SEQ) {
+    if (tid < kQ) {  // sSegW is ordered by the barriers of the cumulative sum
+      int before = 0;
+      for (int w = 0; w < wave; ++w) before += sSegW[w];
+      const uint64_t upto = lane == 63 ? ~0ull : ((2ull << lane) - 1);
+      sSeg[tid] = before + (int)__builtin_popcountll(starts & upto);
     }
   }
 
@@ -481,13 +531,23 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
   }
 
   uint2 zv[2][4];
-  __syncthreads();  // sDelta, sWp
+  __syncthreads();  // sDelta, sWp, sSeg
+  if constexpr (SEQ) {  // the entering state reaches only the steps before the first start
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (sSeg[32 * blk[q] + 16 * half + lane % 16] != 0)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) acc[q][pt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
 
-  // ---- Y_diag += x^T M^T, piece by piece
+  // ---- Y_diag += x^T M^T, piece by piece (mask: the chunk holds a document
+  // start, so M also keeps only pairs of steps of one document)
   const uint16_t* CBbase = p.ws_cb + ((b * p.nchunks + c) * p.ngroups + g) * (int64_t)(kQ * kQ);
+  const bool mask = SEQ && sSeg[kQ - 1] != 0;  // uniform
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int i = 32 * blk[q] + 16 * half + lane % 16;  // this lane's row (chunk-local)
+    const int segi = SEQ ? sSeg[i] : 0;
     const int dpiece = 32 * blk[q] / kJB;               // the piece holding the block's rows (at most 3)
     const float csi = sCs[i];
     const uint16_t* cbrow = CBbase + i * kQ + 8 * (lane / 16);
@@ -530,6 +590,14 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
           cb[2 * e + 1] = __builtin_bit_cast(float, cbv[piece][ks][e] & 0xffff0000u);
         }
         float m[8];
+        uint32_t same = 0xffu;  // bit e: step j0 + e is in row i's document
+        if (mask) {
+          const int4 s0 = *reinterpret_cast<const int4*>(&sSeg[j0]);
+          const int4 s1 = *reinterpret_cast<const int4*>(&sSeg[j0 + 4]);
+          same = (uint32_t)(s0.x == segi) | (uint32_t)(s0.y == segi) << 1 | (uint32_t)(s0.z == segi) << 2 |
+                 (uint32_t)(s0.w == segi) << 3 | (uint32_t)(s1.x == segi) << 4 | (uint32_t)(s1.y == segi) << 5 |
+                 (uint32_t)(s1.z == segi) << 6 | (uint32_t)(s1.w == segi) << 7;
+        }
         if (diag) {
           const float4 c0 = *reinterpret_cast<const float4*>(&sCs[j0]);
           const float4 c1 = *reinterpret_cast<const float4*>(&sCs[j0 + 4]);
@@ -540,14 +608,17 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const float v = cb[e] * exp2_hw((csi - csj[e]) * kLog2e) * dj[e];
-            m[e] = j0 + e <= i ? v : 0.0f;
+            m[e] = j0 + e <= i && ((same >> e) & 1u) ? v : 0.0f;
           }
         } else {
           const float4 w0 = *reinterpret_cast<const float4*>(&sWp[j0]);
           const float4 w1 = *reinterpret_cast<const float4*>(&sWp[j0 + 4]);
           const float wj[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) m[e] = cb[e] * (wj[e] * ei);
+          for (int e = 0; e < 8; ++e) {
+            m[e] = cb[e] * (wj[e] * ei);
+            if (SEQ) m[e] = ((same >> e) & 1u) ? m[e] : 0.0f;
+          }
         }
         u32x4v bop;
 #pragma unroll
@@ -595,15 +666,19 @@ __global__ void __launch_bounds__(kScanThreads, 4) ssd_scan_kernel(SsdParams p) 
   }
 }
 
-template <int IO, int N>
-hipError_t launch_ssd_n(const SsdParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((ssd_state_kernel<IO, N>), dim3((uint32_t)(p.batch * p.nheads * (N / kNS))), dim3(kSsdThreads), 0,
-                     st, p);
+template <int IO, int N, bool SEQ>
+hipError_t launch_ssd_seq(const SsdParams& p, hipStream_t st) {
+  hipLaunchKernelGGL((ssd_state_kernel<IO, N, SEQ>), dim3((uint32_t)(p.batch * p.nheads * (N / kNS))),
+                     dim3(kSsdThreads), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((ssd_scan_kernel<IO, N>), dim3((uint32_t)(p.batch * p.nchunks * p.nheads)), dim3(kScanThreads), 0,
-                     st, p);
+  hipLaunchKernelGGL((ssd_scan_kernel<IO, N, SEQ>), dim3((uint32_t)(p.batch * p.nchunks * p.nheads)),
+                     dim3(kScanThreads), 0, st, p);
   return hipGetLastError();
+}
+template <int IO, int N>
+hipError_t launch_ssd_n(const SsdParams& p, hipStream_t st) {
+  return p.seq_idx ? launch_ssd_seq<IO, N, true>(p, st) : launch_ssd_seq<IO, N, false>(p, st);
 }
 
 template <int IO>

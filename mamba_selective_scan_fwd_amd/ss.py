@@ -86,7 +86,7 @@ def load_library(path: str = LIB_PATH):
     lib.ss_ssd_workspace_size.restype = ctypes.c_size_t
     lib.ss_ssd_workspace_size.argtypes = [SP]
     lib.ss_ssd_fwd.restype = ctypes.c_int
-    lib.ss_ssd_fwd.argtypes = [SP] + [_vp] * 11 + [_vp, ctypes.c_size_t, _vp]
+    lib.ss_ssd_fwd.argtypes = [SP] + [_vp] * 12 + [_vp, ctypes.c_size_t, _vp]
     lib.ss_copy_probe.restype = ctypes.c_int
     lib.ss_copy_probe.argtypes = [_vp, _vp, ctypes.c_size_t, _vp]
     lib.ss_alu_probe.restype = ctypes.c_int
@@ -452,9 +452,10 @@ def conv1d_step(x_t, w, window, bias=None, silu=True, window_out=None, out=None)
 
 
 def ssd_fwd(x, dt, A, Bm, Cm, D=None, z=None, dt_bias=None, dt_softplus=True, h0=None, return_final_state=False,
-            y=None, workspace=None):
+            y=None, workspace=None, seq_idx=None):
     """Mamba-2 SSD scan on the matrix cores.  x, z: (B, L, H, 64); dt: (B, L, H); Bm, Cm: (B, L, G, N)
-    in fp16 or bf16; A, D, dt_bias: (H,) fp32; h0: (B, H, 64, N) fp32.  Returns y, or (y, final_state)."""
+    in fp16 or bf16; A, D, dt_bias: (H,) fp32; h0: (B, H, 64, N) fp32; seq_idx: (B, L) int32 document
+    ids (the state restarts at every change).  Returns y, or (y, final_state)."""
     lib = load_library()
     io = x.dtype
     if io not in (torch.float16, torch.bfloat16):
@@ -470,6 +471,7 @@ def ssd_fwd(x, dt, A, Bm, Cm, D=None, z=None, dt_bias=None, dt_softplus=True, h0
     D = _prep(D, torch.float32, "D", (Hn,))
     dt_bias = _prep(dt_bias, torch.float32, "dt_bias", (Hn,))
     h0 = _prep(h0, torch.float32, "h0", (Bsz, Hn, P, N))
+    seq_idx = _prep(seq_idx, torch.int32, "seq_idx", (Bsz, L))
     pr = ss_ssd_problem(Bsz, L, Hn, G, P, N, _IO[io], 1 if dt_softplus else 0)
     y = torch.empty_like(x) if y is None else _prep(y, io, "y", (Bsz, L, Hn, P))
     fin = torch.empty((Bsz, Hn, P, N), dtype=torch.float32, device=x.device) if return_final_state else None
@@ -480,7 +482,8 @@ def ssd_fwd(x, dt, A, Bm, Cm, D=None, z=None, dt_bias=None, dt_softplus=True, h0
     if workspace is None or workspace.numel() * workspace.element_size() < wsz:
         workspace = torch.empty((wsz + 255) // 256 * 64, dtype=torch.float32, device=x.device)
     _check(lib.ss_ssd_fwd(ctypes.byref(pr), _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(D), _ptr(z),
-                          _ptr(dt_bias), _ptr(h0), _ptr(y), _ptr(fin), _ptr(workspace), wsz, _stream(x.device)))
+                          _ptr(dt_bias), _ptr(seq_idx), _ptr(h0), _ptr(y), _ptr(fin), _ptr(workspace), wsz,
+                          _stream(x.device)))
     return (y, fin) if return_final_state else y
 
 

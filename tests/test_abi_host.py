@@ -180,7 +180,7 @@ def test_ssd_rejects_bad_problem(kw, code):
     lib = ss.load_library()
     p = _ssd_prob(**kw)
     assert lib.ss_ssd_workspace_size(ctypes.byref(p)) == 0
-    assert lib.ss_ssd_fwd(ctypes.byref(p), *([FAKE] * 5), None, None, None, None, FAKE, None, FAKE, 1 << 30,
+    assert lib.ss_ssd_fwd(ctypes.byref(p), *([FAKE] * 5), None, None, None, None, None, FAKE, None, FAKE, 1 << 30,
                           None) == code
 
 
@@ -192,12 +192,19 @@ def test_ssd_workspace_and_validation():
     # 2 chunks x 2 rows x 2 groups: C B^T (256 x 256) bf16
     assert p.ngroups == 2
     assert wsz == 16 * 4096 * 2 + 8 * 256 * 256 * 2
-    assert lib.ss_ssd_fwd(ctypes.byref(p), *([FAKE] * 5), None, None, None, None, FAKE, None, FAKE, wsz - 1,
+    assert lib.ss_ssd_fwd(ctypes.byref(p), *([FAKE] * 5), None, None, None, None, None, FAKE, None, FAKE, wsz - 1,
                           None) == 5
-    assert lib.ss_ssd_fwd(ctypes.byref(p), None, *([FAKE] * 4), None, None, None, None, FAKE, None, FAKE, wsz,
+    assert lib.ss_ssd_fwd(ctypes.byref(p), None, *([FAKE] * 4), None, None, None, None, None, FAKE, None, FAKE, wsz,
                           None) == 1
-    assert lib.ss_ssd_fwd(ctypes.byref(p), *([FAKE] * 5), None, None, None, FAKE + 4, FAKE, None, FAKE, wsz,
-                          None) == 4
+    assert lib.ss_ssd_fwd(ctypes.byref(p), *([FAKE] * 5), None, None, None, None, FAKE + 4, FAKE, None, FAKE, wsz,
+                          None) == 4   # h0 misaligned
+    assert lib.ss_ssd_fwd(ctypes.byref(p), *([FAKE] * 5), None, None, None, FAKE + 4, None, FAKE, None, FAKE, wsz,
+                          None) == 4   # document ids misaligned
+    long_row = _ssd_prob(batch=1, nheads=2, ngroups=2, seqlen=(1 << 29) + 1)
+    wl = lib.ss_ssd_workspace_size(ctypes.byref(long_row))
+    assert wl > 0
+    assert lib.ss_ssd_fwd(ctypes.byref(long_row), *([FAKE] * 5), None, None, None, FAKE, None, FAKE, None, FAKE, wl,
+                          None) == 5   # document ids on a row past 2^29 steps
 
 
 def test_ssd_rejects_overlapping_buffers():
@@ -207,13 +214,13 @@ def test_ssd_rejects_overlapping_buffers():
     p = _ssd_prob()
     wsz = lib.ss_ssd_workspace_size(ctypes.byref(p))
     G = 1 << 32                                   # far-apart, aligned fake device addresses
-    x, dt, A, Bm, Cm, y, fin, ws, h0 = (G * k for k in range(1, 10))
+    x, dt, A, Bm, Cm, y, fin, ws, h0, seq = (G * k for k in range(1, 11))
 
     def call(**kw):
-        a = dict(x=x, dt=dt, A=A, Bm=Bm, Cm=Cm, D=None, z=None, dt_bias=None, h0=h0, y=y, fin=fin, ws=ws)
+        a = dict(x=x, dt=dt, A=A, Bm=Bm, Cm=Cm, D=None, z=None, dt_bias=None, seq=seq, h0=h0, y=y, fin=fin, ws=ws)
         a.update(kw)
         return lib.ss_ssd_fwd(ctypes.byref(p), a["x"], a["dt"], a["A"], a["Bm"], a["Cm"], a["D"], a["z"],
-                              a["dt_bias"], a["h0"], a["y"], a["fin"], a["ws"], wsz, None)
+                              a["dt_bias"], a["seq"], a["h0"], a["y"], a["fin"], a["ws"], wsz, None)
 
     assert call(y=Cm + 256) == 5          # y overlaps C
     assert call(y=Bm) == 5                # y is B
@@ -223,6 +230,8 @@ def test_ssd_rejects_overlapping_buffers():
     assert call(ws=x + 1024) == 5         # workspace overlaps x
     assert call(ws=h0) == 5               # workspace is h0
     assert call(h0=fin + 256) == 5        # h0 partly overlaps the final state
+    assert call(y=seq) == 5               # y is the document ids
+    assert call(ws=seq + 64) == 5         # workspace overlaps the document ids
 
 
 def test_fwd_bwd_reject_overlapping_buffers():

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from _util import TOL, f64, rel_err, say
+from _util import TOL, f64, inputs, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -162,6 +162,90 @@ def test_mamba2_layer_shape_sampled_heads():
     y, fin = _run(q)
     heads = [0, 5, 11, 17, 23]
     yr, fr = _ref(q, heads=heads)
+    hi = torch.as_tensor(heads).cuda()
+    assert rel_err(f64(y.index_select(2, hi)), yr) <= TOL["bf16"]
+    assert rel_err(f64(fin.index_select(1, hi)), fr) <= TOL["bf16"]
+
+
+# --------------------------------------------------------------- documents
+# "niverel-mamba" README, "seq_idx strict reset": for Mamba-2 the SSM state
+# resets to zero at every document boundary; h0 feeds a row's first document.
+
+def _run_docs(q, seq, use=("D", "z", "dt_bias", "h0")):
+    ss = _ss()
+    g = {k: v.cuda() for k, v in q.items()}
+    y, fin = ss.ssd_fwd(g["x"], g["dt"], g["A"], g["Bm"], g["Cm"], D=g["D"] if "D" in use else None,
+                        z=g["z"] if "z" in use else None, dt_bias=g["dt_bias"] if "dt_bias" in use else None,
+                        h0=g["h0"] if "h0" in use else None, seq_idx=seq.cuda(), return_final_state=True)
+    torch.cuda.synchronize()
+    return y, fin
+
+
+def _ref_docs(q, seq, use=("D", "z", "dt_bias", "h0"), heads=None):
+    sel = (lambda a, ax: a) if heads is None else (lambda a, ax: a.index_select(ax, torch.as_tensor(heads)))
+    return oracle.ssd_fwd(f64(sel(q["x"], 2)), f64(sel(q["dt"], 2)), f64(sel(q["A"], 0)), f64(q["Bm"]), f64(q["Cm"]),
+                          D=f64(sel(q["D"], 0)) if "D" in use else None, z=f64(sel(q["z"], 2)) if "z" in use else None,
+                          dt_bias=f64(sel(q["dt_bias"], 0)) if "dt_bias" in use else None,
+                          h0=f64(sel(q["h0"], 1)) if "h0" in use else None, seq_idx=seq.numpy())
+
+
+@pytest.mark.parametrize("case", inputs.SEQ_CASES)
+def test_documents_nine_cases(case):
+    """The nine structural cases over three 256-step chunks (boundaries on chunk edges, inside
+    chunks, at step 1, consecutive), with the initial state, every operand, two groups."""
+    say("ssd documents case=%s" % case)
+    q = _data(2, 700, 4, 2, 64, "bf16", seed=40)
+    seq = inputs.make_seq_idx(case, 2, 700, seed=41)
+    y, fin = _run_docs(q, seq)
+    yr, fr = _ref_docs(q, seq)
+    ey, ef = rel_err(f64(y), yr), rel_err(f64(fin), fr)
+    say("  errors y=%.2e final=%.2e" % (ey, ef))
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("io,N", [("f16", 128), ("bf16", 32)])
+def test_documents_long_rows(io, N):
+    """L = 4096 (16 chunks) with documents of U[1, 700] steps, so most chunks hold a start and
+    some documents span several chunks."""
+    q = _data(2, 4096, 2, 1, N, io, seed=42)
+    seq = inputs.packed_documents(4096, 2, 700, seed=43)
+    say("ssd documents long rows io=%s N=%d" % (io, N))
+    y, fin = _run_docs(q, seq)
+    yr, fr = _ref_docs(q, seq)
+    assert rel_err(f64(y), yr) <= TOL[io] and rel_err(f64(fin), fr) <= TOL[io]
+
+
+def test_packed_row_equals_documents_on_device():
+    """A row of three documents (300, 1 and 451 steps) gives, step for step, what the three run
+    one by one give (h0 for the first only, zero for the others)."""
+    ss = _ss()
+    lens = [300, 1, 451]
+    L = sum(lens)
+    q = _data(1, L, 4, 2, 64, "bf16", seed=44)
+    seq = torch.tensor(sum([[k] * n for k, n in enumerate(lens)], []), dtype=torch.int32).reshape(1, L)
+    g = {k: v.cuda() for k, v in q.items()}
+    y, fin = ss.ssd_fwd(g["x"], g["dt"], g["A"], g["Bm"], g["Cm"], D=g["D"], z=g["z"], dt_bias=g["dt_bias"],
+                        h0=g["h0"], seq_idx=seq.cuda(), return_final_state=True)
+    parts, t = [], 0
+    for k, n in enumerate(lens):
+        s = lambda a: a[:, t:t + n].contiguous()
+        yk, fk = ss.ssd_fwd(s(g["x"]), s(g["dt"]), g["A"], s(g["Bm"]), s(g["Cm"]), D=g["D"], z=s(g["z"]),
+                            dt_bias=g["dt_bias"], h0=g["h0"] if k == 0 else None, return_final_state=True)
+        parts.append(yk)
+        t += n
+    torch.cuda.synchronize()
+    assert rel_err(f64(y), f64(torch.cat(parts, dim=1))) <= TOL["bf16"]
+    assert rel_err(f64(fin), f64(fk)) <= TOL["bf16"]
+
+
+def test_documents_mamba2_layer_shape_sampled_heads():
+    """The benchmarked layer (B=8, L=2048, 24 heads of 64, d_state 128, one group, bf16) packed
+    with documents of U[1, 512] steps and an initial state: five heads against the oracle."""
+    q = _data(8, 2048, 24, 1, 128, "bf16", seed=45)
+    seq = inputs.packed_documents(2048, 8, 512, seed=46)
+    y, fin = _run_docs(q, seq)
+    heads = [0, 7, 12, 18, 23]
+    yr, fr = _ref_docs(q, seq, heads=heads)
     hi = torch.as_tensor(heads).cuda()
     assert rel_err(f64(y.index_select(2, hi)), yr) <= TOL["bf16"]
     assert rel_err(f64(fin.index_select(1, hi)), fr) <= TOL["bf16"]
