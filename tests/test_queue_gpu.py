@@ -116,3 +116,41 @@ def test_config3_ragged_queue_every_channel():
     ey, el, _ = full_compare(prob, y, last)
     say("  y %.2e  last %.2e" % (ey, el))
     assert ey <= TOL["bf16"] and el <= TOL["bf16"]
+
+
+def test_queue_graph_replays_match_eager():
+    """The work queue (its clearing kernel and the persistent scan) captured in a HIP graph and
+    replayed three times, with eager work between the replays: every replay equals the eager
+    result bit for bit, so its counter and flags start cleared on each replay."""
+    ss = _ss()
+    L = 1100
+    prob = inputs.make_problem(3, 2048, 16, L, "bf16", seed=67)
+    lens = torch.tensor([1100, 5, 640], dtype=torch.int32, device="cuda")
+    g = to_dev(prob)
+    y_e = torch.empty_like(g["u"])
+    s_e = torch.empty((3, 2048, 16), dtype=torch.float32, device="cuda")
+    ss.FwdCall(g["u"], g["delta"], g["A"], g["Bm"], g["Cm"], D=g["D"], z=g["z"], delta_bias=g["bias"],
+               lengths=lens, y=y_e, last_state=s_e)()
+    torch.cuda.synchronize()
+    y = torch.empty_like(y_e)
+    s = torch.empty_like(s_e)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call = ss.FwdCall(g["u"], g["delta"], g["A"], g["Bm"], g["Cm"], D=g["D"], z=g["z"], delta_bias=g["bias"],
+                          lengths=lens, y=y, last_state=s, stream=side)
+        call()  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ss.FwdCall(g["u"], g["delta"], g["A"], g["Bm"], g["Cm"], D=g["D"], z=g["z"], delta_bias=g["bias"],
+                   lengths=lens, y=y, last_state=s, stream=torch.cuda.current_stream())()
+    for rep in range(3):
+        y.fill_(float("nan"))
+        junk = torch.randn(1 << 16, device="cuda").mul_(2.0).sum()  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        say("queue graph replay %d" % rep)
+        assert torch.equal(y, y_e) and torch.equal(s, s_e)
