@@ -96,6 +96,18 @@ def test_lengths_documents_and_h0():
     _check(prob, seq=seq, h0=h0)
 
 
+def test_empty_and_one_step_rows():
+    """Rows of length 0 (the output is exactly zero and the final state is h0) and 1 next to a
+    full row, on a plan whose rows end in different chunks and groups."""
+    Bsz, Dd, L = 4, 16, 5000
+    prob = inputs.make_problem(Bsz, Dd, 16, L, "f32", seed=311)
+    prob["lengths"] = torch.tensor([0, L, 1, 4097], dtype=torch.int32)
+    h0 = torch.from_numpy(np.random.default_rng(312).standard_normal((Bsz, Dd, 16))).float()
+    say("lookback empty rows plan=%s" % (plan(Bsz, Dd, L),))
+    y, last, _ = _check(prob, h0=h0)
+    assert torch.equal(last[0].cpu(), h0[0])
+
+
 def test_dstate_below_16_and_h0():
     prob = inputs.make_problem(2, 16, 7, 2500, "bf16", seed=305)
     h0 = torch.from_numpy(np.random.default_rng(306).standard_normal((2, 16, 7))).float()

@@ -203,6 +203,20 @@ def test_documents_nine_cases(case):
     assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("L", [1, 2, 255, 256, 257, 513])
+def test_documents_short_and_edge_lengths(L):
+    """Document ids on rows that end at, just before or just past a chunk edge (a document
+    starting at step 1 and at the chunk's last step included)."""
+    q = _data(2, L, 2, 1, 64, "bf16", seed=47)
+    ids = np.zeros((2, L), dtype=np.int32)
+    for b, cut in enumerate([1, max(1, L - 1)]):
+        ids[b, cut:] = 1
+    seq = torch.from_numpy(ids)
+    y, fin = _run_docs(q, seq)
+    yr, fr = _ref_docs(q, seq)
+    assert rel_err(f64(y), yr) <= TOL["bf16"] and rel_err(f64(fin), fr) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("io,N", [("f16", 128), ("bf16", 32)])
 def test_documents_long_rows(io, N):
     """L = 4096 (16 chunks) with documents of U[1, 700] steps, so most chunks hold a start and
