@@ -106,7 +106,13 @@ constexpr int kBCStride = kTile + 4;
 // per-step writes and the per-row reads free of bank conflicts); channels
 // 272 floats apart (16 banks).
 constexpr int kSChan = 16 * 16 + 16;
-// Sum-over-channels tiles: per wave [16 steps][16 states][4 channels].
+// Sum-over-channels tiles: per wave [16 steps][16 states][4 channels], the
+// channel slot of states 8..15 swapped in pairs (cw ^ 2).  LDS has 32 banks
+// and serves a 4-byte access a half-wave at a time; a half-wave is channels
+// {0, 1} (or {2, 3}) x 16 states, which without the swap would put states n
+// and n + 8 in the same banks (measured with the bank-conflict counter on a
+// one-wave probe).  The channel sum adds the slots as (0 + 1) + (2 + 3),
+// which the swap only reorders as a whole, so the sums are unchanged.
 constexpr int kCTile = 16 * 16 * kChPerWave;
 
 // AGG needs only the chunk's B and C; MAIN adds its reduction tiles.
@@ -316,8 +322,8 @@ __device__ __forceinline__ void bwd_block(float& g, float& dA_acc, const float (
         const float dy0b = row_bcast<jj>(o.dy0[I]);
         const float a = as[jj];               // decay of step s (0 at a document start)
         const float gh = fmaf(dy0b, cqj, g);  // dLoss/dh_t
-        t4w[(jj * 16 + n) * kChPerWave + cw] = dy0b * hs[jj + 1];
-        t3w[(jj * 16 + n) * kChPerWave + cw] = gh * row_bcast<jj>(dtu_f);
+        t4w[(jj * 16 + n) * kChPerWave + (cw ^ (2 * (n >> 3)))] = dy0b * hs[jj + 1];
+        t3w[(jj * 16 + n) * kChPerWave + (cw ^ (2 * (n >> 3)))] = gh * row_bcast<jj>(dtu_f);
         t1c[swz(jj, n)] = gh * bqj;
         g = gh * a;                                 // to h_{t-1}
         const float q = g * hs[jj];                 // gh * a * h_{t-1}

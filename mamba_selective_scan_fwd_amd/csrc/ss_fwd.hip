@@ -60,8 +60,16 @@ constexpr uint32_t kTileNone = 0x7fff0000u;
 
 constexpr int kBCStride = kTile + 4;     // padded LDS row of the B tile (floats)
 constexpr int kCTRow = 20;               // padded LDS row of the transposed C tile
-constexpr int kPRow = 20;                // padded LDS row of the state tile (16 states + 4)
-constexpr int kPChan = 16 * kPRow + 16;  // per-channel state tile; 336 = 16 mod 64 banks
+// The state tile of a channel: 16 steps x 16 states, element (j, n) at
+// j*16 + 4*((n>>2) ^ ((j>>2)&3)) + (n&3), channels 272 floats apart.  LDS has
+// 32 banks and serves a 4-byte write a half-wave (two channels) at a time:
+// 272 = 16 (mod 32) keeps the two channels of a step's write in different
+// banks; the XOR swizzle lets the row reads (lane l reads step l's 16 states
+// as 4 x 16 bytes, group k from position k ^ ((l>>2)&3), so the groups come
+// back in order) run without conflicts too, which a padded row of 20 cannot
+// give together with conflict-free writes (both checked with the
+// bank-conflict counter on a one-wave probe).
+constexpr int kPChan = 16 * 16 + 16;
 
 // FINAL keeps C and the state tiles for the readout; the chunk-summary pass
 // only needs B.
@@ -223,8 +231,9 @@ __device__ __forceinline__ void prep_owned(Owned& o, const RawOwned<IO>& r, int 
 // block's 16 B values are read into registers up front, so no LDS wait sits
 // between two steps of the recurrence.
 template <int I, bool FINAL, bool RESET, int... J>
-__device__ __forceinline__ void scan_block(float& h, const Owned& o, float A2, const float* sBrow, float* pcol,
-                                           uint64_t starts, std::integer_sequence<int, J...>) {
+__device__ __forceinline__ void scan_block(float& h, const Owned& o, float A2, const float* sBrow,
+                                           float* const (&pcol)[4], uint64_t starts,
+                                           std::integer_sequence<int, J...>) {
   float bq[16];
   *reinterpret_cast<float4*>(&bq[0]) = *reinterpret_cast<const float4*>(sBrow + 16 * I + 0);
   *reinterpret_cast<float4*>(&bq[4]) = *reinterpret_cast<const float4*>(sBrow + 16 * I + 4);
@@ -234,7 +243,7 @@ __device__ __forceinline__ void scan_block(float& h, const Owned& o, float A2, c
       [&] {
         const float a = reset_decay<RESET, 16 * I + J>(exp2_hw(row_bcast<J>(o.dt[I]) * A2), starts);
         h = fmaf(a, h, row_bcast<J>(o.dtu[I]) * bq[J]);
-        if constexpr (FINAL) pcol[J * kPRow] = h;
+        if constexpr (FINAL) pcol[J >> 2][J * 16] = h;  // element (J, n) of the swizzled tile
       }(),
       ...);
   h = fresh(h);
@@ -266,12 +275,12 @@ __device__ __forceinline__ CRow load_crow(const float* crow) {
 // y = sum_n C[t][n] h_t[n] + D u in two FMA chains (the skip starts the first).
 // ybase is the byte offset of the lane's step 0 of the tile in its y row.
 template <int IO, int I, int FL, bool FULL>
-__device__ __forceinline__ void finish_block(const Owned& o, const float* prow, const CRow& c, float Dd,
+__device__ __forceinline__ void finish_block(const Owned& o, const float* const (&prow)[4], const CRow& c, float Dd,
                                              const Views& v, uint32_t ybase, int l, int nvalid, int nstop) {
-  const float4 h0 = *reinterpret_cast<const float4*>(prow + 0);
-  const float4 h1 = *reinterpret_cast<const float4*>(prow + 4);
-  const float4 h2 = *reinterpret_cast<const float4*>(prow + 8);
-  const float4 h3 = *reinterpret_cast<const float4*>(prow + 12);
+  const float4 h0 = *reinterpret_cast<const float4*>(prow[0]);  // states 0..3 of step l
+  const float4 h1 = *reinterpret_cast<const float4*>(prow[1]);
+  const float4 h2 = *reinterpret_cast<const float4*>(prow[2]);
+  const float4 h3 = *reinterpret_cast<const float4*>(prow[3]);
   float ya = fmaf(c.c0.x, h0.x, Dd * o.u[I]);
   float yb = c.c0.y * h0.y;
   ya = fmaf(c.c0.z, h0.z, ya); yb = fmaf(c.c0.w, h0.w, yb);
@@ -360,9 +369,18 @@ __device__ __forceinline__ void scan_chunk(const FwdParams& p, FwdSmem<FINAL>& s
       make_rsrc(SEQ ? static_cast<const void*>(p.seq_idx + b * p.seqlen) : p.u, SEQ ? (uint32_t)L * 4u : 0u);
   uint32_t id_t = 0, id_prev = 0;
 
-  float* pwave = state_tile<FINAL>(sm, wave) + cw * kPChan;
-  float* pcol = pwave + n;                // column n of this channel's state tile
-  const float* prow = pwave + l * kPRow;  // row l (step l of the block)
+  // this lane's places in its channel's state tile: column n at rows of each
+  // swizzle group (writes), the 4 state groups of row l (reads)
+  float* pcol[4] = {};
+  const float* prow[4] = {};
+  if constexpr (FINAL) {
+    float* const pwave = state_tile<FINAL>(sm, wave) + cw * kPChan;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      pcol[c] = pwave + 4 * ((n >> 2) ^ c) + (n & 3);
+      prow[c] = pwave + l * 16 + 4 * (c ^ ((l >> 2) & 3));
+    }
+  }
 
   RawOwned<IO> raw;
   BCRaw<IO, PAIR> bcr;
