@@ -91,7 +91,7 @@ typedef struct ss_problem {
  * groups of consecutive chunks.  Any other problem (batch <= 256) can
  * use a work queue, which ss_fwd takes for ragged rows (`lengths` given) and
  * for more 16-channel row blocks than the GPU holds at once when they do not
- * fill it evenly: units of 512 steps of a 16-channel block, handed out
+ * fill it evenly: units of 2048 steps of a 16-channel block, handed out
  * longest row first, each continuing from the state its block reached at the
  * end of the previous unit; its workspace holds a control block, a flag per
  * unit and that state per (channel, unit).  Returns 0 for an invalid problem.

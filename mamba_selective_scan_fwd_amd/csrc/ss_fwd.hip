@@ -1,4 +1,4 @@
-// ss_fwd.hip -- selective-scan forward, decode step and chunk-carry kernels (gfx950).
+// ss_fwd.hip -- selective-scan forward: whole-row, time-chunked (look-back) and work-queue scans, decode step (gfx950).
 //
 // The recurrence (page "Mamba", Part IV Stages 4-6): per channel (b, d) and
 // state n,  h_t[n] = exp(Delta_t A[d,n]) h_{t-1}[n] + Delta_t B[b,n,t] u_t,

@@ -55,9 +55,9 @@ def test_sizes():
     p = _prob(batch=8, dim=1536, seqlen=2048)
     assert lib.ss_ckpt_count(ctypes.byref(p)) == 8 * 1536 * 32 * 16
     assert lib.ss_fwd_workspace_min(ctypes.byref(p)) == 0    # enough channels: no time split
-    # the optional work queue: control block, a flag per (row block, 512-step unit), a state per
+    # the optional work queue: control block, a flag per (row block, 2048-step unit), a state per
     # (channel, unit)
-    q = 256 + ((8 * 96 * 4 * 4 + 255) // 256) * 256 + 8 * 1536 * 4 * 16 * 4
+    q = 256 + ((8 * 96 * 1 * 4 + 255) // 256) * 256 + 8 * 1536 * 1 * 16 * 4
     assert lib.ss_fwd_workspace_size(ctypes.byref(p)) == q
     p1 = _prob(batch=1, dim=16, seqlen=32768)
     assert lib.ss_fwd_workspace_min(ctypes.byref(p1)) > 0    # few channels: time-chunked

@@ -1,7 +1,7 @@
 """The forward's work queue against the float64 oracle.
 
 ss_fwd takes the queue for ragged rows and for more 16-channel row blocks than the GPU holds
-at once when they do not fill it evenly: units of 512 steps of a row block, handed out longest
+at once when they do not fill it evenly: units of 2048 steps of a row block, handed out longest
 row first, each continuing from the state the previous unit of its row block published.  These
 problems are large enough not to split time (4 x 1024 channels, 5 x 2560), so every one runs
 the queue; y, the final state and the per-64-step checkpoints are compared over the whole
@@ -61,21 +61,21 @@ def _check(prob, y, last, ck, lens=None, seq=None, h0=None, tol=None):
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_queue_ragged_rows(io):
-    """Rows of length 0, 1, 513 (a unit and one step) and the whole row."""
-    L = 1000
+    """Rows of length 0, 1, 2049 (a unit and one step) and the whole row (three units)."""
+    L = 4200
     prob = inputs.make_problem(4, 1024, 16, L, io, seed=61)
-    lens = np.array([0, 1, 513, L])
+    lens = np.array([0, 1, 2049, L])
     say("queue ragged %s lengths %s" % (io, lens.tolist()))
     y, last, ck = _run(prob, lengths=torch.tensor(lens, dtype=torch.int32, device="cuda"))
     _check(prob, y, last, ck, lens=lens)
 
 
 def test_queue_ragged_documents_and_initial_state():
-    """Ragged rows with packed documents and an initial state: the unit boundaries (512 steps)
+    """Ragged rows with packed documents and an initial state: the unit boundaries (2048 steps)
     cut documents, and the state a unit continues from must carry the resets and h0."""
-    L = 1500
+    L = 4600
     prob = inputs.make_problem(4, 1024, 16, L, "f32", seed=62)
-    lens = np.array([1300, 511, 1500, 1024])
+    lens = np.array([4100, 2047, 4600, 2048])
     seq = inputs.packed_documents(L, 4, 300, seed=63).to("cuda")
     h0 = torch.randn((4, 1024, 16), dtype=torch.float32, device="cuda")
     say("queue ragged + documents + h0, lengths %s" % lens.tolist())
@@ -86,8 +86,8 @@ def test_queue_ragged_documents_and_initial_state():
 def test_queue_uneven_row_blocks():
     """No lengths, but 5 x 160 = 800 row blocks: more than 3 per CU and not a multiple of the
     slots, so the queue balances them."""
-    prob = inputs.make_problem(5, 2560, 16, 700, "f16", seed=64)
-    say("queue uneven 5 x 2560, L=700, f16")
+    prob = inputs.make_problem(5, 2560, 16, 2100, "f16", seed=64)
+    say("queue uneven 5 x 2560, L=2100, f16")
     y, last, ck = _run(prob)
     _check(prob, y, last, ck)
 
@@ -96,9 +96,9 @@ def test_queue_matches_the_direct_scan_bit_for_bit():
     """The queue changes only the schedule: with a workspace too small for it the same problem
     runs one workgroup per row block, and every output is bit-identical."""
     ss = _ss()
-    L = 1200
+    L = 4400
     prob = inputs.make_problem(4, 1024, 16, L, "bf16", seed=65)
-    lens = torch.tensor([700, 1200, 3, 1100], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([2500, 4400, 3, 4100], dtype=torch.int32, device="cuda")
     g = to_dev(prob)
     yq, lq, cq = _run(prob, lengths=lens)
     yd, ld, cd = ss.fwd(g["u"], g["delta"], g["A"], g["Bm"], g["Cm"], D=g["D"], z=g["z"], delta_bias=g["bias"],
@@ -123,9 +123,9 @@ def test_queue_graph_replays_match_eager():
     replayed three times, with eager work between the replays: every replay equals the eager
     result bit for bit, so its counter and flags start cleared on each replay."""
     ss = _ss()
-    L = 1100
+    L = 2600
     prob = inputs.make_problem(3, 2048, 16, L, "bf16", seed=67)
-    lens = torch.tensor([1100, 5, 640], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([2600, 5, 2100], dtype=torch.int32, device="cuda")
     g = to_dev(prob)
     y_e = torch.empty_like(g["u"])
     s_e = torch.empty((3, 2048, 16), dtype=torch.float32, device="cuda")
