@@ -309,9 +309,16 @@ __device__ __forceinline__ void finish_block(const Owned& o, const float* const 
 // of the chunk (exact zeros past the row's length) and the checkpoints that
 // fall in the chunk, including those past the row's length through
 // ckpt_stop.  RANK: the waves lower their arbitration rank as they progress.
-template <int IO, bool FINAL, bool PAIR, bool SEQ, int FL, bool RANK>
+// The entry state is ready on the call (no hook), or a hook sets it once the
+// chunk's first loads are in flight, so that their latency overlaps its waits
+// for other workgroups.
+struct EntryReady {
+  __device__ void operator()(float&) const {}
+};
+template <int IO, bool FINAL, bool PAIR, bool SEQ, int FL, bool RANK, typename Entry = EntryReady>
 __device__ __forceinline__ void scan_chunk(const FwdParams& p, FwdSmem<FINAL>& sm, int64_t b, int64_t cb,
-                                           int64_t chunk, int ckpt_stop, float& h, float& dt_sum, bool& any_start) {
+                                           int64_t chunk, int ckpt_stop, float& h, float& dt_sum, bool& any_start,
+                                           const Entry& entry = Entry{}) {
   constexpr uint32_t s = io_bytes<IO>();
   const int tid = threadIdx.x;
   const int wave = uniform(tid / 64);
@@ -388,8 +395,9 @@ __device__ __forceinline__ void scan_chunk(const FwdParams& p, FwdSmem<FINAL>& s
     if constexpr (SEQ) load_doc_ids(ids, t_begin + lane, id_t, id_prev);
     load_owned<IO, GATE>(raw, v, lane_off, (uint32_t)t_begin * s);
     load_bc<IO, PAIR>(bcr, v, bc_off, (uint32_t)t_begin * s, FINAL);
-    store_bc<IO, PAIR, FINAL>(sm, 0, bcr, tid, t_valid_end - t_begin, stage_n_ok);
   }
+  entry(h);  // every thread calls it
+  if (t_begin < t_tile_end) store_bc<IO, PAIR, FINAL>(sm, 0, bcr, tid, t_valid_end - t_begin, stage_n_ok);
   __syncthreads();
   int buf = 0;
   for (int t0 = t_begin; t0 < t_tile_end; t0 += kTile) {
@@ -580,20 +588,24 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_queue_kernel(FwdParams p) {
         for (int t = t_begin + l; t < t_stop; t += 16) store_io<IO>(p.y, ch * p.seqlen + t, 0.0f);
       continue;
     }
-    float h = 0.0f;
-    if (k == 0) {
-      if (p.h0 && ch_ok && n_ok) h = p.h0[ch * p.dstate + n];
-    } else {
-      if (tid == 0) wait_published(p.q_flags + (b * cbs + cb) * K + (k - 1), p.q_ctrl + 1);
-      __syncthreads();
-      if (ch_ok)
-        h = __hip_atomic_load(p.q_carry + (ch * K + (k - 1)) * kStates + n, __ATOMIC_RELAXED,
-                              __HIP_MEMORY_SCOPE_AGENT);
-    }
-    float dt_sum = 0.0f;
+    // the state the previous unit of this row block reached (waited for once
+    // this unit's first loads are issued)
+    auto entry = [&](float& h) {
+      h = 0.0f;
+      if (k == 0) {
+        if (p.h0 && ch_ok && n_ok) h = p.h0[ch * p.dstate + n];
+      } else {
+        if (tid == 0) wait_published(p.q_flags + (b * cbs + cb) * K + (k - 1), p.q_ctrl + 1);
+        __syncthreads();
+        if (ch_ok)
+          h = __hip_atomic_load(p.q_carry + (ch * K + (k - 1)) * kStates + n, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+      }
+    };
+    float h = 0.0f, dt_sum = 0.0f;
     bool any_start = false;
     // the row's last valid chunk also writes the checkpoints past its end
-    scan_chunk<IO, true, PAIR, SEQ, FL, false>(p, sm, b, cb, k, k == kv ? L : t_stop, h, dt_sum, any_start);
+    scan_chunk<IO, true, PAIR, SEQ, FL, false>(p, sm, b, cb, k, k == kv ? L : t_stop, h, dt_sum, any_start, entry);
     if (k < kv) {
       if (ch_ok) __hip_atomic_store(p.q_carry + (ch * K + k) * kStates + n, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __builtin_amdgcn_s_waitcnt(0);  // the state has reached the coherent level
@@ -710,25 +722,28 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_lookback_kernel(FwdParams p) 
     __syncthreads();  // the shared tiles are free for the readout
   }
 
-  // 2. the map from the group's entry to this chunk's entry: the pairs of the
-  // group's chunks before this one
-  float Pe = 1.0f, Se = 0.0f;
-  if (i > 0) compose_published(pairs + g * G * kStates, kStates, (int)i, ch_ok, p.q_ctrl + 1, Pe, Se);
+  // 2-4 run inside the readout's start, once its first loads are in flight
+  auto entry = [&](float& h) {
+    // 2. the map from the group's entry to this chunk's entry: the pairs of
+    // the group's chunks before this one
+    float Pe = 1.0f, Se = 0.0f;
+    if (i > 0) compose_published(pairs + g * G * kStates, kStates, (int)i, ch_ok, p.q_ctrl + 1, Pe, Se);
 
-  // 3. the last chunk of a group that has a successor publishes the group's
-  // pair (so the last group never does: ngroups - 1 group pairs)
-  if (i == G - 1 && c < K - 1) publish_pair(gpairs + g * kStates, ch_ok, P * Pe, fmaf(P, Se, S));
+    // 3. the last chunk of a group that has a successor publishes the
+    // group's pair (so the last group never does: ngroups - 1 group pairs)
+    if (i == G - 1 && c < K - 1) publish_pair(gpairs + g * kStates, ch_ok, P * Pe, fmaf(P, Se, S));
 
-  // 4. the state entering the group: the pairs of the groups before it,
-  // applied to zero (the first chunk's pair holds the initial state)
-  float Pg = 1.0f, H = 0.0f;
-  if (g > 0) compose_published(gpairs, kStates, (int)g, ch_ok, p.q_ctrl + 1, Pg, H);
+    // 4. the state entering the group: the pairs of the groups before it,
+    // applied to zero (the first chunk's pair holds the initial state)
+    float Pg = 1.0f, H = 0.0f;
+    if (g > 0) compose_published(gpairs, kStates, (int)g, ch_ok, p.q_ctrl + 1, Pg, H);
+    h = c == 0 ? h_init : fmaf(Pe, H, Se);
+  };
 
   // 5. rerun the chunk from its entry state and write y
-  float h = c == 0 ? h_init : fmaf(Pe, H, Se);
-  float dt_sum = 0.0f;
+  float h = 0.0f, dt_sum = 0.0f;
   bool any_start = false;
-  scan_chunk<IO, true, PAIR, SEQ, FL, false>(p, sm, b, cb, c, t_stop, h, dt_sum, any_start);
+  scan_chunk<IO, true, PAIR, SEQ, FL, false>(p, sm, b, cb, c, t_stop, h, dt_sum, any_start, entry);
   if (p.last_state && ch_ok && n_ok && c == K - 1) p.last_state[ch * p.dstate + n] = h;
 }
 
