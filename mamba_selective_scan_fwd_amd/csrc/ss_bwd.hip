@@ -603,7 +603,9 @@ __global__ void __launch_bounds__(kThreads, MAIN ? 2 : 7) ss_bwd_chunk_kernel(Bw
       __syncthreads();
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int idx = tid + kThreads * r;  // (step, state) pair
+        // (step, state) pair; the opaque copy keeps the compiler from holding
+        // these addresses in registers (spilled) through the whole walk
+        const int idx = opaque(tid) + kThreads * r;
         const int st = idx / kStates, sn = idx % kStates;
         float vb = 0.0f, vc = 0.0f;
 #pragma unroll

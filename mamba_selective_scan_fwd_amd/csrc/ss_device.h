@@ -145,6 +145,14 @@ __device__ __forceinline__ float fresh(float v) {
   asm volatile("" : "+v"(v));
   return v;
 }
+// The same for a per-lane integer: addresses computed from it are rebuilt
+// where they are used instead of being kept live (or spilled) from an
+// earlier computation.
+template <typename T>
+__device__ __forceinline__ T opaque(T v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
 // ---- cross-lane moves inside a 16-lane DPP row ------------------------------
 // value of lane J of this lane's row (DPP row_newbcast; folds into the VALU
