@@ -225,24 +225,28 @@ __device__ __forceinline__ void prep(BwdOwned& o, const BwdRaw<IO>& r, int64_t t
   }
 }
 
-// ---- AGG: reverse walk of one chunk with a zero carry ------------------------
+// ---- AGG: one chunk's gradient with a zero carry --------------------------------
+// The reverse recurrence g_{t-1} = a_t (g_t + dy0_t C_t[n]) run from g = 0
+// over the chunk, unrolled: the gradient reaching the chunk's entry is
+// sum_t P_t dy0_t C_t[n], P_t = prod_{s <= t} a_s = exp2(A log2(e) cs_t), cs_t
+// the chunk's running sum of Delta through step t (P_t = 0 from the chunk's
+// first document start on).  The terms are independent of one another, so
+// each step takes one FMA into the sum and nothing waits on the step before.
 template <int I, bool RESET, int... J>
-__device__ __forceinline__ void agg_block(float& g, const BwdOwned& o, float A2, const float* sCrow, uint64_t starts,
-                                          std::integer_sequence<int, J...>) {
-  // J runs 0..15; step s = 16 I + (15 - J) goes backwards
+__device__ __forceinline__ void agg_block(float& G, const BwdOwned& o, float cs, float A2, const float* sCrow,
+                                          int first, std::integer_sequence<int, J...>) {
   float4 c4;
   (
       [&] {
-        constexpr int jj = 15 - J;
-        constexpr int s = 16 * I + jj;
-        if constexpr (jj % 4 == 3) c4 = *reinterpret_cast<const float4*>(sCrow + s - 3);
-        const float cj = (jj % 4 == 0) ? c4.x : (jj % 4 == 1) ? c4.y : (jj % 4 == 2) ? c4.z : c4.w;
-        const float a = reset_decay<RESET, s>(exp2_hw(row_bcast<jj>(o.dt[I]) * A2), starts);
-        const float G = fmaf(row_bcast<jj>(o.dy0[I]), cj, g);
-        g = G * a;
+        constexpr int s = 16 * I + J;
+        if constexpr (J % 4 == 0) c4 = *reinterpret_cast<const float4*>(sCrow + s);
+        const float cj = (J % 4 == 0) ? c4.x : (J % 4 == 1) ? c4.y : (J % 4 == 2) ? c4.z : c4.w;
+        float P = exp2_hw(row_bcast<J>(cs) * A2);
+        if constexpr (RESET) P = s >= first ? 0.0f : P;
+        G = fmaf(P, row_bcast<J>(o.dy0[I]) * cj, G);
       }(),
       ...);
-  g = fresh(g);
+  G = fresh(G);
   __builtin_amdgcn_sched_barrier(0);  // no hoisting across blocks (registers)
 }
 
@@ -485,20 +489,31 @@ __global__ void __launch_bounds__(kThreads, MAIN ? 2 : 7) ss_bwd_chunk_kernel(Bw
       // chunks in which no document starts take the copy without the resets
       const bool reset = SEQ && starts != 0;
       if constexpr (!MAIN) {
-        float g = g_last;
+        // running sums of Delta at the lane's owned steps 16 i + l
+        float cs[4], run = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float r = row_scan(o.dt[i]);
+          cs[i] = run + r;
+          run += row_bcast<15>(r);  // the block's total
+        }
+        const int first = starts != 0 ? (int)__builtin_ctzll(starts) : kTile;  // uniform
+        float G = 0.0f;
         auto walk = [&](auto reset_tag) {
           constexpr bool R = decltype(reset_tag)::value;
-          agg_block<3, R>(g, o, A2, sCrow, starts, seq);
-          agg_block<2, R>(g, o, A2, sCrow, starts, seq);
-          agg_block<1, R>(g, o, A2, sCrow, starts, seq);
-          agg_block<0, R>(g, o, A2, sCrow, starts, seq);
+          agg_block<0, R>(G, o, cs[0], A2, sCrow, first, seq);
+          agg_block<1, R>(G, o, cs[1], A2, sCrow, first, seq);
+          agg_block<2, R>(G, o, cs[2], A2, sCrow, first, seq);
+          agg_block<3, R>(G, o, cs[3], A2, sCrow, first, seq);
         };
         if (reset) walk(std::bool_constant<SEQ>{});
         else walk(std::false_type{});
-        const float dsum = row_sum((o.dt[0] + o.dt[1]) + (o.dt[2] + o.dt[3]));
+        // the whole chunk's decay, which also carries the caller's gradient of
+        // the final state (last chunk) to the chunk's entry
+        const float P = starts != 0 ? 0.0f : exp2_hw(A2 * run);
         if (ch_ok) {
-          p.aggP[wslot] = starts != 0 ? 0.0f : exp2_hw(A2 * dsum);
-          p.aggG[wslot] = g;
+          p.aggP[wslot] = P;
+          p.aggG[wslot] = fmaf(P, g_last, G);
         }
       } else {
         float* t1c = sm.T1[wave] + cw * kSChan;  // this channel's sum-over-states tiles

@@ -166,6 +166,20 @@ template <int K>
 __device__ __forceinline__ float row_ror(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + K, 0xf, 0xf, false));
 }
+// value of lane l - K of this lane's row, 0 for the first K lanes (DPP row_shr
+// with bound_ctrl)
+template <int K>
+__device__ __forceinline__ float row_shr(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 + K, 0xf, 0xf, true));
+}
+// inclusive running sum over the lanes 0..l of this lane's row
+__device__ __forceinline__ float row_scan(float v) {
+  v += row_shr<1>(v);
+  v += row_shr<2>(v);
+  v += row_shr<4>(v);
+  v += row_shr<8>(v);
+  return v;
+}
 // sum over the 16 lanes of a row, result in every lane of the row
 __device__ __forceinline__ float row_sum(float v) {
   v += row_ror<8>(v);
