@@ -18,9 +18,9 @@
 //                     chunks in order: S_c on MFMA (K = Q) added into the
 //                     decayed state held in the accumulators, each chunk's
 //                     entry state written in the I/O dtype, the final state
-//                     in fp32; the workgroups of a group also share out its
-//                     C B^T (summed in fp32, kept as bf16; once per group
-//                     rather than per head);
+//                     in fp32; after the walk the workgroups of a group
+//                     share out its C B^T (summed in fp32, kept as bf16;
+//                     once per group rather than per head);
 //   ssd_scan_kernel   per (batch, chunk, head): Y_off = C H_in on MFMA, then
 //                     per 64-step piece of the chunk's columns M = the decay-
 //                     masked, Delta-scaled C B^T built in registers and
@@ -243,10 +243,9 @@ struct CbTile {
 // The j-sum runs on the matrix cores: x * w and B are copied to LDS as
 // time-major rows and read back as operand fragments with the transposing LDS
 // read; wave w holds rows p in [16w, 16w + 16).  The next chunk's x, B and dt
-// are loaded once this chunk's are in LDS, while it is being multiplied.  The
-// waves of a group's workgroups (heads x slices x 4) also share out its C B^T
-// tiles, one per wave and chunk while there are waves enough; the first
-// tile's operands are loaded at the top of the chunk's iteration.
+// are loaded once this chunk's are in LDS, while it is being multiplied.  After
+// the walk the waves of a group's workgroups (heads x slices x 4) share out
+// the C B^T tiles of every chunk of the row.
 constexpr int kNS = 32;  // states per slice
 template <int IO, int N, bool SEQ>
 __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) {
@@ -309,8 +308,6 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
   load_chunk(0);
   for (int64_t c = 0; c < p.nchunks; ++c) {
     const int64_t t0 = c * kQ;
-    CbTile<IO, N> cbt;
-    if (cb_slot < kCbTiles) cbt.load(p, b, c, g, cb_slot, lane);
     {  // Delta of step tid (0 past the sequence)
       float d = 0.0f;
       if (t0 + tid < p.seqlen) {
@@ -386,12 +383,24 @@ __global__ void __launch_bounds__(kSsdThreads, 3) ssd_state_kernel(SsdParams p) 
         acc[nt] = M::run(as_vec<IO>(a), as_vec<IO>(bb), acc[nt]);
       }
     }
-    if (cb_slot < kCbTiles) cbt.finish(p, b, c, g, lane);
-    for (int idx = cb_slot + cb_slots; idx < kCbTiles; idx += cb_slots) {  // few waves per group: the rest in turn
-      cbt.load(p, b, c, g, idx, lane);
-      cbt.finish(p, b, c, g, lane);
-    }
     __syncthreads();
+  }
+  // C B^T of every chunk, shared out over the waves of the group's
+  // workgroups after the walk (so that its operands hold no registers through
+  // it), each tile's operands loaded while the previous tile is multiplied
+  {
+    const int64_t total = p.nchunks * kCbTiles;
+    int64_t item = cb_slot;
+    CbTile<IO, N> cur;
+    if (item < total) cur.load(p, b, item / kCbTiles, g, (int)(item % kCbTiles), lane);
+    while (item < total) {
+      const int64_t nxt = item + cb_slots;
+      CbTile<IO, N> nx;
+      if (nxt < total) nx.load(p, b, nxt / kCbTiles, g, (int)(nxt % kCbTiles), lane);
+      cur.finish(p, b, item / kCbTiles, g, lane);
+      cur = nx;
+      item = nxt;
+    }
   }
   if (p.final_state) {
 #pragma unroll
