@@ -274,7 +274,9 @@ template <int IO, int W>
 __global__ void __launch_bounds__(256) ss_conv1d_step_kernel(ConvStepParams p) {
   const int64_t ch = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (ch >= p.batch * p.dim) return;
-  const int64_t d = ch % p.dim;
+  // batch * dim < 2^31 (the host bounds the grid): a 32-bit remainder, off the
+  // 64-bit division's longer path to the weight loads
+  const int64_t d = (int64_t)((uint32_t)ch % (uint32_t)p.dim);
   float win[W];
 #pragma unroll
   for (int k = 0; k < W - 1; ++k) win[k] = p.window_in[ch * (W - 1) + k];

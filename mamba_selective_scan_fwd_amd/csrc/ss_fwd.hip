@@ -761,10 +761,13 @@ template <int IO>
 __global__ void __launch_bounds__(kThreads) ss_step_kernel(StepParams p) {
   const int tid = threadIdx.x;
   const int n = tid % 16;
-  const int64_t ch = (int64_t)blockIdx.x * kChPerBlock + tid / 16;
-  const bool ok = ch < p.batch * p.dim;
-  const int64_t b = ok ? ch / p.dim : 0;
-  const int64_t d = ok ? ch % p.dim : 0;
+  // the host keeps batch * dim below 2^26, so every index here fits 32 bits
+  // (a 64-bit division here sits on the step's critical path)
+  const uint32_t dim = (uint32_t)p.dim;
+  const uint32_t ch = blockIdx.x * (uint32_t)kChPerBlock + (uint32_t)tid / 16u;
+  const bool ok = ch < (uint32_t)(p.batch * p.dim);
+  const uint32_t b = ok ? ch / dim : 0u;
+  const uint32_t d = ok ? ch - b * dim : 0u;
   const bool n_ok = n < p.dstate;
 
   const float u = ok ? load_io<IO>(p.u, ch) : 0.0f;
