@@ -491,8 +491,9 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_chunk_kernel(FwdParams p) {
   // fastest: the blocks that share one batch row's B and C tiles run on one
   // XCD, so each row's B and C come from HBM about once.
   const uint32_t lb = xcd_logical_block();
-  const int64_t cb = lb % p.ch_blocks;
-  const int64_t b = lb / p.ch_blocks;
+  const uint32_t ncb = (uint32_t)p.ch_blocks;
+  const int64_t b = lb / ncb;
+  const int64_t cb = lb - (uint32_t)b * ncb;
   const int64_t dd = cb * kChPerBlock + d;
   const bool ch_ok = dd < p.dim, n_ok = n < p.dstate;
   const int64_t ch = b * p.dim + dd;
@@ -692,14 +693,20 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_lookback_kernel(FwdParams p) 
   __shared__ FwdSmem<true> sm;
   const int tid = threadIdx.x;
   const int n = tid % 16;
-  const int64_t nrb = p.batch * p.ch_blocks;  // (batch row, channel block) pairs
-  const int64_t K = p.nchunks, G = p.group, NG = p.ngroups;
-  const int64_t c = blockIdx.x / nrb, rb = blockIdx.x % nrb;
-  const int64_t b = rb / p.ch_blocks, cb = rb % p.ch_blocks;
+  // the launch has fewer than 2^23 workgroups: 32-bit index arithmetic (a
+  // 64-bit division here delays the first loads by a few hundred cycles, on
+  // a path that waits for other workgroups twice)
+  const uint32_t nrb = (uint32_t)(p.batch * p.ch_blocks);  // (batch row, channel block) pairs
+  const uint32_t ncb = (uint32_t)p.ch_blocks;
+  const int64_t K = p.nchunks, NG = p.ngroups;
+  const uint32_t G = (uint32_t)p.group;
+  const uint32_t c32 = blockIdx.x / nrb, rb = blockIdx.x - c32 * nrb;
+  const int64_t c = c32;
+  const int64_t b = rb / ncb, cb = rb - (uint32_t)b * ncb;
   const int64_t d = ss_lane_channel(tid, cb * kChPerBlock);
   const bool ch_ok = d < p.dim, n_ok = n < p.dstate;
   const int64_t ch = b * p.dim + d;
-  const int64_t g = c / G, i = c % G;
+  const int64_t g = c32 / G, i = c32 - (uint32_t)g * G;
   const int L = (int)p.seqlen;
   const int t_stop = (int)((c + 1) * p.chunk_len) < L ? (int)((c + 1) * p.chunk_len) : L;
   const float h_init = (c == 0 && p.h0 && ch_ok && n_ok) ? p.h0[ch * p.dstate + n] : 0.0f;
