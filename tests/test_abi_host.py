@@ -81,6 +81,18 @@ def test_bwd_rejects_grids_beyond_the_dispatch_limit():
     for ok in (_prob(batch=4, dim=1536, seqlen=4097), _prob(batch=1 << 12, dim=1 << 12, seqlen=64)):
         assert lib.ss_bwd_workspace_size(ctypes.byref(ok)) > 0
 
+def test_channel_limit_is_exact():
+    """batch * dim is bounded at 2^26 - 8 (one workgroup per 16 channels, twice over, within
+    2^23 - 1 workgroups): the last accepted and the first rejected count, in both factors; the
+    decode step's 32-bit channel indices rely on it."""
+    lib = ss.load_library()
+    lim = (1 << 26) - 8
+    assert lib.ss_ckpt_count(ctypes.byref(_prob(batch=1, dim=lim, seqlen=1))) == lim * 16
+    assert lib.ss_ckpt_count(ctypes.byref(_prob(batch=lim // 8, dim=8, seqlen=1))) == lim * 16
+    assert lib.ss_ckpt_count(ctypes.byref(_prob(batch=1, dim=lim + 1, seqlen=1))) == 0
+    assert lib.ss_ckpt_count(ctypes.byref(_prob(batch=(lim + 8) // 8, dim=8, seqlen=1))) == 0
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), 2), (dict(dim=-1), 2), (dict(seqlen=0), 2), (dict(seqlen=(1 << 24) + 1), 2),
     (dict(dstate=0), 2), (dict(dstate=17), 5), (dict(io_dtype=3), 3)])
