@@ -431,9 +431,10 @@ __global__ void __launch_bounds__(kThreads, MAIN ? 2 : 7) ss_bwd_chunk_kernel(Bw
         const int e = j + 16 * q;
         const bool ok = sn < p.dstate && t0 + e < t_end;
         const uint32_t off = ((uint32_t)sn * L + (uint32_t)(t0 + e)) * s;
-        const float bv = bits_f32<IO>(bload<IO>(rB, off));
+        // AGG reads only C
+        const float bv = MAIN ? bits_f32<IO>(bload<IO>(rB, off)) : 0.0f;
         const float cv = bits_f32<IO>(bload<IO>(rC, off));
-        sm.B[sn][e] = ok ? bv : 0.0f;
+        if constexpr (MAIN) sm.B[sn][e] = ok ? bv : 0.0f;
         sm.C[sn][e] = ok ? cv : 0.0f;
       }
     }
