@@ -40,10 +40,15 @@ template <int IO, int W, bool SEQ, bool INIT>
 __global__ void __launch_bounds__(kConvThreads) ss_conv1d_kernel(ConvParams p) {
   constexpr uint32_t s = io_bytes<IO>();
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x / p.tblocks;  // b * dim + d
-  const int t_base = (int)(blockIdx.x % p.tblocks) * kConvSpan;
+  // the grid is below 2^23 workgroups: 32-bit index arithmetic (64-bit
+  // divisions here delayed every workgroup's first loads)
+  const uint32_t tb = (uint32_t)p.tblocks, dim = (uint32_t)p.dim;
+  const uint32_t row32 = blockIdx.x / tb;
+  const int64_t row = row32;  // b * dim + d
+  const int t_base = (int)(blockIdx.x - row32 * tb) * kConvSpan;
   const int L = (int)p.seqlen;
-  const int64_t b = row / p.dim, d = row % p.dim;
+  const uint32_t b32 = row32 / dim;
+  const int64_t b = b32, d = row32 - b32 * dim;
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(static_cast<const char*>(p.x) + row * p.seqlen * s, (uint32_t)L * s);
   const __amdgpu_buffer_rsrc_t yr = make_rsrc(static_cast<char*>(p.out) + row * p.seqlen * s, (uint32_t)L * s);
@@ -180,10 +185,16 @@ template <int IO, int W, bool SEQ, bool INIT>
 __global__ void __launch_bounds__(kConvThreads) ss_conv1d_vec_kernel(ConvParams p) {
   constexpr uint32_t s = io_bytes<IO>();
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x / p.tblocks;
-  const int t0 = (int)(blockIdx.x % p.tblocks) * kVecSpan + kVecPerLane * tid;
+  // the grid is below 2^23 workgroups: 32-bit index arithmetic (64-bit
+  // divisions here delayed every workgroup's first loads: 20.8 -> 19.8 us on
+  // the mamba-130m x branch)
+  const uint32_t tb = (uint32_t)p.tblocks, dim = (uint32_t)p.dim;
+  const uint32_t row32 = blockIdx.x / tb;
+  const int64_t row = row32;
+  const int t0 = (int)(blockIdx.x - row32 * tb) * kVecSpan + kVecPerLane * tid;
   const int L = (int)p.seqlen;
-  const int64_t b = row / p.dim, d = row % p.dim;
+  const uint32_t b32 = row32 / dim;
+  const int64_t b = b32, d = row32 - b32 * dim;
 
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(static_cast<const char*>(p.x) + row * p.seqlen * s, (uint32_t)L * s);
   const __amdgpu_buffer_rsrc_t yr = make_rsrc(static_cast<char*>(p.out) + row * p.seqlen * s, (uint32_t)L * s);
