@@ -115,7 +115,8 @@ constexpr int kSChan = 16 * 16 + 16;
 // which the swap only reorders as a whole, so the sums are unchanged.
 constexpr int kCTile = 16 * 16 * kChPerWave;
 
-// AGG needs only the chunk's B and C; MAIN adds its reduction tiles.
+// AGG stages only the chunk's C (its B tile goes unused); MAIN uses B and C and
+// adds its reduction tiles.
 template <bool MAIN>
 struct BwdSmem {
   float B[kStates][kBCStride];
