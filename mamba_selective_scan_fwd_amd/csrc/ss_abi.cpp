@@ -106,7 +106,10 @@ FwdPlan plan_fwd(const ss_problem* p) {
     k = (kTargetWaves + waves - 1) / waves;  // at most kTargetWaves / 4 chunks
     if (k > tiles) k = tiles;
   }
-  const int64_t tiles_per_chunk = (tiles + k - 1) / k;
+  int64_t tiles_per_chunk = (tiles + k - 1) / k;
+  // a time-chunked scan works on both halves of a chunk at once: an even
+  // number of tiles per chunk
+  if (k > 1) tiles_per_chunk += tiles_per_chunk & 1;
   pl.chunk_len = tiles_per_chunk * kTile;
   pl.nchunks = (p->seqlen + pl.chunk_len - 1) / pl.chunk_len;
   pl.workspace = pl.nchunks > 1 ? chunk_layout(p, pl.nchunks).total : 0;

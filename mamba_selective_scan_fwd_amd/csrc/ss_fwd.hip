@@ -19,8 +19,10 @@
 // 16-wide reduction, not a contraction.
 //
 // Time chunking (for problems with too few channels to fill 256 CUs): the
-// sequence is cut into K chunks of a multiple of 64 steps, one workgroup per
-// (chunk, 16-channel block), all in one launch (ss_fwd_lookback_kernel).
+// sequence is cut into K chunks of an even number of 64-step tiles, one
+// workgroup per (chunk, 16-channel block), all in one launch
+// (ss_fwd_lookback_kernel); the workgroup's two 256-thread halves take the
+// two halves of the chunk at once.
 // Each workgroup first scans its chunk from a zero state (the first chunk
 // from the caller's initial state) to get the chunk's pair (P, S) = (prod of
 // exp(Delta A) over the chunk, state reached); pairs compose with the
@@ -318,9 +320,9 @@ struct EntryReady {
 template <int IO, bool FINAL, bool PAIR, bool SEQ, int FL, bool RANK, typename Entry = EntryReady>
 __device__ __forceinline__ void scan_chunk(const FwdParams& p, FwdSmem<FINAL>& sm, int64_t b, int64_t cb,
                                            int64_t chunk, int ckpt_stop, float& h, float& dt_sum, bool& any_start,
-                                           const Entry& entry = Entry{}) {
+                                           const Entry& entry = Entry{}, int iters = 0) {
   constexpr uint32_t s = io_bytes<IO>();
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x % kThreads;  // within its 256-thread part of the workgroup
   const int wave = uniform(tid / 64);
   const int lane = tid % 64;
   const int cw = lane / 16;  // channel within the wave
@@ -400,7 +402,12 @@ __device__ __forceinline__ void scan_chunk(const FwdParams& p, FwdSmem<FINAL>& s
   if (t_begin < t_tile_end) store_bc<IO, PAIR, FINAL>(sm, 0, bcr, tid, t_valid_end - t_begin, stage_n_ok);
   __syncthreads();
   int buf = 0;
-  for (int t0 = t_begin; t0 < t_tile_end; t0 += kTile) {
+  // at least `iters` passes of the loop, so that every part of a workgroup
+  // meets the same barriers; passes past the chunk's last tile only sync
+  const int own_tiles = (t_tile_end - t_begin) / kTile;
+  const int n_iter = iters > own_tiles ? iters : own_tiles;
+  for (int it = 0, t0 = t_begin; it < n_iter; ++it, t0 += kTile) {
+   if (t0 < t_tile_end) {
     const int nvalid = t_valid_end - t0;  // steps of this tile that advance the state
     const int nstop = t_stop - t0;        // steps of this tile that exist in the chunk
     if constexpr (RANK) rank_by_progress(t0 - t_begin, t_tile_end - t_begin);
@@ -467,6 +474,7 @@ __device__ __forceinline__ void scan_chunk(const FwdParams& p, FwdSmem<FINAL>& s
     }
 
     if (more) store_bc<IO, PAIR, FINAL>(sm, buf ^ 1, bcr, tid, t_valid_end - t1, stage_n_ok);
+   }
     __syncthreads();
     buf ^= 1;
   }
@@ -629,7 +637,7 @@ __global__ void __launch_bounds__(256) ss_queue_clear_kernel(int32_t* ctrl, int3
 // ---- time-chunked scan in one launch ----------------------------------------
 // Workgroup i runs unit i of the order (chunk, batch row, channel block), so
 // a workgroup waits only on workgroups numbered below it.  Those are running
-// or done: the launch has at most 2 x 256 - 2 workgroups of 40 KB of LDS (four
+// or done: the launch has at most 2 x 256 - 2 workgroups of 78 KB of LDS (two
 // fit per CU), all resident at once on an otherwise idle GPU, and the hardware
 // hands out workgroups in order of their number.  (An atomic counter handing
 // out units would not need either fact, but its atomics serialise: the last
@@ -688,10 +696,16 @@ __device__ __forceinline__ void compose_published(const uint64_t* slot, int64_t 
   }
 }
 
+// A workgroup is two 256-thread parts, each the four waves of the row block
+// on one half of the chunk (the chunk is an even number of 64-step tiles):
+// both halves scan at once, at two waves per SIMD, and meet in LDS, where
+// the first half's pair gives the second half its entry state.
 template <int IO, bool PAIR, bool SEQ, int FL>
-__global__ void __launch_bounds__(kThreads) ss_fwd_lookback_kernel(FwdParams p) {
-  __shared__ FwdSmem<true> sm;
-  const int tid = threadIdx.x;
+__global__ void __launch_bounds__(2 * kThreads) ss_fwd_lookback_kernel(FwdParams p) {
+  __shared__ FwdSmem<true> sm[2];
+  __shared__ float sHalf[2][2][kThreads];  // each half's pair (P, S), per lane
+  __shared__ float sEntry[kThreads];       // the chunk's entry state, per lane
+  const int tid = threadIdx.x % kThreads, half = threadIdx.x / kThreads;  // half: uniform per wave
   const int n = tid % 16;
   // the launch has fewer than 2^23 workgroups: 32-bit index arithmetic (a
   // 64-bit division here delays the first loads by a few hundred cycles, on
@@ -708,50 +722,62 @@ __global__ void __launch_bounds__(kThreads) ss_fwd_lookback_kernel(FwdParams p) 
   const int64_t ch = b * p.dim + d;
   const int64_t g = c32 / G, i = c32 - (uint32_t)g * G;
   const int L = (int)p.seqlen;
-  const int t_stop = (int)((c + 1) * p.chunk_len) < L ? (int)((c + 1) * p.chunk_len) : L;
+  // this half as a chunk of its own: half the length, index 2c + half
+  FwdParams q = p;
+  q.chunk_len = p.chunk_len / 2;
+  const int64_t sc = 2 * c + half;
+  const int m = (int)(q.chunk_len / kTile);  // tiles per half
+  const int sub_stop = (int)((sc + 1) * q.chunk_len) < L ? (int)((sc + 1) * q.chunk_len) : L;
   const float h_init = (c == 0 && p.h0 && ch_ok && n_ok) ? p.h0[ch * p.dstate + n] : 0.0f;
   uint64_t* const pairs = p.pairs + ch * K * kStates + n;                 // this lane's chunk slots
   uint64_t* const gpairs = p.gpairs + ch * (NG - 1) * kStates + n;       // and group slots
 
-  // 1. the chunk's own pair (the last chunk's is never needed).  The first
-  // chunk's pair absorbs the initial state: P = 0, S = the state it reaches.
-  float P = 0.0f, S = 0.0f;
-  if (c < K - 1) {
-    float h = h_init, dt_sum = 0.0f;
+  // 1. each half's pair from a zero state (the first chunk's first half from
+  // the initial state, with P = 0 so that the pair carries it), then the
+  // chunk's, composed from both in LDS and published (the last chunk's is
+  // never needed, but its second half needs the first half's pair)
+  {
+    float hh = half == 0 ? h_init : 0.0f, dt_sum = 0.0f;
     bool any_start = false;
-    scan_chunk<IO, false, PAIR, SEQ, FL & kFlSoftplus, false>(p, reinterpret_cast<FwdSmem<false>&>(sm), b, cb, c,
-                                                              t_stop, h, dt_sum, any_start);
+    scan_chunk<IO, false, PAIR, SEQ, FL & kFlSoftplus, false>(q, reinterpret_cast<FwdSmem<false>&>(sm[half]), b, cb,
+                                                              sc, sub_stop, hh, dt_sum, any_start, EntryReady{}, m);
     const float A2 = (ch_ok && n_ok) ? p.A[d * p.dstate + n] * kLog2e : 0.0f;
     const float dsum = row_sum(dt_sum);
-    P = (c == 0 || any_start) ? 0.0f : exp2_hw(A2 * dsum);
-    S = h;
-    publish_pair(pairs + c * kStates, ch_ok, P, S);
-    __syncthreads();  // the shared tiles are free for the readout
+    sHalf[half][0][tid] = ((c == 0 && half == 0) || any_start) ? 0.0f : exp2_hw(A2 * dsum);
+    sHalf[half][1][tid] = hh;
   }
+  __syncthreads();  // both halves' pairs are in LDS; the shared tiles are free for the readout
+  const float PA = sHalf[0][0][tid], SA = sHalf[0][1][tid];
+  const float P = sHalf[1][0][tid] * PA, S = fmaf(sHalf[1][0][tid], SA, sHalf[1][1][tid]);
+  if (half == 0 && c < K - 1) publish_pair(pairs + c * kStates, ch_ok, P, S);
 
-  // 2-4 run inside the readout's start, once its first loads are in flight
+  // 2-4 run inside the readout's start, once its first loads are in flight;
+  // the first half waits, the second takes the entry state from it in LDS
   auto entry = [&](float& h) {
-    // 2. the map from the group's entry to this chunk's entry: the pairs of
-    // the group's chunks before this one
-    float Pe = 1.0f, Se = 0.0f;
-    if (i > 0) compose_published(pairs + g * G * kStates, kStates, (int)i, ch_ok, p.q_ctrl + 1, Pe, Se);
-
-    // 3. the last chunk of a group that has a successor publishes the
-    // group's pair (so the last group never does: ngroups - 1 group pairs)
-    if (i == G - 1 && c < K - 1) publish_pair(gpairs + g * kStates, ch_ok, P * Pe, fmaf(P, Se, S));
-
-    // 4. the state entering the group: the pairs of the groups before it,
-    // applied to zero (the first chunk's pair holds the initial state)
-    float Pg = 1.0f, H = 0.0f;
-    if (g > 0) compose_published(gpairs, kStates, (int)g, ch_ok, p.q_ctrl + 1, Pg, H);
-    h = c == 0 ? h_init : fmaf(Pe, H, Se);
+    if (half == 0) {
+      // 2. the map from the group's entry to this chunk's entry: the pairs of
+      // the group's chunks before this one
+      float Pe = 1.0f, Se = 0.0f;
+      if (i > 0) compose_published(pairs + g * G * kStates, kStates, (int)i, ch_ok, p.q_ctrl + 1, Pe, Se);
+      // 3. the last chunk of a group that has a successor publishes the
+      // group's pair (so the last group never does: ngroups - 1 group pairs)
+      if (i == G - 1 && c < K - 1) publish_pair(gpairs + g * kStates, ch_ok, P * Pe, fmaf(P, Se, S));
+      // 4. the state entering the group: the pairs of the groups before it,
+      // applied to zero (the first chunk's pair holds the initial state)
+      float Pg = 1.0f, H = 0.0f;
+      if (g > 0) compose_published(gpairs, kStates, (int)g, ch_ok, p.q_ctrl + 1, Pg, H);
+      sEntry[tid] = c == 0 ? h_init : fmaf(Pe, H, Se);
+    }
+    __syncthreads();  // every thread of both halves calls the hook once
+    const float he = sEntry[tid];
+    h = half == 0 ? he : fmaf(PA, he, SA);
   };
 
-  // 5. rerun the chunk from its entry state and write y
+  // 5. rerun each half from its entry state and write y
   float h = 0.0f, dt_sum = 0.0f;
   bool any_start = false;
-  scan_chunk<IO, true, PAIR, SEQ, FL, false>(p, sm, b, cb, c, t_stop, h, dt_sum, any_start, entry);
-  if (p.last_state && ch_ok && n_ok && c == K - 1) p.last_state[ch * p.dstate + n] = h;
+  scan_chunk<IO, true, PAIR, SEQ, FL, false>(q, sm[half], b, cb, sc, sub_stop, h, dt_sum, any_start, entry, m);
+  if (p.last_state && ch_ok && n_ok && c == K - 1 && half == 1) p.last_state[ch * p.dstate + n] = h;
 }
 
 // Before a launch of the one-launch time-chunked scan: the error word to zero,
@@ -810,7 +836,7 @@ hipError_t launch_fwd_flags(const FwdParams& p, int64_t nchunks, hipStream_t st)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((ss_fwd_lookback_kernel<IO, PAIR, SEQ, FL>), dim3((uint32_t)(blocks_per_chunk * nchunks)),
-                       dim3(kThreads), 0, st, p);
+                       dim3(2 * kThreads), 0, st, p);
     return hipGetLastError();
   }
   if (p.q_ctrl) {

@@ -28,13 +28,17 @@ def _ss():
 
 def plan(Bsz, Dd, L):
     """(K, G, number of groups) the library's planner picks (it splits time below 1024
-    wavefronts of 16 states x 4 channels, into chunks of whole 64-step tiles)."""
+    wavefronts of 16 states x 4 channels, into chunks of an even number of 64-step tiles,
+    whose two halves a workgroup scans at once)."""
     waves = Bsz * ((Dd + 15) // 16) * 4
     tiles = (L + 63) // 64
     k = 1
     if waves < 1024:
         k = min((1024 + waves - 1) // waves, tiles)
-    chunk = ((tiles + k - 1) // k) * 64
+    tpc = (tiles + k - 1) // k
+    if k > 1:
+        tpc += tpc & 1
+    chunk = tpc * 64
     K = (L + chunk - 1) // chunk
     G = 1
     while G * G < K:
@@ -67,11 +71,11 @@ def _check(prob, seq=None, h0=None, workspace=None):
 
 # (B, D, L, io) -> K, G, groups
 SHAPES = [
-    ((1, 4080, 65, "f16"), (2, 2, 1)),      # two chunks, one group
-    ((1, 16, 192, "f32"), (3, 2, 2)),       # the second group has one chunk
-    ((1, 16, 1088, "f16"), (17, 8, 3)),     # a last group of one chunk
-    ((1, 5, 4000, "bf16"), (63, 8, 8)),     # a partial channel block, ragged last chunk
-    ((3, 16, 16389, "f32"), (86, 16, 6)),   # 192-step chunks, three row blocks
+    ((1, 4080, 200, "f16"), (2, 2, 1)),     # two chunks, one group; the last chunk's halves of 64 and 8 steps
+    ((1, 16, 320, "f32"), (3, 2, 2)),       # the second group has one chunk, whose second half is empty
+    ((1, 16, 2176, "f16"), (17, 8, 3)),     # a last group of one chunk
+    ((1, 5, 4000, "bf16"), (32, 8, 4)),     # a partial channel block, ragged last chunk (one partial half)
+    ((3, 16, 16389, "f32"), (65, 16, 5)),   # 256-step chunks (two tiles a half), three row blocks
 ]
 
 
