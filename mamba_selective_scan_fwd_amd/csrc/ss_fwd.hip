@@ -178,11 +178,18 @@ __device__ __forceinline__ void load_bc(BCRaw<IO, PAIR>& r, const Views& v, uint
 
 // B (row-major, for the state lanes) and C (transposed, for the step owners)
 // of steps at or past the valid end are staged as exact zeros, so data past a
-// row's length (padding, NaN) never reaches the state or the output.
-template <int IO, bool PAIR, bool FINAL>
+// row's length (padding, NaN) never reaches the state or the output.  MASKED =
+// false is the copy for a tile whose 64 steps all advance the state, staged
+// with all 16 state rows present: every element is kept, so no per-lane
+// compare or select is issued.
+template <int IO, bool PAIR, bool FINAL, bool MASKED = true>
 __device__ __forceinline__ void store_bc(FwdSmem<FINAL>& sm, int buf, const BCRaw<IO, PAIR>& r, int tid, int nvalid,
                                          bool n_ok) {
   const int n = tid / 16, j = tid % 16;
+  if constexpr (!MASKED) {
+    n_ok = true;
+    nvalid = kTile;
+  }
 #pragma unroll
   for (int k = 0; k < BCRaw<IO, PAIR>::kN; ++k) {
     if constexpr (PAIR) {
@@ -317,7 +324,7 @@ __device__ __forceinline__ void finish_block(const Owned& o, const float* const 
 struct EntryReady {
   __device__ void operator()(float&) const {}
 };
-template <int IO, bool FINAL, bool PAIR, bool SEQ, int FL, bool RANK, typename Entry = EntryReady>
+template <int IO, bool FINAL, bool PAIR, bool SEQ, int FL, bool RANK, bool PAD = false, typename Entry = EntryReady>
 __device__ __forceinline__ void scan_chunk(const FwdParams& p, FwdSmem<FINAL>& sm, int64_t b, int64_t cb,
                                            int64_t chunk, int ckpt_stop, float& h, float& dt_sum, bool& any_start,
                                            const Entry& entry = Entry{}, int iters = 0) {
@@ -368,6 +375,7 @@ __device__ __forceinline__ void scan_chunk(const FwdParams& p, FwdSmem<FINAL>& s
   const uint32_t lane_off = (lane_elem0 + (uint32_t)l) * s;  // byte offset of the lane's owned step 0
   const uint32_t bc_off = bc_lane_off<IO, PAIR>((uint32_t)L, tid);
   const bool stage_n_ok = tid / 16 < p.dstate;
+  const bool stage_all_n = p.dstate == kStates;  // uniform: every staged state row is valid
 
   const float A2 = (ch_ok && n_ok) ? p.A[d * p.dstate + n] * kLog2e : 0.0f;
   const float bias = (ch_ok && p.bias) ? p.bias[d] : 0.0f;
@@ -391,7 +399,7 @@ __device__ __forceinline__ void scan_chunk(const FwdParams& p, FwdSmem<FINAL>& s
     }
   }
 
-  RawOwned<IO> raw;
+  RawOwned<IO> raw, raw2;  // the tile's raw operands and the next tile's, alternating by pass
   BCRaw<IO, PAIR> bcr;
   if (t_begin < t_tile_end) {
     if constexpr (SEQ) load_doc_ids(ids, t_begin + lane, id_t, id_prev);
@@ -405,9 +413,14 @@ __device__ __forceinline__ void scan_chunk(const FwdParams& p, FwdSmem<FINAL>& s
   // at least `iters` passes of the loop, so that every part of a workgroup
   // meets the same barriers; passes past the chunk's last tile only sync
   const int own_tiles = (t_tile_end - t_begin) / kTile;
-  const int n_iter = iters > own_tiles ? iters : own_tiles;
-  for (int it = 0, t0 = t_begin; it < n_iter; ++it, t0 += kTile) {
-   if (t0 < t_tile_end) {
+  const int n_iter = (PAD && iters > own_tiles) ? iters : own_tiles;
+  // One pass per tile.  The two raw sets alternate (a pass converts one and
+  // loads the next tile into the other), so the loop's back edge copies no
+  // registers: with one set, this tile's lazily converted values and the next
+  // tile's loads are live together and the back edge moves one into the other.
+  int t0 = t_begin;
+  auto pass = [&](const RawOwned<IO>& raw, RawOwned<IO>& raw_next) {
+   if (!PAD || t0 < t_tile_end) {  // without PAD every pass has a tile
     const int nvalid = t_valid_end - t0;  // steps of this tile that advance the state
     const int nstop = t_stop - t0;        // steps of this tile that exist in the chunk
     if constexpr (RANK) rank_by_progress(t0 - t_begin, t_tile_end - t_begin);
@@ -440,7 +453,7 @@ __device__ __forceinline__ void scan_chunk(const FwdParams& p, FwdSmem<FINAL>& s
       constexpr bool FULL = decltype(full_tag)::value;
       Owned o;
       prep_owned<IO, FL, FULL>(o, raw, l, nvalid, bias, dt_sum);
-      load_owned<IO, GATE>(raw, v, lane_off, next_off);
+      load_owned<IO, GATE>(raw_next, v, lane_off, next_off);
       load_bc<IO, PAIR>(bcr, v, bc_off, next_off, FINAL);
 #define SS_BLOCK(I)                                                                          \
       {                                                                                      \
@@ -473,10 +486,20 @@ __device__ __forceinline__ void scan_chunk(const FwdParams& p, FwdSmem<FINAL>& s
       else run_tile(std::false_type{}, std::false_type{});
     }
 
-    if (more) store_bc<IO, PAIR, FINAL>(sm, buf ^ 1, bcr, tid, t_valid_end - t1, stage_n_ok);
+    if (more) {
+      if (stage_all_n && t_valid_end - t1 >= kTile)
+        store_bc<IO, PAIR, FINAL, false>(sm, buf ^ 1, bcr, tid, kTile, true);
+      else
+        store_bc<IO, PAIR, FINAL>(sm, buf ^ 1, bcr, tid, t_valid_end - t1, stage_n_ok);
+    }
    }
     __syncthreads();
     buf ^= 1;
+    t0 += kTile;
+  };
+  for (int it = 0; it < n_iter; it += 2) {
+    pass(raw, raw2);
+    if (it + 1 < n_iter) pass(raw2, raw);
   }
 
   if constexpr (FINAL) {
@@ -739,8 +762,8 @@ __global__ void __launch_bounds__(2 * kThreads) ss_fwd_lookback_kernel(FwdParams
   {
     float hh = half == 0 ? h_init : 0.0f, dt_sum = 0.0f;
     bool any_start = false;
-    scan_chunk<IO, false, PAIR, SEQ, FL & kFlSoftplus, false>(q, reinterpret_cast<FwdSmem<false>&>(sm[half]), b, cb,
-                                                              sc, sub_stop, hh, dt_sum, any_start, EntryReady{}, m);
+    scan_chunk<IO, false, PAIR, SEQ, FL & kFlSoftplus, false, true>(q, reinterpret_cast<FwdSmem<false>&>(sm[half]), b,
+                                                                    cb, sc, sub_stop, hh, dt_sum, any_start, EntryReady{}, m);
     const float A2 = (ch_ok && n_ok) ? p.A[d * p.dstate + n] * kLog2e : 0.0f;
     const float dsum = row_sum(dt_sum);
     sHalf[half][0][tid] = ((c == 0 && half == 0) || any_start) ? 0.0f : exp2_hw(A2 * dsum);
@@ -776,7 +799,7 @@ __global__ void __launch_bounds__(2 * kThreads) ss_fwd_lookback_kernel(FwdParams
   // 5. rerun each half from its entry state and write y
   float h = 0.0f, dt_sum = 0.0f;
   bool any_start = false;
-  scan_chunk<IO, true, PAIR, SEQ, FL, false>(q, sm[half], b, cb, sc, sub_stop, h, dt_sum, any_start, entry, m);
+  scan_chunk<IO, true, PAIR, SEQ, FL, false, true>(q, sm[half], b, cb, sc, sub_stop, h, dt_sum, any_start, entry, m);
   if (p.last_state && ch_ok && n_ok && c == K - 1 && half == 1) p.last_state[ch * p.dstate + n] = h;
 }
 
